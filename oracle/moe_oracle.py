@@ -1,0 +1,264 @@
+"""CPU oracle for the MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import or call this module.  The GPU library never routes through it, and it
+shares no code, tables or constants with the GPU path.
+
+Plain, slow, fp64 NumPy.  Each function cites the page passage it follows.
+Pages (by site and title):
+  [lmnt]   lmnt.cn MoE walkthrough (news/351908): §1.2 per-token flow,
+           §2.1 gate scoring equation, §2.2 TopK, §3.1 dispatch, §3.2 combine
+           equation, §3.3 capacity equation, §5.2 load-balance code,
+           §5.3 router z-loss equation.
+  [csdn]   "MoE逐token路由与活跃参数率实战解析": §3.1 worked top-2 example,
+           §4.2 MoELayer code.
+  [yunthe] "MoE混合专家模型实战：专家路由与稀疏激活的推理成本优化方案":
+           section "MoE架构的稀疏激活原理与Transformer实现" (output equation,
+           reference forward), section "专家负载均衡与辅助损失函数设计"
+           (Switch aux loss, per-expert bias b_i, capacity drop).
+  [wiblog] "MoE 专家路由如何实现稀疏激活": section on fine-grained and shared
+           experts.
+
+Readings taken where the pages are silent or disagree (all in the design
+notes as well):
+  * logits are the fp32 rounding of the dot product computed in fp64, plus
+    the router bias and logit offset added in fp64 before that one rounding;
+  * top-K orders by (score descending, expert index ascending); NaN scores
+    order as -inf; a per-expert selection bias changes only the choice, the
+    weights use the unbiased logits;
+  * capacity drops keep, per expert, the first C (token, slot) pairs in token
+    order; a dropped pair contributes zero and the remaining weights are not
+    renormalised;
+  * GELU is the exact erf form; the shared expert enters with weight 1;
+  * aux loss f_e is the mean over tokens of the pre-drop selection mask
+    ([yunthe] form, sum f = K), P_e the mean full-N softmax of the logits.
+
+Pins: every function here is pinned by tests/test_oracle_pins.py against
+brute force, closed forms, the corrected worked example, special cases and
+textbook routines.  Absolute output values at the large workload sizes are
+"parity unpinned" beyond that: the pages print none, and the oracle runs the
+same code at every size.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import Callable, Optional, Sequence, Union
+
+import numpy as np
+
+try:  # exact erf, vectorised
+    from scipy.special import erf as _erf
+except Exception:  # pragma: no cover - scipy is present in this image
+    _erf = np.vectorize(math.erf, otypes=[np.float64])
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# a1: router scoring.  [lmnt] §2.1: scores come from W_g . x, W_g being
+# d_model x N; [yunthe] reference forward: the router is a Linear layer
+# (with bias in nn.Linear's default form).
+def router_logits(x, w_router, b_router=None, logit_offset=None) -> np.ndarray:
+    """logits[t, e] = fp32( sum_j x[t, j] * W_r[e, j] + b_r[e] + off[e] ).
+
+    x: [T, d]; w_router: [N, d] (nn.Linear [out, in]); b_router, logit_offset: [N]
+    or None.  Products and sums in fp64; one rounding to fp32 at the end."""
+    z = _f64(x) @ _f64(w_router).T
+    if b_router is not None:
+        z = z + _f64(b_router)[None, :]
+    if logit_offset is not None:
+        z = z + _f64(logit_offset)[None, :]
+    return z.astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# a2: TopK first, then softmax over the K chosen logits.
+# [lmnt] §2.1 (score = Softmax(TopK(W_g x)); the K logits are normalised within
+# the candidate set); [yunthe] reference forward (topk then F.softmax over the
+# K values); [yunthe] load-balancing section: a per-expert bias b_i adjusts the
+# routing score.
+def selection_scores(logits: np.ndarray, sel_bias=None) -> np.ndarray:
+    """s = fp32(logits + b) (selection only); s = logits when b is None."""
+    s = np.asarray(logits, dtype=np.float32)
+    if sel_bias is not None:
+        s = (s + np.asarray(sel_bias, dtype=np.float32)[None, :]).astype(np.float32)
+    return s
+
+
+def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
+    """idx[t, :] = the k experts with the largest score, ordered by
+    (score descending, expert index ascending).  NaN orders as -inf."""
+    s = np.asarray(scores, dtype=np.float64).copy()
+    s[np.isnan(s)] = -np.inf
+    T, N = s.shape
+    if not (1 <= k <= N):
+        raise ValueError("need 1 <= k <= N")
+    expert = np.broadcast_to(np.arange(N), (T, N))
+    # lexsort: last key is primary -> primary -s ascending, then expert ascending
+    order = np.lexsort((expert, -s), axis=-1)
+    return order[:, :k].astype(np.int32)
+
+
+def topk_softmax(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w[t, k] = exp(l[t, idx_k]) / sum_k' exp(l[t, idx_k']) over the K chosen
+    (unbiased) logits, in fp64."""
+    sel = np.take_along_axis(_f64(logits), idx.astype(np.int64), axis=1)
+    m = sel.max(axis=1, keepdims=True)
+    e = np.exp(sel - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# a3: dispatch with an optional capacity.
+# [lmnt] §3.1 (reorder from token order to contiguous per-expert blocks),
+# §3.3 (capacity = ceil(T / N * capacity_factor); over-capacity tokens skip the
+# expert and pass on through the residual).
+def capacity_from_factor(T: int, n_experts: int, capacity_factor: float) -> int:
+    """ceil(T / N * capacity_factor), in exact rational arithmetic."""
+    return math.ceil(Fraction(T, n_experts) * Fraction(capacity_factor))
+
+
+def dispatch(idx: np.ndarray, n_experts: int, capacity: Optional[int] = None) -> dict:
+    """Enumerate (token, slot) pairs token-major; within each expert keep pairs
+    in token order; a pair is kept iff fewer than ``capacity`` earlier pairs
+    went to its expert.  Returns
+      counts [N]          pre-drop pairs per expert,
+      kept [N]            min(counts, C),
+      expert_offsets [N+1] exclusive scan of kept,
+      slot_row [T, K]     row of the pair in the permuted buffer, -1 if dropped,
+      row_token [M]       token of each permuted row (M = kept total),
+      n_dropped           T*K - M."""
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    N = n_experts
+    counts = np.zeros(N, dtype=np.int64)
+    pos = np.zeros((T, K), dtype=np.int64)
+    for t in range(T):               # token order ...
+        for k in range(K):           # ... then slot order within the token
+            e = int(idx[t, k])
+            pos[t, k] = counts[e]
+            counts[e] += 1
+    cap = np.iinfo(np.int64).max if capacity is None or capacity <= 0 else int(capacity)
+    kept = np.minimum(counts, cap)
+    offsets = np.zeros(N + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(kept)
+    M = int(offsets[-1])
+    slot_row = np.full((T, K), -1, dtype=np.int64)
+    row_token = np.full(M, -1, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            if pos[t, k] < cap:
+                r = offsets[idx[t, k]] + pos[t, k]
+                slot_row[t, k] = r
+                row_token[r] = t
+    return dict(counts=counts.astype(np.int32), kept=kept.astype(np.int32),
+                expert_offsets=offsets.astype(np.int32), slot_row=slot_row.astype(np.int32),
+                row_token=row_token.astype(np.int32), n_dropped=int(T * K - M))
+
+
+# --------------------------------------------------------------------------
+# a4/a5: expert FFN = Linear -> GELU -> Linear.  [yunthe] reference forward
+# (nn.Linear(d_model, d_ff), nn.GELU(), nn.Linear(d_ff, d_model)); [csdn] §4.2
+# create_simple_moe_layer (same form).  nn.GELU's default is the erf form.
+def gelu(z):
+    """GELU(z) = z/2 * (1 + erf(z / sqrt(2)))."""
+    z = _f64(z)
+    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)))
+
+
+def expert_ffn(x_rows, w1, b1, w2, b2):
+    """E(x) = W2 . GELU(W1 . x + b1) + b2 for each row; W1 [f, d], W2 [d, f]."""
+    h = _f64(x_rows) @ _f64(w1).T
+    if b1 is not None:
+        h = h + _f64(b1)[None, :]
+    y = gelu(h) @ _f64(w2).T
+    if b2 is not None:
+        y = y + _f64(b2)[None, :]
+    return y
+
+
+# --------------------------------------------------------------------------
+# a7: Switch auxiliary loss.  [yunthe] "专家负载均衡与辅助损失函数设计":
+# alpha * N * sum(f * P), f = mean over tokens of the 0/1 selection mask,
+# P = mean over tokens of the softmax router probabilities; [lmnt] §5.1-5.2
+# (same product, P from the full softmax of the router logits).
+def aux_loss(logits: np.ndarray, idx: np.ndarray, n_experts: int, alpha: float) -> float:
+    T, K = idx.shape
+    N = n_experts
+    mask = np.zeros((T, N), dtype=np.float64)
+    for k in range(K):
+        mask[np.arange(T), idx[:, k]] = 1.0
+    f = mask.mean(axis=0)
+    z = _f64(logits)
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p = p / p.sum(axis=1, keepdims=True)
+    P = p.mean(axis=0)
+    return float(alpha * N * np.sum(f * P))
+
+
+# [lmnt] §5.3 router z-loss: beta * mean_t (logsumexp_e logits[t, e])^2.
+def router_z_loss(logits: np.ndarray, beta: float) -> float:
+    z = _f64(logits)
+    m = z.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+    return float(beta * np.mean(lse ** 2))
+
+
+# --------------------------------------------------------------------------
+# The whole layer.  Structure follows [yunthe]'s reference forward: a loop
+# over the K slots and, inside it, over the experts, adding w * E_e(x) into the
+# rows of the tokens that chose expert e in that slot ([lmnt] §3.2 combine
+# equation: output[t] = sum over selected e of weight[t, e] * E_e(x_t)); the
+# capacity mask of [lmnt] §3.3 removes dropped pairs; a shared expert
+# ([wiblog], shared-expert isolation) is added for every token.
+ExpertSource = Union[Sequence, Callable[[int], tuple]]
+
+
+def moe_forward(x, w_router, experts: ExpertSource, top_k: int, *, n_experts: Optional[int] = None,
+                b_router=None, logit_offset=None, sel_bias=None, shared=None,
+                capacity: Optional[int] = None, aux_alpha: float = 0.0,
+                out_tokens: Optional[np.ndarray] = None) -> dict:
+    """experts: sequence of (W1 [f, d], b1 [f] | None, W2 [d, f], b2 [d] | None)
+    or a callable e -> that tuple.  shared: None or (Ws1 [f_s, d], Ws2 [d, f_s]).
+    capacity: None or <= 0 for dropless, else C.  out_tokens: compute ``out``
+    only for these token indices (other rows stay 0); routing, dispatch and the
+    aux loss always cover every token."""
+    x64 = _f64(x)
+    T = x64.shape[0]
+    N = n_experts if n_experts is not None else np.asarray(w_router).shape[0]
+    get = experts if callable(experts) else (lambda e: experts[e])
+
+    logits = router_logits(x64, w_router, b_router, logit_offset)
+    scores = selection_scores(logits, sel_bias)
+    idx = topk_select(scores, top_k)
+    w = topk_softmax(logits, idx)
+    disp = dispatch(idx, N, capacity)
+    kept_pair = disp["slot_row"] >= 0
+
+    active = np.zeros(T, dtype=bool)
+    if out_tokens is None:
+        active[:] = True
+    else:
+        active[np.asarray(out_tokens)] = True
+
+    out = np.zeros_like(x64)
+    for k in range(top_k):
+        expert_of = idx[:, k]
+        for e in range(N):
+            mask = (expert_of == e) & kept_pair[:, k] & active
+            if not mask.any():
+                continue
+            w1, b1, w2, b2 = get(e)
+            out[mask] += w[mask, k][:, None] * expert_ffn(x64[mask], w1, b1, w2, b2)
+    if shared is not None:
+        ws1, ws2 = shared
+        out[active] += expert_ffn(x64[active], ws1, None, ws2, None)
+
+    res = dict(logits=logits, scores=scores, idx=idx, w=w, out=out, **disp)
+    if aux_alpha:
+        res["aux"] = aux_loss(logits, idx, N, aux_alpha)
+    return res

@@ -1,0 +1,415 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: a worked
+example printed on the pages (corrected, see tests/golden/), closed forms,
+special cases that reduce to textbook routines, exact rational arithmetic,
+and brute force on tiny inputs written independently here (scalar Python
+loops, or every expert run densely and then masked).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.stats import norm
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rest = line.split(":", 1)
+            vals[key.strip()] = [float(v) for v in rest.split()]
+    return vals
+
+
+def _bf16_values(rng, shape, scale=1.0):
+    """Random values exactly representable in bfloat16 (8 significant bits)."""
+    a = (rng.standard_normal(shape) * scale).astype(np.float32)
+    u = a.view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- worked example
+def test_csdn_worked_example_corrected():
+    g = _read_golden("csdn_top2_worked_example.txt")
+    logits = np.array([g["logits"]], dtype=np.float32)
+    k = int(g["k"][0])
+    idx = O.topk_select(O.selection_scores(logits), k)
+    assert idx.tolist() == [[int(v) for v in g["idx"]]]
+    w = O.topk_softmax(logits, idx)
+    np.testing.assert_allclose(w[0], g["weights"], rtol=1e-6)
+    # the page's printed numbers are not what its rule gives
+    assert abs(w[0, 0] - g["page_printed_weights"][0]) > 0.01
+    # TopK-then-softmax equals the full softmax renormalised over the chosen set
+    p = np.exp(logits[0].astype(np.float64))
+    p /= p.sum()
+    np.testing.assert_allclose(w[0], p[idx[0]] / p[idx[0]].sum(), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- selection
+def test_tie_break_lowest_index_and_uniform_weights():
+    logits = np.full((5, 6), 0.25, dtype=np.float32)
+    idx = O.topk_select(O.selection_scores(logits), 3)
+    assert (idx == np.array([0, 1, 2])).all()
+    w = O.topk_softmax(logits, idx)
+    np.testing.assert_allclose(w, 1.0 / 3.0, rtol=0, atol=1e-15)
+
+
+def test_partial_ties_and_nan():
+    s = np.array([[1.0, 3.0, 3.0, np.nan, 2.0, 3.0]], dtype=np.float32)
+    assert O.topk_select(s, 4).tolist() == [[1, 2, 5, 4]]
+    # NaN orders as -inf, but K = N still yields N distinct valid indices
+    assert O.topk_select(s, 6).tolist() == [[1, 2, 5, 4, 0, 3]]
+
+
+def test_topk_matches_brute_force_sort():
+    rng = np.random.default_rng(7)
+    s = rng.integers(-3, 4, size=(40, 9)).astype(np.float32)   # many exact ties
+    idx = O.topk_select(s, 4)
+    for t in range(s.shape[0]):
+        ref = sorted(range(9), key=lambda e: (-float(s[t, e]), e))[:4]
+        assert idx[t].tolist() == ref
+
+
+def test_selection_bias_changes_choice_not_weights():
+    logits = np.array([[1.0, 0.9, 0.0]], dtype=np.float32)
+    bias = np.array([0.0, 0.0, 2.0], dtype=np.float32)
+    s = O.selection_scores(logits, bias)
+    idx = O.topk_select(s, 2)
+    assert idx.tolist() == [[2, 0]]
+    w = O.topk_softmax(logits, idx)
+    np.testing.assert_allclose(w[0], [1 / (1 + math.e), math.e / (1 + math.e)], rtol=1e-12)
+
+
+def _round_to_f32_exact(q: Fraction) -> np.float32:
+    """Correct rounding of a rational to fp32 (nearest, ties to even)."""
+    c = np.float32(float(q))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        err = abs(Fraction(float(cand)) - q)
+        key = (err, int(np.array(cand).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return np.float32(best[1])
+
+
+def test_router_logits_are_rounded_exact_dot():
+    rng = np.random.default_rng(3)
+    T, d, N = 7, 24, 5
+    x = _bf16_values(rng, (T, d))
+    w = _bf16_values(rng, (N, d), d ** -0.5)
+    b = rng.standard_normal(N).astype(np.float32)
+    off = rng.standard_normal(N).astype(np.float32)
+    got = O.router_logits(x, w, b, off)
+    assert got.dtype == np.float32
+    for t in range(T):
+        for e in range(N):
+            q = sum((Fraction(float(x[t, j])) * Fraction(float(w[e, j])) for j in range(d)),
+                    Fraction(0))
+            q += Fraction(float(b[e])) + Fraction(float(off[e]))
+            assert got[t, e] == _round_to_f32_exact(q), (t, e)
+
+
+# ---------------------------------------------------------------- dispatch
+def _random_distinct_idx(rng, T, N, K):
+    return np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("cap", [None, 1, 5, 1000])
+def test_dispatch_matches_stable_argsort(cap):
+    rng = np.random.default_rng(11)
+    T, N, K = 50, 7, 3
+    idx = _random_distinct_idx(rng, T, N, K)
+    d = O.dispatch(idx, N, cap)
+    flat = idx.ravel()
+    order = np.argsort(flat, kind="stable")         # textbook stable sort of pair ids
+    cnt = np.bincount(flat, minlength=N)
+    C = 10 ** 9 if cap is None else cap
+    kept = np.minimum(cnt, C)
+    assert d["counts"].tolist() == cnt.tolist()
+    assert d["kept"].tolist() == kept.tolist()
+    assert d["expert_offsets"].tolist() == [0] + np.cumsum(kept).tolist()
+    exp_slot = np.full(T * K, -1)
+    rows = []
+    start = 0
+    for e in range(N):
+        pairs = order[start:start + cnt[e]]
+        start += cnt[e]
+        for j, p in enumerate(pairs[:C]):
+            exp_slot[p] = len(rows)
+            rows.append(p // K)
+    assert d["slot_row"].ravel().tolist() == exp_slot.tolist()
+    assert d["row_token"].tolist() == rows
+    assert d["n_dropped"] == int(np.maximum(cnt - C, 0).sum())
+
+
+def test_capacity_closed_forms():
+    assert O.capacity_from_factor(8192, 64, 1.25) == 160
+    assert O.capacity_from_factor(64, 8, 1.25) == 10
+    assert O.capacity_from_factor(10, 3, 1.0) == 4
+    assert O.capacity_from_factor(12, 3, 1.0) == 4
+
+
+# ---------------------------------------------------------------- GELU
+def test_gelu_identities_and_libm():
+    z = np.linspace(-8, 8, 2001)
+    g = O.gelu(z)
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(g - O.gelu(-z), z, rtol=0, atol=1e-12)
+    ref = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in z])
+    np.testing.assert_allclose(g, ref, rtol=1e-7, atol=1e-12)
+    np.testing.assert_allclose(g, z * norm.cdf(z), rtol=1e-7, atol=1e-12)
+
+
+# ---------------------------------------------------------------- aux loss
+def test_aux_uniform_gives_alpha_k():
+    T, N, K, alpha = 16, 8, 2, 0.01
+    logits = np.zeros((T, N), dtype=np.float32)
+    idx = np.array([[(t * K + j) % N for j in range(K)] for t in range(T)], dtype=np.int32)
+    assert O.aux_loss(logits, idx, N, alpha) == pytest.approx(alpha * K, rel=1e-12)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_aux_all_to_one_expert_gives_alpha_n(K):
+    T, N, alpha = 10, 6, 0.02
+    logits = np.zeros((T, N), dtype=np.float32)
+    logits[:, 0] = 1e4                                # P_0 = 1
+    idx = np.array([list(range(K)) for _ in range(T)], dtype=np.int32)
+    assert O.aux_loss(logits, idx, N, alpha) == pytest.approx(alpha * N, rel=1e-12)
+
+
+def test_aux_lmnt_form_times_k_equals_yunthe_form():
+    rng = np.random.default_rng(5)
+    T, N, K, alpha = 33, 9, 3, 0.01
+    logits = rng.standard_normal((T, N)).astype(np.float32)
+    idx = _random_distinct_idx(rng, T, N, K)
+    counts = np.bincount(idx.ravel(), minlength=N).astype(np.float64)
+    f_lmnt = counts / (T * K)                          # counts / (T * K)
+    z = logits.astype(np.float64)
+    p = np.exp(z) / np.exp(z).sum(axis=1, keepdims=True)
+    lmnt = N * np.sum(f_lmnt * p.mean(axis=0)) * alpha
+    assert O.aux_loss(logits, idx, N, alpha) == pytest.approx(lmnt * K, rel=1e-12)
+
+
+def test_z_loss_closed_form():
+    T, N, beta = 4, 8, 1e-3
+    logits = np.zeros((T, N), dtype=np.float32)       # logsumexp = ln N
+    assert O.router_z_loss(logits, beta) == pytest.approx(beta * math.log(N) ** 2, rel=1e-12)
+
+
+# ---------------------------------------------------------------- whole layer
+def _tiny_problem(rng, T, d, f, N, *, biases=True, fs=0):
+    x = _bf16_values(rng, (T, d))
+    wr = _bf16_values(rng, (N, d), d ** -0.5)
+    experts = []
+    for _ in range(N):
+        w1 = _bf16_values(rng, (f, d), d ** -0.5)
+        w2 = _bf16_values(rng, (d, f), f ** -0.5)
+        b1 = rng.standard_normal(f) * 0.1 if biases else None
+        b2 = rng.standard_normal(d) * 0.1 if biases else None
+        experts.append((w1, b1, w2, b2))
+    shared = None
+    if fs:
+        shared = (_bf16_values(rng, (fs, d), d ** -0.5), _bf16_values(rng, (d, fs), fs ** -0.5))
+    return x, wr, experts, shared
+
+
+def _scalar_reference(x, wr, experts, K, br, off, sb, shared, C):
+    """Pure-Python scalar loops with math.erf / math.exp, written from the
+    pages' steps: score, TopK, softmax over K, capacity in token order,
+    weighted sum of expert outputs, plus the shared expert."""
+    T, d = len(x), len(x[0])
+    N = len(wr)
+
+    def ffn(w1, b1, w2, b2, v):
+        f = len(w1)
+        h = []
+        for i in range(f):
+            z = sum(w1[i][j] * v[j] for j in range(d)) + (b1[i] if b1 is not None else 0.0)
+            h.append(0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0))))
+        return [sum(w2[o][i] * h[i] for i in range(f)) + (b2[o] if b2 is not None else 0.0)
+                for o in range(d)]
+
+    load = [0] * N
+    outs, idxs, ws = [], [], []
+    for t in range(T):
+        logit = []
+        for e in range(N):
+            s = math.fsum([x[t][j] * wr[e][j] for j in range(d)])
+            if br is not None:
+                s = s + float(br[e])
+            if off is not None:
+                s = s + float(off[e])
+            logit.append(float(np.float32(s)))
+        score = [float(np.float32(np.float32(logit[e]) + np.float32(sb[e] if sb is not None else 0.0)))
+                 for e in range(N)]
+        chosen = sorted(range(N), key=lambda e: (-score[e], e))[:K]
+        m = max(logit[e] for e in chosen)
+        ex = [math.exp(logit[e] - m) for e in chosen]
+        wt = [v / sum(ex) for v in ex]
+        y = [0.0] * d
+        for kk, e in enumerate(chosen):
+            kept = C is None or load[e] < C
+            load[e] += 1
+            if kept:
+                ye = ffn(*experts[e], x[t])
+                y = [a + wt[kk] * b for a, b in zip(y, ye)]
+        if shared is not None:
+            ys = ffn(shared[0], None, shared[1], None, x[t])
+            y = [a + b for a, b in zip(y, ys)]
+        outs.append(y)
+        idxs.append(chosen)
+        ws.append(wt)
+    return np.array(outs), np.array(idxs), np.array(ws), load
+
+
+@pytest.mark.parametrize("cap", [None, 2])
+def test_whole_layer_scalar_brute_force(cap):
+    rng = np.random.default_rng(1)
+    T, d, f, N, K = 9, 8, 12, 5, 2
+    x, wr, experts, shared = _tiny_problem(rng, T, d, f, N, fs=6)
+    br = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    off = rng.standard_normal(N).astype(np.float32)
+    sb = rng.uniform(-0.5, 0.5, N).astype(np.float32)
+    res = O.moe_forward(x, wr, experts, K, b_router=br, logit_offset=off, sel_bias=sb,
+                        shared=shared, capacity=cap)
+    y, idx, w, load = _scalar_reference(x.tolist(), wr.tolist(),
+                                        [tuple(None if a is None else a.tolist() for a in ex)
+                                         for ex in experts],
+                                        K, br, off, sb, (shared[0].tolist(), shared[1].tolist()), cap)
+    assert res["idx"].tolist() == idx.tolist()
+    np.testing.assert_allclose(res["w"], w, rtol=1e-12)
+    assert res["counts"].tolist() == load
+    np.testing.assert_allclose(res["out"], y, rtol=1e-10, atol=1e-12)
+
+
+def test_whole_layer_dense_then_masked():
+    """Every expert run on every token, then masked by the routing."""
+    rng = np.random.default_rng(2)
+    T, d, f, N, K = 16, 16, 24, 8, 3
+    x, wr, experts, _ = _tiny_problem(rng, T, d, f, N)
+    res = O.moe_forward(x, wr, experts, K)
+    logits = (x @ wr.T).astype(np.float32).astype(np.float64)
+    M = np.zeros((T, N))
+    W = np.zeros((T, N))
+    for t in range(T):
+        order = sorted(range(N), key=lambda e: (-logits[t, e], e))[:K]
+        z = np.exp(logits[t, order] - logits[t, order].max())
+        M[t, order] = 1.0
+        W[t, order] = z / z.sum()
+    dense = np.zeros((N, T, d))
+    for e, (w1, b1, w2, b2) in enumerate(experts):
+        h = x @ w1.T + b1
+        h = h * norm.cdf(h)
+        dense[e] = h @ w2.T + b2
+    y = np.einsum("te,te,etd->td", M, W, dense)
+    np.testing.assert_allclose(res["out"], y, rtol=1e-10, atol=1e-12)
+
+
+def test_single_expert_is_dense_ffn():
+    rng = np.random.default_rng(4)
+    T, d, f = 11, 16, 20
+    x, wr, experts, _ = _tiny_problem(rng, T, d, f, 1)
+    res = O.moe_forward(x, wr, experts, 1)
+    w1, b1, w2, b2 = experts[0]
+    h = x @ w1.T + b1
+    y = (h * norm.cdf(h)) @ w2.T + b2
+    np.testing.assert_allclose(res["out"], y, rtol=1e-10, atol=1e-12)
+    assert (res["w"] == 1.0).all()
+
+
+def test_k_equals_n_is_soft_router():
+    rng = np.random.default_rng(6)
+    T, d, f, N = 10, 8, 8, 4
+    x, wr, experts, _ = _tiny_problem(rng, T, d, f, N)
+    res = O.moe_forward(x, wr, experts, N)
+    logits = res["logits"].astype(np.float64)
+    p = np.exp(logits - logits.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    y = sum(p[:, e:e + 1] * O.expert_ffn(x, *experts[e]) for e in range(N))
+    np.testing.assert_allclose(res["out"], y, rtol=1e-10, atol=1e-12)
+
+
+def test_overflow_tokens_are_dropped_in_token_order():
+    rng = np.random.default_rng(8)
+    T, d, f, N, C = 20, 8, 8, 4, 6
+    x, wr, experts, _ = _tiny_problem(rng, T, d, f, N)
+    off = np.zeros(N, dtype=np.float32)
+    off[0] = 1e4
+    res = O.moe_forward(x, wr, experts, 1, logit_offset=off, capacity=C)
+    assert (res["idx"][:, 0] == 0).all()
+    assert res["slot_row"][:C, 0].tolist() == list(range(C))
+    assert (res["slot_row"][C:, 0] == -1).all()
+    assert res["n_dropped"] == T - C
+    assert (res["out"][C:] == 0.0).all()
+    assert np.abs(res["out"][:C]).sum() > 0
+
+
+def test_capacity_at_least_max_count_equals_dropless():
+    rng = np.random.default_rng(9)
+    T, d, f, N, K = 24, 8, 8, 4, 2
+    x, wr, experts, _ = _tiny_problem(rng, T, d, f, N)
+    a = O.moe_forward(x, wr, experts, K)
+    b = O.moe_forward(x, wr, experts, K, capacity=int(a["counts"].max()))
+    for key in ("idx", "slot_row", "row_token", "expert_offsets"):
+        assert (a[key] == b[key]).all()
+    assert (a["out"] == b["out"]).all()
+
+
+def test_out_tokens_subset_matches_full():
+    rng = np.random.default_rng(10)
+    T, d, f, N, K = 20, 8, 8, 4, 2
+    x, wr, experts, shared = _tiny_problem(rng, T, d, f, N, fs=8)
+    a = O.moe_forward(x, wr, experts, K, shared=shared, capacity=7)
+    sub = np.array([0, 3, 19])
+    b = O.moe_forward(x, wr, experts, K, shared=shared, capacity=7, out_tokens=sub)
+    np.testing.assert_allclose(a["out"][sub], b["out"][sub], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- invariants
+def _check_invariants(res, T, N, K, C):
+    idx = res["idx"]
+    assert all(len(set(r)) == K for r in idx.tolist())
+    assert ((idx >= 0) & (idx < N)).all()
+    np.testing.assert_allclose(res["w"].sum(1), 1.0, rtol=0, atol=1e-12)
+    assert int(res["counts"].sum()) == T * K
+    if C:
+        assert (res["kept"] <= C).all()
+    assert int(res["kept"].sum()) + res["n_dropped"] == T * K
+
+
+def test_invariants_tiny_fp32_workload():
+    from mixture_experts_layer_prefix_amd import configs, inputs
+    s = configs.TINY_FP32
+    inp = inputs.make_inputs(s)
+    res = O.moe_forward(inp.f32("x"), inp.f32("w_router"),
+                        [tuple(None if a is None else np.asarray(a, np.float64) for a in inp.expert(e))
+                         for e in range(s.n_experts)],
+                        s.top_k, b_router=inp.b_router)
+    _check_invariants(res, s.T, s.n_experts, s.top_k, None)
+
+
+def test_switch_zipf_offsets_make_experts_overflow():
+    """The Zipf-offset reading must make several experts overflow C = 160."""
+    from mixture_experts_layer_prefix_amd import configs, inputs
+    s = configs.SWITCH_CAPACITY
+    inp = inputs.make_inputs(s, materialize_experts=False)
+    logits = O.router_logits(inp.f32("x"), inp.f32("w_router"), None, inp.logit_offset)
+    idx = O.topk_select(O.selection_scores(logits), s.top_k)
+    C = O.capacity_from_factor(s.T, s.n_experts, s.capacity_factor)
+    d = O.dispatch(idx, s.n_experts, C)
+    res = dict(idx=idx, w=O.topk_softmax(logits, idx), **d)
+    _check_invariants(res, s.T, s.n_experts, s.top_k, C)
+    overflow = int((d["counts"] > C).sum())
+    print(f"switch workload: {overflow} experts overflow, {d['n_dropped']} of {s.T} tokens dropped")
+    assert overflow >= 2
+    assert 0 < d["n_dropped"] < s.T // 2
