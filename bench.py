@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: router + Top-K,
+dispatch, grouped-GEMM expert FFN (GELU fused), combine (and the aux loss for
+workloads that define it), through the C ABI.  The stages are enqueued one by
+one (the same kernels moe_layer_forward enqueues), with HIP events recorded
+on the launch stream around each stage, so the grouped-GEMM stage's own
+duration is measured live inside the timed region.
+
+Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped prefill
+layer (T=4096, d=4096, f=14336, N=8, top-2, bf16).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 MI355X; grouped-GEMM % MFMA peak, decode % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_8x7b_prefill")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    return ap.parse_args()
+
+
+def algorithmic(shape, counts, M):
+    """Algorithmic FLOPs and minimum HBM bytes of the grouped-GEMM stage."""
+    d, f, fs = shape.d_model, shape.d_ff, shape.d_ff_shared
+    T = shape.T
+    eb = 4 if shape.dtype == "f32" else 2
+    touched = int((counts > 0).sum())
+    flops = 2 * 2 * M * d * f + (2 * 2 * T * d * fs if fs else 0)
+    wbytes = touched * 2 * d * f * eb + (2 * d * fs * eb if fs else 0)
+    # x_perm read, h written and read back, y_perm written (+ shared x, h_s, y_s)
+    abytes = (M * d + 2 * M * f + M * d) * eb
+    if fs:
+        abytes += (T * d + 2 * T * fs + T * d) * eb
+    return flops, wbytes + abytes, touched
+
+
+def cpu_baseline(shape, inp, n_tok):
+    """The CPU oracle as it stands, on the first n_tok tokens of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from mixture_experts_layer_prefix_amd import inputs
+    from oracle import moe_oracle as O
+
+    n_tok = min(n_tok, shape.T)
+    cap = None
+    if shape.capacity_factor is not None:
+        cap = O.capacity_from_factor(n_tok, shape.n_experts, shape.capacity_factor)
+    get = lambda e: tuple(None if a is None else (inputs.bf16_widen(a) if a.dtype == np.uint16 else a)
+                          for a in inp.expert(e))
+    shared = (inp.f32("ws1"), inp.f32("ws2")) if shape.d_ff_shared else None
+    x = inp.f32("x")[:n_tok]
+    t0 = time.perf_counter()
+    O.moe_forward(x, inp.f32("w_router"), get, shape.top_k, n_experts=shape.n_experts,
+                  b_router=inp.b_router, logit_offset=inp.logit_offset, sel_bias=inp.sel_bias,
+                  shared=shared, capacity=cap, aux_alpha=shape.aux_alpha)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n_tok} of {shape.T} tokens of {shape.name} (routing, dispatch, "
+                      f"expert FFN, combine{', aux' if shape.aux_alpha else ''}), one run, "
+                      f"{dt:.1f} s, fp64 NumPy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_prefix_amd import configs, inputs, moe
+
+    shape = configs.BY_NAME[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    moe.lib()
+    log(f"workload {shape.name}: generating seeded inputs ...")
+    t0 = time.time()
+    inp = inputs.make_inputs(shape, seed=args.seed)
+    t = inputs.to_torch(inp, dev)
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    cfg = moe.config_for(shape)
+    W = moe.make_weights(t)
+    T, N, K, d = cfg.T, cfg.n_experts, cfg.top_k, cfg.d_model
+    dt = torch.float32 if shape.dtype == "f32" else torch.bfloat16
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    logits = torch.empty(T, N, **f32)
+    idx = torch.empty(T, K, **i32)
+    w = torch.empty(T, K, **f32)
+    counts = torch.empty(N, **i32)
+    offsets = torch.empty(N + 1, **i32)
+    slot_row = torch.empty(T, K, **i32)
+    row_token = torch.empty(T * K, **i32)
+    x_perm = torch.empty(T * K, d, dtype=dt, device=dev)
+    ndrop = torch.empty(1, **i32)
+    y_perm = torch.empty(T * K, d, dtype=dt, device=dev)
+    y_shared = torch.empty(T, d, dtype=dt, device=dev) if cfg.d_ff_shared else None
+    out = torch.empty(T, d, dtype=dt, device=dev)
+    loss = torch.empty(1, **f32)
+    ws_d = moe.alloc_workspace(cfg, "dispatch", dev)
+    ws_f = moe.alloc_workspace(cfg, "expert_ffn", dev)
+    ws_a = moe.alloc_workspace(cfg, "aux", dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    names = ("route", "dispatch", "expert_ffn", "combine") + (("aux",) if cfg.aux_alpha else ())
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        moe.moe_route(cfg, t["x"], W, logits, idx, w, stream=sp)
+        if ev: ev[1].record(stream)
+        moe.moe_dispatch(cfg, idx, t["x"], counts, offsets, slot_row, row_token, x_perm, ndrop,
+                         ws_d, stream=sp)
+        if ev: ev[2].record(stream)
+        moe.moe_expert_ffn(cfg, x_perm, offsets, W, t["x"] if cfg.d_ff_shared else None, y_perm,
+                           y_shared, ws_f, stream=sp)
+        if ev: ev[3].record(stream)
+        moe.moe_combine(cfg, y_perm, slot_row, w, y_shared, out, stream=sp)
+        if ev: ev[4].record(stream)
+        if cfg.aux_alpha:
+            moe.moe_aux_loss(cfg, logits, counts, loss, ws_a, stream=sp)
+            if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # the staged path must reproduce the whole-layer entry point bit for bit
+    layer_out = torch.empty_like(out)
+    moe.moe_layer_forward(cfg, t["x"], W, layer_out, None, None, None,
+                          moe.alloc_workspace(cfg, "layer", dev), stream=sp)
+    torch.cuda.synchronize()
+    assert torch.equal(layer_out, out), "staged path and moe_layer_forward differ"
+    del layer_out
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage_ms = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1])
+                                  for s in range(args.steps)])) for i, n in enumerate(names)}
+    step_ms = float(np.mean([evs[s][0].elapsed_time(evs[s][-1]) for s in range(args.steps)]))
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = T / (ms_per_step / 1e3)
+
+    counts_h = counts.cpu().numpy()
+    M = int(offsets[-1].item())
+    flops, nbytes, touched = algorithmic(shape, counts_h, M)
+    ffn_s = stage_ms["expert_ffn"] / 1e3
+    ai = flops / nbytes
+    if shape.dtype == "f32":
+        roof = {"bound": "alu", "achieved": round(flops / ffn_s / 1e12, 2),
+                "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s"}
+    elif ai >= RIDGE:
+        roof = {"bound": "mfma", "achieved": round(flops / ffn_s / 1e12, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nbytes / ffn_s / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = ("moe_expert_ffn: grouped GEMM1 (+GELU) and GEMM2 over the ragged expert "
+                      "blocks" + (" and the shared expert" if cfg.d_ff_shared else ""))
+    roof["per_launch"] = {"flops": flops, "min_bytes": nbytes, "rows": M,
+                          "touched_experts": touched, "ms": round(stage_ms["expert_ffn"], 4)}
+
+    res = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": shape.dtype, "data": "synthetic (seeded, N(0,1) x, N(0,1/fan_in) weights)",
+        "config": {"workload": shape.name, "T": T, "d_model": d, "d_ff": cfg.d_ff,
+                   "n_experts": N, "top_k": K, "capacity": cfg.capacity,
+                   "d_ff_shared": cfg.d_ff_shared, "parallelism": "single GPU"},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "event_ms_per_step": round(step_ms, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(shape, inp, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

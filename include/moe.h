@@ -1,0 +1,201 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward hot path of a Mixture-of-Experts
+ * (MoE) layer on one AMD MI355X (gfx950) GPU.
+ *
+ * The layer (per token x_t, N routed experts, top-K):
+ *   logits = W_r . x_t (+ b_r) (+ offset)            router scoring
+ *   sel    = TopK(logits + sel_bias), w = softmax over the K chosen logits
+ *   dispatch: (token, slot) pairs -> contiguous per-expert row blocks,
+ *             at most C rows per expert when a capacity is set
+ *   E_e(x) = W2_e . GELU(W1_e . x + b1_e) + b2_e     per-expert FFN
+ *   out_t  = sum_k w[t,k] * E_{sel_k}(x_t) (+ E_shared(x_t))
+ *   aux    = alpha * N * sum_e f_e * P_e             Switch load-balance loss
+ *
+ * Sources (by page title and section):
+ *   lmnt.cn MoE walkthrough (news/351908): §1.2 per-token flow; §2.1 gate
+ *     scoring equation (score = Softmax(TopK(W_g x))); §3.1 dispatch; §3.2
+ *     combine equation; §3.3 capacity equation; §5.1-5.2 balance loss.
+ *   yunthe.com "MoE混合专家模型实战": "MoE架构的稀疏激活原理与Transformer实现"
+ *     (output equation, reference forward, grouped GEMM over same-expert
+ *     tokens); "专家负载均衡与辅助损失函数设计" (aux loss, per-expert bias b_i,
+ *     capacity drop).
+ *   wiblog.cn "MoE 专家路由如何实现稀疏激活": fine-grained and shared experts.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every buffer.  The library never allocates
+ *     device memory, never frees, and never synchronises the stream; every
+ *     call only enqueues kernels on `stream` and returns.
+ *   - Pointers marked [dev] are device pointers, 16-byte aligned; [host]
+ *     pointers are read during the call only.
+ *   - Layout: row-major; weight matrices use the nn.Linear [out, in] layout,
+ *     so the reduction dimension is contiguous.  dtype MOE_BF16 means
+ *     bfloat16 storage with fp32 accumulation; MOE_F32 means fp32 throughout.
+ *   - Sizes: buffers are sized for the worst case M_max = T*K permuted rows.
+ *     Data-dependent counts stay on the device.
+ *   - Errors: arguments are checked on the host before any launch; a non-OK
+ *     return enqueues nothing.  moe_last_error() gives a thread-local message.
+ *     A failed launch returns MOE_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Limits: 1 <= K <= N <= 256, K <= 64, T >= 1, d_model, d_ff and
+ *     d_ff_shared multiples of 64, T*K*max(d_model, d_ff) < 2^31.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs on every call.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or config */
+  MOE_ERR_UNSUPPORTED = -2, /* valid MoE shape outside this build's limits */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+  MOE_ERR_HIP = -4          /* a kernel launch failed                      */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef struct {
+  int32_t T;           /* tokens in the batch                                  */
+  int32_t d_model;     /* d                                                    */
+  int32_t d_ff;        /* f, hidden width of every routed expert               */
+  int32_t n_experts;   /* N routed experts                                     */
+  int32_t top_k;       /* K experts per token                                  */
+  int32_t capacity;    /* C: <= 0 dropless; else at most C rows per expert     */
+  int32_t d_ff_shared; /* 0: no shared expert; else its hidden width f_s       */
+  int32_t dtype;       /* moe_dtype_t of x, expert weights, intermediates, out */
+  float aux_alpha;     /* alpha of the aux loss (used by moe_layer_forward)    */
+} moe_config_t;
+
+typedef struct {
+  const void *w_router;     /* [dev] [N, d] dtype                                  */
+  const float *b_router;    /* [dev] [N] fp32 or NULL: added to the logits         */
+  const float *logit_offset;/* [dev] [N] fp32 or NULL: added to the logits         */
+  const float *sel_bias;    /* [dev] [N] fp32 or NULL: added for selection only    */
+  const void *w1;           /* [dev] [N, f, d] dtype                               */
+  const void *b1;           /* [dev] [N, f] dtype or NULL                          */
+  const void *w2;           /* [dev] [N, d, f] dtype                               */
+  const void *b2;           /* [dev] [N, d] dtype or NULL                          */
+  const void *ws1;          /* [dev] [f_s, d] dtype (shared expert) or NULL        */
+  const void *ws2;          /* [dev] [d, f_s] dtype (shared expert) or NULL        */
+} moe_weights_t;
+
+typedef enum {
+  MOE_STAGE_ROUTE = 0,
+  MOE_STAGE_DISPATCH = 1,
+  MOE_STAGE_EXPERT_FFN = 2,
+  MOE_STAGE_COMBINE = 3,
+  MOE_STAGE_AUX = 4,
+  MOE_STAGE_LAYER = 5
+} moe_stage_t;
+
+/* Bytes of device workspace the entry point of `stage` needs for `cfg`
+ * (0 if none; (size_t)-1 if cfg is invalid).  Any buffer of at least this
+ * size, 256-byte aligned, may be passed as `ws`; its contents on entry do
+ * not matter and are clobbered. */
+size_t moe_workspace_size(const moe_config_t *cfg, moe_stage_t stage);
+
+/* capacity = ceil(T / N * capacity_factor), computed exactly for the binary
+ * value of capacity_factor (lmnt.cn walkthrough §3.3, capacity equation).
+ * Returns -1 for T < 1, N < 1 or capacity_factor not finite and > 0. */
+int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double capacity_factor);
+
+/* Router scoring and Top-K routing (lmnt.cn §2.1 gate scoring equation and
+ * the TopK-then-Softmax order; yunthe.com reference forward; yunthe.com
+ * per-expert bias b_i for selection).
+ *   x        [dev] [T, d] dtype
+ *   logits   [dev] [T, N] fp32 out, or NULL.  logits = fp32 rounding of the
+ *            dot product accumulated in fp64, plus b_router and
+ *            logit_offset added in fp64 before that single rounding.
+ *   topk_idx [dev] [T, K] int32 out: the K experts with the largest
+ *            fp32(logit + sel_bias), ordered by (score desc, index asc);
+ *            NaN scores order as -inf.
+ *   topk_w   [dev] [T, K] fp32 out: softmax over the K chosen unbiased logits
+ *            (computed in fp64, rounded once).
+ *   ws       may be NULL (needs 0 bytes). */
+int moe_route(const moe_config_t *cfg, const void *x, const moe_weights_t *w, float *logits,
+              int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/* Dispatch: permute tokens from token order to contiguous per-expert blocks
+ * (lmnt.cn §3.1), with the capacity limit of lmnt.cn §3.3.  (token, slot)
+ * pairs are taken token-major; within an expert they keep token order; a pair
+ * is kept iff fewer than C earlier pairs chose its expert.
+ *   topk_idx       [dev] [T, K] int32 in.  Indices outside [0, N) are ignored
+ *                  (slot_row -1, counted as dropped).
+ *   x              [dev] [T, d] dtype in.
+ *   counts         [dev] [N] int32 out: pre-drop pairs per expert.
+ *   expert_offsets [dev] [N+1] int32 out: exclusive scan of min(counts, C).
+ *   slot_row       [dev] [T, K] int32 out: row of the pair in x_perm, -1 if dropped.
+ *   row_token      [dev] [T*K] int32 out: token of each row (first M rows valid,
+ *                  M = expert_offsets[N]).
+ *   x_perm         [dev] [T*K, d] dtype out: x_perm[r] = x[row_token[r]] (first M rows).
+ *   n_dropped      [dev] [1] int32 out: T*K - M.
+ *   ws             [dev] >= moe_workspace_size(cfg, MOE_STAGE_DISPATCH) bytes. */
+int moe_dispatch(const moe_config_t *cfg, const int32_t *topk_idx, const void *x,
+                 int32_t *counts, int32_t *expert_offsets, int32_t *slot_row,
+                 int32_t *row_token, void *x_perm, int32_t *n_dropped, void *ws,
+                 size_t ws_bytes, hipStream_t stream);
+
+/* Per-expert FFN as grouped GEMMs over the ragged expert blocks (yunthe.com
+ * reference forward: Linear, GELU, Linear; batched per expert as a grouped
+ * GEMM).  GELU is the exact erf form, fused into the first GEMM's epilogue.
+ *   x_perm         [dev] [T*K, d] dtype in (first expert_offsets[N] rows used).
+ *   expert_offsets [dev] [N+1] int32 in (as written by moe_dispatch).
+ *   x              [dev] [T, d] dtype in: input of the shared expert; may be
+ *                  NULL when cfg->d_ff_shared == 0.
+ *   y_perm         [dev] [T*K, d] dtype out: E_e(x_perm[r]) for the rows of e.
+ *   y_shared       [dev] [T, d] dtype out: E_shared(x_t); NULL iff no shared expert.
+ *   ws             [dev] >= moe_workspace_size(cfg, MOE_STAGE_EXPERT_FFN) bytes
+ *                  (holds the hidden activations). */
+int moe_expert_ffn(const moe_config_t *cfg, const void *x_perm, const int32_t *expert_offsets,
+                   const moe_weights_t *w, const void *x, void *y_perm, void *y_shared,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine: restore token order and sum the K expert outputs weighted by the
+ * routing weights (lmnt.cn §3.2 combine equation; yunthe.com output
+ * equation), in slot order k = 0..K-1, fp32 accumulation; dropped slots
+ * (slot_row -1) contribute 0 and the other weights are not renormalised;
+ * then the shared expert's output is added with weight 1 (wiblog.cn shared
+ * expert).  The residual add is the caller's.
+ *   y_perm   [dev] [T*K, d] dtype in;  slot_row [dev] [T, K] int32 in;
+ *   topk_w   [dev] [T, K] fp32 in;     y_shared [dev] [T, d] dtype in or NULL;
+ *   out      [dev] [T, d] dtype out. */
+int moe_combine(const moe_config_t *cfg, const void *y_perm, const int32_t *slot_row,
+                const float *topk_w, const void *y_shared, void *out, hipStream_t stream);
+
+/* Switch auxiliary load-balance loss (yunthe.com "专家负载均衡与辅助损失函数设计";
+ * lmnt.cn §5.1): alpha * N * sum_e f_e * P_e, with f_e = counts[e] / T (mean
+ * of the pre-drop 0/1 selection mask, so sum f = K) and P_e the mean over
+ * tokens of softmax_N(logits[t])_e.  Computed in fp64 with a fixed reduction
+ * order; written as fp32.
+ *   logits [dev] [T, N] fp32 in;  counts [dev] [N] int32 in (from moe_dispatch);
+ *   loss_out [dev] [1] fp32 out;  alpha = cfg->aux_alpha;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes. */
+int moe_aux_loss(const moe_config_t *cfg, const float *logits, const int32_t *counts,
+                 float *loss_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole layer: route -> dispatch -> expert FFN (+ shared expert) ->
+ * combine (-> aux loss when aux_out != NULL).  Same kernels and results as
+ * calling the stages in order.
+ *   x [dev] [T, d] dtype in;  out [dev] [T, d] dtype out;
+ *   aux_out [dev] [1] fp32 out or NULL;  counts_out [dev] [N] int32 out or NULL;
+ *   n_dropped_out [dev] [1] int32 out or NULL;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_LAYER) bytes. */
+int moe_layer_forward(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
+                      void *out, float *aux_out, int32_t *counts_out, int32_t *n_dropped_out,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Thread-local text of the last non-OK return on this thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,221 @@
+// Dispatch: permute (token, slot) pairs from token order into contiguous
+// per-expert row blocks, with an optional per-expert capacity.
+//
+// What it computes (lmnt.cn MoE walkthrough §3.1: reorder the input from
+// "by token" to "by expert" so each expert gets one contiguous block; §3.3
+// capacity equation: over-capacity tokens skip the expert):
+//   pairs p = t*K + k in token-major order; e = idx[p];
+//   pos(p)  = #{p' < p : idx[p'] = e}            (stable, token order)
+//   kept    = pos(p) < C;  counts[e] = #pairs of e; kept_e = min(counts[e], C)
+//   off     = exclusive scan of kept_e;  row = off[e] + pos(p)
+//   slot_row[p] = kept ? row : -1;  row_token[row] = t;  x_perm[row] = x[t].
+//
+// Four launches, all deterministic (no result depends on atomic order):
+//   1. hist:    each workgroup counts its 256-token chunk per expert (LDS).
+//   2. scan:    one workgroup turns the per-chunk counts into per-chunk
+//               starting positions, counts, kept counts, offsets, n_dropped.
+//   3. rank:    one wavefront per chunk walks its pairs in order, 64 at a
+//               time; lanes with equal experts are matched with ballots, so
+//               each pair's position is its chunk start + earlier matches.
+//   4. permute: one wavefront per token reads x[t] once (16-byte loads) and
+//               writes it to each of its kept rows.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int DB = kDispatchTokensPerBlock;
+constexpr int MAXN = 256;
+
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                   int N, int32_t* __restrict__ blkcnt) {
+  __shared__ int hist[MAXN];
+  for (int e = threadIdx.x; e < N; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * DB * K;
+  const int64_t p1 = min((int64_t)(blockIdx.x + 1) * DB, (int64_t)T) * K;
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+    const int e = idx[p];
+    if (e >= 0 && e < N) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += blockDim.x) blkcnt[(int64_t)blockIdx.x * N + e] = hist[e];
+}
+
+// One workgroup of 256 threads; thread e owns expert e (N <= 256).
+__global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ blkcnt, int nblk,
+                                                   int N, int cap, int64_t pairs,
+                                                   int32_t* __restrict__ blkoff,
+                                                   int32_t* __restrict__ counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ n_dropped) {
+  __shared__ int wsum[4];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < N) {
+    for (int b = 0; b < nblk; ++b) {
+      blkoff[(int64_t)b * N + e] = run;
+      run += blkcnt[(int64_t)b * N + e];
+    }
+    counts[e] = run;
+  }
+  const int kept = (e < N) ? min(run, cap) : 0;
+  // exclusive scan of kept over e: wave-level inclusive scan, then wave sums
+  const int lane = e & 63, wave = e >> 6;
+  int v = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  const int excl = base + v - kept;
+  if (e < N) offsets[e] = excl;
+  if (e == N - 1) {
+    offsets[N] = excl + kept;
+    n_dropped[0] = (int32_t)(pairs - (int64_t)(excl + kept));
+  }
+}
+
+// One wavefront per chunk of DB tokens.
+__global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                  int N, int cap,
+                                                  const int32_t* __restrict__ blkoff,
+                                                  const int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ slot_row,
+                                                  int32_t* __restrict__ row_token) {
+  __shared__ int run[MAXN];
+  __shared__ int off_s[MAXN];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < N; e += 64) {
+    run[e] = blkoff[(int64_t)blockIdx.x * N + e];
+    off_s[e] = offsets[e];
+  }
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * DB * K;
+  const int64_t p1 = min((int64_t)(blockIdx.x + 1) * DB, (int64_t)T) * K;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t pb = p0; pb < p1; pb += 64) {
+    const int64_t p = pb + lane;
+    const bool inb = p < p1;
+    const int e = inb ? idx[p] : -1;
+    const bool valid = inb && e >= 0 && e < N;
+    // lanes holding the same valid expert: AND of per-bit ballots
+    uint64_t match = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t ones = __ballot(bit);
+      match &= bit ? ones : ~ones;
+    }
+    if (!valid) match = 0;
+    int pos = 0;
+    if (valid) {
+      const int rank = __popcll(match & below);
+      const int start = run[e];
+      pos = start + rank;
+      const uint64_t above = (lane == 63) ? 0ull : (match >> (lane + 1));
+      if (above == 0) run[e] = start + __popcll(match);   // last lane of its group
+    }
+    if (inb) {
+      int r = -1;
+      if (valid && pos < cap) {
+        r = off_s[e] + pos;
+        row_token[r] = (int32_t)(p / K);
+      }
+      slot_row[p] = r;
+    }
+    __syncthreads();
+  }
+}
+
+// One wavefront per token; rows are copied as 16-byte units.
+__global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      uint4* __restrict__ x_perm, int T, int K,
+                                                      int row_vec) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t* sr = slot_row + (int64_t)t * K;
+  bool any = false;
+  for (int k = 0; k < K; ++k) any |= sr[k] >= 0;
+  if (!any) return;
+  const uint4* src = x + (int64_t)t * row_vec;
+  constexpr int U = 4;
+  for (int c0 = lane; c0 < row_vec; c0 += 64 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * 64;
+      if (c < row_vec) v[u] = src[c];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int r = sr[k];
+      if (r < 0) continue;
+      uint4* dst = x_perm + (int64_t)r * row_vec;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * 64;
+        if (c < row_vec) dst[c] = v[u];
+      }
+    }
+  }
+}
+
+// One workgroup: tiles of BM rows over each expert's kept block.
+__global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets, int N,
+                                                       int BM, int2* __restrict__ map,
+                                                       int32_t* __restrict__ count) {
+  __shared__ int wsum[4];
+  const int e = threadIdx.x;
+  int o0 = 0, n = 0;
+  if (e < N) {
+    o0 = offsets[e];
+    n = (offsets[e + 1] - o0 + BM - 1) / BM;
+  }
+  const int lane = e & 63, wave = e >> 6;
+  int v = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  const int start = base + v - n;
+  for (int i = 0; i < n; ++i) map[start + i] = make_int2(e, o0 + i * BM);
+  if (e == N - 1) count[0] = start + n;
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_bytes, int T, int K,
+                           int N, int capacity, int32_t* counts, int32_t* offsets,
+                           int32_t* slot_row, int32_t* row_token, void* x_perm,
+                           int32_t* n_dropped, int32_t* blkcnt, int32_t* blkoff, hipStream_t s) {
+  const int nblk = dispatch_blocks(T);
+  const int cap = capacity > 0 ? capacity : 0x7fffffff;
+  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, T, K, N, blkcnt);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blkcnt, nblk, N, cap,
+                     (int64_t)T * K, blkoff, counts, offsets, n_dropped);
+  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(64), 0, s, topk_idx, T, K, N, cap, blkoff,
+                     offsets, slot_row, row_token);
+  hipLaunchKernelGGL(permute_kernel, dim3((T + 3) / 4), dim3(256), 0, s,
+                     static_cast<const uint4*>(x), slot_row, static_cast<uint4*>(x_perm), T, K,
+                     (int)(row_bytes / 16));
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_map(const int32_t* offsets, int N, int BM, int2* map, int32_t* count,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(256), 0, s, offsets, N, BM, map, count);
+  return hipGetLastError();
+}
+
+}  // namespace moe

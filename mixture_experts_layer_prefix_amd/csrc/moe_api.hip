@@ -1,0 +1,503 @@
+// Host side of libmoe.so: argument checks, workspace carving, launch order.
+// The entry points and their contracts are declared in include/moe.h.
+#include <math.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Returns an empty string when the config is usable, else the reason.
+std::string check_config(const moe_config_t* c, int* code) {
+  *code = MOE_ERR_INVALID_ARG;
+  if (!c) return "config is NULL";
+  if (c->T < 1) return "T must be >= 1";
+  if (c->n_experts < 1) return "n_experts must be >= 1";
+  if (c->top_k < 1 || c->top_k > c->n_experts) return "top_k must satisfy 1 <= K <= N";
+  if (c->d_model < 1 || c->d_ff < 1) return "d_model and d_ff must be >= 1";
+  if (c->d_ff_shared < 0) return "d_ff_shared must be >= 0";
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return "dtype must be MOE_F32 or MOE_BF16";
+  if (!isfinite(c->aux_alpha)) return "aux_alpha must be finite";
+  *code = MOE_ERR_UNSUPPORTED;
+  if (c->n_experts > 256) return "n_experts > 256 is not supported";
+  if (c->top_k > 64) return "top_k > 64 is not supported";
+  if (c->d_model % 64 || c->d_ff % 64 || c->d_ff_shared % 64)
+    return "d_model, d_ff and d_ff_shared must be multiples of 64";
+  const int64_t mmax = (int64_t)c->T * c->top_k;
+  const int64_t wide = c->d_model > c->d_ff ? c->d_model : c->d_ff;
+  const int64_t wide_s = c->d_ff_shared > c->d_model ? c->d_ff_shared : c->d_model;
+  if (mmax * wide >= (int64_t(1) << 31) || (int64_t)c->T * wide_s >= (int64_t(1) << 31))
+    return "T*K*max(d_model, d_ff) must be < 2^31";
+  *code = MOE_OK;
+  return "";
+}
+
+// ---------------------------------------------------------------- workspace
+enum GemmPath { PATH_F32 = 0, PATH_TILED = 1, PATH_SKINNY = 2 };
+
+GemmPath gemm_path(const moe_config_t* c) {
+  if (c->dtype == MOE_F32) return PATH_F32;
+  // Decode-shaped: on average at most 8 rows per routed expert.
+  if ((int64_t)c->T * c->top_k <= 8LL * c->n_experts) return PATH_SKINNY;
+  return PATH_TILED;
+}
+
+int gemm_bm(const moe_config_t* c) {
+  return gemm_path(c) == PATH_F32 ? moe::gemm_f32_bm() : moe::gemm_bf16_bm();
+}
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+struct DispatchWs {
+  int32_t* blkcnt;
+  int32_t* blkoff;
+};
+struct FfnWs {
+  int2* tile_map;
+  int32_t* tile_count;
+  void* h;
+  void* h_shared;
+};
+struct AuxWs {
+  double* ppart;
+};
+struct LayerWs {
+  float* logits;
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* slot_row;
+  int32_t* row_token;
+  int32_t* n_dropped;
+  void* x_perm;
+  void* y_perm;
+  void* y_shared;
+  DispatchWs disp;
+  FfnWs ffn;
+  AuxWs aux;
+};
+
+void carve_dispatch(Carver& cv, const moe_config_t* c, DispatchWs* w) {
+  const size_t n = (size_t)moe::dispatch_blocks(c->T) * c->n_experts * sizeof(int32_t);
+  w->blkcnt = cv.take<int32_t>(n);
+  w->blkoff = cv.take<int32_t>(n);
+}
+
+void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w) {
+  const int64_t mmax = (int64_t)c->T * c->top_k;
+  const size_t eb = elem_bytes(c->dtype);
+  const int tiles = moe::max_m_tiles(mmax, c->n_experts, gemm_bm(c));
+  w->tile_map = cv.take<int2>((size_t)tiles * sizeof(int2));
+  w->tile_count = cv.take<int32_t>(sizeof(int32_t));
+  w->h = cv.take<void>((size_t)mmax * c->d_ff * eb);
+  w->h_shared = c->d_ff_shared ? cv.take<void>((size_t)c->T * c->d_ff_shared * eb) : nullptr;
+}
+
+void carve_aux(Carver& cv, const moe_config_t* c, AuxWs* w) {
+  w->ppart = cv.take<double>((size_t)moe::aux_blocks(c->T) * c->n_experts * sizeof(double));
+}
+
+void carve_layer(Carver& cv, const moe_config_t* c, LayerWs* w) {
+  const int64_t T = c->T, K = c->top_k, N = c->n_experts, mmax = T * K;
+  const size_t eb = elem_bytes(c->dtype);
+  w->logits = cv.take<float>(T * N * sizeof(float));
+  w->idx = cv.take<int32_t>(mmax * sizeof(int32_t));
+  w->w = cv.take<float>(mmax * sizeof(float));
+  w->counts = cv.take<int32_t>(N * sizeof(int32_t));
+  w->offsets = cv.take<int32_t>((N + 1) * sizeof(int32_t));
+  w->slot_row = cv.take<int32_t>(mmax * sizeof(int32_t));
+  w->row_token = cv.take<int32_t>(mmax * sizeof(int32_t));
+  w->n_dropped = cv.take<int32_t>(sizeof(int32_t));
+  w->x_perm = cv.take<void>((size_t)mmax * c->d_model * eb);
+  w->y_perm = cv.take<void>((size_t)mmax * c->d_model * eb);
+  w->y_shared = c->d_ff_shared ? cv.take<void>((size_t)T * c->d_model * eb) : nullptr;
+  carve_dispatch(cv, c, &w->disp);
+  carve_ffn(cv, c, &w->ffn);
+  carve_aux(cv, c, &w->aux);
+}
+
+size_t stage_bytes(const moe_config_t* c, moe_stage_t stage) {
+  Carver cv{nullptr};
+  switch (stage) {
+    case MOE_STAGE_ROUTE:
+    case MOE_STAGE_COMBINE:
+      return 0;
+    case MOE_STAGE_DISPATCH: {
+      DispatchWs w;
+      carve_dispatch(cv, c, &w);
+      return cv.off;
+    }
+    case MOE_STAGE_EXPERT_FFN: {
+      FfnWs w;
+      carve_ffn(cv, c, &w);
+      return cv.off;
+    }
+    case MOE_STAGE_AUX: {
+      AuxWs w;
+      carve_aux(cv, c, &w);
+      return cv.off;
+    }
+    case MOE_STAGE_LAYER: {
+      LayerWs w;
+      carve_layer(cv, c, &w);
+      return cv.off;
+    }
+  }
+  return (size_t)-1;
+}
+
+int check_ws(const moe_config_t* c, moe_stage_t stage, const void* ws, size_t ws_bytes) {
+  const size_t need = stage_bytes(c, stage);
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                       " bytes, got " + std::to_string(ws_bytes));
+  return MOE_OK;
+}
+
+#define MOE_CHECK_CFG(c)                          \
+  do {                                            \
+    int code_;                                    \
+    std::string why_ = check_config((c), &code_); \
+    if (code_ != MOE_OK) return fail(code_, why_); \
+  } while (0)
+
+#define MOE_REQUIRE_PTR(p, name)                                                 \
+  do {                                                                           \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL");  \
+    if (!aligned16(p))                                                           \
+      return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned"); \
+  } while (0)
+
+#define MOE_OPTIONAL_PTR(p, name)                                                \
+  do {                                                                           \
+    if ((p) && !aligned16(p))                                                    \
+      return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is not 16-byte aligned"); \
+  } while (0)
+
+int hip_status(hipError_t e, const char* where) {
+  if (e != hipSuccess)
+    return fail(MOE_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- stages (checked)
+int do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
+             int32_t* idx, float* tw, hipStream_t s) {
+  return hip_status(moe::launch_route(c->dtype, x, w->w_router, w->b_router, w->logit_offset,
+                                      w->sel_bias, logits, idx, tw, c->T, c->d_model,
+                                      c->n_experts, c->top_k, s),
+                    "moe_route launch");
+}
+
+int do_dispatch(const moe_config_t* c, const int32_t* idx, const void* x, int32_t* counts,
+                int32_t* offsets, int32_t* slot_row, int32_t* row_token, void* x_perm,
+                int32_t* n_dropped, const DispatchWs& dw, hipStream_t s) {
+  return hip_status(
+      moe::launch_dispatch(idx, x, (size_t)c->d_model * elem_bytes(c->dtype), c->T, c->top_k,
+                           c->n_experts, c->capacity, counts, offsets, slot_row, row_token,
+                           x_perm, n_dropped, dw.blkcnt, dw.blkoff, s),
+      "moe_dispatch launch");
+}
+
+hipError_t run_gemm(GemmPath path, const moe::GemmArgs& a, bool gelu, hipStream_t s) {
+  switch (path) {
+    case PATH_F32:
+      return moe::launch_gemm_f32(a, gelu, s);
+    case PATH_SKINNY:
+      return moe::launch_gemm_skinny_bf16(a, gelu, 0, s);
+    default:
+      return moe::launch_gemm_bf16(a, gelu, s);
+  }
+}
+
+int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
+           const moe_weights_t* w, const void* x, void* y_perm, void* y_shared, const FfnWs& fw,
+           hipStream_t s) {
+  const GemmPath path = gemm_path(c);
+  const int64_t mmax = (int64_t)c->T * c->top_k;
+  const int N = c->n_experts;
+  const bool has_shared = c->d_ff_shared > 0;
+  hipError_t e = hipSuccess;
+  if (path != PATH_SKINNY) {
+    e = moe::launch_tile_map(offsets, N, gemm_bm(c), fw.tile_map, fw.tile_count, s);
+    if (e != hipSuccess) return hip_status(e, "tile map launch");
+  }
+  moe::GemmArgs g1{};
+  g1.A = x_perm;
+  g1.W = w->w1;
+  g1.bias = w->b1;
+  g1.C = fw.h;
+  g1.offsets = offsets;
+  g1.tile_map = path == PATH_SKINNY ? nullptr : fw.tile_map;
+  g1.tile_count = fw.tile_count;
+  g1.Kd = c->d_model;
+  g1.Nd = c->d_ff;
+  g1.E = N;
+  g1.max_tiles = moe::max_m_tiles(mmax, N, gemm_bm(c));
+  moe::GemmArgs g2 = g1;
+  g2.A = fw.h;
+  g2.W = w->w2;
+  g2.bias = w->b2;
+  g2.C = y_perm;
+  g2.Kd = c->d_ff;
+  g2.Nd = c->d_model;
+
+  // The shared expert rides in the same launch when its width matches.
+  moe::GemmArgs s1{}, s2{};
+  const bool fuse_shared = has_shared && c->d_ff_shared == c->d_ff;
+  if (has_shared) {
+    s1.As = x;
+    s1.Ws = w->ws1;
+    s1.Cs = fw.h_shared;
+    s1.Ts = c->T;
+    s1.Kd = c->d_model;
+    s1.Nd = c->d_ff_shared;
+    s1.E = 0;
+    s2 = s1;
+    s2.As = fw.h_shared;
+    s2.Ws = w->ws2;
+    s2.Cs = y_shared;
+    s2.Kd = c->d_ff_shared;
+    s2.Nd = c->d_model;
+    if (fuse_shared) {
+      g1.As = s1.As; g1.Ws = s1.Ws; g1.Cs = s1.Cs; g1.Ts = s1.Ts;
+      g2.As = s2.As; g2.Ws = s2.Ws; g2.Cs = s2.Cs; g2.Ts = s2.Ts;
+    }
+  }
+  // Shared problems that cannot share the launch run on their own, with the
+  // same kernel family (the skinny kernel treats "expert E" as the shared one).
+  const GemmPath spath = path;
+  e = run_gemm(path, g1, true, s);
+  if (e != hipSuccess) return hip_status(e, "expert GEMM1 launch");
+  if (has_shared && !fuse_shared) {
+    e = run_gemm(spath, s1, true, s);
+    if (e != hipSuccess) return hip_status(e, "shared GEMM1 launch");
+  }
+  e = run_gemm(path, g2, false, s);
+  if (e != hipSuccess) return hip_status(e, "expert GEMM2 launch");
+  if (has_shared && !fuse_shared) {
+    e = run_gemm(spath, s2, false, s);
+    if (e != hipSuccess) return hip_status(e, "shared GEMM2 launch");
+  }
+  return MOE_OK;
+}
+
+int do_combine(const moe_config_t* c, const void* y_perm, const int32_t* slot_row,
+               const float* tw, const void* y_shared, void* out, hipStream_t s) {
+  return hip_status(moe::launch_combine(c->dtype, y_perm, slot_row, tw, y_shared, out, c->T,
+                                        c->d_model, c->top_k, s),
+                    "moe_combine launch");
+}
+
+int do_aux(const moe_config_t* c, const float* logits, const int32_t* counts, float* loss,
+           const AuxWs& aw, hipStream_t s) {
+  return hip_status(moe::launch_aux(logits, counts, c->T, c->n_experts, c->aux_alpha, aw.ppart,
+                                    loss, s),
+                    "moe_aux_loss launch");
+}
+
+int check_weights(const moe_config_t* c, const moe_weights_t* w, bool router, bool experts) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (router) {
+    MOE_REQUIRE_PTR(w->w_router, "w_router");
+    MOE_OPTIONAL_PTR(w->b_router, "b_router");
+    MOE_OPTIONAL_PTR(w->logit_offset, "logit_offset");
+    MOE_OPTIONAL_PTR(w->sel_bias, "sel_bias");
+  }
+  if (experts) {
+    MOE_REQUIRE_PTR(w->w1, "w1");
+    MOE_REQUIRE_PTR(w->w2, "w2");
+    MOE_OPTIONAL_PTR(w->b1, "b1");
+    MOE_OPTIONAL_PTR(w->b2, "b2");
+    if (c->d_ff_shared) {
+      MOE_REQUIRE_PTR(w->ws1, "ws1");
+      MOE_REQUIRE_PTR(w->ws2, "ws2");
+    }
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_config_t* cfg, moe_stage_t stage) {
+  int code;
+  if (!check_config(cfg, &code).empty()) return (size_t)-1;
+  if ((int)stage < MOE_STAGE_ROUTE || (int)stage > MOE_STAGE_LAYER) return (size_t)-1;
+  return stage_bytes(cfg, stage);
+}
+
+int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double cf) {
+  if (T < 1 || n_experts < 1 || !(cf > 0.0) || !isfinite(cf)) return -1;
+  // cf = m * 2^ex exactly, m a 53-bit integer; ceil(T * m * 2^ex / N) in
+  // 128-bit integer arithmetic.
+  int ex;
+  const double fr = frexp(cf, &ex);          // cf = fr * 2^ex, fr in [0.5, 1)
+  const unsigned __int128 m = (unsigned __int128)ldexp(fr, 53);
+  ex -= 53;
+  unsigned __int128 num = m * (unsigned __int128)T;
+  unsigned __int128 den = (unsigned __int128)n_experts;
+  if (ex >= 0) {
+    if (ex > 60) return -1;
+    num <<= ex;
+  } else {
+    if (-ex > 120) return -1;
+    den <<= -ex;
+  }
+  const unsigned __int128 q = (num + den - 1) / den;
+  if (q > 0x7fffffff) return -1;
+  return (int32_t)q;
+}
+
+int moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w, float* logits,
+              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(x, "x");
+  int r = check_weights(cfg, w, true, false);
+  if (r != MOE_OK) return r;
+  MOE_OPTIONAL_PTR(logits, "logits");
+  MOE_REQUIRE_PTR(topk_idx, "topk_idx");
+  MOE_REQUIRE_PTR(topk_w, "topk_w");
+  return do_route(cfg, x, w, logits, topk_idx, topk_w, stream);
+}
+
+int moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, const void* x,
+                 int32_t* counts, int32_t* expert_offsets, int32_t* slot_row,
+                 int32_t* row_token, void* x_perm, int32_t* n_dropped, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(topk_idx, "topk_idx");
+  MOE_REQUIRE_PTR(x, "x");
+  MOE_REQUIRE_PTR(counts, "counts");
+  MOE_REQUIRE_PTR(expert_offsets, "expert_offsets");
+  MOE_REQUIRE_PTR(slot_row, "slot_row");
+  MOE_REQUIRE_PTR(row_token, "row_token");
+  MOE_REQUIRE_PTR(x_perm, "x_perm");
+  MOE_REQUIRE_PTR(n_dropped, "n_dropped");
+  int r = check_ws(cfg, MOE_STAGE_DISPATCH, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  DispatchWs dw;
+  carve_dispatch(cv, cfg, &dw);
+  return do_dispatch(cfg, topk_idx, x, counts, expert_offsets, slot_row, row_token, x_perm,
+                     n_dropped, dw, stream);
+}
+
+int moe_expert_ffn(const moe_config_t* cfg, const void* x_perm, const int32_t* expert_offsets,
+                   const moe_weights_t* w, const void* x, void* y_perm, void* y_shared, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(x_perm, "x_perm");
+  MOE_REQUIRE_PTR(expert_offsets, "expert_offsets");
+  int r = check_weights(cfg, w, false, true);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(y_perm, "y_perm");
+  if (cfg->d_ff_shared) {
+    MOE_REQUIRE_PTR(x, "x");
+    MOE_REQUIRE_PTR(y_shared, "y_shared");
+  } else if (y_shared) {
+    return fail(MOE_ERR_INVALID_ARG, "y_shared given but the layer has no shared expert");
+  }
+  r = check_ws(cfg, MOE_STAGE_EXPERT_FFN, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  FfnWs fw;
+  carve_ffn(cv, cfg, &fw);
+  return do_ffn(cfg, x_perm, expert_offsets, w, x, y_perm, y_shared, fw, stream);
+}
+
+int moe_combine(const moe_config_t* cfg, const void* y_perm, const int32_t* slot_row,
+                const float* topk_w, const void* y_shared, void* out, hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(y_perm, "y_perm");
+  MOE_REQUIRE_PTR(slot_row, "slot_row");
+  MOE_REQUIRE_PTR(topk_w, "topk_w");
+  MOE_OPTIONAL_PTR(y_shared, "y_shared");
+  MOE_REQUIRE_PTR(out, "out");
+  return do_combine(cfg, y_perm, slot_row, topk_w, y_shared, out, stream);
+}
+
+int moe_aux_loss(const moe_config_t* cfg, const float* logits, const int32_t* counts,
+                 float* loss_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(logits, "logits");
+  MOE_REQUIRE_PTR(counts, "counts");
+  if (!loss_out) return fail(MOE_ERR_INVALID_ARG, "loss_out is NULL");
+  int r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  AuxWs aw;
+  carve_aux(cv, cfg, &aw);
+  return do_aux(cfg, logits, counts, loss_out, aw, stream);
+}
+
+int moe_layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_t* w, void* out,
+                      float* aux_out, int32_t* counts_out, int32_t* n_dropped_out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(x, "x");
+  int r = check_weights(cfg, w, true, true);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(out, "out");
+  MOE_OPTIONAL_PTR(counts_out, "counts_out");
+  r = check_ws(cfg, MOE_STAGE_LAYER, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  LayerWs lw;
+  carve_layer(cv, cfg, &lw);
+  int32_t* counts = counts_out ? counts_out : lw.counts;
+  int32_t* ndrop = n_dropped_out ? n_dropped_out : lw.n_dropped;
+
+  r = do_route(cfg, x, w, lw.logits, lw.idx, lw.w, stream);
+  if (r != MOE_OK) return r;
+  r = do_dispatch(cfg, lw.idx, x, counts, lw.offsets, lw.slot_row, lw.row_token, lw.x_perm,
+                  ndrop, lw.disp, stream);
+  if (r != MOE_OK) return r;
+  r = do_ffn(cfg, lw.x_perm, lw.offsets, w, x, lw.y_perm, lw.y_shared, lw.ffn, stream);
+  if (r != MOE_OK) return r;
+  r = do_combine(cfg, lw.y_perm, lw.slot_row, lw.w, lw.y_shared, out, stream);
+  if (r != MOE_OK) return r;
+  if (aux_out) {
+    r = do_aux(cfg, lw.logits, counts, aux_out, lw.aux, stream);
+    if (r != MOE_OK) return r;
+  }
+  return MOE_OK;
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Internal declarations shared by the HIP translation units of libmoe.so.
+// Device helpers for bf16 storage and the launchers each kernel file exports
+// to the host API (moe_api.hip).  Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- bf16 storage
+// bf16 values travel as raw uint16 bit patterns; widening is exact.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Exact GELU, z/2 * (1 + erf(z / sqrt(2))).
+__device__ __forceinline__ float gelu_erf(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns the hipError_t of its launch(es).
+
+// Router logits (fp64 accumulation) + Top-K + softmax over the K chosen.
+hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* b_router,
+                        const float* logit_offset, const float* sel_bias, float* logits,
+                        int32_t* topk_idx, float* topk_w, int T, int d, int N, int K,
+                        hipStream_t s);
+
+// Dispatch: histogram, scan, stable rank and row copy.
+constexpr int kDispatchTokensPerBlock = 256;
+inline int dispatch_blocks(int T) { return (T + kDispatchTokensPerBlock - 1) / kDispatchTokensPerBlock; }
+hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_bytes, int T, int K,
+                           int N, int capacity, int32_t* counts, int32_t* offsets,
+                           int32_t* slot_row, int32_t* row_token, void* x_perm,
+                           int32_t* n_dropped, int32_t* blkcnt, int32_t* blkoff, hipStream_t s);
+
+// Tile map over the ragged expert blocks: for each BM-row tile, (expert, first row).
+hipError_t launch_tile_map(const int32_t* offsets, int N, int BM, int2* map, int32_t* count,
+                           hipStream_t s);
+inline int max_m_tiles(int64_t M_max, int N, int BM) {
+  return static_cast<int>((M_max + BM - 1) / BM) + N;
+}
+
+// Arguments of one grouped GEMM C = A . W_e^T (+ bias_e) (GELU) over the
+// ragged expert row blocks, plus an optional dense "shared" problem.
+struct GemmArgs {
+  const void* A;        // [rows, Kd] routed activations
+  const void* W;        // [E, Nd, Kd] stacked weights
+  const void* bias;     // [E, Nd] or null
+  void* C;              // [rows, Nd]
+  const int32_t* offsets;   // [E+1]
+  const int2* tile_map;     // routed tiles
+  const int32_t* tile_count;
+  const void* As;       // shared problem: [Ts, Kd] (null if none)
+  const void* Ws;       // [Nd, Kd]
+  void* Cs;             // [Ts, Nd]
+  int Ts;
+  int Kd, Nd;
+  int E;
+  int max_tiles;        // grid rows reserved for routed tiles
+};
+
+// Prefill-shaped grouped GEMM (bf16 MFMA), BM rows per tile.
+int gemm_bf16_bm();
+hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s);
+// fp32 grouped GEMM (VALU), BM rows per tile.
+int gemm_f32_bm();
+hipError_t launch_gemm_f32(const GemmArgs& a, bool gelu, hipStream_t s);
+// Decode-shaped grouped GEMM (bf16): streams each touched expert's weights once.
+hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int max_rows_per_expert,
+                                   hipStream_t s);
+
+// Combine.
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* slot_row,
+                          const float* topk_w, const void* y_shared, void* out, int T, int d,
+                          int K, hipStream_t s);
+
+// Aux loss: per-block partial sums of softmax probabilities, then the final sum.
+constexpr int kAuxTokensPerBlock = 64;
+inline int aux_blocks(int T) { return (T + kAuxTokensPerBlock - 1) / kAuxTokensPerBlock; }
+hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
+                      double* ppart, float* loss_out, hipStream_t s);
+
+}  // namespace moe

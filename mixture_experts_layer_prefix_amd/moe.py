@@ -1,0 +1,218 @@
+"""Thin Python binding of libmoe.so (declared in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe.so.  Torch tensors serve as device memory and torch's current stream
+as the HIP stream.  If the library is not built, every call raises; there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5}
+ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
+                "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_layer_forward",
+                "moe_last_error")
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("aux_alpha", ctypes.c_float)]
+
+
+_WEIGHT_FIELDS = ("w_router", "b_router", "logit_offset", "sel_bias", "w1", "b1", "w2", "b2",
+                  "ws1", "ws2")
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libmoe error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mixture_experts_layer_prefix_amd.csrc.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    cfgp, wp = ctypes.POINTER(MoeConfig), ctypes.POINTER(MoeWeights)
+    L.moe_workspace_size.argtypes = [cfgp, ctypes.c_int]
+    L.moe_workspace_size.restype = sz
+    L.moe_capacity_from_factor.argtypes = [i32, i32, ctypes.c_double]
+    L.moe_capacity_from_factor.restype = i32
+    L.moe_route.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_ffn.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, sz, vp]
+    L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+    L.moe_aux_loss.argtypes = [cfgp, vp, vp, vp, vp, sz, vp]
+    L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
+    for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
+                 "moe_layer_forward"):
+        getattr(L, name).restype = ctypes.c_int
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(code: int):
+    if code != MOE_OK:
+        raise MoEError(code, lib().moe_last_error().decode())
+
+
+def _p(t) -> Optional[int]:
+    """Device pointer of a tensor (or None)."""
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------- config / weights
+def capacity_from_factor(T: int, n_experts: int, capacity_factor: float) -> int:
+    c = lib().moe_capacity_from_factor(T, n_experts, float(capacity_factor))
+    if c < 0:
+        raise ValueError("invalid capacity arguments")
+    return c
+
+
+def make_config(T, d_model, d_ff, n_experts, top_k, *, capacity=0, d_ff_shared=0, dtype="bf16",
+                aux_alpha=0.0) -> MoeConfig:
+    return MoeConfig(T=T, d_model=d_model, d_ff=d_ff, n_experts=n_experts, top_k=top_k,
+                     capacity=capacity or 0, d_ff_shared=d_ff_shared,
+                     dtype=MOE_F32 if dtype in ("f32", MOE_F32) else MOE_BF16,
+                     aux_alpha=float(aux_alpha))
+
+
+def config_for(shape, T: Optional[int] = None) -> MoeConfig:
+    """MoeConfig of a workload shape (configs.MoEShape), optionally with another T."""
+    T = shape.T if T is None else T
+    cap = 0
+    if shape.capacity_factor is not None:
+        cap = capacity_from_factor(T, shape.n_experts, shape.capacity_factor)
+    return make_config(T, shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, capacity=cap,
+                       d_ff_shared=shape.d_ff_shared, dtype=shape.dtype, aux_alpha=shape.aux_alpha)
+
+
+def make_weights(t: Dict[str, object]) -> MoeWeights:
+    """MoeWeights from a dict of device tensors (missing or None -> NULL)."""
+    return MoeWeights(**{n: _p(t.get(n)) for n in _WEIGHT_FIELDS})
+
+
+def workspace_size(cfg: MoeConfig, stage: str = "layer") -> int:
+    n = lib().moe_workspace_size(ctypes.byref(cfg), STAGES[stage])
+    if n == ctypes.c_size_t(-1).value:
+        raise MoEError(MOE_ERR_INVALID_ARG, "invalid config")
+    return n
+
+
+def alloc_workspace(cfg: MoeConfig, stage: str = "layer", device="cuda"):
+    import torch
+    n = workspace_size(cfg, stage)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_p(ws), ws.numel() * ws.element_size())
+
+
+# ---------------------------------------------------------------- entry points
+def moe_route(cfg, x, w: MoeWeights, logits, topk_idx, topk_w, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_route(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(logits), _p(topk_idx),
+                           _p(topk_w), p, n, _stream(stream)))
+
+
+def moe_dispatch(cfg, topk_idx, x, counts, expert_offsets, slot_row, row_token, x_perm,
+                 n_dropped, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_dispatch(ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts),
+                              _p(expert_offsets), _p(slot_row), _p(row_token), _p(x_perm),
+                              _p(n_dropped), p, n, _stream(stream)))
+
+
+def moe_expert_ffn(cfg, x_perm, expert_offsets, w: MoeWeights, x, y_perm, y_shared, ws,
+                   stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), _p(x_perm), _p(expert_offsets),
+                                ctypes.byref(w), _p(x), _p(y_perm), _p(y_shared), p, n,
+                                _stream(stream)))
+
+
+def moe_combine(cfg, y_perm, slot_row, topk_w, y_shared, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(cfg), _p(y_perm), _p(slot_row), _p(topk_w),
+                             _p(y_shared), _p(out), _stream(stream)))
+
+
+def moe_aux_loss(cfg, logits, counts, loss_out, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_aux_loss(ctypes.byref(cfg), _p(logits), _p(counts), _p(loss_out), p, n,
+                              _stream(stream)))
+
+
+def moe_layer_forward(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,
+                      n_dropped_out=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_layer_forward(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(out),
+                                   _p(aux_out), _p(counts_out), _p(n_dropped_out), p, n,
+                                   _stream(stream)))
+
+
+# ---------------------------------------------------------------- convenience
+class MoELayer:
+    """Holds a config, device weights and a workspace; ``forward`` enqueues
+    moe_layer_forward on the current stream and returns device tensors."""
+
+    def __init__(self, cfg: MoeConfig, tensors: Dict[str, object], device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.tensors = tensors
+        self.w = make_weights(tensors)
+        self.ws = alloc_workspace(cfg, "layer", device)
+        self.dtype = torch.float32 if cfg.dtype == MOE_F32 else torch.bfloat16
+        self.device = device
+        N = cfg.n_experts
+        wr = tensors["w_router"]
+        if tuple(wr.shape) != (N, cfg.d_model):
+            raise ValueError(f"router weight {tuple(wr.shape)} does not match N={N}, "
+                             f"d_model={cfg.d_model}")
+        if tuple(tensors["w1"].shape) != (N, cfg.d_ff, cfg.d_model):
+            raise ValueError("w1 must be [N, d_ff, d_model] and match the router's N")
+        if tuple(tensors["w2"].shape) != (N, cfg.d_model, cfg.d_ff):
+            raise ValueError("w2 must be [N, d_model, d_ff] and match the router's N")
+
+    def forward(self, x, aux: bool = False, out=None, stream=None):
+        import torch
+        if tuple(x.shape) != (self.cfg.T, self.cfg.d_model) or x.dtype != self.dtype:
+            raise ValueError("x must be [T, d_model] in the layer dtype")
+        out = torch.empty_like(x) if out is None else out
+        aux_t = torch.empty(1, dtype=torch.float32, device=x.device) if aux else None
+        counts = torch.empty(self.cfg.n_experts, dtype=torch.int32, device=x.device)
+        ndrop = torch.empty(1, dtype=torch.int32, device=x.device)
+        moe_layer_forward(self.cfg, x, self.w, out, aux_t, counts, ndrop, self.ws, stream)
+        return out, aux_t, counts, ndrop

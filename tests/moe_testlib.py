@@ -1,0 +1,143 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI, run
+the CPU oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from mixture_experts_layer_prefix_amd import inputs, moe
+from oracle import moe_oracle as O
+
+BF16_TOL = 1e-2     # relative L2 of the layer output, bf16 storage / fp32 accumulation
+F32_TOL = 1e-5      # relative L2 of the layer output, fp32 layer
+W_TOL = 1e-6        # relative error of each routing weight
+AUX_TOL = 1e-5      # relative error of the aux loss
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_expert_source(inp):
+    def get(e):
+        return tuple(None if a is None else (inputs.bf16_widen(a) if a.dtype == np.uint16 else a)
+                     for a in inp.expert(e))
+    return get
+
+
+def oracle_run(inp, capacity, out_tokens=None):
+    s = inp.shape
+    shared = None
+    if s.d_ff_shared:
+        shared = (inp.f32("ws1"), inp.f32("ws2"))
+    return O.moe_forward(inp.f32("x"), inp.f32("w_router"), oracle_expert_source(inp), s.top_k,
+                         n_experts=s.n_experts, b_router=inp.b_router,
+                         logit_offset=inp.logit_offset, sel_bias=inp.sel_bias, shared=shared,
+                         capacity=capacity, aux_alpha=s.aux_alpha, out_tokens=out_tokens)
+
+
+def device_tensors(inp, device="cuda"):
+    return inputs.to_torch(inp, device)
+
+
+def run_stages(cfg, t, device="cuda"):
+    """Every entry point in turn; returns host numpy copies of all outputs."""
+    import torch
+    T, N, K, d = cfg.T, cfg.n_experts, cfg.top_k, cfg.d_model
+    dt = torch.float32 if cfg.dtype == moe.MOE_F32 else torch.bfloat16
+    W = moe.make_weights(t)
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    logits = torch.empty(T, N, **f32)
+    idx = torch.empty(T, K, **i32)
+    w = torch.empty(T, K, **f32)
+    moe.moe_route(cfg, t["x"], W, logits, idx, w)
+    counts = torch.empty(N, **i32)
+    offsets = torch.empty(N + 1, **i32)
+    slot_row = torch.empty(T, K, **i32)
+    row_token = torch.full((T * K,), -7, **i32)
+    x_perm = torch.empty(T * K, d, dtype=dt, device=device)
+    ndrop = torch.empty(1, **i32)
+    moe.moe_dispatch(cfg, idx, t["x"], counts, offsets, slot_row, row_token, x_perm, ndrop,
+                     moe.alloc_workspace(cfg, "dispatch", device))
+    y_perm = torch.empty(T * K, d, dtype=dt, device=device)
+    y_shared = torch.empty(T, d, dtype=dt, device=device) if cfg.d_ff_shared else None
+    moe.moe_expert_ffn(cfg, x_perm, offsets, W, t["x"] if cfg.d_ff_shared else None, y_perm,
+                       y_shared, moe.alloc_workspace(cfg, "expert_ffn", device))
+    out = torch.empty(T, d, dtype=dt, device=device)
+    moe.moe_combine(cfg, y_perm, slot_row, w, y_shared, out)
+    loss = torch.empty(1, **f32)
+    moe.moe_aux_loss(cfg, logits, counts, loss, moe.alloc_workspace(cfg, "aux", device))
+    torch.cuda.synchronize()
+    M = int(offsets[-1].item())
+    res = dict(logits=logits, idx=idx, w=w, counts=counts, expert_offsets=offsets,
+               slot_row=slot_row, row_token=row_token[:M], n_dropped=ndrop, out=out.float(),
+               aux=loss)
+    res = {k: v.cpu().numpy() for k, v in res.items()}
+    res["n_dropped"] = int(res["n_dropped"][0])
+    res["aux"] = float(res["aux"][0])
+    res["x_perm_ok"] = bool(torch.equal(x_perm[:M], t["x"][row_token[:M].long()]))
+    res["y_perm"] = y_perm
+    return res
+
+
+def run_layer(cfg, t, aux=True, device="cuda"):
+    import torch
+    layer = moe.MoELayer(cfg, t, device)
+    out, aux_t, counts, nd = layer.forward(t["x"], aux=aux)
+    torch.cuda.synchronize()
+    r = dict(out=out, counts=counts.cpu().numpy(), n_dropped=int(nd.item()))
+    if aux:
+        r["aux"] = float(aux_t.item())
+    return r
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def ulp_diff_f32(a, b):
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ai - bi)
+
+
+def report_decision_mismatch(g_logits, o_logits, sel_bias, g_idx, o_idx):
+    bad = np.nonzero((g_idx != o_idx).any(axis=1))[0]
+    for t in bad[:5]:
+        s = O.selection_scores(o_logits[t:t + 1], sel_bias)[0]
+        srt = np.sort(s)[::-1]
+        say(f"  token {t}: gpu idx {g_idx[t].tolist()} oracle idx {o_idx[t].tolist()} "
+            f"score gaps {np.diff(srt[:g_idx.shape[1] + 1]).tolist()}")
+    return bad
+
+
+def check_routing_and_dispatch(g, o, inp, capacity):
+    """Integer results bit-exact, floats within tolerance."""
+    s = inp.shape
+    # logits: same fp32 value (allow one ulp where fp64 sum order differs)
+    ud = ulp_diff_f32(g["logits"], o["logits"])
+    assert ud.max() <= 1, f"logits differ by up to {ud.max()} ulp"
+    if (ud > 0).any():
+        say(f"  note: {(ud > 0).sum()} logits differ by one ulp")
+    # the selection and dispatch steps, applied to the GPU's own logits
+    g_sel = O.topk_select(O.selection_scores(g["logits"], inp.sel_bias), s.top_k)
+    assert (g_sel == g["idx"]).all(), "top-K of the GPU logits differs from the GPU idx"
+    gd = O.dispatch(g["idx"], s.n_experts, capacity)
+    for key in ("counts", "expert_offsets", "slot_row", "row_token"):
+        assert (gd[key] == g[key]).all(), f"{key} differs from dispatch of the GPU idx"
+    assert gd["n_dropped"] == g["n_dropped"]
+    # independent: the oracle's own routing
+    bad = report_decision_mismatch(g["logits"], o["logits"], inp.sel_bias, g["idx"], o["idx"])
+    assert len(bad) == 0, f"{len(bad)} tokens routed differently"
+    for key in ("counts", "expert_offsets", "slot_row", "row_token"):
+        assert (o[key] == g[key]).all(), key
+    assert o["n_dropped"] == g["n_dropped"]
+    werr = np.abs(g["w"].astype(np.float64) - o["w"]) / np.maximum(np.abs(o["w"]), 1e-30)
+    assert werr.max() <= W_TOL, f"routing weight rel err {werr.max()}"
+    assert g["x_perm_ok"], "x_perm rows are not exact copies of x[row_token]"
