@@ -27,6 +27,25 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
 }
 
+// GELU with erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + ... + a5 t^5) exp(-x^2),
+// t = 1 / (1 + p x), |error| <= 1.5e-7; odd symmetry for x < 0.  One
+// reciprocal, one exp2 and a few fma: far cheaper than a full libm erf, and
+// its error is 1e-4 of a bf16 ulp of the result.
+__device__ __forceinline__ float gelu_as(float z) {
+  const float x = fabsf(z) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  p *= t;
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
+  const float erf_abs = fmaf(-p, e, 1.0f);
+  const float erf_z = copysignf(erf_abs, z);
+  return 0.5f * z * (1.0f + erf_z);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }

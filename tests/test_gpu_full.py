@@ -1,0 +1,83 @@
+"""GPU parity at the five workload sizes, in the launch configuration bench.py
+times (the same C-ABI stage calls).
+
+Routing, dispatch and aux loss are compared over every token (integers bit-
+exact).  The expert FFN and the layer output are compared on sampled rows
+the oracle computes one by one: sampled tokens' output rows, and sampled
+permuted rows of y_perm against E_e(x[token]) directly."""
+import gc
+
+import numpy as np
+import pytest
+
+from mixture_experts_layer_prefix_amd import configs as C
+from mixture_experts_layer_prefix_amd import inputs, moe
+from oracle import moe_oracle as O
+
+from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, check_routing_and_dispatch, device_tensors,
+                         oracle_expert_source, oracle_run, rel_l2, run_stages, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_tokens(shape, o, n=10):
+    rng = np.random.default_rng(123)
+    toks = set(rng.choice(shape.T, size=min(n, shape.T), replace=False).tolist())
+    toks |= {0, shape.T - 1}
+    dropped = np.nonzero((o["slot_row"] < 0).any(axis=1))[0]
+    toks |= set(dropped[:2].tolist())
+    busiest = int(np.argmax(o["counts"]))
+    toks |= set(np.nonzero((o["idx"] == busiest).any(axis=1))[0][:2].tolist())
+    return np.array(sorted(toks))
+
+
+@pytest.mark.parametrize("shape", C.ALL, ids=[s.name for s in C.ALL])
+def test_full_size(shape):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    say(f"full-size case {shape.name}: T={shape.T} d={shape.d_model} f={shape.d_ff} "
+        f"N={shape.n_experts} K={shape.top_k} fs={shape.d_ff_shared}")
+    inp = inputs.make_inputs(shape, seed=0)
+    cfg = moe.config_for(shape)
+    cap = cfg.capacity if cfg.capacity > 0 else None
+    t = device_tensors(inp)
+    g = run_stages(cfg, t)
+    say("  gpu done; oracle routing over all tokens ...")
+    o_route = oracle_run(inp, cap, out_tokens=np.array([], dtype=np.int64))
+    check_routing_and_dispatch(g, o_route, inp, cap)
+    say(f"  routing/dispatch bit-exact; dropped {g['n_dropped']}, "
+        f"touched experts {(g['counts'] > 0).sum()}")
+    if shape.aux_alpha:
+        assert abs(g["aux"] - o_route["aux"]) <= AUX_TOL * abs(o_route["aux"])
+        say(f"  aux {g['aux']:.8f} vs oracle {o_route['aux']:.8f}")
+
+    toks = _sample_tokens(shape, o_route)
+    o = oracle_run(inp, cap, out_tokens=toks)
+    tol = F32_TOL if shape.dtype == "f32" else BF16_TOL
+    err = rel_l2(g["out"][toks], o["out"][toks])
+    say(f"  sampled {len(toks)} tokens: out rel-L2 {err:.3e} (tol {tol})")
+    assert err <= tol
+    if cap is not None and shape.d_ff_shared == 0:
+        full_drop = (o["slot_row"] < 0).all(axis=1)
+        assert (g["out"][full_drop] == 0).all()
+
+    # sampled permuted rows: y_perm[r] against E_e(x[row_token[r]])
+    M = int(g["expert_offsets"][-1])
+    rows = np.unique(np.concatenate([np.random.default_rng(7).choice(M, size=min(8, M),
+                                                                     replace=False),
+                                     [0, M - 1]]))
+    get = oracle_expert_source(inp)
+    offs = g["expert_offsets"]
+    yp = g["y_perm"][torch.from_numpy(rows).long().cuda()].float().cpu().numpy()
+    ref = []
+    x = inp.f32("x")
+    for r in rows:
+        e = int(np.searchsorted(offs, r, side="right") - 1)
+        ref.append(O.expert_ffn(x[g["row_token"][r]][None, :], *get(e))[0])
+    err_y = rel_l2(yp, np.array(ref))
+    say(f"  sampled {len(rows)} permuted rows: y_perm rel-L2 {err_y:.3e}")
+    assert err_y <= tol
+    del t, g, o, o_route, inp
+    gc.collect()
+    torch.cuda.empty_cache()
