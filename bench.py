@@ -42,7 +42,9 @@ def parse():
     ap.add_argument("--workload", default="mixtral_8x7b_prefill")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=128)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 1 GiB device copy and exit (counter calibration)")
     return ap.parse_args()
 
 
@@ -62,32 +64,83 @@ def algorithmic(shape, counts, M):
 
 
 def cpu_baseline(shape, inp, n_tok):
-    """The CPU oracle as it stands, on the first n_tok tokens of the workload."""
+    """The CPU oracle as it stands, on the first n tokens of the workload.
+
+    The sample starts at n_tok tokens and grows (at most three times) until
+    one run takes at least 10 s or covers the whole batch; the last run is
+    reported."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from mixture_experts_layer_prefix_amd import inputs
     from oracle import moe_oracle as O
 
-    n_tok = min(n_tok, shape.T)
-    cap = None
-    if shape.capacity_factor is not None:
-        cap = O.capacity_from_factor(n_tok, shape.n_experts, shape.capacity_factor)
     get = lambda e: tuple(None if a is None else (inputs.bf16_widen(a) if a.dtype == np.uint16 else a)
                           for a in inp.expert(e))
     shared = (inp.f32("ws1"), inp.f32("ws2")) if shape.d_ff_shared else None
-    x = inp.f32("x")[:n_tok]
-    t0 = time.perf_counter()
-    O.moe_forward(x, inp.f32("w_router"), get, shape.top_k, n_experts=shape.n_experts,
-                  b_router=inp.b_router, logit_offset=inp.logit_offset, sel_bias=inp.sel_bias,
-                  shared=shared, capacity=cap, aux_alpha=shape.aux_alpha)
-    dt = time.perf_counter() - t0
+    x_all = inp.f32("x")
+
+    def run(n):
+        cap = None
+        if shape.capacity_factor is not None:
+            cap = O.capacity_from_factor(n, shape.n_experts, shape.capacity_factor)
+        t0 = time.perf_counter()
+        O.moe_forward(x_all[:n], inp.f32("w_router"), get, shape.top_k, n_experts=shape.n_experts,
+                      b_router=inp.b_router, logit_offset=inp.logit_offset,
+                      sel_bias=inp.sel_bias, shared=shared, capacity=cap,
+                      aux_alpha=shape.aux_alpha)
+        return time.perf_counter() - t0
+
+    n = min(n_tok, shape.T)
+    dt = run(n)
+    for _ in range(3):          # grow the sample until it is >= 10 s of work or the whole batch
+        if dt >= 10.0 or n >= shape.T:
+            break
+        n = min(shape.T, max(2 * n, int(n * 15.0 / max(dt, 1e-3))))
+        dt = run(n)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": int(threads),
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {n_tok} of {shape.T} tokens of {shape.name} (routing, dispatch, "
-                      f"expert FFN, combine{', aux' if shape.aux_alpha else ''}), one run, "
-                      f"{dt:.1f} s, fp64 NumPy"}
+            "sample": f"first {n} of {shape.T} tokens of {shape.name} (routing, dispatch, "
+                      f"expert FFN, combine{', aux' if shape.aux_alpha else ''} on those tokens), "
+                      f"one run, {dt:.1f} s, fp64 NumPy, BLAS threads {int(threads)}"}
+
+
+def traffic_from_profile(shape):
+    """HBM bytes per launch of the grouped-GEMM stage from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the plain-copy
+    calibration recorded there; None when the GEMM sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{shape.name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("gemm_bf16.hip", "gemm_common.h", "moe_api.hip"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_layer_prefix_amd", "csrc", f), "rb").read())
+    if vals.get("gemm_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """One plain device copy of 1 GiB (for scaling the HBM byte counters)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}))
 
 
 def main():
@@ -96,6 +149,10 @@ def main():
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import numpy as np
     import torch
@@ -131,6 +188,7 @@ def main():
     y_shared = torch.empty(T, d, dtype=dt, device=dev) if cfg.d_ff_shared else None
     out = torch.empty(T, d, dtype=dt, device=dev)
     loss = torch.empty(1, **f32)
+    ws_r = moe.alloc_workspace(cfg, "route", dev)
     ws_d = moe.alloc_workspace(cfg, "dispatch", dev)
     ws_f = moe.alloc_workspace(cfg, "expert_ffn", dev)
     ws_a = moe.alloc_workspace(cfg, "aux", dev)
@@ -140,7 +198,7 @@ def main():
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        moe.moe_route(cfg, t["x"], W, logits, idx, w, stream=sp)
+        moe.moe_route(cfg, t["x"], W, logits, idx, w, ws_r, stream=sp)
         if ev: ev[1].record(stream)
         moe.moe_dispatch(cfg, idx, t["x"], counts, offsets, slot_row, row_token, x_perm, ndrop,
                          ws_d, stream=sp)
@@ -194,7 +252,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(nbytes / ffn_s / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = traffic_from_profile(shape)
     roof["kernel"] = ("moe_expert_ffn: grouped GEMM1 (+GELU) and GEMM2 over the ragged expert "
                       "blocks" + (" and the shared expert" if cfg.d_ff_shared else ""))
     roof["per_launch"] = {"flops": flops, "min_bytes": nbytes, "rows": M,

@@ -118,7 +118,8 @@ int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double capacity_f
  *            NaN scores order as -inf.
  *   topk_w   [dev] [T, K] fp32 out: softmax over the K chosen unbiased logits
  *            (computed in fp64, rounded once).
- *   ws       may be NULL (needs 0 bytes). */
+ *   ws       [dev] >= moe_workspace_size(cfg, MOE_STAGE_ROUTE) bytes (fp64
+ *            partial dot products). */
 int moe_route(const moe_config_t *cfg, const void *x, const moe_weights_t *w, float *logits,
               int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
               hipStream_t stream);

@@ -13,8 +13,9 @@
 // one token row at a time (lane = expert, up to 4 experts per lane), forms
 // the row's softmax and adds it to per-lane sums; the 4 wavefronts' sums are
 // added in wavefront order into ppart[block, e].
-// Pass 2: one workgroup adds ppart over blocks in block order per expert,
-// multiplies by f_e and reduces over experts with a fixed tree.
+// Pass 2: one workgroup; a wavefront per expert adds ppart over the blocks
+// (lanes stride over blocks, then a fixed butterfly), multiplies by f_e, and
+// the experts' terms are reduced with a fixed tree.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -66,21 +67,25 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict
                                                         const int32_t* __restrict__ counts, int T,
                                                         int N, float alpha,
                                                         float* __restrict__ loss) {
-  __shared__ double red[256];
-  const int e = threadIdx.x;
-  double term = 0.0;
-  if (e < N) {
+  __shared__ double term[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wavefront w takes experts w, w+4, ...; its lanes stride over the blocks
+  // (each lane sums its blocks in order, then a fixed butterfly)
+  for (int e = wave; e < N; e += 4) {
     double P = 0.0;
-    for (int b = 0; b < nblk; ++b) P += ppart[(int64_t)b * N + e];
-    term = ((double)counts[e] / (double)T) * (P / (double)T);
+    for (int b = lane; b < nblk; b += 64) P += ppart[(int64_t)b * N + e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) P += __shfl_xor(P, off, 64);
+    if (lane == 0) term[e] = ((double)counts[e] / (double)T) * (P / (double)T);
   }
-  red[e] = term;
+  __syncthreads();
+  if (threadIdx.x >= N) term[threadIdx.x] = 0.0;
   __syncthreads();
   for (int h = 128; h >= 1; h >>= 1) {
-    if (e < h) red[e] += red[e + h];
+    if (threadIdx.x < h) term[threadIdx.x] += term[threadIdx.x + h];
     __syncthreads();
   }
-  if (e == 0) loss[0] = (float)((double)alpha * (double)N * red[0]);
+  if (threadIdx.x == 0) loss[0] = (float)((double)alpha * (double)N * term[0]);
 }
 
 }  // namespace

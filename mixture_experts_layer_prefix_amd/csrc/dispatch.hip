@@ -166,17 +166,44 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
   }
 }
 
-// One workgroup: tiles of BM rows over each expert's kept block.
-__global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict__ offsets, int N,
-                                                       int BM, int2* __restrict__ map,
-                                                       int32_t* __restrict__ count) {
+// Tile list of a grouped GEMM (one workgroup; thread e owns expert e).
+// Shared-problem tiles come first, then expert by expert.  Within an expert
+// (or the shared problem) with mt m-tiles, tiles go in windows of about 32
+// -- one XCD's worth of CUs: groups of gm = min(mt, 8) m-tiles by bands of
+// max(1, 32 / gm) n-tiles, m fastest, so the tiles of a window read each
+// weight tile once and each activation panel once between them.
+__device__ __forceinline__ int4 band_tile(int j, int mt, int ntn, int BN, int e, int o0, int o1,
+                                          int BM) {
+  const int gm = min(mt, 8);
+  const int g = j / (gm * ntn), r0 = j % (gm * ntn);       // m-group, index inside it
+  const int gsz = min(gm, mt - g * gm);                      // m-tiles in this group
+  const int band = max(1, 32 / gm);
+  const int b = r0 / (band * gsz), r = r0 % (band * gsz);
+  const int nt = b * band + r / gsz, i = g * gm + r % gsz;
+  (void)ntn;
+  return make_int4(e, o0 + i * BM, min(o0 + (i + 1) * BM, o1), nt * BN);
+}
+
+__global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restrict__ offsets, int N,
+                                                        int BM, int BN, int Nd, int Ts,
+                                                        int4* __restrict__ list,
+                                                        int32_t* __restrict__ count) {
   __shared__ int wsum[4];
+  __shared__ int s_base[MAXN + 1], s_mt[MAXN], s_o0[MAXN], s_o1[MAXN];
   const int e = threadIdx.x;
-  int o0 = 0, n = 0;
+  const int ntn = (Nd + BN - 1) / BN;
+  const int ms = (Ts + BM - 1) / BM;
+  const int shared_tiles = ms * ntn;
+  int o0 = 0, o1 = 0, mt = 0;
   if (e < N) {
     o0 = offsets[e];
-    n = (offsets[e + 1] - o0 + BM - 1) / BM;
+    o1 = offsets[e + 1];
+    mt = (o1 - o0 + BM - 1) / BM;
+    s_mt[e] = mt;
+    s_o0[e] = o0;
+    s_o1[e] = o1;
   }
+  const int n = mt * ntn;
   const int lane = e & 63, wave = e >> 6;
   int v = n;
 #pragma unroll
@@ -186,11 +213,27 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const int32_t* __restrict
   }
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  const int start = base + v - n;
-  for (int i = 0; i < n; ++i) map[start + i] = make_int2(e, o0 + i * BM);
-  if (e == N - 1) count[0] = start + n;
+  int base = 0, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) base += wsum[w];
+    total += wsum[w];
+  }
+  if (e < N) s_base[e] = base + v - n;
+  if (e == 0) s_base[N] = total;
+  __syncthreads();
+  // every thread writes tiles: find the expert owning routed tile j (the last
+  // expert whose first tile is <= j; experts without tiles share the next base)
+  for (int j = threadIdx.x; j < total; j += blockDim.x) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_base[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    list[shared_tiles + j] = band_tile(j - s_base[lo], s_mt[lo], ntn, BN, lo, s_o0[lo], s_o1[lo], BM);
+  }
+  for (int j = threadIdx.x; j < shared_tiles; j += blockDim.x)
+    list[j] = band_tile(j, ms, ntn, BN, -1, 0, Ts, BM);
+  if (threadIdx.x == 0) count[0] = shared_tiles + total;
 }
 
 }  // namespace
@@ -212,9 +255,10 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
   return hipGetLastError();
 }
 
-hipError_t launch_tile_map(const int32_t* offsets, int N, int BM, int2* map, int32_t* count,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(tile_map_kernel, dim3(1), dim3(256), 0, s, offsets, N, BM, map, count);
+hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
+                            int4* list, int32_t* count, hipStream_t s) {
+  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(256), 0, s, offsets, N, BM, BN, Nd, Ts, list,
+                     count);
   return hipGetLastError();
 }
 

@@ -68,7 +68,7 @@ __device__ __forceinline__ void wait_stages(int ahead) {
 template <bool GELU>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
   static_assert(NST == 4, "wait_stages assumes up to 2 younger stages in flight");
-  const TileRef tr = map_tile<BM, BN>(a);
+  const TileRef tr = map_tile(a);
   if (!tr.valid) return;
 
   __shared__ __attribute__((aligned(1024))) uint16_t lds[NST * STAGE];
@@ -212,9 +212,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
 }  // namespace
 
 int gemm_bf16_bm() { return BM; }
+int gemm_bf16_bn() { return BN; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
-  const int grid = gemm_grid(a, BM, BN);
+  const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
   if (gelu)
     hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(grid), dim3(NTHR), 0, s, a);

@@ -14,7 +14,7 @@ constexpr int BM = 64, BN = 64, BK = 16, NTHR = 256;
 
 template <bool GELU>
 __global__ __launch_bounds__(NTHR) void gemm_f32_kernel(GemmArgs a) {
-  const TileRef tr = map_tile<BM, BN>(a);
+  const TileRef tr = map_tile(a);
   if (!tr.valid) return;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
@@ -79,9 +79,10 @@ __global__ __launch_bounds__(NTHR) void gemm_f32_kernel(GemmArgs a) {
 }  // namespace
 
 int gemm_f32_bm() { return BM; }
+int gemm_f32_bn() { return BN; }
 
 hipError_t launch_gemm_f32(const GemmArgs& a, bool gelu, hipStream_t s) {
-  const int grid = gemm_grid(a, BM, BN);
+  const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
   if (gelu)
     hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid), dim3(NTHR), 0, s, a);

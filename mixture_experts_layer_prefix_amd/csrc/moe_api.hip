@@ -62,6 +62,11 @@ GemmPath gemm_path(const moe_config_t* c) {
 int gemm_bm(const moe_config_t* c) {
   return gemm_path(c) == PATH_F32 ? moe::gemm_f32_bm() : moe::gemm_bf16_bm();
 }
+int gemm_bn(const moe_config_t* c) {
+  return gemm_path(c) == PATH_F32 ? moe::gemm_f32_bn() : moe::gemm_bf16_bn();
+}
+// The shared expert rides in the routed launches when its width matches.
+bool fuse_shared(const moe_config_t* c) { return c->d_ff_shared > 0 && c->d_ff_shared == c->d_ff; }
 
 struct Carver {
   char* base;
@@ -74,13 +79,17 @@ struct Carver {
   }
 };
 
+struct RouteWs {
+  double* part;         // fp64 partial dot products, one slab per model-dim slice
+};
 struct DispatchWs {
   int32_t* blkcnt;
   int32_t* blkoff;
 };
 struct FfnWs {
-  int2* tile_map;
-  int32_t* tile_count;
+  int4* list[4];        // tile lists: GEMM1, GEMM2, shared GEMM1, shared GEMM2
+  int64_t bound[4];     // their capacities (tiles)
+  int32_t* count;       // [4] tile counts
   void* h;
   void* h_shared;
 };
@@ -99,10 +108,16 @@ struct LayerWs {
   void* x_perm;
   void* y_perm;
   void* y_shared;
+  RouteWs route;
   DispatchWs disp;
   FfnWs ffn;
   AuxWs aux;
 };
+
+void carve_route(Carver& cv, const moe_config_t* c, RouteWs* w) {
+  const int S = moe::route_splits(c->T, c->d_model, c->n_experts);
+  w->part = cv.take<double>((size_t)S * c->T * c->n_experts * sizeof(double));
+}
 
 void carve_dispatch(Carver& cv, const moe_config_t* c, DispatchWs* w) {
   const size_t n = (size_t)moe::dispatch_blocks(c->T) * c->n_experts * sizeof(int32_t);
@@ -113,9 +128,16 @@ void carve_dispatch(Carver& cv, const moe_config_t* c, DispatchWs* w) {
 void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w) {
   const int64_t mmax = (int64_t)c->T * c->top_k;
   const size_t eb = elem_bytes(c->dtype);
-  const int tiles = moe::max_m_tiles(mmax, c->n_experts, gemm_bm(c));
-  w->tile_map = cv.take<int2>((size_t)tiles * sizeof(int2));
-  w->tile_count = cv.take<int32_t>(sizeof(int32_t));
+  const int N = c->n_experts, bm = gemm_bm(c), bn = gemm_bn(c);
+  const int ts = fuse_shared(c) ? c->T : 0;
+  const int tsu = (c->d_ff_shared && !fuse_shared(c)) ? c->T : 0;
+  w->bound[0] = moe::max_tiles(mmax, N, ts, bm, bn, c->d_ff);
+  w->bound[1] = moe::max_tiles(mmax, N, ts, bm, bn, c->d_model);
+  w->bound[2] = tsu ? moe::max_tiles(0, 0, tsu, bm, bn, c->d_ff_shared) : 0;
+  w->bound[3] = tsu ? moe::max_tiles(0, 0, tsu, bm, bn, c->d_model) : 0;
+  for (int i = 0; i < 4; ++i)
+    w->list[i] = cv.take<int4>((size_t)(w->bound[i] > 0 ? w->bound[i] : 1) * sizeof(int4));
+  w->count = cv.take<int32_t>(4 * sizeof(int32_t));
   w->h = cv.take<void>((size_t)mmax * c->d_ff * eb);
   w->h_shared = c->d_ff_shared ? cv.take<void>((size_t)c->T * c->d_ff_shared * eb) : nullptr;
 }
@@ -138,6 +160,7 @@ void carve_layer(Carver& cv, const moe_config_t* c, LayerWs* w) {
   w->x_perm = cv.take<void>((size_t)mmax * c->d_model * eb);
   w->y_perm = cv.take<void>((size_t)mmax * c->d_model * eb);
   w->y_shared = c->d_ff_shared ? cv.take<void>((size_t)T * c->d_model * eb) : nullptr;
+  carve_route(cv, c, &w->route);
   carve_dispatch(cv, c, &w->disp);
   carve_ffn(cv, c, &w->ffn);
   carve_aux(cv, c, &w->aux);
@@ -146,9 +169,13 @@ void carve_layer(Carver& cv, const moe_config_t* c, LayerWs* w) {
 size_t stage_bytes(const moe_config_t* c, moe_stage_t stage) {
   Carver cv{nullptr};
   switch (stage) {
-    case MOE_STAGE_ROUTE:
     case MOE_STAGE_COMBINE:
       return 0;
+    case MOE_STAGE_ROUTE: {
+      RouteWs w;
+      carve_route(cv, c, &w);
+      return cv.off;
+    }
     case MOE_STAGE_DISPATCH: {
       DispatchWs w;
       carve_dispatch(cv, c, &w);
@@ -213,9 +240,9 @@ int hip_status(hipError_t e, const char* where) {
 
 // ---------------------------------------------------------------- stages (checked)
 int do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
-             int32_t* idx, float* tw, hipStream_t s) {
+             int32_t* idx, float* tw, const RouteWs& rw, hipStream_t s) {
   return hip_status(moe::launch_route(c->dtype, x, w->w_router, w->b_router, w->logit_offset,
-                                      w->sel_bias, logits, idx, tw, c->T, c->d_model,
+                                      w->sel_bias, logits, idx, tw, rw.part, c->T, c->d_model,
                                       c->n_experts, c->top_k, s),
                     "moe_route launch");
 }
@@ -230,41 +257,44 @@ int do_dispatch(const moe_config_t* c, const int32_t* idx, const void* x, int32_
       "moe_dispatch launch");
 }
 
-hipError_t run_gemm(GemmPath path, const moe::GemmArgs& a, bool gelu, hipStream_t s) {
-  switch (path) {
-    case PATH_F32:
-      return moe::launch_gemm_f32(a, gelu, s);
-    case PATH_SKINNY:
-      return moe::launch_gemm_skinny_bf16(a, gelu, 0, s);
-    default:
-      return moe::launch_gemm_bf16(a, gelu, s);
-  }
-}
-
 int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
            const moe_weights_t* w, const void* x, void* y_perm, void* y_shared, const FfnWs& fw,
            hipStream_t s) {
   const GemmPath path = gemm_path(c);
-  const int64_t mmax = (int64_t)c->T * c->top_k;
-  const int N = c->n_experts;
+  const int N = c->n_experts, T = c->T;
   const bool has_shared = c->d_ff_shared > 0;
-  hipError_t e = hipSuccess;
-  if (path != PATH_SKINNY) {
-    e = moe::launch_tile_map(offsets, N, gemm_bm(c), fw.tile_map, fw.tile_count, s);
-    if (e != hipSuccess) return hip_status(e, "tile map launch");
-  }
+  const bool fused = fuse_shared(c);
+  const int bm = gemm_bm(c), bn = gemm_bn(c);
+
+  // One GEMM launch: build its tile list (tiled kernels), then run it.
+  auto gemm = [&](moe::GemmArgs g, int list, const int32_t* offs, int Nr, int Ts, bool gelu,
+                  const char* what) -> int {
+    hipError_t e = hipSuccess;
+    if (path != PATH_SKINNY) {
+      e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, fw.list[list], fw.count + list, s);
+      if (e != hipSuccess) return hip_status(e, "tile list launch");
+      g.tile_list = fw.list[list];
+      g.tile_count = fw.count + list;
+      g.grid_tiles = fw.bound[list];
+    }
+    if (path == PATH_F32)
+      e = moe::launch_gemm_f32(g, gelu, s);
+    else if (path == PATH_SKINNY)
+      e = moe::launch_gemm_skinny_bf16(g, gelu, 0, s);
+    else
+      e = moe::launch_gemm_bf16(g, gelu, s);
+    return e == hipSuccess ? MOE_OK : hip_status(e, what);
+  };
+
   moe::GemmArgs g1{};
   g1.A = x_perm;
   g1.W = w->w1;
   g1.bias = w->b1;
   g1.C = fw.h;
   g1.offsets = offsets;
-  g1.tile_map = path == PATH_SKINNY ? nullptr : fw.tile_map;
-  g1.tile_count = fw.tile_count;
   g1.Kd = c->d_model;
   g1.Nd = c->d_ff;
   g1.E = N;
-  g1.max_tiles = moe::max_m_tiles(mmax, N, gemm_bm(c));
   moe::GemmArgs g2 = g1;
   g2.A = fw.h;
   g2.W = w->w2;
@@ -272,43 +302,37 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
   g2.C = y_perm;
   g2.Kd = c->d_ff;
   g2.Nd = c->d_model;
-
-  // The shared expert rides in the same launch when its width matches.
   moe::GemmArgs s1{}, s2{};
-  const bool fuse_shared = has_shared && c->d_ff_shared == c->d_ff;
   if (has_shared) {
     s1.As = x;
     s1.Ws = w->ws1;
     s1.Cs = fw.h_shared;
-    s1.Ts = c->T;
+    s1.Ts = T;
     s1.Kd = c->d_model;
     s1.Nd = c->d_ff_shared;
-    s1.E = 0;
     s2 = s1;
     s2.As = fw.h_shared;
     s2.Ws = w->ws2;
     s2.Cs = y_shared;
     s2.Kd = c->d_ff_shared;
     s2.Nd = c->d_model;
-    if (fuse_shared) {
-      g1.As = s1.As; g1.Ws = s1.Ws; g1.Cs = s1.Cs; g1.Ts = s1.Ts;
-      g2.As = s2.As; g2.Ws = s2.Ws; g2.Cs = s2.Cs; g2.Ts = s2.Ts;
+    if (fused) {
+      g1.As = s1.As; g1.Ws = s1.Ws; g1.Cs = s1.Cs; g1.Ts = T;
+      g2.As = s2.As; g2.Ws = s2.Ws; g2.Cs = s2.Cs; g2.Ts = T;
     }
   }
-  // Shared problems that cannot share the launch run on their own, with the
-  // same kernel family (the skinny kernel treats "expert E" as the shared one).
-  const GemmPath spath = path;
-  e = run_gemm(path, g1, true, s);
-  if (e != hipSuccess) return hip_status(e, "expert GEMM1 launch");
-  if (has_shared && !fuse_shared) {
-    e = run_gemm(spath, s1, true, s);
-    if (e != hipSuccess) return hip_status(e, "shared GEMM1 launch");
+  const int tsf = fused ? T : 0;
+  int r = gemm(g1, 0, offsets, N, tsf, true, "expert GEMM1 launch");
+  if (r != MOE_OK) return r;
+  if (has_shared && !fused) {
+    r = gemm(s1, 2, nullptr, 0, T, true, "shared GEMM1 launch");
+    if (r != MOE_OK) return r;
   }
-  e = run_gemm(path, g2, false, s);
-  if (e != hipSuccess) return hip_status(e, "expert GEMM2 launch");
-  if (has_shared && !fuse_shared) {
-    e = run_gemm(spath, s2, false, s);
-    if (e != hipSuccess) return hip_status(e, "shared GEMM2 launch");
+  r = gemm(g2, 1, offsets, N, tsf, false, "expert GEMM2 launch");
+  if (r != MOE_OK) return r;
+  if (has_shared && !fused) {
+    r = gemm(s2, 3, nullptr, 0, T, false, "shared GEMM2 launch");
+    if (r != MOE_OK) return r;
   }
   return MOE_OK;
 }
@@ -383,8 +407,6 @@ int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double cf) {
 
 int moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w, float* logits,
               int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   MOE_CHECK_CFG(cfg);
   MOE_REQUIRE_PTR(x, "x");
   int r = check_weights(cfg, w, true, false);
@@ -392,7 +414,12 @@ int moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w, fl
   MOE_OPTIONAL_PTR(logits, "logits");
   MOE_REQUIRE_PTR(topk_idx, "topk_idx");
   MOE_REQUIRE_PTR(topk_w, "topk_w");
-  return do_route(cfg, x, w, logits, topk_idx, topk_w, stream);
+  r = check_ws(cfg, MOE_STAGE_ROUTE, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  RouteWs rw;
+  carve_route(cv, cfg, &rw);
+  return do_route(cfg, x, w, logits, topk_idx, topk_w, rw, stream);
 }
 
 int moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, const void* x,
@@ -482,7 +509,7 @@ int moe_layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_
   int32_t* counts = counts_out ? counts_out : lw.counts;
   int32_t* ndrop = n_dropped_out ? n_dropped_out : lw.n_dropped;
 
-  r = do_route(cfg, x, w, lw.logits, lw.idx, lw.w, stream);
+  r = do_route(cfg, x, w, lw.logits, lw.idx, lw.w, lw.route, stream);
   if (r != MOE_OK) return r;
   r = do_dispatch(cfg, lw.idx, x, counts, lw.offsets, lw.slot_row, lw.row_token, lw.x_perm,
                   ndrop, lw.disp, stream);

@@ -59,11 +59,14 @@ template <> struct Elem<uint16_t> {
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch(es).
 
-// Router logits (fp64 accumulation) + Top-K + softmax over the K chosen.
+// Router logits (fp64 MFMA, split over the model dimension) + Top-K +
+// softmax over the K chosen.  `part` holds route_splits(T, d, N) * T * N
+// doubles.
+int route_splits(int T, int d, int N);
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* b_router,
                         const float* logit_offset, const float* sel_bias, float* logits,
-                        int32_t* topk_idx, float* topk_w, int T, int d, int N, int K,
-                        hipStream_t s);
+                        int32_t* topk_idx, float* topk_w, double* part, int T, int d, int N,
+                        int K, hipStream_t s);
 
 // Dispatch: histogram, scan, stable rank and row copy.
 constexpr int kDispatchTokensPerBlock = 256;
@@ -73,11 +76,17 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
                            int32_t* slot_row, int32_t* row_token, void* x_perm,
                            int32_t* n_dropped, int32_t* blkcnt, int32_t* blkoff, hipStream_t s);
 
-// Tile map over the ragged expert blocks: for each BM-row tile, (expert, first row).
-hipError_t launch_tile_map(const int32_t* offsets, int N, int BM, int2* map, int32_t* count,
-                           hipStream_t s);
+// Tile list of a grouped GEMM with BM x BN tiles over Nd output columns: one
+// int4 {expert (-1: shared problem), first row, end row, first column} per
+// workgroup tile, shared-problem tiles first, then expert by expert; count[0]
+// receives the number of tiles.
+hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
+                            int4* list, int32_t* count, hipStream_t s);
 inline int max_m_tiles(int64_t M_max, int N, int BM) {
   return static_cast<int>((M_max + BM - 1) / BM) + N;
+}
+inline int64_t max_tiles(int64_t M_max, int N, int Ts, int BM, int BN, int Nd) {
+  return ((int64_t)max_m_tiles(M_max, N, BM) + (Ts + BM - 1) / BM) * ((Nd + BN - 1) / BN);
 }
 
 // Arguments of one grouped GEMM C = A . W_e^T (+ bias_e) (GELU) over the
@@ -87,8 +96,8 @@ struct GemmArgs {
   const void* W;        // [E, Nd, Kd] stacked weights
   const void* bias;     // [E, Nd] or null
   void* C;              // [rows, Nd]
-  const int32_t* offsets;   // [E+1]
-  const int2* tile_map;     // routed tiles
+  const int32_t* offsets;   // [E+1] (skinny and fp32 kernels)
+  const int4* tile_list;    // tiled kernels: tiles in execution order
   const int32_t* tile_count;
   const void* As;       // shared problem: [Ts, Kd] (null if none)
   const void* Ws;       // [Nd, Kd]
@@ -96,14 +105,16 @@ struct GemmArgs {
   int Ts;
   int Kd, Nd;
   int E;
-  int max_tiles;        // grid rows reserved for routed tiles
+  int64_t grid_tiles;   // upper bound on the tile count (grid size)
 };
 
 // Prefill-shaped grouped GEMM (bf16 MFMA), BM rows per tile.
 int gemm_bf16_bm();
+int gemm_bf16_bn();
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s);
 // fp32 grouped GEMM (VALU), BM rows per tile.
 int gemm_f32_bm();
+int gemm_f32_bn();
 hipError_t launch_gemm_f32(const GemmArgs& a, bool gelu, hipStream_t s);
 // Decode-shaped grouped GEMM (bf16): streams each touched expert's weights once.
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int max_rows_per_expert,

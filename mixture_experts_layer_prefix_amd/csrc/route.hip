@@ -1,4 +1,4 @@
-// Router scoring fused with Top-K selection and the softmax over the K chosen
+// Router scoring, then Top-K selection and the softmax over the K chosen
 // logits.
 //
 // What it computes (lmnt.cn MoE walkthrough §2.1, gate scoring equation
@@ -15,11 +15,18 @@
 //                NaN ordering as -inf;
 //   w[t,k]     = exp(logit[idx_k] - max) / sum over the K chosen, in fp64.
 //
-// Layout: one workgroup of 256 threads owns RT = 16 tokens and all N <= 256
-// experts.  The logits tile [16, NPAD] is accumulated in fp64 registers
-// (each thread 4x4 outputs, split-K across threads when N is small), reduced
-// in a fixed order through LDS, and kept in LDS; then each wavefront selects
-// the Top-K of one token row at a time with a 64-lane arg-max reduction.
+// Two kernels:
+//   1. router GEMM on the fp64 matrix cores (v_mfma_f64_16x16x4f64): each
+//      workgroup takes a tile of tokens x experts and one slice of the model
+//      dimension, and writes fp64 partial dot products.  The slice count S
+//      is chosen so that even a handful of tokens fills the chip; S = 1 for
+//      large batches.  Each lane feeds the MFMA from 16 consecutive elements
+//      of its row (one 32- or 64-byte load), so the k order inside a 64-wide
+//      chunk is permuted identically for x and W_r -- the dot product does
+//      not depend on it;
+//   2. select: one wavefront per token sums the S partials in slice order,
+//      adds the router bias and offset in fp64, rounds once to fp32, writes
+//      the logits, and picks the Top-K with a 64-lane arg-max reduction.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -27,195 +34,244 @@
 namespace moe {
 namespace {
 
-constexpr int RT = 16;     // tokens per workgroup
-constexpr int KC = 16;     // reduction chunk staged in LDS
-constexpr int NTHR = 256;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+constexpr int KC = 64;   // model-dimension chunk per iteration (16 per lane group)
+
+template <typename T>
+struct Row16;
+// 16 consecutive bf16 (8 dwords)
+template <>
+struct Row16<uint16_t> {
+  uint4 v[2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    v[0] = reinterpret_cast<const uint4*>(p)[0];
+    v[1] = reinterpret_cast<const uint4*>(p)[1];
+  }
+  __device__ __forceinline__ double get(int i) const {
+    const uint32_t w = (i < 8 ? (&v[0].x)[i >> 1] : (&v[1].x)[(i - 8) >> 1]);
+    const uint32_t b = (i & 1) ? (w & 0xffff0000u) : (w << 16);
+    return (double)__uint_as_float(b);
+  }
+};
+// 16 consecutive fp32 (16 dwords)
+template <>
+struct Row16<float> {
+  uint4 v[4];
+  __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const uint4*>(p)[i];
+  }
+  __device__ __forceinline__ double get(int i) const {
+    return (double)__uint_as_float((&v[i >> 2].x)[i & 3]);
+  }
+};
+
+// Workgroup: 4 wavefronts stacked along tokens; wavefront tile = (WT*16)
+// tokens x (WE*16) experts.  grid = (token tiles, expert tiles, slices).
+template <typename T, int WT, int WE>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const T* __restrict__ x,
+                                                          const T* __restrict__ wr,
+                                                          double* __restrict__ part, int Ttok,
+                                                          int d, int N, int klen) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = (blockIdx.x * 4 + wave) * WT * 16;
+  const int e0 = blockIdx.y * WE * 16;
+  const int kb = blockIdx.z * klen, ke = min(d, kb + klen);
+  if (t0 >= Ttok) return;
+  const int g = lane >> 4;        // lane group: k offset 16*g inside a chunk
+  const int r = lane & 15;        // row inside a 16-row MFMA tile
+
+  const T* xrow[WT];
+  const T* wrow[WE];
+#pragma unroll
+  for (int i = 0; i < WT; ++i) xrow[i] = x + (int64_t)min(t0 + i * 16 + r, Ttok - 1) * d + g * 16;
+#pragma unroll
+  for (int j = 0; j < WE; ++j) wrow[j] = wr + (int64_t)min(e0 + j * 16 + r, N - 1) * d + g * 16;
+
+  f64x4 acc[WT][WE];
+#pragma unroll
+  for (int i = 0; i < WT; ++i)
+#pragma unroll
+    for (int j = 0; j < WE; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  for (int k0 = kb; k0 < ke; k0 += KC) {
+    Row16<T> xa[WT], wb[WE];
+#pragma unroll
+    for (int i = 0; i < WT; ++i) xa[i].load(xrow[i] + k0);
+#pragma unroll
+    for (int j = 0; j < WE; ++j) wb[j].load(wrow[j] + k0);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      double a[WT], b[WE];
+#pragma unroll
+      for (int i = 0; i < WT; ++i) a[i] = xa[i].get(s);
+#pragma unroll
+      for (int j = 0; j < WE; ++j) b[j] = wb[j].get(s);
+#pragma unroll
+      for (int i = 0; i < WT; ++i)
+#pragma unroll
+        for (int j = 0; j < WE; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // 16x16 fp64 accumulator: element v of lane l is row 4*v + l/16, column l%16.
+  double* out = part + (int64_t)blockIdx.z * Ttok * N;
+#pragma unroll
+  for (int i = 0; i < WT; ++i)
+#pragma unroll
+    for (int j = 0; j < WE; ++j) {
+      const int e = e0 + j * 16 + r;
+      if (e >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + i * 16 + v * 4 + g;
+        if (t < Ttok) out[(int64_t)t * N + e] = acc[i][j][v];
+      }
+    }
+}
 
 __device__ __forceinline__ bool better(float sa, int ea, float sb, int eb) {
   return sa > sb || (sa == sb && ea < eb);
 }
 
-template <typename T, int NPAD, int TI, int TJ>
-__global__ __launch_bounds__(NTHR) void route_kernel(
-    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ b_router,
+// One wavefront per token (4 per workgroup); lane = expert (4 per lane, N <= 256).
+__global__ __launch_bounds__(256) void select_kernel(
+    const double* __restrict__ part, int S, const float* __restrict__ b_router,
     const float* __restrict__ logit_offset, const float* __restrict__ sel_bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int Ttok, int d, int N, int K) {
-  constexpr int TG = RT / TI;             // token groups
-  constexpr int EG = NPAD / TJ;           // expert groups
-  constexpr int S = NTHR / (TG * EG);     // split of each chunk across threads
-  static_assert(TG * EG * S == NTHR, "thread tiling");
-  static_assert(KC % S == 0, "split must divide the chunk");
-
-  struct Tiles {
-    double xs[RT][KC + 1];
-    double ws[NPAD][KC + 1];
-  };
-  __shared__ union {
-    Tiles t;
-    double part[S][RT * NPAD];
-  } sm;
-  __shared__ float lg[RT][NPAD];
-
-  const int tid = threadIdx.x;
-  const int sidx = tid / (TG * EG);
-  const int rem = tid % (TG * EG);
-  const int tg = rem / EG;
-  const int eg = rem % EG;
-  const int t0 = blockIdx.x * RT;
-
-  double acc[TI][TJ];
+    int Ttok, int N, int K) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Ttok) return;
+  const int lane = threadIdx.x & 63;
+  float lg[4], sc[4];
+  bool taken[4];
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = 0.0;
-
-  for (int k0 = 0; k0 < d; k0 += KC) {
-    for (int i = tid; i < RT * KC; i += NTHR) {
-      const int tt = i / KC, kk = i % KC, t = t0 + tt;
-      sm.t.xs[tt][kk] = (t < Ttok) ? (double)Elem<T>::load(x, (int64_t)t * d + k0 + kk) : 0.0;
-    }
-    for (int i = tid; i < NPAD * KC; i += NTHR) {
-      const int e = i / KC, kk = i % KC;
-      sm.t.ws[e][kk] = (e < N) ? (double)Elem<T>::load(wr, (int64_t)e * d + k0 + kk) : 0.0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < KC / S; ++q) {
-      const int kk = sidx + q * S;
-      double xv[TI], wv[TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) xv[i] = sm.t.xs[tg + TG * i][kk];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) wv[j] = sm.t.ws[eg + EG * j][kk];
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = fma(xv[i], wv[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) sm.part[sidx][(tg + TG * i) * NPAD + eg + EG * j] = acc[i][j];
-  __syncthreads();
-
-  for (int o = tid; o < RT * NPAD; o += NTHR) {
-    const int tt = o / NPAD, e = o % NPAD, t = t0 + tt;
-    float v = -INFINITY;
+  for (int v = 0; v < 4; ++v) {
+    const int e = lane + 64 * v;
+    lg[v] = -INFINITY;
+    sc[v] = -INFINITY;
+    taken[v] = false;
     if (e < N) {
-      double z = sm.part[0][o];
-      for (int q = 1; q < S; ++q) z += sm.part[q][o];
+      double z = part[(int64_t)t * N + e];
+      for (int s = 1; s < S; ++s) z += part[((int64_t)s * Ttok + t) * N + e];
       if (b_router) z += (double)b_router[e];
       if (logit_offset) z += (double)logit_offset[e];
-      v = (float)z;
-      if (logits && t < Ttok) logits[(int64_t)t * N + e] = v;
+      lg[v] = (float)z;
+      if (logits) logits[(int64_t)t * N + e] = lg[v];
+      float sv = lg[v];
+      if (sel_bias) sv = __fadd_rn(sv, sel_bias[e]);
+      sc[v] = isnan(sv) ? -INFINITY : sv;
     }
-    lg[tt][e] = v;
   }
-  __syncthreads();
-
-  // ---- Top-K + softmax over the K chosen: one wavefront per token row.
-  constexpr int VPL = (NPAD + 63) / 64;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  for (int tt = wave; tt < RT; tt += NTHR / 64) {
-    const int t = t0 + tt;
-    if (t >= Ttok) break;
-    float sc[VPL];
-    bool taken[VPL];
+  int my_e = 0;
+  float my_logit = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float bs = -INFINITY, bl = 0.f;
+    int be = 0x7fffffff;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
+    for (int v = 0; v < 4; ++v) {
       const int e = lane + 64 * v;
-      float s = -INFINITY;
-      if (e < N) {
-        s = lg[tt][e];
-        if (sel_bias) s = __fadd_rn(s, sel_bias[e]);
-        if (isnan(s)) s = -INFINITY;
-      }
-      sc[v] = s;
-      taken[v] = false;
-    }
-    int my_e = 0;
-    float my_logit = 0.f;
-    for (int k = 0; k < K; ++k) {
-      float bs = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const int e = lane + 64 * v;
-        if (!taken[v] && better(sc[v], e, bs, be)) {
-          bs = sc[v];
-          be = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float os = __shfl_xor(bs, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (better(os, oe, bs, be)) {
-          bs = os;
-          be = oe;
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        if (lane + 64 * v == be) taken[v] = true;
-      if (lane == k) {
-        my_e = be;
-        my_logit = lg[tt][min(be, NPAD - 1)];
+      if (e < N && !taken[v] && better(sc[v], e, bs, be)) {
+        bs = sc[v];
+        be = e;
+        bl = lg[v];
       }
     }
-    double m = (lane < K) ? (double)my_logit : -INFINITY;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
-    double ex = (lane < K) ? exp((double)my_logit - m) : 0.0;
-    double sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if (lane < K) {
-      topk_idx[(int64_t)t * K + lane] = my_e;
-      topk_w[(int64_t)t * K + lane] = (float)(ex / sum);
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float os = __shfl_xor(bs, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      const float ol = __shfl_xor(bl, off, 64);
+      if (better(os, oe, bs, be)) {
+        bs = os;
+        be = oe;
+        bl = ol;
+      }
     }
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (lane + 64 * v == be) taken[v] = true;
+    if (lane == k) {
+      my_e = be;
+      my_logit = bl;
+    }
+  }
+  double m = (lane < K) ? (double)my_logit : -INFINITY;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+  const double ex = (lane < K) ? exp((double)my_logit - m) : 0.0;
+  double sum = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane < K) {
+    topk_idx[(int64_t)t * K + lane] = my_e;
+    topk_w[(int64_t)t * K + lane] = (float)(ex / sum);
   }
 }
 
-template <typename E, int NPAD, int TI, int TJ>
-hipError_t launch_t(const void* x, const void* wr, const float* br, const float* off,
-                    const float* sb, float* logits, int32_t* idx, float* w, int T, int d, int N,
-                    int K, hipStream_t s) {
-  dim3 grid((T + RT - 1) / RT);
-  hipLaunchKernelGGL((route_kernel<E, NPAD, TI, TJ>), grid, dim3(NTHR), 0, s,
-                     static_cast<const E*>(x), static_cast<const E*>(wr), br, off, sb, logits,
-                     idx, w, T, d, N, K);
-  return hipGetLastError();
+struct Shape {
+  int wt, we, tiles_t, tiles_e;
+};
+Shape shape_for(int T, int N) {
+  Shape s;
+  if (N <= 16) {
+    s.wt = 2;
+    s.we = 1;
+  } else {
+    s.wt = 1;
+    s.we = 4;
+  }
+  s.tiles_t = (T + 4 * s.wt * 16 - 1) / (4 * s.wt * 16);
+  s.tiles_e = (N + s.we * 16 - 1) / (s.we * 16);
+  return s;
 }
 
-template <typename E>
-hipError_t launch_dt(const void* x, const void* wr, const float* br, const float* off,
-                     const float* sb, float* logits, int32_t* idx, float* w, int T, int d, int N,
-                     int K, hipStream_t s) {
-  if (N <= 8) return launch_t<E, 8, 4, 2>(x, wr, br, off, sb, logits, idx, w, T, d, N, K, s);
-  if (N <= 16) return launch_t<E, 16, 4, 4>(x, wr, br, off, sb, logits, idx, w, T, d, N, K, s);
-  if (N <= 32) return launch_t<E, 32, 4, 4>(x, wr, br, off, sb, logits, idx, w, T, d, N, K, s);
-  if (N <= 64) return launch_t<E, 64, 4, 4>(x, wr, br, off, sb, logits, idx, w, T, d, N, K, s);
-  if (N <= 128) return launch_t<E, 128, 4, 4>(x, wr, br, off, sb, logits, idx, w, T, d, N, K, s);
-  return launch_t<E, 256, 4, 4>(x, wr, br, off, sb, logits, idx, w, T, d, N, K, s);
+template <typename T>
+hipError_t launch_gemm_t(const Shape& sh, int S, int klen, const void* x, const void* wr,
+                         double* part, int Ttok, int d, int N, hipStream_t s) {
+  dim3 grid(sh.tiles_t, sh.tiles_e, S);
+  if (sh.we == 1)
+    hipLaunchKernelGGL((router_gemm_kernel<T, 2, 1>), grid, dim3(256), 0, s,
+                       static_cast<const T*>(x), static_cast<const T*>(wr), part, Ttok, d, N,
+                       klen);
+  else
+    hipLaunchKernelGGL((router_gemm_kernel<T, 1, 4>), grid, dim3(256), 0, s,
+                       static_cast<const T*>(x), static_cast<const T*>(wr), part, Ttok, d, N,
+                       klen);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+// Slices of the model dimension: enough workgroups to fill the chip, each
+// slice a whole number of 64-wide chunks, no empty slice.
+int route_splits(int T, int d, int N) {
+  const Shape sh = shape_for(T, N);
+  const int tiles = sh.tiles_t * sh.tiles_e;
+  const int chunks = d / KC;
+  int S = (256 + tiles - 1) / tiles;
+  if (S > chunks) S = chunks;
+  if (S < 1) S = 1;
+  const int per = (chunks + S - 1) / S;
+  return (chunks + per - 1) / per;
+}
+
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* b_router,
                         const float* logit_offset, const float* sel_bias, float* logits,
-                        int32_t* topk_idx, float* topk_w, int T, int d, int N, int K,
-                        hipStream_t s) {
-  if (dtype == 0)
-    return launch_dt<float>(x, w_router, b_router, logit_offset, sel_bias, logits, topk_idx,
-                            topk_w, T, d, N, K, s);
-  return launch_dt<uint16_t>(x, w_router, b_router, logit_offset, sel_bias, logits, topk_idx,
-                             topk_w, T, d, N, K, s);
+                        int32_t* topk_idx, float* topk_w, double* part, int T, int d, int N,
+                        int K, hipStream_t s) {
+  const Shape sh = shape_for(T, N);
+  const int S = route_splits(T, d, N);
+  const int chunks = d / KC;
+  const int klen = ((chunks + S - 1) / S) * KC;
+  hipError_t e = (dtype == 0)
+                     ? launch_gemm_t<float>(sh, S, klen, x, w_router, part, T, d, N, s)
+                     : launch_gemm_t<uint16_t>(sh, S, klen, x, w_router, part, T, d, N, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_kernel, dim3((T + 3) / 4), dim3(256), 0, s, part, S, b_router,
+                     logit_offset, sel_bias, logits, topk_idx, topk_w, T, N, K);
+  return hipGetLastError();
 }
 
 }  // namespace moe

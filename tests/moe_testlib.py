@@ -53,7 +53,7 @@ def run_stages(cfg, t, device="cuda"):
     logits = torch.empty(T, N, **f32)
     idx = torch.empty(T, K, **i32)
     w = torch.empty(T, K, **f32)
-    moe.moe_route(cfg, t["x"], W, logits, idx, w)
+    moe.moe_route(cfg, t["x"], W, logits, idx, w, moe.alloc_workspace(cfg, "route", device))
     counts = torch.empty(N, **i32)
     offsets = torch.empty(N + 1, **i32)
     slot_row = torch.empty(T, K, **i32)

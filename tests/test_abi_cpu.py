@@ -48,7 +48,8 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails it
 
 def _route(cfg, x=FAKE, wr=FAKE, idx=FAKE, w=FAKE):
     W = moe.MoeWeights(w_router=wr)
-    return moe.lib().moe_route(ctypes.byref(cfg), x, ctypes.byref(W), None, idx, w, None, 0, None)
+    return moe.lib().moe_route(ctypes.byref(cfg), x, ctypes.byref(W), None, idx, w, FAKE * 256,
+                               1 << 40, None)
 
 
 @pytest.mark.parametrize("kw, code", [
@@ -103,9 +104,9 @@ def test_null_and_misaligned_pointers_rejected():
 def test_workspace_checks():
     cfg = _cfg()
     L = moe.lib()
-    for stage in ("dispatch", "expert_ffn", "aux", "layer"):
+    for stage in ("route", "dispatch", "expert_ffn", "aux", "layer"):
         assert moe.workspace_size(cfg, stage) > 0
-    assert moe.workspace_size(cfg, "route") == 0 and moe.workspace_size(cfg, "combine") == 0
+    assert moe.workspace_size(cfg, "combine") == 0
     assert moe.workspace_size(cfg, "layer") >= moe.workspace_size(cfg, "expert_ffn")
     need = moe.workspace_size(cfg, "dispatch")
     args = [ctypes.byref(cfg)] + [FAKE] * 8
