@@ -4,29 +4,33 @@
 // the note after it: each expert is Linear -> GELU -> Linear, and production
 // code batches the tokens of one expert into a grouped GEMM):
 //   C[r, n] = epi( sum_k A[r, k] * W_e[n, k] + bias_e[n] ) for every row r of
-//   expert e's block, epi = exact GELU for the first Linear, identity for the
+//   expert e's block, epi = GELU for the first Linear, identity for the
 //   second.  bf16 operands, fp32 accumulation, bf16 result.
 //
 // Design for CDNA4:
-//   - workgroup tile BM x BN = 256 x 256, BK = 32; 4 wavefronts in 2 x 2,
-//     each owning 128 x 128 outputs as 4 x 4 tiles of
-//     v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, one
-//     workgroup per CU), so each LDS byte read feeds 64 MFMA flops;
-//   - operands move global -> LDS with 16-byte direct-to-LDS loads (no
-//     VGPR staging); one wave instruction fills 16 LDS rows of 64 bytes.
-//     The 16-byte chunks of a row are XOR-swizzled (swz below): the lane that
-//     fills physical chunk p of row r loads logical chunk p ^ swz(r), so the
-//     fragment reads (16 bytes per lane, 32 rows per half-wave) hit every
-//     bank exactly once per 16 lanes;
-//   - four LDS stages (4 x 32 KiB): the loads of k-step i+3 are issued while
-//     the MFMAs of step i run, so each load has three k-steps to land; one
-//     barrier per k-step; fragment registers are double-buffered so the LDS
-//     reads of the second k-substep overlap the MFMAs of the first;
+//   - workgroup tile BM x BN = 256 x 256, BK = 32, 8 wavefronts = two groups
+//     of four; the hardware places wavefront w on SIMD w mod 4, so every SIMD
+//     holds one wavefront of each group.  Group g owns output rows
+//     [g*BM/2, (g+1)*BM/2); wavefront j of a group owns columns [64j, 64j+64)
+//     as (BM/64) x 2 tiles of v_mfma_f32_32x32x16_bf16;
+//   - ping-pong: in each k-step, while one group issues its 16 MFMAs from
+//     fragments already in registers (at raised wave priority), the other
+//     group reads its fragments for the next MFMA burst from LDS and issues
+//     its share of the global loads; one barrier per k-step swaps the roles,
+//     so each SIMD's MFMA pipe runs the two groups' bursts back to back while
+//     memory work hides in their shadow;
+//   - operands move global -> LDS with 16-byte direct-to-LDS loads (no VGPR
+//     staging); a wave instruction fills 16 LDS rows of 64 bytes; group 0
+//     loads the A half of a stage, group 1 the W half.  The 16-byte chunks of
+//     a row are XOR-swizzled (swz below) so fragment reads hit every bank
+//     once per 16 lanes;
+//   - four LDS stages (4 x 32 KiB); loads run two to three k-steps ahead;
+//     after the last k-step every lane drains its loads before the epilogue;
 //   - the MFMA takes the weight fragment as its first operand, so each lane
 //     ends up with 4 consecutive output columns of one row and the epilogue
-//     writes 8-byte runs;
-//   - rows past an expert's end read a clamped valid row and are not stored;
-//   - the GELU epilogue uses the Abramowitz-Stegun 7.1.26 erf (gelu_as).
+//     writes 8-byte runs; the GELU epilogue uses the Abramowitz-Stegun 7.1.26
+//     erf (gelu_as);
+//   - rows past an expert's end read a clamped valid row and are not stored.
 #include "gemm_common.h"
 
 namespace moe {
@@ -35,14 +39,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
-constexpr int NTHR = 256;
+constexpr int BN = 256, BK = 32;
+constexpr int NTHR = 512;
 constexpr int CH = BK / 8;                 // 16-byte chunks per LDS row (64-byte rows)
-constexpr int RPI = 64 / CH;               // LDS rows filled by one wave instruction
-constexpr int A_INS = BM / RPI / 4;        // direct loads per lane per stage (A)
-constexpr int B_INS = BN / RPI / 4;        // (B)
-constexpr int LOADS = A_INS + B_INS;       // vector-memory ops per lane per stage
-constexpr int STAGE = (BM + BN) * BK;      // bf16 elements per LDS stage
+constexpr int RPI = 64 / CH;               // LDS rows filled by one wave instruction (16)
+constexpr int LB = BN / RPI / 4;           // direct loads per group-1 wavefront per stage (W half)
 
 // Chunk swizzle of LDS row r (rows of 64 bytes, 4 chunks).  A ds_read_b128
 // serves 16 lanes per cycle over 64 four-byte banks (256 bytes); the 16 lanes
@@ -55,19 +56,18 @@ __device__ __forceinline__ void lds_load16(const uint16_t* g, uint16_t* l) {
                                    16, 0, 0);
 }
 
-// Wait until at most `ahead` stages of this lane's loads are still in flight.
-__device__ __forceinline__ void wait_stages(int ahead) {
-  if (ahead >= 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
-  else if (ahead == 1)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
+// s_barrier with a compiler memory fence: no LDS access moves across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <bool GELU>
+// BM = 256 or 128 rows per tile; each group owns BM/2 rows (MI tiles of 32).
+template <int BM, bool GELU>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
-  static_assert(NST == 4, "wait_stages assumes up to 2 younger stages in flight");
+  constexpr int MI = BM / 64;                 // 32-row MFMA tiles per wavefront
+  constexpr int LA = BM / RPI / 4;            // direct loads per group-0 wavefront (A half)
+  constexpr int STAGE = (BM + BN) * BK;       // bf16 elements per LDS stage
+  // LDS stages: 4 x 32 KiB for 256-row tiles; 6 x 24 KiB for 128-row tiles,
+  // which stream weights from HBM and need more bytes in flight.
+  constexpr int NST = BM == 256 ? 4 : 6;
   const TileRef tr = map_tile(a);
   if (!tr.valid) return;
 
@@ -89,109 +89,132 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
     C = static_cast<uint16_t*>(a.C);
   }
   const int rows = tr.row_end - tr.row0;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave >> 2, wj = wave & 3;
 
-  // Direct-load sources: lane -> (row r_in of a RPI-row group, physical chunk
-  // pc), loading logical chunk pc ^ swz(row) of that row.
+  // Direct loads of this wavefront: group 0 fills the A half of a stage (LA
+  // instructions), group 1 the W half (LB); instruction i covers LDS rows
+  // (wj*L + i)*RPI .. +RPI of its half.  Lane -> (row r_in, physical chunk),
+  // loading logical chunk pc ^ swz(row).
   const int r_in = lane / CH;
-  uint32_t a_off[A_INS], b_off[B_INS];
+  const uint16_t* src = grp == 0 ? A : W;
+  constexpr int LMAX = LA > LB ? LA : LB;
+  const int nload = grp == 0 ? LA : LB;
+  uint32_t off[LMAX];
 #pragma unroll
-  for (int j = 0; j < A_INS; ++j) {
-    const int row = (j * 4 + wave) * RPI + r_in;
+  for (int i = 0; i < LMAX; ++i) {
+    const int row = (wj * nload + i) * RPI + r_in;
     const int lchunk = (lane % CH) ^ swz(row);
-    a_off[j] = (uint32_t)(tr.row0 + min(row, rows - 1)) * (uint32_t)Kd + lchunk * 8;
+    const int g_row = grp == 0 ? tr.row0 + min(row, rows - 1) : min(tr.n0 + row, Nd - 1);
+    off[i] = (uint32_t)g_row * (uint32_t)Kd + lchunk * 8;
   }
-#pragma unroll
-  for (int j = 0; j < B_INS; ++j) {
-    const int row = (j * 4 + wave) * RPI + r_in;
-    const int lchunk = (lane % CH) ^ swz(row);
-    const int n = min(tr.n0 + row, Nd - 1);
-    b_off[j] = (uint32_t)n * (uint32_t)Kd + lchunk * 8;
-  }
-
+  const int half = grp == 0 ? 0 : BM * BK;
   auto issue = [&](int stage, int k0) {
-    uint16_t* base = lds + stage * STAGE;
+    uint16_t* base = lds + stage * STAGE + half;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j)
-      lds_load16(A + a_off[j] + k0, base + (j * 4 + wave) * RPI * BK);
-#pragma unroll
-    for (int j = 0; j < B_INS; ++j)
-      lds_load16(W + b_off[j] + k0, base + BM * BK + (j * 4 + wave) * RPI * BK);
+    for (int i = 0; i < LMAX; ++i)
+      if (i < nload) lds_load16(src + off[i] + k0, base + (wj * nload + i) * RPI * BK);
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[4][4];
+  f32x16 acc[2][MI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < MI; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int KT = Kd / BK;
   const int sw = swz(lane & 31);   // the same for every fragment row this lane reads
-  bf16x8 fa[2][4], fb[2][4];
-  auto read_frags = [&](const uint16_t* As, int kk, int buf) {
-    const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
+  bf16x8 fa[MI][2], fb[2][2];
+  auto read_frags = [&](int stage) {
+    const uint16_t* As = lds + stage * STAGE;
     const uint16_t* Bs = As + BM * BK;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      fa[buf][mi] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + mi * 32 + (lane & 31)) * BK + pc);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-      fb[buf][ni] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 128 + ni * 32 + (lane & 31)) * BK + pc);
+      for (int mi = 0; mi < MI; ++mi)
+        fa[mi][kk] = *reinterpret_cast<const bf16x8*>(
+            As + (grp * (BM / 2) + mi * 32 + (lane & 31)) * BK + pc);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        fb[ni][kk] = *reinterpret_cast<const bf16x8*>(
+            Bs + (wj * 64 + ni * 32 + (lane & 31)) * BK + pc);
+    }
   };
-  auto mfmas = [&](int buf) {
+  auto mfmas = [&]() {
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][ni], fa[buf][mi], acc[ni][mi], 0, 0, 0);
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni][kk], fa[mi][kk],
+                                                                acc[ni][mi], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  // Prologue: the first NST-1 stages in flight.
+  const int KT = Kd / BK;
+  // Prologue: stages 0 .. NST-2 in flight (chunks past the end re-read the
+  // last chunk into stages nobody reads, so every k-step issues the same
+  // number of loads and the wait counts below are constants).
 #pragma unroll
-  for (int st = 0; st < NST - 1; ++st)
-    if (st < KT) issue(st, st * BK);
+  for (int st = 0; st < NST - 1; ++st) issue(st, min(st, KT - 1) * BK);
+  if (grp == 0)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LA * (NST - 2)) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LB * (NST - 2)) : "memory");
+  barrier();
+  if (grp == 0) read_frags(0);
 
   for (int kt = 0; kt < KT; ++kt) {
-    // Stage kt has landed for every lane once each waited for its own loads
-    // and all passed the barrier.  The barrier also ends every wavefront's
-    // use of the stage consumed in iteration kt-1 (its fragments all fed
-    // MFMAs before the barrier), which is refilled next.  A bare s_barrier:
-    // __syncthreads() would add a fence that drains every load in flight.
-    wait_stages(min(NST - 2, KT - 1 - kt));
-    __builtin_amdgcn_s_barrier();
-    const uint16_t* As = lds + (kt % NST) * STAGE;
-    read_frags(As, 0, 0);
-    if (kt + NST - 1 < KT) issue((kt + NST - 1) % NST, (kt + NST - 1) * BK);
-    read_frags(As, 1, 1);
-    mfmas(0);
-    mfmas(1);
-    // interleave the fragment reads of k-substep 1 and the next stage's loads
-    // with the MFMAs of k-substep 0
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    const int nxt = min(kt + NST - 1, KT - 1) * BK;
+    // Phase A: group 0 runs its MFMAs on stage kt; group 1 reads its stage-kt
+    // fragments and loads its half of stage kt+NST-1 into the buffer freed
+    // by the previous k-step's last barrier.
+    if (grp == 0) {
+      mfmas();
+    } else {
+      read_frags(kt % NST);
+      issue((kt + NST - 1) % NST, nxt);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+    // Each lane's own loads of stage kt+1 have landed (group 1 has NST-2
+    // younger stages in flight, group 0 NST-3), and group 1's reads of stage
+    // kt are complete; after the barrier every half of stage kt+1 is in LDS
+    // and nobody reads stage kt any more.
+    if (grp == 0)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LA * (NST - 3)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LB * (NST - 2)) : "memory");
+    barrier();
+    // Phase B: group 1 runs its MFMAs on stage kt; group 0 reads its stage
+    // kt+1 fragments and loads its half of stage kt+NST-1.  No second
+    // barrier: group 0's stage-kt+1 reads feed its next MFMA burst, which
+    // precedes the next barrier, so they are complete before that buffer is
+    // refilled two k-steps later.
+    if (grp == 1) {
+      mfmas();
+    } else {
+      if (kt + 1 < KT) read_frags((kt + 1) % NST);
+      issue((kt + NST - 1) % NST, nxt);
+    }
   }
+  // no direct-to-LDS load may still be in flight when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Epilogue.  The 32x32 accumulator of (ni, mi) holds C^T: element v of lane l
   // is output row mi*32 + l%32, column ni*32 + (v/4)*8 + (l/32)*4 + v%4.
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int ml = wm * 128 + mi * 32 + (lane & 31);
+  for (int mi = 0; mi < MI; ++mi) {
+    const int ml = grp * (BM / 2) + mi * 32 + (lane & 31);
     if (ml >= rows) continue;
     uint16_t* crow = C + (int64_t)(tr.row0 + ml) * Nd;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < 2; ++ni) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = tr.n0 + wn * 128 + ni * 32 + g * 8 + (lane >> 5) * 4;
+        const int n = tr.n0 + wj * 64 + ni * 32 + g * 8 + (lane >> 5) * 4;
         if (n >= Nd) continue;
         float z[4];
 #pragma unroll
@@ -211,16 +234,22 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
 
 }  // namespace
 
-int gemm_bf16_bm() { return BM; }
 int gemm_bf16_bn() { return BN; }
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
+hipError_t launch_gemm_bf16(const GemmArgs& a, int bm, bool gelu, hipStream_t s) {
   const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
-  if (gelu)
-    hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(grid), dim3(NTHR), 0, s, a);
-  else
-    hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(grid), dim3(NTHR), 0, s, a);
+  if (bm == 128) {
+    if (gelu)
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, true>), dim3(grid), dim3(NTHR), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, false>), dim3(grid), dim3(NTHR), 0, s, a);
+  } else {
+    if (gelu)
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, true>), dim3(grid), dim3(NTHR), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, false>), dim3(grid), dim3(NTHR), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -108,10 +108,10 @@ struct GemmArgs {
   int64_t grid_tiles;   // upper bound on the tile count (grid size)
 };
 
-// Prefill-shaped grouped GEMM (bf16 MFMA), BM rows per tile.
-int gemm_bf16_bm();
+// Prefill-shaped grouped GEMM (bf16 MFMA): tiles of bm (256 or 128) x
+// gemm_bf16_bn() rows x columns.
 int gemm_bf16_bn();
-hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, int bm, bool gelu, hipStream_t s);
 // fp32 grouped GEMM (VALU), BM rows per tile.
 int gemm_f32_bm();
 int gemm_f32_bn();
