@@ -7,30 +7,28 @@
 //   expert e's block, epi = GELU for the first Linear, identity for the
 //   second.  bf16 operands, fp32 accumulation, bf16 result.
 //
-// Design for CDNA4:
-//   - workgroup tile BM x BN = 256 x 256, BK = 32, 8 wavefronts = two groups
-//     of four; the hardware places wavefront w on SIMD w mod 4, so every SIMD
-//     holds one wavefront of each group.  Group g owns output rows
-//     [g*BM/2, (g+1)*BM/2); wavefront j of a group owns columns [64j, 64j+64)
-//     as (BM/64) x 2 tiles of v_mfma_f32_32x32x16_bf16;
-//   - ping-pong: in each k-step, while one group issues its 16 MFMAs from
-//     fragments already in registers (at raised wave priority), the other
-//     group reads its fragments for the next MFMA burst from LDS and issues
-//     its share of the global loads; one barrier per k-step swaps the roles,
-//     so each SIMD's MFMA pipe runs the two groups' bursts back to back while
-//     memory work hides in their shadow;
-//   - operands move global -> LDS with 16-byte direct-to-LDS loads (no VGPR
-//     staging); a wave instruction fills 16 LDS rows of 64 bytes; group 0
-//     loads the A half of a stage, group 1 the W half.  The 16-byte chunks of
-//     a row are XOR-swizzled (swz below) so fragment reads hit every bank
-//     once per 16 lanes;
-//   - four LDS stages (4 x 32 KiB); loads run two to three k-steps ahead;
-//     after the last k-step every lane drains its loads before the epilogue;
-//   - the MFMA takes the weight fragment as its first operand, so each lane
-//     ends up with 4 consecutive output columns of one row and the epilogue
-//     writes 8-byte runs; the GELU epilogue uses the Abramowitz-Stegun 7.1.26
-//     erf (gelu_as);
-//   - rows past an expert's end read a clamped valid row and are not stored.
+// Two kernels, both fed by 16-byte direct-to-LDS loads (global -> LDS with
+// no VGPR staging; one wave instruction fills 16 LDS rows of 64 bytes) with
+// BK = 32 and the 16-byte chunks of each LDS row XOR-swizzled (swz below) so
+// fragment reads hit every bank once per 16 lanes.  Both give the MFMA the
+// weight fragment as its first operand, so each lane ends up with 4
+// consecutive output columns of one row; rows past an expert's end read a
+// clamped valid row and are not stored; the GELU epilogue uses the
+// Abramowitz-Stegun 7.1.26 erf (gelu_as).
+//
+// 256 x 256 tiles (many rows per expert): gemm_bf16_w4_kernel, four
+// wavefronts of 128 x 128 with the accumulators in the accumulation
+// registers; see the comment at the kernel.  One wavefront can pull only
+// about 32 bytes per clock out of LDS on this chip, and this shape needs 512
+// fragment bytes per MFMA (16 bytes per clock at full MFMA rate).
+//
+// 128 x 256 tiles (about one tile of rows per expert, weights streamed from
+// HBM): gemm_bf16_kernel<128>, eight wavefronts in two groups of four that
+// ping-pong -- in each k-step, while one group issues its 16 MFMAs from
+// fragments already in registers (at raised wave priority), the other group
+// reads its next fragments from LDS and issues its share of the loads; one
+// barrier per k-step swaps the roles.  Six LDS stages keep more weight bytes
+// in flight.
 #include "gemm_common.h"
 
 namespace moe {
@@ -38,9 +36,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 256, BK = 32;
 constexpr int NTHR = 512;
+constexpr int W4_NS = 4;             // LDS stages of the 256-row kernel
 constexpr int CH = BK / 8;                 // 16-byte chunks per LDS row (64-byte rows)
 constexpr int RPI = 64 / CH;               // LDS rows filled by one wave instruction (16)
 constexpr int LB = BN / RPI / 4;           // direct loads per group-1 wavefront per stage (W half)
@@ -59,7 +60,8 @@ __device__ __forceinline__ void lds_load16(const uint16_t* g, uint16_t* l) {
 // s_barrier with a compiler memory fence: no LDS access moves across it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// BM = 256 or 128 rows per tile; each group owns BM/2 rows (MI tiles of 32).
+// Ping-pong kernel; launched with BM = 128 rows per tile (it also builds for
+// 256).  Each group owns BM/2 rows (MI tiles of 32).
 template <int BM, bool GELU>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
   constexpr int MI = BM / 64;                 // 32-row MFMA tiles per wavefront
@@ -232,6 +234,211 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
   }
 }
 
+
+// 256-row tiles: four wavefronts (one per SIMD) in a 2 x 2 arrangement, each
+// owning 128 x 128 outputs as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 whose
+// 256 fp32 accumulators per lane sit in the accumulation registers.  A
+// wavefront reads 512 bytes of fragments from LDS per MFMA (a 128 x 64
+// wavefront tile needs 768), which matters because one wavefront draws at
+// most about 32 bytes per clock from LDS on this chip.
+//
+// Each k-step has two halves of 16 MFMAs (k 0-15 and 16-31 of the step).
+// While one half's MFMAs run on one register set of fragments, the other set
+// is filled from LDS for the next half, and the wavefront issues its share of
+// the direct-to-LDS loads of the stage NS-1 steps ahead (A rows in the first
+// half, W rows in the second).  One barrier per k-step, between the halves:
+// before it every lane has its own loads of the next stage landed and its
+// reads of the current stage done, so after it the next stage is whole and
+// the current one may be refilled.
+template <bool GELU, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+gemm_bf16_w4_kernel(GemmArgs a) {
+  constexpr int TM = 256;
+  constexpr int STAGE = (TM + BN) * BK;   // bf16 elements per LDS stage (32 KiB)
+  constexpr int NL = TM / RPI / 4;        // direct loads per wavefront per operand per stage (4)
+  const TileRef tr = map_tile(a);
+  if (!tr.valid) return;
+
+  // the output tile is staged through the same LDS after the main loop
+  constexpr int CST = BN + 8;            // staged row stride in bf16 (528 bytes)
+  constexpr int LDS_ELEMS = NS * STAGE > TM * CST ? NS * STAGE : TM * CST;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+
+  const int Kd = a.Kd, Nd = a.Nd;
+  const uint16_t* A;
+  const uint16_t* W;
+  const uint16_t* bias = nullptr;
+  uint16_t* C;
+  if (tr.shared) {
+    A = static_cast<const uint16_t*>(a.As);
+    W = static_cast<const uint16_t*>(a.Ws);
+    C = static_cast<uint16_t*>(a.Cs);
+  } else {
+    A = static_cast<const uint16_t*>(a.A);
+    W = static_cast<const uint16_t*>(a.W) + (int64_t)tr.e * Nd * Kd;
+    if (a.bias) bias = static_cast<const uint16_t*>(a.bias) + (int64_t)tr.e * Nd;
+    C = static_cast<uint16_t*>(a.C);
+  }
+  const int rows = tr.row_end - tr.row0;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Wavefront w fills LDS rows [64w, 64w+64) of both operand halves of a
+  // stage: instruction i covers rows (4w+i)*16 .. +16; lane -> (row r_in,
+  // physical chunk), loading logical chunk pc ^ swz(row).
+  const int r_in = lane / CH;
+  uint32_t offA[NL], offB[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int row = (wave * NL + i) * RPI + r_in;
+    const int lchunk = (lane % CH) ^ swz(row);
+    offA[i] = (uint32_t)(tr.row0 + min(row, rows - 1)) * (uint32_t)Kd + lchunk * 8;
+    offB[i] = (uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8;
+  }
+  auto issue_a = [&](int buf, int k0) {
+    uint16_t* base = lds + buf * STAGE + wave * NL * RPI * BK;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) lds_load16(A + offA[i] + k0, base + i * RPI * BK);
+  };
+  auto issue_b = [&](int buf, int k0) {
+    uint16_t* base = lds + buf * STAGE + TM * BK + wave * NL * RPI * BK;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) lds_load16(W + offB[i] + k0, base + i * RPI * BK);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int sw = swz(lane & 31);   // the same for every fragment row this lane reads
+  const int arow = (wm * 128 + (lane & 31)) * BK, brow = (wn * 128 + (lane & 31)) * BK;
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto read_half = [&](bf16x8 (&fa)[4], bf16x8 (&fb)[4], int buf, int kk) {
+    const uint16_t* As = lds + buf * STAGE;
+    const uint16_t* Bs = As + TM * BK;
+    const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[i] = *reinterpret_cast<const bf16x8*>(As + arow + i * 32 * BK + pc);
+      fb[i] = *reinterpret_cast<const bf16x8*>(Bs + brow + i * 32 * BK + pc);
+    }
+  };
+  auto mfma_half = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[ni][mi], 0, 0, 0);
+  };
+  // interleave one half: 16 MFMAs with 8 fragment reads and 4 direct loads
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
+
+  const int KT = Kd / BK;
+  // Prologue: stages 0 .. NS-2 in flight (chunks past the end re-read the
+  // last chunk into buffers nobody reads again, so every k-step issues the
+  // same number of loads and the wait counts are constants).
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    issue_a(st, min(st, KT - 1) * BK);
+    issue_b(st, min(st, KT - 1) * BK);
+  }
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL * (NS - 2)) : "memory");
+  barrier();
+  read_half(fa0, fb0, 0, 0);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt % NS, nbuf = (kt + NS - 1) % NS;
+    const int nk = min(kt + NS - 1, KT - 1) * BK;
+    // first half: MFMAs on set 0; set 1 <- second half of this stage; A rows
+    // of stage kt+NS-1 into the buffer last read before the previous barrier
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(fa1, fb1, buf, 1);
+    issue_a(nbuf, nk);
+    mfma_half(fa0, fb0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // own loads of stage kt+1 landed (younger: NS-3 whole stages and this
+    // step's A rows), own reads of stage kt done
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * NL * (NS - 3) + NL) : "memory");
+    barrier();
+    // second half: MFMAs on set 1; set 0 <- first half of stage kt+1 (in the
+    // last step this reads a stale buffer that nobody uses); W rows of stage
+    // kt+NS-1
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(fa0, fb0, (kt + 1) % NS, 0);
+    issue_b(nbuf, nk);
+    mfma_half(fa1, fb1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // no direct-to-LDS load may still be in flight when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue.  The 32x32 accumulator of (ni, mi) holds C^T: element v of lane l
+  // is output row mi*32 + l%32, column ni*32 + (v/4)*8 + (l/32)*4 + v%4.
+  // Bias and GELU are applied in registers, the bf16 tile goes to LDS, and
+  // the workgroup then writes whole 512-byte rows with 16-byte stores.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  barrier();
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int nl = wn * 128 + ni * 32 + g * 8 + (lane >> 5) * 4;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+        // columns past Nd (partial tiles) read a valid chunk and are not stored
+        const uint2 braw = *reinterpret_cast<const uint2*>(bias + min(tr.n0 + nl, Nd - 4));
+        bv[0] = __uint_as_float(braw.x << 16);
+        bv[1] = __uint_as_float(braw.x & 0xffff0000u);
+        bv[2] = __uint_as_float(braw.y << 16);
+        bv[3] = __uint_as_float(braw.y & 0xffff0000u);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int ml = wm * 128 + mi * 32 + (lane & 31);
+        float z[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          z[q] = acc[ni][mi][g * 4 + q] + bv[q];
+          if (GELU) z[q] = gelu_as(z[q]);
+        }
+        // v_cvt_pk_bf16_f32: round to nearest even, two values per instruction
+        const bf16x4 pk = __builtin_convertvector((f32x4){z[0], z[1], z[2], z[3]}, bf16x4);
+        *reinterpret_cast<bf16x4*>(lds + ml * CST + nl) = pk;
+      }
+    }
+  }
+  __syncthreads();
+  // 256 threads x 16 bytes = 8 rows of 256 columns per pass
+  const int cc = (threadIdx.x & 31) * 8;
+  const int ncol = tr.n0 + cc;
+#pragma unroll 4
+  for (int p = 0; p < TM / 8; ++p) {
+    const int ml = p * 8 + (threadIdx.x >> 5);
+    if (ml < rows && ncol < Nd)
+      *reinterpret_cast<uint4*>(C + (int64_t)(tr.row0 + ml) * Nd + ncol) =
+          *reinterpret_cast<const uint4*>(lds + ml * CST + cc);
+  }
+}
+
 }  // namespace
 
 int gemm_bf16_bn() { return BN; }
@@ -246,9 +453,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, int bm, bool gelu, hipStream_t s)
       hipLaunchKernelGGL((gemm_bf16_kernel<128, false>), dim3(grid), dim3(NTHR), 0, s, a);
   } else {
     if (gelu)
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, true>), dim3(grid), dim3(NTHR), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, W4_NS>), dim3(grid), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, false>), dim3(grid), dim3(NTHR), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, W4_NS>), dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
