@@ -181,24 +181,32 @@ __device__ __forceinline__ int4 band_tile(int j, int mt, int ntn, int BN, int e,
   const int b = r0 / (band * gsz), r = r0 % (band * gsz);
   const int nt = b * band + r / gsz, i = g * gm + r % gsz;
   (void)ntn;
-  return make_int4(e, o0 + i * BM, min(o0 + (i + 1) * BM, o1), nt * BN);
+  // the last m-tile runs to the block's end (it may hold a folded remainder)
+  return make_int4(e, o0 + i * BM, i == mt - 1 ? o1 : o0 + (i + 1) * BM, nt * BN);
+}
+
+// m-tiles of a block of `rows` rows; a last remainder of at most `merge` rows
+// joins the previous full tile
+__device__ __forceinline__ int m_tiles(int rows, int BM, int merge) {
+  const int mt = (rows + BM - 1) / BM;
+  return (mt >= 2 && rows - (mt - 1) * BM <= merge) ? mt - 1 : mt;
 }
 
 __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restrict__ offsets, int N,
-                                                        int BM, int BN, int Nd, int Ts,
+                                                        int BM, int BN, int Nd, int Ts, int merge,
                                                         int4* __restrict__ list,
                                                         int32_t* __restrict__ count) {
   __shared__ int wsum[4];
   __shared__ int s_base[MAXN + 1], s_mt[MAXN], s_o0[MAXN], s_o1[MAXN];
   const int e = threadIdx.x;
   const int ntn = (Nd + BN - 1) / BN;
-  const int ms = (Ts + BM - 1) / BM;
+  const int ms = m_tiles(Ts, BM, merge);
   const int shared_tiles = ms * ntn;
   int o0 = 0, o1 = 0, mt = 0;
   if (e < N) {
     o0 = offsets[e];
     o1 = offsets[e + 1];
-    mt = (o1 - o0 + BM - 1) / BM;
+    mt = m_tiles(o1 - o0, BM, merge);
     s_mt[e] = mt;
     s_o0[e] = o0;
     s_o1[e] = o1;
@@ -256,9 +264,9 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
 }
 
 hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
-                            int4* list, int32_t* count, hipStream_t s) {
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(256), 0, s, offsets, N, BM, BN, Nd, Ts, list,
-                     count);
+                            int merge, int4* list, int32_t* count, hipStream_t s) {
+  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(256), 0, s, offsets, N, BM, BN, Nd, Ts, merge,
+                     list, count);
   return hipGetLastError();
 }
 

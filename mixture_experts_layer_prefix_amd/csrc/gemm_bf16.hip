@@ -29,6 +29,8 @@
 // reads its next fragments from LDS and issues its share of the loads; one
 // barrier per k-step swaps the roles.  Six LDS stages keep more weight bytes
 // in flight.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -235,35 +237,70 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(GemmArgs a) {
 }
 
 
-// 256-row tiles: four wavefronts (one per SIMD) in a 2 x 2 arrangement, each
-// owning 128 x 128 outputs as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 whose
-// 256 fp32 accumulators per lane sit in the accumulation registers.  A
-// wavefront reads 512 bytes of fragments from LDS per MFMA (a 128 x 64
-// wavefront tile needs 768), which matters because one wavefront draws at
-// most about 32 bytes per clock from LDS on this chip.
+// 256-row tiles: four wavefronts, one per SIMD.  The wave arrangement is
+// chosen per tile from its valid row count R:
+//   256 < R <= 320: 2 x 2 wavefronts of 128 x 128 plus, per wavefront, 32
+//                   more rows x 128 columns held in ordinary VGPRs: the tile
+//                   list folds a remainder of up to 64 rows into an expert's
+//                   last full tile, which streams the weight rows anyway,
+//   128 < R <= 256: 2 x 2 wavefronts of 128 x 128 (4 x 4 MFMA tiles of 32 x 32),
+//   64 < R <= 128:  1 x 4 wavefronts of 128 x 64,
+//   R <= 64:        1 x 4 wavefronts of  64 x 64;
+// A rows past the arrangement's height are neither loaded nor multiplied.
+// The loads of this kernel run at the L2's pace (an expert's weight panel
+// is streamed once per m-tile), so a separate tile for a short remainder
+// would cost nearly as much as a full one.
+// The 2 x 2 arrangement keeps 256 fp32 accumulators per lane in the
+// accumulation registers and reads 512 bytes of fragments from LDS per MFMA
+// (a 128 x 64 wavefront tile needs 768); one wavefront draws at most about
+// 32 bytes per clock from LDS on this chip.
 //
-// Each k-step has two halves of 16 MFMAs (k 0-15 and 16-31 of the step).
-// While one half's MFMAs run on one register set of fragments, the other set
-// is filled from LDS for the next half, and the wavefront issues its share of
-// the direct-to-LDS loads of the stage NS-1 steps ahead (A rows in the first
+// Each k-step has two halves (k 0-15 and 16-31 of the step).  While one
+// half's MFMAs run on one register set of fragments, the other set is filled
+// from LDS for the next half, and the wavefront issues its share of the
+// direct-to-LDS loads of the stage NS-1 steps ahead (A rows in the first
 // half, W rows in the second).  One barrier per k-step, between the halves:
 // before it every lane has its own loads of the next stage landed and its
 // reads of the current stage done, so after it the next stage is whole and
 // the current one may be refilled.
-template <bool GELU, int NS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
-gemm_bf16_w4_kernel(GemmArgs a) {
-  constexpr int TM = 256;
-  constexpr int STAGE = (TM + BN) * BK;   // bf16 elements per LDS stage (32 KiB)
-  constexpr int NL = TM / RPI / 4;        // direct loads per wavefront per operand per stage (4)
-  const TileRef tr = map_tile(a);
-  if (!tr.valid) return;
+template <int L>
+struct W4Layout;
+template <>
+struct W4Layout<0> {   // 128 < R <= 256
+  static constexpr int WN = 2, MI = 4, NI = 4, AROWS = 256;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<1> {   // 64 < R <= 128
+  static constexpr int WN = 4, MI = 4, NI = 2, AROWS = 128;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<2> {   // R <= 64
+  static constexpr int WN = 4, MI = 2, NI = 2, AROWS = 64;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<3> {   // 256 < R <= 320
+  static constexpr int WN = 2, MI = 4, NI = 4, AROWS = 320;
+  static constexpr bool EXTRA = true;
+};
 
-  // the output tile is staged through the same LDS after the main loop
-  constexpr int CST = BN + 8;            // staged row stride in bf16 (528 bytes)
-  constexpr int LDS_ELEMS = NS * STAGE > TM * CST ? NS * STAGE : TM * CST;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+constexpr int W4_TM = 256;
+constexpr int W4_MERGE = 64;                  // remainder rows folded into the previous tile
+constexpr int W4_AR = W4_TM + W4_MERGE;       // A rows held per LDS stage
+constexpr int W4_STAGE = (W4_AR + BN) * BK;   // bf16 elements per LDS stage (36 KiB)
+constexpr int W4_CST = BN + 8;                // staged output row stride in bf16 (528 bytes)
 
+template <bool GELU, int NS, int LAY>
+__device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
+                                        f32x16 (&acc)[4][4]) {
+  using Lay = W4Layout<LAY>;
+  constexpr int MI = Lay::MI, NI = Lay::NI, WN = Lay::WN;
+  constexpr bool EX = Lay::EXTRA;
+  constexpr int NLA = Lay::AROWS / RPI / 4;   // direct loads per wavefront per stage, A rows
+  constexpr int NLB = W4_TM / RPI / 4;        // W rows (4)
+  constexpr int NLS = NLA + NLB;
   const int Kd = a.Kd, Nd = a.Nd;
   const uint16_t* A;
   const uint16_t* W;
@@ -282,72 +319,92 @@ gemm_bf16_w4_kernel(GemmArgs a) {
   const int rows = tr.row_end - tr.row0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
+  constexpr int WROWS = MI * 32, WCOLS = NI * 32;   // wavefront tile
 
-  // Wavefront w fills LDS rows [64w, 64w+64) of both operand halves of a
-  // stage: instruction i covers rows (4w+i)*16 .. +16; lane -> (row r_in,
-  // physical chunk), loading logical chunk pc ^ swz(row).
+  // Wavefront w fills A rows [NLA*16*w, +NLA*16) and W rows [64w, 64w+64) of
+  // a stage; instruction i covers 16 rows; lane -> (row r_in, physical
+  // chunk), loading logical chunk pc ^ swz(row).
   const int r_in = lane / CH;
-  uint32_t offA[NL], offB[NL];
+  uint32_t offA[NLA], offB[NLB];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int row = (wave * NL + i) * RPI + r_in;
+  for (int i = 0; i < NLA; ++i) {
+    const int row = (wave * NLA + i) * RPI + r_in;
     const int lchunk = (lane % CH) ^ swz(row);
     offA[i] = (uint32_t)(tr.row0 + min(row, rows - 1)) * (uint32_t)Kd + lchunk * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < NLB; ++i) {
+    const int row = (wave * NLB + i) * RPI + r_in;
+    const int lchunk = (lane % CH) ^ swz(row);
     offB[i] = (uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8;
   }
   auto issue_a = [&](int buf, int k0) {
-    uint16_t* base = lds + buf * STAGE + wave * NL * RPI * BK;
+    uint16_t* base = lds + buf * W4_STAGE + wave * NLA * RPI * BK;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) lds_load16(A + offA[i] + k0, base + i * RPI * BK);
+    for (int i = 0; i < NLA; ++i) lds_load16(A + offA[i] + k0, base + i * RPI * BK);
   };
   auto issue_b = [&](int buf, int k0) {
-    uint16_t* base = lds + buf * STAGE + TM * BK + wave * NL * RPI * BK;
+    uint16_t* base = lds + buf * W4_STAGE + W4_AR * BK + wave * NLB * RPI * BK;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) lds_load16(W + offB[i] + k0, base + i * RPI * BK);
+    for (int i = 0; i < NLB; ++i) lds_load16(W + offB[i] + k0, base + i * RPI * BK);
   };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int sw = swz(lane & 31);   // the same for every fragment row this lane reads
-  const int arow = (wm * 128 + (lane & 31)) * BK, brow = (wn * 128 + (lane & 31)) * BK;
-  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-  auto read_half = [&](bf16x8 (&fa)[4], bf16x8 (&fb)[4], int buf, int kk) {
-    const uint16_t* As = lds + buf * STAGE;
-    const uint16_t* Bs = As + TM * BK;
+  const int arow = (wm * WROWS + (lane & 31)) * BK, brow = (wn * WCOLS + (lane & 31)) * BK;
+  // rows 256 + 32*wm .. +32 of a 320-row tile (EX only)
+  const int xrow = (W4_TM + wm * 32 + (lane & 31)) * BK;
+  constexpr int MX = MI + (EX ? 1 : 0);   // A fragments per half
+  bf16x8 fa0[MX], fb0[NI], fa1[MX], fb1[NI];
+  f32x16 accx[EX ? NI : 1];
+  if constexpr (EX) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) accx[i][v] = 0.f;
+  }
+  auto read_half = [&](bf16x8 (&fa)[MX], bf16x8 (&fb)[NI], int buf, int kk) {
+    const uint16_t* As = lds + buf * W4_STAGE;
+    const uint16_t* Bs = As + W4_AR * BK;
     const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i)
       fa[i] = *reinterpret_cast<const bf16x8*>(As + arow + i * 32 * BK + pc);
+    if constexpr (EX) fa[MI] = *reinterpret_cast<const bf16x8*>(As + xrow + pc);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
       fb[i] = *reinterpret_cast<const bf16x8*>(Bs + brow + i * 32 * BK + pc);
-    }
   };
-  auto mfma_half = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+  auto mfma_half = [&](const bf16x8 (&fa)[MX], const bf16x8 (&fb)[NI]) {
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NI; ++ni) {
+      // The folded rows' accumulators live in ordinary VGPRs (the 256
+      // accumulation registers hold the main 256 x 256): the compiler keeps
+      // all MFMA results in one register class, so these four are written
+      // out with VGPR operands.  Their fragments come from LDS reads, which
+      // the compiler's wait counts cover; each accx[ni] is next read by the
+      // same MFMA a whole half later, and the epilogue pads before reading.
+      if constexpr (EX)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+            : "+v"(accx[ni])
+            : "v"(fb[ni]), "v"(fa[MI]));
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
         acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[ni][mi], 0, 0, 0);
+    }
   };
-  // interleave one half: 16 MFMAs with 8 fragment reads and 4 direct loads
-  auto interleave = [&]() {
+  // one half: MI*NI MFMAs interleaved with MI+NI fragment reads and `nv`
+  // direct loads
+  auto interleave = [&](auto nv_tag) {
+    constexpr int NV = decltype(nv_tag)::value;
+    constexpr int NM = MX * NI, ND = MX + NI;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i >= ND - NV && i < ND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    static_assert(ND <= NM && NV <= ND, "every read and load sits between two MFMAs");
   };
 
   const int KT = Kd / BK;
@@ -359,7 +416,7 @@ gemm_bf16_w4_kernel(GemmArgs a) {
     issue_a(st, min(st, KT - 1) * BK);
     issue_b(st, min(st, KT - 1) * BK);
   }
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL * (NS - 2)) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLS * (NS - 2)) : "memory");
   barrier();
   read_half(fa0, fb0, 0, 0);
 
@@ -372,11 +429,11 @@ gemm_bf16_w4_kernel(GemmArgs a) {
     read_half(fa1, fb1, buf, 1);
     issue_a(nbuf, nk);
     mfma_half(fa0, fb0);
-    interleave();
+    interleave(std::integral_constant<int, NLA>{});
     __builtin_amdgcn_sched_barrier(0);
     // own loads of stage kt+1 landed (younger: NS-3 whole stages and this
     // step's A rows), own reads of stage kt done
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * NL * (NS - 3) + NL) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(NLS * (NS - 3) + NLA) : "memory");
     barrier();
     // second half: MFMAs on set 1; set 0 <- first half of stage kt+1 (in the
     // last step this reads a stale buffer that nobody uses); W rows of stage
@@ -385,23 +442,22 @@ gemm_bf16_w4_kernel(GemmArgs a) {
     read_half(fa0, fb0, (kt + 1) % NS, 0);
     issue_b(nbuf, nk);
     mfma_half(fa1, fb1);
-    interleave();
+    interleave(std::integral_constant<int, NLB>{});
     __builtin_amdgcn_sched_barrier(0);
   }
-  // no direct-to-LDS load may still be in flight when the workgroup ends
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // no direct-to-LDS load may still be in flight past this point
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
   // Epilogue.  The 32x32 accumulator of (ni, mi) holds C^T: element v of lane l
   // is output row mi*32 + l%32, column ni*32 + (v/4)*8 + (l/32)*4 + v%4.
   // Bias and GELU are applied in registers, the bf16 tile goes to LDS, and
   // the workgroup then writes whole 512-byte rows with 16-byte stores.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier();
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  for (int ni = 0; ni < NI; ++ni) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int nl = wn * 128 + ni * 32 + g * 8 + (lane >> 5) * 4;
+      const int nl = wn * WCOLS + ni * 32 + g * 8 + (lane >> 5) * 4;
       float bv[4] = {0.f, 0.f, 0.f, 0.f};
       if (bias) {
         // columns past Nd (partial tiles) read a valid chunk and are not stored
@@ -412,8 +468,8 @@ gemm_bf16_w4_kernel(GemmArgs a) {
         bv[3] = __uint_as_float(braw.y & 0xffff0000u);
       }
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int ml = wm * 128 + mi * 32 + (lane & 31);
+      for (int mi = 0; mi < MI; ++mi) {
+        const int ml = wm * WROWS + mi * 32 + (lane & 31);
         float z[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -422,7 +478,7 @@ gemm_bf16_w4_kernel(GemmArgs a) {
         }
         // v_cvt_pk_bf16_f32: round to nearest even, two values per instruction
         const bf16x4 pk = __builtin_convertvector((f32x4){z[0], z[1], z[2], z[3]}, bf16x4);
-        *reinterpret_cast<bf16x4*>(lds + ml * CST + nl) = pk;
+        *reinterpret_cast<bf16x4*>(lds + ml * W4_CST + nl) = pk;
       }
     }
   }
@@ -430,18 +486,80 @@ gemm_bf16_w4_kernel(GemmArgs a) {
   // 256 threads x 16 bytes = 8 rows of 256 columns per pass
   const int cc = (threadIdx.x & 31) * 8;
   const int ncol = tr.n0 + cc;
-#pragma unroll 4
-  for (int p = 0; p < TM / 8; ++p) {
-    const int ml = p * 8 + (threadIdx.x >> 5);
-    if (ml < rows && ncol < Nd)
+  const int nrow = min(rows, W4_TM);
+  for (int ml = threadIdx.x >> 5; ml < nrow; ml += 8)
+    if (ncol < Nd)
       *reinterpret_cast<uint4*>(C + (int64_t)(tr.row0 + ml) * Nd + ncol) =
-          *reinterpret_cast<const uint4*>(lds + ml * CST + cc);
+          *reinterpret_cast<const uint4*>(lds + ml * W4_CST + cc);
+  if constexpr (EX) {
+    // the folded remainder: rows 256 .. R-1, staged as LDS rows 0 .. 63.
+    // 24 wait states between the last MFMA writing accx and its first VALU
+    // read (the tie to accx keeps the pad after those MFMAs)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(accx[0]), "+v"(accx[1]), "+v"(accx[2]), "+v"(accx[3]));
+    __syncthreads();
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = wn * WCOLS + ni * 32 + g * 8 + (lane >> 5) * 4;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+          const uint2 braw = *reinterpret_cast<const uint2*>(bias + min(tr.n0 + nl, Nd - 4));
+          bv[0] = __uint_as_float(braw.x << 16);
+          bv[1] = __uint_as_float(braw.x & 0xffff0000u);
+          bv[2] = __uint_as_float(braw.y << 16);
+          bv[3] = __uint_as_float(braw.y & 0xffff0000u);
+        }
+        float z[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          z[q] = accx[ni][g * 4 + q] + bv[q];
+          if (GELU) z[q] = gelu_as(z[q]);
+        }
+        const bf16x4 pk = __builtin_convertvector((f32x4){z[0], z[1], z[2], z[3]}, bf16x4);
+        *reinterpret_cast<bf16x4*>(lds + (wm * 32 + (lane & 31)) * W4_CST + nl) = pk;
+      }
+    }
+    __syncthreads();
+    for (int ml = threadIdx.x >> 5; ml < rows - W4_TM; ml += 8)
+      if (ncol < Nd)
+        *reinterpret_cast<uint4*>(C + (int64_t)(tr.row0 + W4_TM + ml) * Nd + ncol) =
+            *reinterpret_cast<const uint4*>(lds + ml * W4_CST + cc);
   }
+}
+
+template <bool GELU, int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+gemm_bf16_w4_kernel(GemmArgs a) {
+  // the output tile is staged through the same LDS after the main loop
+  constexpr int LDS_ELEMS = NS * W4_STAGE > W4_TM * W4_CST ? NS * W4_STAGE : W4_TM * W4_CST;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+  const TileRef tr = map_tile(a);
+  if (!tr.valid) return;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int rows = tr.row_end - tr.row0;
+  if (rows > W4_TM)
+    w4_tile<GELU, NS, 3>(a, tr, lds, acc);
+  else if (rows > 128)
+    w4_tile<GELU, NS, 0>(a, tr, lds, acc);
+  else if (rows > 64)
+    w4_tile<GELU, NS, 1>(a, tr, lds, acc);
+  else
+    w4_tile<GELU, NS, 2>(a, tr, lds, acc);
 }
 
 }  // namespace
 
 int gemm_bf16_bn() { return BN; }
+
+int gemm_bf16_merge_rows(int bm) { return bm == W4_TM ? W4_MERGE : 0; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, int bm, bool gelu, hipStream_t s) {
   const int grid = gemm_grid(a);

@@ -274,7 +274,9 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
                   const char* what) -> int {
     hipError_t e = hipSuccess;
     if (path != PATH_SKINNY) {
-      e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, fw.list[list], fw.count + list, s);
+      const int merge = path == PATH_TILED ? moe::gemm_bf16_merge_rows(bm) : 0;
+      e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.list[list],
+                                fw.count + list, s);
       if (e != hipSuccess) return hip_status(e, "tile list launch");
       g.tile_list = fw.list[list];
       g.tile_count = fw.count + list;

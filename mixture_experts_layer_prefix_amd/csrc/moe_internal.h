@@ -79,9 +79,11 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
 // Tile list of a grouped GEMM with BM x BN tiles over Nd output columns: one
 // int4 {expert (-1: shared problem), first row, end row, first column} per
 // workgroup tile, shared-problem tiles first, then expert by expert; count[0]
-// receives the number of tiles.
+// receives the number of tiles.  A block's last remainder of at most `merge`
+// rows (when the block has a full tile) is folded into its last full tile,
+// which then spans up to BM + merge rows.
 hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
-                            int4* list, int32_t* count, hipStream_t s);
+                            int merge, int4* list, int32_t* count, hipStream_t s);
 inline int max_m_tiles(int64_t M_max, int N, int BM) {
   return static_cast<int>((M_max + BM - 1) / BM) + N;
 }
@@ -111,6 +113,8 @@ struct GemmArgs {
 // Prefill-shaped grouped GEMM (bf16 MFMA): tiles of bm (256 or 128) x
 // gemm_bf16_bn() rows x columns.
 int gemm_bf16_bn();
+// Remainder rows the bm-row kernel folds into an expert's last full tile.
+int gemm_bf16_merge_rows(int bm);
 hipError_t launch_gemm_bf16(const GemmArgs& a, int bm, bool gelu, hipStream_t s);
 // fp32 grouped GEMM (VALU), BM rows per tile.
 int gemm_f32_bm();

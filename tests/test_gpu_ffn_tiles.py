@@ -1,0 +1,90 @@
+"""GPU parity of moe_expert_ffn on hand-chosen expert row counts.
+
+The grouped GEMM picks its tile shape per expert block from the number of
+rows left in the block and folds a short remainder into the block's last full
+tile, so the counts below put the last tile of the blocks on every side of the
+64-, 128-, 256- and 320-row boundaries (and leave some experts empty).  Each expert's rows are checked against the oracle's
+E(x) = W2 GELU(W1 x + b1) + b2, and the rows past the last expert's block must
+stay untouched."""
+import numpy as np
+import pytest
+
+from mixture_experts_layer_prefix_amd import inputs, moe
+from oracle import moe_oracle as O
+
+from moe_testlib import BF16_TOL, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FC1   # a bf16 NaN pattern the kernels never write
+
+# counts per expert; the tile height is chosen from count mod 256 (the last tile)
+COUNTS = {
+    # T*K >= 200*N: 256-row tiles; a remainder of up to 64 rows after a full
+    # tile is folded into it (257, 319, 320, 1057, 1088), 65 or more is not (321)
+    "tiles256": [0, 1, 63, 64, 65, 128, 129, 256, 257, 319, 320, 321, 384, 511, 700, 1057,
+                 1088],
+    # T*K < 200*N: 128-row tiles
+    "tiles128": [0, 1, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 130, 3, 0, 40],
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    moe.lib()
+
+
+@pytest.mark.parametrize("name", sorted(COUNTS))
+@pytest.mark.parametrize("d,f", [(320, 384), (256, 512)])
+def test_expert_blocks(name, d, f):
+    import torch
+    counts = COUNTS[name]
+    N = len(counts)
+    M = int(sum(counts))
+    spare = 37                         # rows of x_perm / y_perm past the last block
+    rows = M + spare
+    say(f"case {name}: N={N} M={M} d={d} f={f}")
+    rng = np.random.default_rng(1234 + d + f + N)
+    x = inputs.bf16_round(rng.standard_normal((rows, d), dtype=np.float32))
+    w1 = inputs.bf16_round(rng.standard_normal((N, f, d), dtype=np.float32) * d ** -0.5)
+    b1 = inputs.bf16_round(rng.standard_normal((N, f), dtype=np.float32) * 0.1)
+    w2 = inputs.bf16_round(rng.standard_normal((N, d, f), dtype=np.float32) * f ** -0.5)
+    b2 = inputs.bf16_round(rng.standard_normal((N, d), dtype=np.float32) * 0.1)
+    offs = np.zeros(N + 1, dtype=np.int32)
+    offs[1:] = np.cumsum(counts)
+
+    cfg = moe.make_config(rows, d, f, N, 1, dtype="bf16")
+    dev = "cuda"
+
+    def u16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t = {"w_router": u16(w1[:, :1, :].copy()), "w1": u16(w1), "b1": u16(b1), "w2": u16(w2),
+         "b2": u16(b2)}
+    W = moe.make_weights(t)
+    xd = u16(x)
+    y = torch.full((rows, d), 0, dtype=torch.int16, device=dev)
+    y.fill_(SENTINEL)
+    y = y.view(torch.bfloat16)
+    moe.moe_expert_ffn(cfg, xd, torch.from_numpy(offs).to(dev), W, None, y, None,
+                       moe.alloc_workspace(cfg, "expert_ffn", dev))
+    torch.cuda.synchronize()
+    yh = inputs.bf16_widen(y.view(torch.int16).cpu().numpy().view(np.uint16))
+    yraw = y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    assert (yraw[M:] == SENTINEL).all(), "rows past the last expert block were written"
+    xf = inputs.bf16_widen(x)
+    for e in range(N):
+        lo, hi = offs[e], offs[e + 1]
+        if hi == lo:
+            continue
+        ref = O.expert_ffn(xf[lo:hi], inputs.bf16_widen(w1[e]), inputs.bf16_widen(b1[e]),
+                           inputs.bf16_widen(w2[e]), inputs.bf16_widen(b2[e]))
+        got = yh[lo:hi]
+        assert np.isfinite(got).all(), f"expert {e}: rows left unwritten or non-finite"
+        err = rel_l2(got, ref)
+        assert err <= BF16_TOL, (e, counts[e], err)
+    say(f"  {N} expert blocks within {BF16_TOL} rel-L2; spare rows untouched")
