@@ -59,11 +59,10 @@ GemmPath gemm_path(const moe_config_t* c) {
   return PATH_TILED;
 }
 
-// Rows per tile of the tiled bf16 GEMM: 128 when the experts hold few rows
-// on average (fewer than 200), so a tile does not compute mostly empty rows.
+// Rows per tile of the tiled GEMMs (the bf16 kernel shrinks its wave layout
+// for short tiles by itself).
 int gemm_bm(const moe_config_t* c) {
-  if (gemm_path(c) == PATH_F32) return moe::gemm_f32_bm();
-  return (int64_t)c->T * c->top_k < 200LL * c->n_experts ? 128 : 256;
+  return gemm_path(c) == PATH_F32 ? moe::gemm_f32_bm() : moe::gemm_bf16_bm();
 }
 int gemm_bn(const moe_config_t* c) {
   return gemm_path(c) == PATH_F32 ? moe::gemm_f32_bn() : moe::gemm_bf16_bn();
@@ -274,7 +273,7 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
                   const char* what) -> int {
     hipError_t e = hipSuccess;
     if (path != PATH_SKINNY) {
-      const int merge = path == PATH_TILED ? moe::gemm_bf16_merge_rows(bm) : 0;
+      const int merge = path == PATH_TILED ? moe::gemm_bf16_merge_rows() : 0;
       e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.list[list],
                                 fw.count + list, s);
       if (e != hipSuccess) return hip_status(e, "tile list launch");
@@ -287,7 +286,7 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
     else if (path == PATH_SKINNY)
       e = moe::launch_gemm_skinny_bf16(g, gelu, 0, s);
     else
-      e = moe::launch_gemm_bf16(g, bm, gelu, s);
+      e = moe::launch_gemm_bf16(g, gelu, s);
     return e == hipSuccess ? MOE_OK : hip_status(e, what);
   };
 

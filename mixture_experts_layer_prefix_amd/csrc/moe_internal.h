@@ -110,12 +110,13 @@ struct GemmArgs {
   int64_t grid_tiles;   // upper bound on the tile count (grid size)
 };
 
-// Prefill-shaped grouped GEMM (bf16 MFMA): tiles of bm (256 or 128) x
-// gemm_bf16_bn() rows x columns.
+// Prefill-shaped grouped GEMM (bf16 MFMA): tiles of gemm_bf16_bm() x
+// gemm_bf16_bn() rows x columns; an expert block's last remainder of up to
+// gemm_bf16_merge_rows() rows is folded into its last full tile.
+int gemm_bf16_bm();
 int gemm_bf16_bn();
-// Remainder rows the bm-row kernel folds into an expert's last full tile.
-int gemm_bf16_merge_rows(int bm);
-hipError_t launch_gemm_bf16(const GemmArgs& a, int bm, bool gelu, hipStream_t s);
+int gemm_bf16_merge_rows();
+hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s);
 // fp32 grouped GEMM (VALU), BM rows per tile.
 int gemm_f32_bm();
 int gemm_f32_bn();

@@ -3,7 +3,8 @@
 The grouped GEMM picks its tile shape per expert block from the number of
 rows left in the block and folds a short remainder into the block's last full
 tile, so the counts below put the last tile of the blocks on every side of the
-64-, 128-, 256- and 320-row boundaries (and leave some experts empty).  Each expert's rows are checked against the oracle's
+64-, 128-, 256- and 320-row boundaries (and leave some experts empty).  Each
+expert's rows are checked against the oracle's
 E(x) = W2 GELU(W1 x + b1) + b2, and the rows past the last expert's block must
 stay untouched."""
 import numpy as np
@@ -18,14 +19,14 @@ pytestmark = pytest.mark.gpu
 
 SENTINEL = 0x7FC1   # a bf16 NaN pattern the kernels never write
 
-# counts per expert; the tile height is chosen from count mod 256 (the last tile)
+# counts per expert
 COUNTS = {
-    # T*K >= 200*N: 256-row tiles; a remainder of up to 64 rows after a full
-    # tile is folded into it (257, 319, 320, 1057, 1088), 65 or more is not (321)
+    # a remainder of up to 64 rows after a full tile is folded into it
+    # (257, 319, 320, 1057, 1088), 65 or more is not (321)
     "tiles256": [0, 1, 63, 64, 65, 128, 129, 256, 257, 319, 320, 321, 384, 511, 700, 1057,
                  1088],
-    # T*K < 200*N: 128-row tiles
-    "tiles128": [0, 1, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 130, 3, 0, 40],
+    # many experts of about a tile or less (a fine-grained layout)
+    "small_blocks": [0, 1, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 130, 3, 0, 40],
 }
 
 
