@@ -19,11 +19,10 @@
 //   1. router GEMM on the fp64 matrix cores (v_mfma_f64_16x16x4f64): each
 //      workgroup takes a tile of tokens x experts and one slice of the model
 //      dimension, and writes fp64 partial dot products.  The slice count S
-//      is chosen so that even a handful of tokens fills the chip; S = 1 for
-//      large batches.  Each lane feeds the MFMA from 16 consecutive elements
-//      of its row (one 32- or 64-byte load), so the k order inside a 64-wide
-//      chunk is permuted identically for x and W_r -- the dot product does
-//      not depend on it;
+//      is chosen so that there are about four workgroups per CU.  Each lane
+//      feeds the MFMA from 16 consecutive elements of its row (one 32- or
+//      64-byte load), so the k order inside a 64-wide chunk is permuted
+//      identically for x and W_r -- the dot product does not depend on it;
 //   2. select: one wavefront per token sums the S partials in slice order,
 //      adds the router bias and offset in fp64, rounds once to fp32, writes
 //      the logits, and picks the Top-K with a 64-lane arg-max reduction.
@@ -244,13 +243,15 @@ hipError_t launch_gemm_t(const Shape& sh, int S, int klen, const void* x, const 
 
 }  // namespace
 
-// Slices of the model dimension: enough workgroups to fill the chip, each
-// slice a whole number of 64-wide chunks, no empty slice.
+// Slices of the model dimension: about four workgroups per CU, so each CU
+// has several wavefronts per SIMD to cover the latency of the operand loads
+// (they go straight from L2 to registers); each slice a whole number of
+// 64-wide chunks, no empty slice.
 int route_splits(int T, int d, int N) {
   const Shape sh = shape_for(T, N);
   const int tiles = sh.tiles_t * sh.tiles_e;
   const int chunks = d / KC;
-  int S = (256 + tiles - 1) / tiles;
+  int S = (1024 + tiles - 1) / tiles;
   if (S > chunks) S = chunks;
   if (S < 1) S = 1;
   const int per = (chunks + S - 1) / S;
