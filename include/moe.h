@@ -182,6 +182,18 @@ int moe_combine(const moe_config_t *cfg, const void *y_perm, const int32_t *slot
 int moe_aux_loss(const moe_config_t *cfg, const float *logits, const int32_t *counts,
                  float *loss_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Router z-loss (lmnt.cn MoE walkthrough §5.3, router z-loss equation):
+ * beta * (1/T) sum_t (logsumexp_e logits[t, e])^2, which penalises large
+ * router logits.  Computed in fp64 with a fixed reduction order; written as
+ * fp32.
+ *   logits [dev] [T, N] fp32 in (from moe_route);  beta: finite weight;
+ *   loss_out [dev] [1] fp32 out;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes.
+ * Errors: MOE_ERR_INVALID_ARG for NULL logits / loss_out or a non-finite
+ * beta, MOE_ERR_WORKSPACE for a short or misaligned workspace. */
+int moe_router_z_loss(const moe_config_t *cfg, const float *logits, float beta, float *loss_out,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* The whole layer: route -> dispatch -> expert FFN (+ shared expert) ->
  * combine (-> aux loss when aux_out != NULL).  Same kernels and results as
  * calling the stages in order.

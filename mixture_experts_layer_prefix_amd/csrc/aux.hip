@@ -88,7 +88,64 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict
   if (threadIdx.x == 0) loss[0] = (float)((double)alpha * (double)N * term[0]);
 }
 
+// Router z-loss (lmnt.cn MoE walkthrough §5.3): beta * mean_t lse_t^2 with
+// lse_t = logsumexp_e logits[t, e], in fp64.  Pass 1: a wavefront per token
+// row (lane = expert) forms lse = m + log(sum exp(l - m)); each wavefront adds
+// its rows' lse^2 in token order, the 4 wavefronts' sums are added in order
+// into zpart[block].  Pass 2: one wavefront adds zpart over the blocks (lanes
+// stride, then a fixed butterfly).
+__global__ __launch_bounds__(256) void zloss_partial_kernel(const float* __restrict__ logits, int T,
+                                                            int N, double* __restrict__ zpart) {
+  __shared__ double part[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double acc = 0.0;
+  const int t0 = blockIdx.x * TB;
+  for (int tt = wave; tt < TB; tt += 4) {
+    const int t = t0 + tt;
+    if (t >= T) break;
+    const float* row = logits + (int64_t)t * N;
+    double l[4];
+    double m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = lane + 64 * v;
+      l[v] = (e < N) ? (double)row[e] : -INFINITY;
+      m = fmax(m, l[v]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+    double sum = 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sum += (lane + 64 * v < N) ? exp(l[v] - m) : 0.0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const double lse = m + log(sum);
+    acc += lse * lse;
+  }
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) zpart[blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+__global__ __launch_bounds__(64) void zloss_final_kernel(const double* __restrict__ zpart, int nblk,
+                                                         int T, float beta,
+                                                         float* __restrict__ loss) {
+  double z = 0.0;
+  for (int b = threadIdx.x; b < nblk; b += 64) z += zpart[b];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  if (threadIdx.x == 0) loss[0] = (float)((double)beta * (z / (double)T));
+}
+
 }  // namespace
+
+hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,
+                        float* loss_out, hipStream_t s) {
+  const int nblk = aux_blocks(T);
+  hipLaunchKernelGGL(zloss_partial_kernel, dim3(nblk), dim3(256), 0, s, logits, T, N, zpart);
+  hipLaunchKernelGGL(zloss_final_kernel, dim3(1), dim3(64), 0, s, zpart, nblk, T, beta, loss_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
                       double* ppart, float* loss_out, hipStream_t s) {

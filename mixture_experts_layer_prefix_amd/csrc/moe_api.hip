@@ -97,6 +97,7 @@ struct FfnWs {
 };
 struct AuxWs {
   double* ppart;
+  double* zpart;
 };
 struct LayerWs {
   float* logits;
@@ -146,6 +147,7 @@ void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w) {
 
 void carve_aux(Carver& cv, const moe_config_t* c, AuxWs* w) {
   w->ppart = cv.take<double>((size_t)moe::aux_blocks(c->T) * c->n_experts * sizeof(double));
+  w->zpart = cv.take<double>((size_t)moe::aux_blocks(c->T) * sizeof(double));
 }
 
 void carve_layer(Carver& cv, const moe_config_t* c, LayerWs* w) {
@@ -494,6 +496,22 @@ int moe_aux_loss(const moe_config_t* cfg, const float* logits, const int32_t* co
   AuxWs aw;
   carve_aux(cv, cfg, &aw);
   return do_aux(cfg, logits, counts, loss_out, aw, stream);
+}
+
+int moe_router_z_loss(const moe_config_t* cfg, const float* logits, float beta, float* loss_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(logits, "logits");
+  if (!loss_out) return fail(MOE_ERR_INVALID_ARG, "loss_out is NULL");
+  if (!isfinite(beta)) return fail(MOE_ERR_INVALID_ARG, "beta is not finite");
+  int r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  AuxWs aw;
+  carve_aux(cv, cfg, &aw);
+  return hip_status(moe::launch_zloss(logits, cfg->T, cfg->n_experts, beta, aw.zpart, loss_out,
+                                      stream),
+                    "moe_router_z_loss launch");
 }
 
 int moe_layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_t* w, void* out,

@@ -135,5 +135,9 @@ constexpr int kAuxTokensPerBlock = 64;
 inline int aux_blocks(int T) { return (T + kAuxTokensPerBlock - 1) / kAuxTokensPerBlock; }
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
                       double* ppart, float* loss_out, hipStream_t s);
+// Router z-loss: beta * mean_t logsumexp(logits[t])^2 in fp64; zpart holds
+// aux_blocks(T) doubles.
+hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,
+                        float* loss_out, hipStream_t s);
 
 }  // namespace moe

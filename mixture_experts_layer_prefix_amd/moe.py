@@ -18,8 +18,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5}
 ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
-                "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_layer_forward",
-                "moe_last_error")
+                "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_router_z_loss",
+                "moe_layer_forward", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -66,8 +66,10 @@ def lib():
     L.moe_expert_ffn.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, sz, vp]
     L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     L.moe_aux_loss.argtypes = [cfgp, vp, vp, vp, vp, sz, vp]
+    L.moe_router_z_loss.argtypes = [cfgp, vp, ctypes.c_float, vp, vp, sz, vp]
     L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
+                 "moe_router_z_loss",
                  "moe_layer_forward"):
         getattr(L, name).restype = ctypes.c_int
     L.moe_last_error.argtypes = []
@@ -173,6 +175,12 @@ def moe_aux_loss(cfg, logits, counts, loss_out, ws, stream=None):
     p, n = _ws(ws)
     _check(lib().moe_aux_loss(ctypes.byref(cfg), _p(logits), _p(counts), _p(loss_out), p, n,
                               _stream(stream)))
+
+
+def moe_router_z_loss(cfg, logits, beta, loss_out, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_router_z_loss(ctypes.byref(cfg), _p(logits), float(beta), _p(loss_out), p, n,
+                                   _stream(stream)))
 
 
 def moe_layer_forward(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,

@@ -88,6 +88,15 @@ def test_null_and_misaligned_pointers_rejected():
     L = moe.lib()
     assert L.moe_combine(ctypes.byref(cfg), FAKE, FAKE, FAKE, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_aux_loss(ctypes.byref(cfg), FAKE, FAKE, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_z_loss(ctypes.byref(cfg), None, ctypes.c_float(1e-3), FAKE, FAKE * 256,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, ctypes.c_float(1e-3), None, FAKE * 256,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, ctypes.c_float(float("nan")), FAKE,
+                               FAKE * 256, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"beta" in L.moe_last_error()
+    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, ctypes.c_float(1e-3), FAKE, None, 0,
+                               None) == moe.MOE_ERR_WORKSPACE
     W = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=None)
     assert L.moe_expert_ffn(ctypes.byref(cfg), FAKE, FAKE, ctypes.byref(W), None, FAKE, None,
                             FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG

@@ -1,8 +1,8 @@
 """GPU parity at the five workload sizes, in the launch configuration bench.py
 times (the same C-ABI stage calls).
 
-Routing, dispatch and aux loss are compared over every token (integers bit-
-exact).  The expert FFN and the layer output are compared on sampled rows
+Routing, dispatch, aux loss and router z-loss are compared over every token
+(integers bit-exact).  The expert FFN and the layer output are compared on sampled rows
 the oracle computes one by one: sampled tokens' output rows, and sampled
 permuted rows of y_perm against E_e(x[token]) directly."""
 import gc
@@ -51,6 +51,14 @@ def test_full_size(shape):
     if shape.aux_alpha:
         assert abs(g["aux"] - o_route["aux"]) <= AUX_TOL * abs(o_route["aux"])
         say(f"  aux {g['aux']:.8f} vs oracle {o_route['aux']:.8f}")
+    # router z-loss over every token: GPU entry point against the oracle on
+    # the oracle's own logits (equal to the GPU's to an ulp)
+    zl = torch.empty(1, dtype=torch.float32, device="cuda")
+    moe.moe_router_z_loss(cfg, torch.from_numpy(g["logits"]).cuda(), 1e-3, zl,
+                          moe.alloc_workspace(cfg, "aux"))
+    z_ref = O.router_z_loss(o_route["logits"], 1e-3)
+    assert abs(float(zl.item()) - z_ref) <= AUX_TOL * abs(z_ref), (float(zl.item()), z_ref)
+    say(f"  z-loss {float(zl.item()):.8f} vs oracle {z_ref:.8f}")
 
     toks = _sample_tokens(shape, o_route)
     o = oracle_run(inp, cap, out_tokens=toks)

@@ -78,6 +78,13 @@ def _compare(name, shape, inp, cfg):
     else:
         g_aux = g["aux"]
     assert abs(g_aux - aux_ref) <= AUX_TOL * abs(aux_ref), (g_aux, aux_ref)
+    # router z-loss on the same logits (the GPU's logits equal the oracle's
+    # to an ulp; the loss is checked against the oracle on the GPU's logits)
+    z = torch.empty(1, dtype=torch.float32, device="cuda")
+    moe.moe_router_z_loss(cfg, torch.from_numpy(g["logits"]).cuda(), 1e-3, z,
+                          moe.alloc_workspace(cfg, "aux"))
+    z_ref = O.router_z_loss(g["logits"], 1e-3)
+    assert abs(float(z.item()) - z_ref) <= AUX_TOL * abs(z_ref), (float(z.item()), z_ref)
     # the whole-layer entry point runs the same kernels: bitwise equal to the stages
     lay = run_layer(cfg, t, aux=cfg.aux_alpha != 0)
     assert torch.equal(lay["out"].float().cpu(), torch.from_numpy(g["out"]))

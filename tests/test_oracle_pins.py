@@ -206,6 +206,27 @@ def test_z_loss_closed_form():
     assert O.router_z_loss(logits, beta) == pytest.approx(beta * math.log(N) ** 2, rel=1e-12)
 
 
+def test_z_loss_constant_rows():
+    # row t constant c_t: logsumexp = c_t + ln N, so the loss is
+    # beta * mean_t (c_t + ln N)^2 (a dropped max shift or a missing log fails)
+    N, beta = 16, 0.5
+    c = np.array([-30.0, -2.5, 0.0, 1.25, 40.0], dtype=np.float32)
+    logits = np.repeat(c[:, None], N, axis=1)
+    want = beta * np.mean((c.astype(np.float64) + math.log(N)) ** 2)
+    assert O.router_z_loss(logits, beta) == pytest.approx(want, rel=1e-12)
+
+
+def test_z_loss_scalar_brute_force():
+    rng = np.random.default_rng(11)
+    T, N, beta = 7, 5, 1e-3
+    logits = (rng.standard_normal((T, N)) * 3).astype(np.float32)
+    tot = 0.0
+    for t in range(T):
+        lse = math.log(sum(math.exp(float(v)) for v in logits[t]))
+        tot += lse * lse
+    assert O.router_z_loss(logits, beta) == pytest.approx(beta * tot / T, rel=1e-12)
+
+
 # ---------------------------------------------------------------- whole layer
 def _tiny_problem(rng, T, d, f, N, *, biases=True, fs=0):
     x = _bf16_values(rng, (T, d))
