@@ -28,22 +28,27 @@ __device__ __forceinline__ float gelu_erf(float z) {
 }
 
 // GELU with erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + ... + a5 t^5) exp(-x^2),
-// t = 1 / (1 + p x), |error| <= 1.5e-7; odd symmetry for x < 0.  One
-// reciprocal, one exp2 and a few fma: far cheaper than a full libm erf, and
-// its error is 1e-4 of a bf16 ulp of the result.
+// formula 7.1.26: for x >= 0, erf(x) = 1 - P(t) exp(-x^2), P(t) = a1 t + ... +
+// a5 t^5, t = 1 / (1 + p x), |error| <= 1.5e-7; odd symmetry for x < 0.
+// With x = |z| / sqrt(2) both signs of z collapse to
+//   GELU(z) = max(z, 0) - |z|/2 * P(t) * exp(-z^2 / 2),
+// which the code evaluates with the -1/2 folded into the coefficients: one
+// reciprocal, one exp2 and ten other VALU operations (this runs on every
+// element of the first GEMM's output, at a quarter of the MFMA tile's time
+// budget when it was written naively).  Its error is 1e-4 of a bf16 ulp of
+// the result.
 __device__ __forceinline__ float gelu_as(float z) {
-  const float x = fabsf(z) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float p = fmaf(1.061405429f, t, -1.453152027f);
-  p = fmaf(p, t, 1.421413741f);
-  p = fmaf(p, t, -0.284496736f);
-  p = fmaf(p, t, 0.254829592f);
-  p *= t;
-  const float e = __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
-  const float erf_abs = fmaf(-p, e, 1.0f);
-  const float erf_z = copysignf(erf_abs, z);
-  return 0.5f * z * (1.0f + erf_z);
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189f, az, 1.0f));   // p / sqrt(2)
+  float q = fmaf(-0.5307027145f, t, 0.7265760135f);   // -a5/2, -a4/2
+  q = fmaf(q, t, -0.7107068705f);                      // -a3/2
+  q = fmaf(q, t, 0.1422483680f);                       // -a2/2
+  q = fmaf(q, t, -0.1274147960f);                      // -a1/2
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170368f);   // exp(-z^2/2)
+  // max(z, 0) as one v_max_f32 (fmaxf adds a NaN-quieting max in front)
+  float relu;
+  asm("v_max_f32 %0, 0, %1" : "=v"(relu) : "v"(z));
+  return fmaf(az * t, q * e, relu);
 }
 
 template <typename T> struct Elem;
