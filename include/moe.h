@@ -174,8 +174,9 @@ int moe_combine(const moe_config_t *cfg, const void *y_perm, const int32_t *slot
 /* Switch auxiliary load-balance loss (yunthe.com "专家负载均衡与辅助损失函数设计";
  * lmnt.cn §5.1): alpha * N * sum_e f_e * P_e, with f_e = counts[e] / T (mean
  * of the pre-drop 0/1 selection mask, so sum f = K) and P_e the mean over
- * tokens of softmax_N(logits[t])_e.  Computed in fp64 with a fixed reduction
- * order; written as fp32.
+ * tokens of softmax_N(logits[t])_e.  Exponentials in fp32, all sums and
+ * products in fp64, with a fixed reduction order (deterministic); written as
+ * fp32.  Relative error ~1e-7.
  *   logits [dev] [T, N] fp32 in;  counts [dev] [N] int32 in (from moe_dispatch);
  *   loss_out [dev] [1] fp32 out;  alpha = cfg->aux_alpha;
  *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes. */
@@ -184,8 +185,8 @@ int moe_aux_loss(const moe_config_t *cfg, const float *logits, const int32_t *co
 
 /* Router z-loss (lmnt.cn MoE walkthrough §5.3, router z-loss equation):
  * beta * (1/T) sum_t (logsumexp_e logits[t, e])^2, which penalises large
- * router logits.  Computed in fp64 with a fixed reduction order; written as
- * fp32.
+ * router logits.  Exponentials in fp32, sums and logarithm in fp64, with a
+ * fixed reduction order (deterministic); written as fp32.
  *   logits [dev] [T, N] fp32 in (from moe_route);  beta: finite weight;
  *   loss_out [dev] [1] fp32 out;
  *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes.

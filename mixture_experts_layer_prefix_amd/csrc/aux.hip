@@ -1,21 +1,29 @@
-// Switch auxiliary load-balance loss.
+// Switch auxiliary load-balance loss and router z-loss.
 //
-// What it computes (yunthe.com "MoE混合专家模型实战", section
-// "专家负载均衡与辅助损失函数设计": alpha * num_experts * sum(f * P) with f the
-// per-expert mean of the 0/1 selection mask and P the per-expert mean of the
-// softmax router probabilities; lmnt.cn MoE walkthrough §5.1, same product):
+// Aux loss (yunthe.com "MoE混合专家模型实战", section "专家负载均衡与辅助损失函数设计":
+// alpha * num_experts * sum(f * P) with f the per-expert mean of the 0/1
+// selection mask and P the per-expert mean of the softmax router
+// probabilities; lmnt.cn MoE walkthrough §5.1, same product):
 //   P_e  = (1/T) sum_t softmax_N(logits[t])_e
 //   f_e  = counts[e] / T          (pre-drop selections, sum_e f_e = K)
 //   loss = alpha * N * sum_e f_e * P_e
-// in fp64 with a fixed reduction order, so the result is deterministic.
+// Router z-loss (lmnt.cn MoE walkthrough §5.3): beta * mean_t lse_t^2 with
+// lse_t = logsumexp_e logits[t, e].
 //
-// Pass 1: each workgroup of 4 wavefronts takes 64 tokens; a wavefront takes
-// one token row at a time (lane = expert, up to 4 experts per lane), forms
-// the row's softmax and adds it to per-lane sums; the 4 wavefronts' sums are
-// added in wavefront order into ppart[block, e].
-// Pass 2: one workgroup; a wavefront per expert adds ppart over the blocks
-// (lanes stride over blocks, then a fixed butterfly), multiplies by f_e, and
-// the experts' terms are reduced with a fixed tree.
+// Both use a fixed reduction order, so the results are deterministic: the row
+// max and the exponentials in fp32 (relative error ~1e-7 per term, each in
+// (0, 1]), every sum, logarithm, normalisation and product in fp64.
+//
+// Pass 1: a workgroup of 4 wavefronts takes TB = 16 tokens; a wavefront loads
+// its 4 token rows at once (lane = expert, up to 4 experts per lane), then
+// forms each row's softmax (or logsumexp) and adds it to per-lane sums in
+// token order; the 4 wavefronts' sums are added in wavefront order into
+// ppart[block, e] (or zpart[block]).
+// Pass 2, aux: a wavefront per expert adds column e of ppart (lanes stride
+// over the blocks, then a fixed butterfly) and multiplies by f_e; pass 3, one
+// workgroup reduces the experts' terms with a fixed tree.  Z-loss: one
+// wavefront adds zpart (lanes stride over the blocks, then a fixed
+// butterfly).
 #include <math.h>
 
 #include "moe_internal.h"
@@ -24,37 +32,60 @@ namespace moe {
 namespace {
 
 constexpr int TB = kAuxTokensPerBlock;
+constexpr int RPW = TB / 4;            // token rows per wavefront
+
+// Row max and fp32 exponentials of one token row (lane = expert e, e + 64,
+// e + 128, e + 192); returns the row's sum of exponentials in fp64.
+__device__ __forceinline__ double row_exp(const float (&l)[4], int lane, int N, double (&ex)[4],
+                                          float& m) {
+  m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) m = fmaxf(m, l[v]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  double s = 0.0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    ex[v] = (lane + 64 * v < N) ? (double)expf(l[v] - m) : 0.0;
+    s += ex[v];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  return s;
+}
+
+// The wavefront's RPW rows, loaded before any arithmetic so their loads are
+// in flight together; entries past T or N read as -inf (rows past T are
+// skipped by the callers).
+__device__ __forceinline__ void load_rows(const float* __restrict__ logits, int T, int N, int t0,
+                                          int lane, float (&l)[RPW][4]) {
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int t = t0 + r;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = lane + 64 * v;
+      l[r][v] = (t < T && e < N) ? logits[(int64_t)t * N + e] : -INFINITY;
+    }
+  }
+}
 
 __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
                                                           int N, double* __restrict__ ppart) {
   __shared__ double part[4][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TB + wave * RPW;
+  float l[RPW][4];
+  load_rows(logits, T, N, t0, lane, l);
   double ps[4] = {0.0, 0.0, 0.0, 0.0};
-  const int t0 = blockIdx.x * TB;
-  for (int tt = wave; tt < TB; tt += 4) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    const float* row = logits + (int64_t)t * N;
-    double l[4];
-    double m = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int e = lane + 64 * v;
-      l[v] = (e < N) ? (double)row[e] : -INFINITY;
-      m = fmax(m, l[v]);
-    }
+  for (int r = 0; r < RPW; ++r) {
+    if (t0 + r >= T) break;
+    double ex[4];
+    float m;
+    const double inv = 1.0 / row_exp(l[r], lane, N, ex, m);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
-    double ex[4], s = 0.0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      ex[v] = (lane + 64 * v < N) ? exp(l[v] - m) : 0.0;
-      s += ex[v];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) ps[v] += ex[v] / s;
+    for (int v = 0; v < 4; ++v) ps[v] += ex[v] * inv;
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) part[wave][lane + 64 * v] = ps[v];
@@ -63,63 +94,50 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
     ppart[(int64_t)blockIdx.x * N + e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
 }
 
-__global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict__ ppart, int nblk,
+// One wavefront per expert e: lanes stride over the blocks (their loads are
+// independent and unrolled so they are in flight together), a fixed butterfly
+// adds the lanes; term[e] = f_e * P_e.
+__global__ __launch_bounds__(64) void aux_column_kernel(const double* __restrict__ ppart, int nblk,
                                                         const int32_t* __restrict__ counts, int T,
-                                                        int N, float alpha,
-                                                        float* __restrict__ loss) {
-  __shared__ double term[256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // wavefront w takes experts w, w+4, ...; its lanes stride over the blocks
-  // (each lane sums its blocks in order, then a fixed butterfly)
-  for (int e = wave; e < N; e += 4) {
-    double P = 0.0;
-    for (int b = lane; b < nblk; b += 64) P += ppart[(int64_t)b * N + e];
+                                                        int N, double* __restrict__ term) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  double P = 0.0;
+#pragma unroll 8
+  for (int b = lane; b < nblk; b += 64) P += ppart[(int64_t)b * N + e];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) P += __shfl_xor(P, off, 64);
-    if (lane == 0) term[e] = ((double)counts[e] / (double)T) * (P / (double)T);
-  }
-  __syncthreads();
-  if (threadIdx.x >= N) term[threadIdx.x] = 0.0;
-  __syncthreads();
-  for (int h = 128; h >= 1; h >>= 1) {
-    if (threadIdx.x < h) term[threadIdx.x] += term[threadIdx.x + h];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) loss[0] = (float)((double)alpha * (double)N * term[0]);
+  for (int off = 32; off >= 1; off >>= 1) P += __shfl_xor(P, off, 64);
+  if (lane == 0) term[e] = ((double)counts[e] / (double)T) * (P / (double)T);
 }
 
-// Router z-loss (lmnt.cn MoE walkthrough §5.3): beta * mean_t lse_t^2 with
-// lse_t = logsumexp_e logits[t, e], in fp64.  Pass 1: a wavefront per token
-// row (lane = expert) forms lse = m + log(sum exp(l - m)); each wavefront adds
-// its rows' lse^2 in token order, the 4 wavefronts' sums are added in order
-// into zpart[block].  Pass 2: one wavefront adds zpart over the blocks (lanes
-// stride, then a fixed butterfly).
+// The experts' terms in a fixed tree.
+__global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict__ term, int N,
+                                                        float alpha, float* __restrict__ loss) {
+  __shared__ double t[256];
+  const int e = threadIdx.x;
+  t[e] = e < N ? term[e] : 0.0;
+  __syncthreads();
+  for (int h = 128; h >= 1; h >>= 1) {
+    if (e < h) t[e] += t[e + h];
+    __syncthreads();
+  }
+  if (e == 0) loss[0] = (float)((double)alpha * (double)N * t[0]);
+}
+
 __global__ __launch_bounds__(256) void zloss_partial_kernel(const float* __restrict__ logits, int T,
                                                             int N, double* __restrict__ zpart) {
   __shared__ double part[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * TB + wave * RPW;
+  float l[RPW][4];
+  load_rows(logits, T, N, t0, lane, l);
   double acc = 0.0;
-  const int t0 = blockIdx.x * TB;
-  for (int tt = wave; tt < TB; tt += 4) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    const float* row = logits + (int64_t)t * N;
-    double l[4];
-    double m = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int e = lane + 64 * v;
-      l[v] = (e < N) ? (double)row[e] : -INFINITY;
-      m = fmax(m, l[v]);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
-    double sum = 0.0;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sum += (lane + 64 * v < N) ? exp(l[v] - m) : 0.0;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    const double lse = m + log(sum);
+  for (int r = 0; r < RPW; ++r) {
+    if (t0 + r >= T) break;
+    double ex[4];
+    float m;
+    const double s = row_exp(l[r], lane, N, ex, m);
+    const double lse = (double)m + log(s);
     acc += lse * lse;
   }
   if (lane == 0) part[wave] = acc;
@@ -131,6 +149,7 @@ __global__ __launch_bounds__(64) void zloss_final_kernel(const double* __restric
                                                          int T, float beta,
                                                          float* __restrict__ loss) {
   double z = 0.0;
+#pragma unroll 8
   for (int b = threadIdx.x; b < nblk; b += 64) z += zpart[b];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
@@ -148,11 +167,11 @@ hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* z
 }
 
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
-                      double* ppart, float* loss_out, hipStream_t s) {
+                      double* ppart, double* term, float* loss_out, hipStream_t s) {
   const int nblk = aux_blocks(T);
   hipLaunchKernelGGL(aux_partial_kernel, dim3(nblk), dim3(256), 0, s, logits, T, N, ppart);
-  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, s, ppart, nblk, counts, T, N, alpha,
-                     loss_out);
+  hipLaunchKernelGGL(aux_column_kernel, dim3(N), dim3(64), 0, s, ppart, nblk, counts, T, N, term);
+  hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, s, term, N, alpha, loss_out);
   return hipGetLastError();
 }
 

@@ -97,6 +97,7 @@ struct FfnWs {
 };
 struct AuxWs {
   double* ppart;
+  double* term;
   double* zpart;
 };
 struct LayerWs {
@@ -147,6 +148,7 @@ void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w) {
 
 void carve_aux(Carver& cv, const moe_config_t* c, AuxWs* w) {
   w->ppart = cv.take<double>((size_t)moe::aux_blocks(c->T) * c->n_experts * sizeof(double));
+  w->term = cv.take<double>((size_t)c->n_experts * sizeof(double));
   w->zpart = cv.take<double>((size_t)moe::aux_blocks(c->T) * sizeof(double));
 }
 
@@ -353,7 +355,7 @@ int do_combine(const moe_config_t* c, const void* y_perm, const int32_t* slot_ro
 int do_aux(const moe_config_t* c, const float* logits, const int32_t* counts, float* loss,
            const AuxWs& aw, hipStream_t s) {
   return hip_status(moe::launch_aux(logits, counts, c->T, c->n_experts, c->aux_alpha, aw.ppart,
-                                    loss, s),
+                                    aw.term, loss, s),
                     "moe_aux_loss launch");
 }
 

@@ -135,11 +135,12 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* slot_row
                           const float* topk_w, const void* y_shared, void* out, int T, int d,
                           int K, hipStream_t s);
 
-// Aux loss: per-block partial sums of softmax probabilities, then the final sum.
-constexpr int kAuxTokensPerBlock = 64;
+// Aux loss: per-block partial sums of softmax probabilities (ppart holds
+// aux_blocks(T) * N doubles), per-expert terms (term: N doubles), the sum.
+constexpr int kAuxTokensPerBlock = 16;
 inline int aux_blocks(int T) { return (T + kAuxTokensPerBlock - 1) / kAuxTokensPerBlock; }
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
-                      double* ppart, float* loss_out, hipStream_t s);
+                      double* ppart, double* term, float* loss_out, hipStream_t s);
 // Router z-loss: beta * mean_t logsumexp(logits[t])^2 in fp64; zpart holds
 // aux_blocks(T) doubles.
 hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,
