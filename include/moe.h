@@ -183,6 +183,21 @@ int moe_combine(const moe_config_t *cfg, const void *y_perm, const int32_t *slot
 int moe_aux_loss(const moe_config_t *cfg, const float *logits, const int32_t *counts,
                  float *loss_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Routing statistics (lmnt.cn MoE walkthrough §8.2, measuring the routing
+ * distribution: tokens received per expert and the mean routing weight; the
+ * drop count is moe_dispatch's n_dropped): counts_out[e] = number of (t, k) with topk_idx[t, k] == e (before
+ * capacity drops, equal to moe_dispatch's counts); weight_mean_out[e] = the
+ * mean of topk_w[t, k] over those pairs, 0 for an expert nobody chose.  Sums
+ * in fp64 with a fixed order (deterministic); the means are written as fp32.
+ *   topk_idx [dev] [T, K] int32 in;  topk_w [dev] [T, K] fp32 in (moe_route);
+ *   counts_out [dev] [N] int32 out or NULL;  weight_mean_out [dev] [N] fp32 out;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes.
+ * Errors: MOE_ERR_INVALID_ARG for NULL or misaligned required pointers,
+ * MOE_ERR_WORKSPACE for a short or misaligned workspace. */
+int moe_routing_stats(const moe_config_t *cfg, const int32_t *topk_idx, const float *topk_w,
+                      int32_t *counts_out, float *weight_mean_out, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
 /* Router z-loss (lmnt.cn MoE walkthrough §5.3, router z-loss equation):
  * beta * (1/T) sum_t (logsumexp_e logits[t, e])^2, which penalises large
  * router logits.  Exponentials in fp32, sums and logarithm in fp64, with a

@@ -1,4 +1,4 @@
-// Switch auxiliary load-balance loss and router z-loss.
+// Switch auxiliary load-balance loss, router z-loss, routing statistics.
 //
 // Aux loss (yunthe.com "MoE混合专家模型实战", section "专家负载均衡与辅助损失函数设计":
 // alpha * num_experts * sum(f * P) with f the per-expert mean of the 0/1
@@ -156,7 +156,74 @@ __global__ __launch_bounds__(64) void zloss_final_kernel(const double* __restric
   if (threadIdx.x == 0) loss[0] = (float)((double)beta * (z / (double)T));
 }
 
+// Routing statistics (lmnt.cn MoE walkthrough §8.2: tokens per expert and
+// mean routing weight).  Pass 1: a workgroup stages the (expert, weight) pairs
+// of STB tokens in LDS; thread e walks them in token-major order and counts
+// the pairs routed to expert e and adds their weights (fp64).  Pass 2: a
+// wavefront per expert adds the blocks' partials (lanes stride over the
+// blocks, then a fixed butterfly).
+constexpr int STB = kStatsTokensPerBlock;
+
+__global__ __launch_bounds__(256) void stats_partial_kernel(const int32_t* __restrict__ idx,
+                                                            const float* __restrict__ w, int T,
+                                                            int K, int N,
+                                                            int32_t* __restrict__ pcnt,
+                                                            double* __restrict__ pw) {
+  __shared__ int32_t s_idx[STB * 64];
+  __shared__ float s_w[STB * 64];
+  const int64_t p0 = (int64_t)blockIdx.x * STB * K;
+  const int np = (int)(min((int64_t)(blockIdx.x + 1) * STB, (int64_t)T) * K - p0);
+  for (int i = threadIdx.x; i < np; i += 256) {
+    s_idx[i] = idx[p0 + i];
+    s_w[i] = w[p0 + i];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256) {
+    int c = 0;
+    double sw = 0.0;
+    for (int i = 0; i < np; ++i)
+      if (s_idx[i] == e) {
+        ++c;
+        sw += (double)s_w[i];
+      }
+    pcnt[(int64_t)blockIdx.x * N + e] = c;
+    pw[(int64_t)blockIdx.x * N + e] = sw;
+  }
+}
+
+__global__ __launch_bounds__(64) void stats_final_kernel(const int32_t* __restrict__ pcnt,
+                                                         const double* __restrict__ pw, int nblk,
+                                                         int N, int32_t* __restrict__ counts,
+                                                         float* __restrict__ wmean) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  int c = 0;
+  double sw = 0.0;
+#pragma unroll 4
+  for (int b = lane; b < nblk; b += 64) {
+    c += pcnt[(int64_t)b * N + e];
+    sw += pw[(int64_t)b * N + e];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    c += __shfl_xor(c, off, 64);
+    sw += __shfl_xor(sw, off, 64);
+  }
+  if (lane == 0) {
+    if (counts) counts[e] = c;
+    wmean[e] = c > 0 ? (float)(sw / (double)c) : 0.0f;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stats(const int32_t* topk_idx, const float* topk_w, int T, int K, int N,
+                        int32_t* pcnt, double* pw, int32_t* counts, float* wmean, hipStream_t s) {
+  const int nblk = stats_blocks(T);
+  hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, topk_w, T, K, N,
+                     pcnt, pw);
+  hipLaunchKernelGGL(stats_final_kernel, dim3(N), dim3(64), 0, s, pcnt, pw, nblk, N, counts, wmean);
+  return hipGetLastError();
+}
 
 hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,
                         float* loss_out, hipStream_t s) {

@@ -99,6 +99,8 @@ struct AuxWs {
   double* ppart;
   double* term;
   double* zpart;
+  double* spw;          // routing statistics partials
+  int32_t* spcnt;
 };
 struct LayerWs {
   float* logits;
@@ -150,6 +152,8 @@ void carve_aux(Carver& cv, const moe_config_t* c, AuxWs* w) {
   w->ppart = cv.take<double>((size_t)moe::aux_blocks(c->T) * c->n_experts * sizeof(double));
   w->term = cv.take<double>((size_t)c->n_experts * sizeof(double));
   w->zpart = cv.take<double>((size_t)moe::aux_blocks(c->T) * sizeof(double));
+  w->spw = cv.take<double>((size_t)moe::stats_blocks(c->T) * c->n_experts * sizeof(double));
+  w->spcnt = cv.take<int32_t>((size_t)moe::stats_blocks(c->T) * c->n_experts * sizeof(int32_t));
 }
 
 void carve_layer(Carver& cv, const moe_config_t* c, LayerWs* w) {
@@ -498,6 +502,24 @@ int moe_aux_loss(const moe_config_t* cfg, const float* logits, const int32_t* co
   AuxWs aw;
   carve_aux(cv, cfg, &aw);
   return do_aux(cfg, logits, counts, loss_out, aw, stream);
+}
+
+int moe_routing_stats(const moe_config_t* cfg, const int32_t* topk_idx, const float* topk_w,
+                      int32_t* counts_out, float* weight_mean_out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(topk_idx, "topk_idx");
+  MOE_REQUIRE_PTR(topk_w, "topk_w");
+  MOE_OPTIONAL_PTR(counts_out, "counts_out");
+  if (!weight_mean_out) return fail(MOE_ERR_INVALID_ARG, "weight_mean_out is NULL");
+  int r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  AuxWs aw;
+  carve_aux(cv, cfg, &aw);
+  return hip_status(moe::launch_stats(topk_idx, topk_w, cfg->T, cfg->top_k, cfg->n_experts,
+                                      aw.spcnt, aw.spw, counts_out, weight_mean_out, stream),
+                    "moe_routing_stats launch");
 }
 
 int moe_router_z_loss(const moe_config_t* cfg, const float* logits, float beta, float* loss_out,

@@ -141,6 +141,12 @@ constexpr int kAuxTokensPerBlock = 16;
 inline int aux_blocks(int T) { return (T + kAuxTokensPerBlock - 1) / kAuxTokensPerBlock; }
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
                       double* ppart, double* term, float* loss_out, hipStream_t s);
+// Routing statistics: per-expert selection counts and mean routing weight
+// (pcnt / pw hold stats_blocks(T) * N partials each).
+constexpr int kStatsTokensPerBlock = 64;
+inline int stats_blocks(int T) { return (T + kStatsTokensPerBlock - 1) / kStatsTokensPerBlock; }
+hipError_t launch_stats(const int32_t* topk_idx, const float* topk_w, int T, int K, int N,
+                        int32_t* pcnt, double* pw, int32_t* counts, float* wmean, hipStream_t s);
 // Router z-loss: beta * mean_t logsumexp(logits[t])^2 in fp64; zpart holds
 // aux_blocks(T) doubles.
 hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,

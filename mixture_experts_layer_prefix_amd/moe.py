@@ -19,7 +19,7 @@ MOE_F32, MOE_BF16 = 0, 1
 STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5}
 ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
                 "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_router_z_loss",
-                "moe_layer_forward", "moe_last_error")
+                "moe_routing_stats", "moe_layer_forward", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -67,9 +67,10 @@ def lib():
     L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     L.moe_aux_loss.argtypes = [cfgp, vp, vp, vp, vp, sz, vp]
     L.moe_router_z_loss.argtypes = [cfgp, vp, ctypes.c_float, vp, vp, sz, vp]
+    L.moe_routing_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
-                 "moe_router_z_loss",
+                 "moe_router_z_loss", "moe_routing_stats",
                  "moe_layer_forward"):
         getattr(L, name).restype = ctypes.c_int
     L.moe_last_error.argtypes = []
@@ -181,6 +182,12 @@ def moe_router_z_loss(cfg, logits, beta, loss_out, ws, stream=None):
     p, n = _ws(ws)
     _check(lib().moe_router_z_loss(ctypes.byref(cfg), _p(logits), float(beta), _p(loss_out), p, n,
                                    _stream(stream)))
+
+
+def moe_routing_stats(cfg, topk_idx, topk_w, counts_out, weight_mean_out, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_routing_stats(ctypes.byref(cfg), _p(topk_idx), _p(topk_w), _p(counts_out),
+                                   _p(weight_mean_out), p, n, _stream(stream)))
 
 
 def moe_layer_forward(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,

@@ -208,6 +208,21 @@ def router_z_loss(logits: np.ndarray, beta: float) -> float:
     return float(beta * np.mean(lse ** 2))
 
 
+# [lmnt] §8.2 routing-distribution monitoring: tokens received per expert and
+# their mean routing weight (the drop count is the dispatch's).
+def routing_stats(idx: np.ndarray, w: np.ndarray, n_experts: int):
+    T, K = idx.shape
+    counts = np.zeros(n_experts, dtype=np.int64)
+    wsum = np.zeros(n_experts, dtype=np.float64)
+    for t in range(T):
+        for k in range(K):
+            e = int(idx[t, k])
+            counts[e] += 1
+            wsum[e] += float(w[t, k])
+    mean = np.where(counts > 0, wsum / np.maximum(counts, 1), 0.0)
+    return counts, mean
+
+
 # --------------------------------------------------------------------------
 # The whole layer.  Structure follows [yunthe]'s reference forward: a loop
 # over the K slots and, inside it, over the experts, adding w * E_e(x) into the

@@ -97,6 +97,12 @@ def test_null_and_misaligned_pointers_rejected():
     assert b"beta" in L.moe_last_error()
     assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, ctypes.c_float(1e-3), FAKE, None, 0,
                                None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_routing_stats(ctypes.byref(cfg), None, FAKE, None, FAKE, FAKE * 256, 1 << 30,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(ctypes.byref(cfg), FAKE, FAKE, None, None, FAKE * 256, 1 << 30,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE * 256, 16,
+                               None) == moe.MOE_ERR_WORKSPACE
     W = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=None)
     assert L.moe_expert_ffn(ctypes.byref(cfg), FAKE, FAKE, ctypes.byref(W), None, FAKE, None,
                             FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG

@@ -8,8 +8,8 @@ from mixture_experts_layer_prefix_amd import configs as C
 from mixture_experts_layer_prefix_amd import inputs, moe
 from oracle import moe_oracle as O
 
-from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, check_routing_and_dispatch, device_tensors,
-                         oracle_run, rel_l2, run_layer, run_stages, say)
+from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, W_TOL, check_routing_and_dispatch,
+                         device_tensors, oracle_run, rel_l2, run_layer, run_stages, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,14 @@ def _compare(name, shape, inp, cfg):
                           moe.alloc_workspace(cfg, "aux"))
     z_ref = O.router_z_loss(g["logits"], 1e-3)
     assert abs(float(z.item()) - z_ref) <= AUX_TOL * abs(z_ref), (float(z.item()), z_ref)
+    # routing statistics on the GPU's own routing (identical to the oracle's)
+    sc = torch.empty(shape.n_experts, dtype=torch.int32, device="cuda")
+    sm = torch.empty(shape.n_experts, dtype=torch.float32, device="cuda")
+    moe.moe_routing_stats(cfg, torch.from_numpy(g["idx"]).cuda(), torch.from_numpy(g["w"]).cuda(),
+                          sc, sm, moe.alloc_workspace(cfg, "aux"))
+    c_ref, m_ref = O.routing_stats(o["idx"], o["w"], shape.n_experts)
+    assert (sc.cpu().numpy() == c_ref).all()
+    assert np.allclose(sm.cpu().numpy(), m_ref, rtol=W_TOL, atol=0), (sm.cpu().numpy(), m_ref)
     # the whole-layer entry point runs the same kernels: bitwise equal to the stages
     lay = run_layer(cfg, t, aux=cfg.aux_alpha != 0)
     assert torch.equal(lay["out"].float().cpu(), torch.from_numpy(g["out"]))

@@ -227,6 +227,33 @@ def test_z_loss_scalar_brute_force():
     assert O.router_z_loss(logits, beta) == pytest.approx(beta * tot / T, rel=1e-12)
 
 
+def test_routing_stats_uniform_tie():
+    # all logits equal: every token takes experts 0..K-1 with weight 1/K
+    T, N, K = 12, 6, 3
+    logits = np.zeros((T, N), dtype=np.float32)
+    idx = O.topk_select(logits, K)
+    w = O.topk_softmax(logits, idx)
+    counts, mean = O.routing_stats(idx, w, N)
+    assert counts.tolist() == [T] * K + [0] * (N - K)
+    assert np.allclose(mean[:K], 1.0 / K, rtol=1e-15) and (mean[K:] == 0).all()
+
+
+def test_routing_stats_invariants():
+    rng = np.random.default_rng(21)
+    T, N, K = 40, 9, 3
+    idx = _random_distinct_idx(rng, T, N, K)
+    w = rng.random((T, K))
+    w = w / w.sum(axis=1, keepdims=True)
+    counts, mean = O.routing_stats(idx, w, N)
+    assert counts.sum() == T * K
+    assert (counts == np.bincount(idx.ravel(), minlength=N)).all()
+    # sum_e count_e * mean_e = sum of all weights = T (each row sums to 1)
+    assert float((counts * mean).sum()) == pytest.approx(T, rel=1e-12)
+    for e in range(N):
+        sel = w[idx == e]
+        assert mean[e] == pytest.approx(sel.mean() if sel.size else 0.0, rel=1e-12)
+
+
 # ---------------------------------------------------------------- whole layer
 def _tiny_problem(rng, T, d, f, N, *, biases=True, fs=0):
     x = _bf16_values(rng, (T, d))
