@@ -8,8 +8,9 @@ Plain, slow, fp64 NumPy.  Each function cites the page passage it follows.
 Pages (by site and title):
   [lmnt]   lmnt.cn MoE walkthrough (news/351908): §1.2 per-token flow,
            §2.1 gate scoring equation, §2.2 TopK, §3.1 dispatch, §3.2 combine
-           equation, §3.3 capacity equation, §5.2 load-balance code,
-           §5.3 router z-loss equation.
+           equation, §3.3 capacity equation, §4.3 weight quantisation for
+           inference, §5.2 load-balance code, §5.3 router z-loss equation,
+           §8.2 routing statistics.
   [csdn]   "MoE逐token路由与活跃参数率实战解析": §3.1 worked top-2 example,
            §4.2 MoELayer code.
   [yunthe] "MoE混合专家模型实战：专家路由与稀疏激活的推理成本优化方案":
@@ -31,7 +32,10 @@ notes as well):
     renormalised;
   * GELU is the exact erf form; the shared expert enters with weight 1;
   * aux loss f_e is the mean over tokens of the pre-drop selection mask
-    ([yunthe] form, sum f = K), P_e the mean full-N softmax of the logits.
+    ([yunthe] form, sum f = K), P_e the mean full-N softmax of the logits;
+  * INT8 weight-only experts: symmetric, one fp32 scale per output row,
+    s = maxabs / 127 and q = round-half-even(w / s) clamped to +-127, both
+    divisions in fp32; the expert then uses the weights s * q.
 
 Pins: every function here is pinned by tests/test_oracle_pins.py against
 brute force, closed forms, the corrected worked example, special cases and
@@ -221,6 +225,33 @@ def routing_stats(idx: np.ndarray, w: np.ndarray, n_experts: int):
             wsum[e] += float(w[t, k])
     mean = np.where(counts > 0, wsum / np.maximum(counts, 1), 0.0)
     return counts, mean
+
+
+# --------------------------------------------------------------------------
+# [lmnt] §4.3 (inference: expert weights compressed from 16-bit to INT8 halve
+# their memory and bandwidth); [yunthe] deployment section (weight-only
+# quantisation of the experts).  The pages fix no scheme; the reading here is
+# the plain symmetric per-output-channel one, decided in fp32 so the GPU can
+# reproduce every code exactly:
+#   s[r] = fp32(maxabs_k |w[r, k]| / 127),  q[r, k] = rint(fp32(w[r, k] / s[r]))
+# clamped to [-127, 127]; a row of zeros gets s = 0 and q = 0.
+def quantize_int8(w: np.ndarray):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows = w.reshape(-1, w.shape[-1])
+    q = np.zeros(rows.shape, dtype=np.int8)
+    s = np.zeros(rows.shape[0], dtype=np.float32)
+    for r in range(rows.shape[0]):
+        m = np.float32(np.abs(rows[r]).max())
+        if m == 0:
+            continue
+        s[r] = np.float32(m / np.float32(127.0))
+        v = np.rint(rows[r] / s[r])                  # fp32 division, half to even
+        q[r] = np.clip(v, -127, 127).astype(np.int8)
+    return q.reshape(w.shape), s.reshape(w.shape[:-1])
+
+
+def dequantize_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    return _f64(s)[..., None] * q.astype(np.float64)
 
 
 # --------------------------------------------------------------------------

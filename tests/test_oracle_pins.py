@@ -254,6 +254,86 @@ def test_routing_stats_invariants():
         assert mean[e] == pytest.approx(sel.mean() if sel.size else 0.0, rel=1e-12)
 
 
+# ---------------------------------------------------------------- INT8 weights
+def _nearest_f32(x):
+    # the fp32 value nearest the exact rational x, ties to even mantissa
+    from fractions import Fraction
+    f = np.float32(float(x))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda c: (abs(Fraction(float(c)) - x),
+                                     int(np.array(c, dtype=np.float32).view(np.uint32)) & 1))
+
+
+def _rint_half_even(v):
+    from fractions import Fraction
+    r = Fraction(float(v))
+    lo = r.numerator // r.denominator
+    frac = r - lo
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return lo
+
+
+def test_quantize_int8_scalar_brute_force():
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    w = (rng.standard_normal((6, 40)) * rng.choice([1e-3, 1.0, 50.0], size=(6, 1))).astype(
+        np.float32)
+    q, s = O.quantize_int8(w)
+    for r in range(w.shape[0]):
+        m = max(abs(Fraction(float(v))) for v in w[r])
+        assert s[r] == _nearest_f32(m / 127)
+        for k in range(w.shape[1]):
+            quot = _nearest_f32(Fraction(float(w[r, k])) / Fraction(float(s[r])))
+            assert int(q[r, k]) == max(-127, min(127, _rint_half_even(quot)))
+
+
+def test_quantize_int8_properties():
+    rng = np.random.default_rng(32)
+    w = rng.standard_normal((16, 64)).astype(np.float32)
+    w[3] = 0.0                                      # zero row
+    w[5, 7] = -np.abs(w[5]).max() * 2               # negative extreme
+    q, s = O.quantize_int8(w)
+    assert s[3] == 0 and (q[3] == 0).all()
+    for r in range(16):
+        if r == 3:
+            continue
+        k = int(np.abs(w[r]).argmax())
+        assert abs(int(q[r, k])) == 127 and np.sign(q[r, k]) == np.sign(w[r, k])
+        # round trip within half a step, plus the fp32 rounding of w / s
+        # (|w / s| <= 127, so at most 127 * 2^-24 of a step)
+        err = np.abs(O.dequantize_int8(q[r:r + 1], s[r:r + 1])[0] - w[r].astype(np.float64))
+        assert err.max() <= float(s[r]) * (0.5 + 127 * 2.0 ** -23)
+    assert q.min() >= -127 and q.max() <= 127
+
+
+def test_quantize_int8_ties_to_even():
+    # w = (m + 1/2) * s exactly: the code is the even neighbour
+    s = np.float32(0.5)
+    w = np.array([[127 * s, 2.5 * s, 3.5 * s, -2.5 * s, -3.5 * s, 0.5 * s, -0.5 * s]],
+                 dtype=np.float32)
+    q, sc = O.quantize_int8(w)
+    assert sc[0] == s
+    assert q[0].tolist() == [127, 2, 4, -2, -4, 0, 0]
+
+
+def test_int8_expert_equals_dense_ffn_on_dequantized_weights():
+    # an expert with int8 weights is the FFN on s * q (special-case reduction)
+    rng = np.random.default_rng(33)
+    d, f = 16, 24
+    x = rng.standard_normal((5, d))
+    w1 = rng.standard_normal((f, d)).astype(np.float32)
+    w2 = rng.standard_normal((d, f)).astype(np.float32)
+    q1, s1 = O.quantize_int8(w1)
+    q2, s2 = O.quantize_int8(w2)
+    W1 = s1.astype(np.float64)[:, None] * q1
+    W2 = s2.astype(np.float64)[:, None] * q2
+    h = x @ W1.T
+    ref = np.array([[0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in row] for row in h]) @ W2.T
+    got = O.expert_ffn(x, O.dequantize_int8(q1, s1), None, O.dequantize_int8(q2, s2), None)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- whole layer
 def _tiny_problem(rng, T, d, f, N, *, biases=True, fs=0):
     x = _bf16_values(rng, (T, d))
