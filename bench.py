@@ -55,7 +55,11 @@ def algorithmic(shape, counts, M):
     eb = 4 if shape.dtype == "f32" else 2
     touched = int((counts > 0).sum())
     flops = 2 * 2 * M * d * f + (2 * 2 * T * d * fs if fs else 0)
-    wbytes = touched * 2 * d * f * eb + (2 * d * fs * eb if fs else 0)
+    if getattr(shape, "weight_quant", "none") == "int8":
+        # INT8 codes plus one fp32 scale per output row of w1 and w2
+        wbytes = touched * (2 * d * f + 4 * (f + d)) + (2 * d * fs * eb if fs else 0)
+    else:
+        wbytes = touched * 2 * d * f * eb + (2 * d * fs * eb if fs else 0)
     # x_perm read, h written and read back, y_perm written (+ shared x, h_s, y_s)
     abytes = (M * d + 2 * M * f + M * d) * eb
     if fs:
@@ -77,6 +81,13 @@ def cpu_baseline(shape, inp, n_tok):
 
     get = lambda e: tuple(None if a is None else (inputs.bf16_widen(a) if a.dtype == np.uint16 else a)
                           for a in inp.expert(e))
+    if getattr(shape, "weight_quant", "none") == "int8":
+        base = get
+
+        def get(e):
+            w1, b1, w2, b2 = base(e)
+            return (O.dequantize_int8(*O.quantize_int8(w1)), b1,
+                    O.dequantize_int8(*O.quantize_int8(w2)), b2)
     shared = (inp.f32("ws1"), inp.f32("ws2")) if shape.d_ff_shared else None
     x_all = inp.f32("x")
 
@@ -167,6 +178,10 @@ def main():
     t0 = time.time()
     inp = inputs.make_inputs(shape, seed=args.seed)
     t = inputs.to_torch(inp, dev)
+    if shape.weight_quant == "int8":
+        # weight preprocessing, once, outside the timed region
+        t = moe.quantize_expert_weights(t)
+        torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
     cfg = moe.config_for(shape)
@@ -265,7 +280,8 @@ def main():
         "dtype": shape.dtype, "data": "synthetic (seeded, N(0,1) x, N(0,1/fan_in) weights)",
         "config": {"workload": shape.name, "T": T, "d_model": d, "d_ff": cfg.d_ff,
                    "n_experts": N, "top_k": K, "capacity": cfg.capacity,
-                   "d_ff_shared": cfg.d_ff_shared, "parallelism": "single GPU"},
+                   "d_ff_shared": cfg.d_ff_shared, "weight_quant": shape.weight_quant,
+                   "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "event_ms_per_step": round(step_ms, 4),
         "roofline": roof,

@@ -20,6 +20,8 @@
  *     tokens); "专家负载均衡与辅助损失函数设计" (aux loss, per-expert bias b_i,
  *     capacity drop).
  *   wiblog.cn "MoE 专家路由如何实现稀疏激活": fine-grained and shared experts.
+ *   lmnt.cn §4.3 and yunthe.com's deployment section: expert weights stored
+ *     as INT8 for inference (weight-only quantisation).
  *
  * Conventions for every entry point:
  *   - Ownership: the caller owns every buffer.  The library never allocates
@@ -61,6 +63,12 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
+/* Storage of the routed experts' weights w1 / w2.  MOE_WQ_INT8: int8 codes q
+ * with one fp32 scale per output row (w1_scale [N, f], w2_scale [N, d]); the
+ * expert uses the weights scale * q (moe_quantize_int8 makes them).  Only
+ * with dtype MOE_BF16; the shared expert and the router stay in dtype. */
+typedef enum { MOE_WQ_NONE = 0, MOE_WQ_INT8 = 1 } moe_weight_quant_t;
+
 typedef struct {
   int32_t T;           /* tokens in the batch                                  */
   int32_t d_model;     /* d                                                    */
@@ -71,6 +79,7 @@ typedef struct {
   int32_t d_ff_shared; /* 0: no shared expert; else its hidden width f_s       */
   int32_t dtype;       /* moe_dtype_t of x, expert weights, intermediates, out */
   float aux_alpha;     /* alpha of the aux loss (used by moe_layer_forward)    */
+  int32_t weight_quant;/* moe_weight_quant_t of the routed experts' w1 / w2    */
 } moe_config_t;
 
 typedef struct {
@@ -84,6 +93,8 @@ typedef struct {
   const void *b2;           /* [dev] [N, d] dtype or NULL                          */
   const void *ws1;          /* [dev] [f_s, d] dtype (shared expert) or NULL        */
   const void *ws2;          /* [dev] [d, f_s] dtype (shared expert) or NULL        */
+  const float *w1_scale;    /* [dev] [N, f] fp32 with MOE_WQ_INT8, else ignored    */
+  const float *w2_scale;    /* [dev] [N, d] fp32 with MOE_WQ_INT8, else ignored    */
 } moe_weights_t;
 
 typedef enum {
@@ -220,6 +231,21 @@ int moe_router_z_loss(const moe_config_t *cfg, const float *logits, float beta, 
 int moe_layer_forward(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
                       void *out, float *aux_out, int32_t *counts_out, int32_t *n_dropped_out,
                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Weight-only INT8 quantisation of a weight matrix, one fp32 scale per row
+ * (lmnt.cn §4.3: expert weights compressed to INT8 for inference; the pages
+ * fix no scheme, this is the symmetric per-output-channel one):
+ *   scale[r] = fp32(max_c |w[r, c]| / 127)
+ *   q[r, c]  = clamp(round_half_even(fp32(w[r, c] / scale[r])), -127, 127)
+ * with IEEE fp32 divisions, so the codes are reproducible bit for bit; a row
+ * of zeros gets scale 0 and codes 0.  For the experts' w1 [N, f, d] call it
+ * with rows = N*f, cols = d (w2: rows = N*d, cols = f).
+ *   w     [dev] [rows, cols] dtype (MOE_BF16 or MOE_F32) in;
+ *   q     [dev] [rows, cols] int8 out;  scale [dev] [rows] fp32 out.
+ * Errors: MOE_ERR_INVALID_ARG for NULL or misaligned pointers, rows < 1, cols
+ * not a positive multiple of 64, or an unknown dtype. */
+int moe_quantize_int8(const void *w, int32_t dtype, int64_t rows, int32_t cols, int8_t *q,
+                      float *scale, hipStream_t stream);
 
 /* Thread-local text of the last non-OK return on this thread ("" if none). */
 const char *moe_last_error(void);

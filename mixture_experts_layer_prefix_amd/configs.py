@@ -36,6 +36,7 @@ class MoEShape:
     sel_bias: bool = False         # per-expert selection-only bias ~ U(-0.5, 0.5)
     aux_alpha: float = 0.0         # >0: also compute alpha*N*sum(f*P)
     index: int = 0                 # position in the list below; keys the input streams
+    weight_quant: str = "none"     # "int8": routed w1 / w2 quantised per output row
 
     @property
     def M_max(self) -> int:
@@ -67,4 +68,13 @@ DEEPSEEK_FINE = MoEShape(
     dtype="bf16", d_ff_shared=2048, sel_bias=True, index=4)
 
 ALL = [TINY_FP32, MIXTRAL_PREFILL, DECODE, SWITCH_CAPACITY, DEEPSEEK_FINE]
-BY_NAME = {c.name: c for c in ALL}
+
+# The weight-bandwidth-bound workloads again with INT8 routed expert weights
+# (lmnt.cn walkthrough §4.3: experts compressed to INT8 for inference).  Same
+# seeded bf16 weights as the workload they derive from (same index); each
+# side quantises them itself.
+INT8 = [DECODE.with_(name="decode_t32_e64_w8", weight_quant="int8"),
+        SWITCH_CAPACITY.with_(name="switch_top1_capacity_w8", weight_quant="int8"),
+        DEEPSEEK_FINE.with_(name="deepseek_v3_fine_grained_w8", weight_quant="int8")]
+
+BY_NAME = {c.name: c for c in ALL + INT8}

@@ -43,10 +43,15 @@ constexpr int RPI = 64 / CH;               // LDS rows filled by one wave instru
 // each span the 256 bytes once, so the chunk is XORed with the group index.
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
-__device__ __forceinline__ void lds_load16(const uint16_t* g, uint16_t* l) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g), reinterpret_cast<void*>(l),
-                                   16, 0, 0);
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
+
+// INT8 weights: LDS rows of 32 bytes (a 32-wide k-step) in two 16-byte
+// chunks; fragment reads are 8 bytes per lane over 32 consecutive rows, and
+// XORing the chunk with bit 3 of the row puts rows r and r + 8 in different
+// banks (a 2-way conflict remains between r and r + 16).
+__device__ __forceinline__ int swzq(int r) { return (r >> 3) & 1; }
 
 // s_barrier with a compiler memory fence: no LDS access moves across it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -106,28 +111,37 @@ constexpr int W4_AR = W4_TM + W4_MERGE;       // A rows held per LDS stage
 constexpr int W4_STAGE = (W4_AR + BN) * BK;   // bf16 elements per LDS stage (36 KiB)
 constexpr int W4_CST = BN + 8;                // staged output row stride in bf16 (528 bytes)
 
-template <bool GELU, int NS, int LAY>
+// QW: the routed weights are INT8 codes with one fp32 scale per output row
+// (a.wscale); launches with INT8 weights carry no shared-problem tiles.  The
+// codes travel to LDS as bytes (half the bytes of bf16), each fragment is
+// widened to bf16 in registers (exact: |q| <= 127) just before its MFMAs,
+// and the epilogue multiplies by the row scale before the bias.
+template <bool GELU, bool QW, int NS, int LAY>
 __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
   using Lay = W4Layout<LAY>;
   constexpr int MI = Lay::MI, NI = Lay::NI, WN = Lay::WN;
   constexpr bool EX = Lay::EXTRA;
   constexpr int NLA = Lay::AROWS / RPI / 4;   // direct loads per wavefront per stage, A rows
-  constexpr int NLB = W4_TM / RPI / 4;        // W rows (4)
+  // W rows: 16 rows of 64 bytes per wave instruction (bf16), 32 rows of 32
+  // bytes (INT8)
+  constexpr int NLB = QW ? W4_TM / 32 / 4 : W4_TM / RPI / 4;
   constexpr int NLS = NLA + NLB;
   const int Kd = a.Kd, Nd = a.Nd;
   const uint16_t* A;
-  const uint16_t* W;
+  const char* W;                // bf16 or INT8 weights of this tile's expert
   const uint16_t* bias = nullptr;
+  const float* wsc = nullptr;
   uint16_t* C;
   if (tr.shared) {
     A = static_cast<const uint16_t*>(a.As);
-    W = static_cast<const uint16_t*>(a.Ws);
+    W = static_cast<const char*>(a.Ws);
     C = static_cast<uint16_t*>(a.Cs);
   } else {
     A = static_cast<const uint16_t*>(a.A);
-    W = static_cast<const uint16_t*>(a.W) + (int64_t)tr.e * Nd * Kd;
+    W = static_cast<const char*>(a.W) + (int64_t)tr.e * Nd * Kd * (QW ? 1 : 2);
     if (a.bias) bias = static_cast<const uint16_t*>(a.bias) + (int64_t)tr.e * Nd;
+    if (QW) wsc = a.wscale + (int64_t)tr.e * Nd;
     C = static_cast<uint16_t*>(a.C);
   }
   const int rows = tr.row_end - tr.row0;
@@ -147,11 +161,18 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     const int lchunk = (lane % CH) ^ swz(row);
     offA[i] = (uint32_t)(tr.row0 + min(row, rows - 1)) * (uint32_t)Kd + lchunk * 8;
   }
+  // (byte offsets of the W rows)
 #pragma unroll
   for (int i = 0; i < NLB; ++i) {
-    const int row = (wave * NLB + i) * RPI + r_in;
-    const int lchunk = (lane % CH) ^ swz(row);
-    offB[i] = (uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8;
+    if constexpr (QW) {
+      const int row = (wave * NLB + i) * 32 + (lane >> 1);
+      const int lchunk = (lane & 1) ^ swzq(row);
+      offB[i] = (uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 16;
+    } else {
+      const int row = (wave * NLB + i) * RPI + r_in;
+      const int lchunk = (lane % CH) ^ swz(row);
+      offB[i] = ((uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8) * 2;
+    }
   }
   auto issue_a = [&](int buf, int k0) {
     uint16_t* base = lds + buf * W4_STAGE + wave * NLA * RPI * BK;
@@ -159,9 +180,9 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     for (int i = 0; i < NLA; ++i) lds_load16(A + offA[i] + k0, base + i * RPI * BK);
   };
   auto issue_b = [&](int buf, int k0) {
-    uint16_t* base = lds + buf * W4_STAGE + W4_AR * BK + wave * NLB * RPI * BK;
+    char* base = reinterpret_cast<char*>(lds + buf * W4_STAGE + W4_AR * BK) + wave * NLB * 1024;
 #pragma unroll
-    for (int i = 0; i < NLB; ++i) lds_load16(W + offB[i] + k0, base + i * RPI * BK);
+    for (int i = 0; i < NLB; ++i) lds_load16(W + offB[i] + k0 * (QW ? 1 : 2), base + i * 1024);
   };
 
   const int sw = swz(lane & 31);   // the same for every fragment row this lane reads
@@ -169,7 +190,12 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   // rows 256 + 32*wm .. +32 of a 320-row tile (EX only)
   const int xrow = (W4_TM + wm * 32 + (lane & 31)) * BK;
   constexpr int MX = MI + (EX ? 1 : 0);   // A fragments per half
-  bf16x8 fa0[MX], fb0[NI], fa1[MX], fb1[NI];
+  // W fragments: bf16x8, or 8 INT8 codes widened just before their MFMAs
+  using BF = typename std::conditional<QW, uint2, bf16x8>::type;
+  const int browq = (wn * WCOLS + (lane & 31)) * 32 + (lane >> 5) * 8;   // bytes (INT8)
+  const int swq = swzq(lane & 31);
+  bf16x8 fa0[MX], fa1[MX];
+  BF fb0[NI], fb1[NI];
   f32x16 accx[EX ? NI : 1];
   if constexpr (EX) {
 #pragma unroll
@@ -177,7 +203,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
 #pragma unroll
       for (int v = 0; v < 16; ++v) accx[i][v] = 0.f;
   }
-  auto read_half = [&](bf16x8 (&fa)[MX], bf16x8 (&fb)[NI], int buf, int kk) {
+  auto read_half = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int kk) {
     const uint16_t* As = lds + buf * W4_STAGE;
     const uint16_t* Bs = As + W4_AR * BK;
     const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
@@ -186,25 +212,41 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       fa[i] = *reinterpret_cast<const bf16x8*>(As + arow + i * 32 * BK + pc);
     if constexpr (EX) fa[MI] = *reinterpret_cast<const bf16x8*>(As + xrow + pc);
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      fb[i] = *reinterpret_cast<const bf16x8*>(Bs + brow + i * 32 * BK + pc);
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (QW)
+        fb[i] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(Bs) + browq +
+                                                i * 32 * 32 + ((kk ^ swq) * 16));
+      else
+        fb[i] = *reinterpret_cast<const bf16x8*>(Bs + brow + i * 32 * BK + pc);
+    }
   };
-  auto mfma_half = [&](const bf16x8 (&fa)[MX], const bf16x8 (&fb)[NI]) {
+  auto wfrag = [&](const BF& f) -> bf16x8 {
+    if constexpr (QW)
+      return __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(f));
+    else
+      return f;
+  };
+  auto mfma_half = [&](const bf16x8 (&fa)[MX], const BF (&fbr)[NI]) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
+      const bf16x8 fb = wfrag(fbr[ni]);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa[mi], acc[ni][mi], 0, 0, 0);
       // The folded rows' accumulators live in ordinary VGPRs (the 256
       // accumulation registers hold the main 256 x 256): the compiler keeps
       // all MFMA results in one register class, so these four are written
-      // out with VGPR operands.  Their fragments come from LDS reads, which
-      // the compiler's wait counts cover; each accx[ni] is next read by the
-      // same MFMA a whole half later, and the epilogue pads before reading.
+      // out with VGPR operands.  The compiler does not see an MFMA here, so
+      // the hazards it would cover are covered by placement: the weight
+      // fragment (from an LDS read, or widened by VALU code for INT8) was
+      // already read by the compiler's MFMAs just above, which wait as the
+      // hardware requires; fa[MI] comes from an LDS read covered by the wait
+      // counts; each accx[ni] is next read by the same MFMA a whole half
+      // later, and the epilogue pads before reading it.
       if constexpr (EX)
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
             : "+v"(accx[ni])
-            : "v"(fb[ni]), "v"(fa[MI]));
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[ni][mi], 0, 0, 0);
+            : "v"(fb), "v"(fa[MI]));
     }
   };
   // one half: MI*NI MFMAs interleaved with MI+NI fragment reads and `nv`
@@ -281,13 +323,18 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
         bv[2] = __uint_as_float(braw.y << 16);
         bv[3] = __uint_as_float(braw.y & 0xffff0000u);
       }
+      float sv[4] = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (QW) {
+        const float4 sr = *reinterpret_cast<const float4*>(wsc + min(tr.n0 + nl, Nd - 4));
+        sv[0] = sr.x; sv[1] = sr.y; sv[2] = sr.z; sv[3] = sr.w;
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int ml = wm * WROWS + mi * 32 + (lane & 31);
         float z[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          z[q] = acc[ni][mi][g * 4 + q] + bv[q];
+          z[q] = QW ? fmaf(acc[ni][mi][g * 4 + q], sv[q], bv[q]) : acc[ni][mi][g * 4 + q] + bv[q];
           if (GELU) z[q] = gelu_as(z[q]);
         }
         // v_cvt_pk_bf16_f32: round to nearest even, two values per instruction
@@ -325,10 +372,15 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
           bv[2] = __uint_as_float(braw.y << 16);
           bv[3] = __uint_as_float(braw.y & 0xffff0000u);
         }
+        float sv[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (QW) {
+          const float4 sr = *reinterpret_cast<const float4*>(wsc + min(tr.n0 + nl, Nd - 4));
+          sv[0] = sr.x; sv[1] = sr.y; sv[2] = sr.z; sv[3] = sr.w;
+        }
         float z[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          z[q] = accx[ni][g * 4 + q] + bv[q];
+          z[q] = QW ? fmaf(accx[ni][g * 4 + q], sv[q], bv[q]) : accx[ni][g * 4 + q] + bv[q];
           if (GELU) z[q] = gelu_as(z[q]);
         }
         const bf16x4 pk = __builtin_convertvector((f32x4){z[0], z[1], z[2], z[3]}, bf16x4);
@@ -343,7 +395,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   }
 }
 
-template <bool GELU, int NS>
+template <bool GELU, bool QW, int NS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(GemmArgs a) {
   // the output tile is staged through the same LDS after the main loop
@@ -360,13 +412,13 @@ gemm_bf16_w4_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   const int rows = tr.row_end - tr.row0;
   if (rows > W4_TM)
-    w4_tile<GELU, NS, 3>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 3>(a, tr, lds, acc);
   else if (rows > 128)
-    w4_tile<GELU, NS, 0>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 0>(a, tr, lds, acc);
   else if (rows > 64)
-    w4_tile<GELU, NS, 1>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 1>(a, tr, lds, acc);
   else
-    w4_tile<GELU, NS, 2>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 2>(a, tr, lds, acc);
 }
 
 }  // namespace
@@ -378,10 +430,17 @@ int gemm_bf16_merge_rows() { return W4_MERGE; }
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
   const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
-  if (gelu)
-    hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, W4_NS>), dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+  if (a.wscale) {
+    if (gelu)
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, true, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, true, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (gelu)
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, false, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

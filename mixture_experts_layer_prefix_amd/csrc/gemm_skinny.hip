@@ -11,7 +11,8 @@
 // other operand, eight 16-byte loads per lane in flight per step.
 // Workgroup (bx, e): outputs [64*bx, 64*bx + 64) of expert e, one wavefront
 // per 16 outputs; experts with no rows exit at once.  Expert index E stands
-// for the dense shared problem when one is present.
+// for the dense shared problem when one is present (its weights are always
+// in the activation dtype; launches with INT8 routed weights carry none).
 #include "gemm_common.h"
 
 namespace moe {
@@ -25,7 +26,12 @@ constexpr int NPW = 16;                 // output features per wavefront
 constexpr int NPB = NPW * NTHR / 64;    // per workgroup
 constexpr int U = 8;                    // k-steps of 32 in flight
 
-template <bool GELU>
+// INT8 weights (QW): a lane loads 16 codes = one 16-byte load per 64-wide
+// k-block (its slice is k = 64j + 16*(lane/16) .. +16) and feeds two MFMAs
+// with the first and second 8; the activations use the same permutation of
+// k inside the block (the dot product does not depend on it).  The row
+// scale multiplies the result before the bias.
+template <bool GELU, bool QW>
 __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   const int e = blockIdx.y;
   const int Kd = a.Kd, Nd = a.Nd;
@@ -55,6 +61,53 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   const int kq = (lane >> 4) * 8;      // this lane's 8-element slice of each 32-wide k-step
   const uint16_t* wrow = W + (int64_t)(n0 + (lane & 15)) * Kd + kq;
   const float bv = bias ? bf16_to_f32(bias[n0 + (lane & 15)]) : 0.f;
+  if constexpr (QW) {
+    const int8_t* w8 = static_cast<const int8_t*>(a.W) + (int64_t)e * Nd * Kd +
+                       (int64_t)(n0 + (lane & 15)) * Kd + (lane >> 4) * 16;
+    const float sc = a.wscale[(int64_t)e * Nd + n0 + (lane & 15)];
+    constexpr int U8 = 8;             // 64-wide k-blocks in flight
+    for (int g0 = r0; g0 < r1; g0 += 16) {
+      const int ar = g0 + (lane & 15);
+      const bool arow_ok = ar < r1;
+      const uint16_t* arow = A + (int64_t)(arow_ok ? ar : r0) * Kd + (lane >> 4) * 16;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < Kd; k0 += 64 * U8) {
+        const int nb = min(U8, (Kd - k0) / 64);
+        uint4 wv[U8], av[U8][2];
+#pragma unroll
+        for (int u = 0; u < U8; ++u)
+          if (u < nb) wv[u] = *reinterpret_cast<const uint4*>(w8 + k0 + u * 64);
+#pragma unroll
+        for (int u = 0; u < U8; ++u)
+          if (u < nb) {
+            av[u][0] = *reinterpret_cast<const uint4*>(arow + k0 + u * 64);
+            av[u][1] = *reinterpret_cast<const uint4*>(arow + k0 + u * 64 + 8);
+            if (!arow_ok) av[u][0] = av[u][1] = make_uint4(0, 0, 0, 0);
+          }
+#pragma unroll
+        for (int u = 0; u < U8; ++u)
+          if (u < nb) {
+            const bf16x8 w0 = __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(make_uint2(wv[u].x, wv[u].y)));
+            const bf16x8 w1 = __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(make_uint2(wv[u].z, wv[u].w)));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][0]), w0,
+                                                          acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][1]), w1,
+                                                          acc, 0, 0, 0);
+          }
+      }
+      const int col = n0 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = g0 + (lane >> 4) * 4 + v;
+        if (r < r1) {
+          float z = fmaf(acc[v], sc, bv);
+          if (GELU) z = gelu_erf(z);
+          C[(int64_t)r * Nd + col] = f32_to_bf16(z);
+        }
+      }
+    }
+    return;
+  }
 
   for (int g0 = r0; g0 < r1; g0 += 16) {
     const int ar = g0 + (lane & 15);
@@ -105,10 +158,17 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_
   const int E = a.E + (a.As ? 1 : 0);
   if (E == 0) return hipSuccess;
   dim3 grid((a.Nd + NPB - 1) / NPB, E);
-  if (gelu)
-    hipLaunchKernelGGL(gemm_skinny_kernel<true>, grid, dim3(NTHR), 0, s, a);
-  else
-    hipLaunchKernelGGL(gemm_skinny_kernel<false>, grid, dim3(NTHR), 0, s, a);
+  if (a.wscale) {
+    if (gelu)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, true>), grid, dim3(NTHR), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, true>), grid, dim3(NTHR), 0, s, a);
+  } else {
+    if (gelu)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, false>), grid, dim3(NTHR), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, false>), grid, dim3(NTHR), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -35,7 +35,11 @@ std::string check_config(const moe_config_t* c, int* code) {
   if (c->d_ff_shared < 0) return "d_ff_shared must be >= 0";
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return "dtype must be MOE_F32 or MOE_BF16";
   if (!isfinite(c->aux_alpha)) return "aux_alpha must be finite";
+  if (c->weight_quant != MOE_WQ_NONE && c->weight_quant != MOE_WQ_INT8)
+    return "weight_quant must be MOE_WQ_NONE or MOE_WQ_INT8";
   *code = MOE_ERR_UNSUPPORTED;
+  if (c->weight_quant == MOE_WQ_INT8 && c->dtype != MOE_BF16)
+    return "INT8 expert weights need dtype MOE_BF16";
   if (c->n_experts > 256) return "n_experts > 256 is not supported";
   if (c->top_k > 64) return "top_k > 64 is not supported";
   if (c->d_model % 64 || c->d_ff % 64 || c->d_ff_shared % 64)
@@ -68,7 +72,10 @@ int gemm_bn(const moe_config_t* c) {
   return gemm_path(c) == PATH_F32 ? moe::gemm_f32_bn() : moe::gemm_bf16_bn();
 }
 // The shared expert rides in the routed launches when its width matches.
-bool fuse_shared(const moe_config_t* c) { return c->d_ff_shared > 0 && c->d_ff_shared == c->d_ff; }
+// (Not with INT8 routed weights: the shared expert keeps bf16 weights.)
+bool fuse_shared(const moe_config_t* c) {
+  return c->d_ff_shared > 0 && c->d_ff_shared == c->d_ff && c->weight_quant == MOE_WQ_NONE;
+}
 
 struct Carver {
   char* base;
@@ -307,9 +314,12 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
   g1.Kd = c->d_model;
   g1.Nd = c->d_ff;
   g1.E = N;
+  const bool q8 = c->weight_quant == MOE_WQ_INT8;
+  g1.wscale = q8 ? w->w1_scale : nullptr;
   moe::GemmArgs g2 = g1;
   g2.A = fw.h;
   g2.W = w->w2;
+  g2.wscale = q8 ? w->w2_scale : nullptr;
   g2.bias = w->b2;
   g2.C = y_perm;
   g2.Kd = c->d_ff;
@@ -374,6 +384,10 @@ int check_weights(const moe_config_t* c, const moe_weights_t* w, bool router, bo
   if (experts) {
     MOE_REQUIRE_PTR(w->w1, "w1");
     MOE_REQUIRE_PTR(w->w2, "w2");
+    if (c->weight_quant == MOE_WQ_INT8) {
+      MOE_REQUIRE_PTR(w->w1_scale, "w1_scale");
+      MOE_REQUIRE_PTR(w->w2_scale, "w2_scale");
+    }
     MOE_OPTIONAL_PTR(w->b1, "b1");
     MOE_OPTIONAL_PTR(w->b2, "b2");
     if (c->d_ff_shared) {
@@ -502,6 +516,18 @@ int moe_aux_loss(const moe_config_t* cfg, const float* logits, const int32_t* co
   AuxWs aw;
   carve_aux(cv, cfg, &aw);
   return do_aux(cfg, logits, counts, loss_out, aw, stream);
+}
+
+int moe_quantize_int8(const void* w, int32_t dtype, int64_t rows, int32_t cols, int8_t* q,
+                      float* scale, hipStream_t stream) {
+  MOE_REQUIRE_PTR(w, "w");
+  MOE_REQUIRE_PTR(q, "q");
+  MOE_REQUIRE_PTR(scale, "scale");
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32 or MOE_BF16");
+  if (rows < 1) return fail(MOE_ERR_INVALID_ARG, "rows must be >= 1");
+  if (cols < 64 || cols % 64) return fail(MOE_ERR_INVALID_ARG, "cols must be a positive multiple of 64");
+  return hip_status(moe::launch_quantize_int8(w, dtype, rows, cols, q, scale, stream),
+                    "moe_quantize_int8 launch");
 }
 
 int moe_routing_stats(const moe_config_t* cfg, const int32_t* topk_idx, const float* topk_w,

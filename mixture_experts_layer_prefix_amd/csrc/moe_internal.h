@@ -106,6 +106,7 @@ struct GemmArgs {
   const int32_t* offsets;   // [E+1] (skinny and fp32 kernels)
   const int4* tile_list;    // tiled kernels: tiles in execution order
   const int32_t* tile_count;
+  const float* wscale;  // INT8 weights: [E, Nd] fp32 row scales (W is int8); null: W is bf16
   const void* As;       // shared problem: [Ts, Kd] (null if none)
   const void* Ws;       // [Nd, Kd]
   void* Cs;             // [Ts, Nd]
@@ -141,6 +142,24 @@ constexpr int kAuxTokensPerBlock = 16;
 inline int aux_blocks(int T) { return (T + kAuxTokensPerBlock - 1) / kAuxTokensPerBlock; }
 hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
                       double* ppart, double* term, float* loss_out, hipStream_t s);
+// Per-row symmetric INT8 quantisation (dtype 0 fp32, 1 bf16 input).
+hipError_t launch_quantize_int8(const void* w, int dtype, int64_t rows, int cols, int8_t* q,
+                                float* scale, hipStream_t s);
+// int8 -> bf16 of 8 codes (exact: |q| <= 127), two per 32-bit word.
+__device__ __forceinline__ uint4 int8x8_to_bf16x8(uint2 v) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t wd = j < 2 ? v.x : v.y;
+    const int sh = (j & 1) * 16;
+    const float f0 = (float)(int32_t)(int8_t)(wd >> sh);
+    const float f1 = (float)(int32_t)(int8_t)(wd >> (sh + 8));
+    // small integers are exact in fp32 with the low 16 bits zero: the bf16 is
+    // the high half; v_perm_b32 packs the two high halves in one instruction
+    o[j] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
 // Routing statistics: per-expert selection counts and mean routing weight
 // (pcnt / pw hold stats_blocks(T) * N partials each).
 constexpr int kStatsTokensPerBlock = 64;

@@ -16,21 +16,23 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
+MOE_WQ_NONE, MOE_WQ_INT8 = 0, 1
 STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5}
 ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
                 "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_router_z_loss",
-                "moe_routing_stats", "moe_layer_forward", "moe_last_error")
+                "moe_routing_stats", "moe_quantize_int8", "moe_layer_forward", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("aux_alpha", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("aux_alpha", ctypes.c_float),
+                ("weight_quant", ctypes.c_int32)]
 
 
 _WEIGHT_FIELDS = ("w_router", "b_router", "logit_offset", "sel_bias", "w1", "b1", "w2", "b2",
-                  "ws1", "ws2")
+                  "ws1", "ws2", "w1_scale", "w2_scale")
 
 
 class MoeWeights(ctypes.Structure):
@@ -68,9 +70,10 @@ def lib():
     L.moe_aux_loss.argtypes = [cfgp, vp, vp, vp, vp, sz, vp]
     L.moe_router_z_loss.argtypes = [cfgp, vp, ctypes.c_float, vp, vp, sz, vp]
     L.moe_routing_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_quantize_int8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
-                 "moe_router_z_loss", "moe_routing_stats",
+                 "moe_router_z_loss", "moe_routing_stats", "moe_quantize_int8",
                  "moe_layer_forward"):
         getattr(L, name).restype = ctypes.c_int
     L.moe_last_error.argtypes = []
@@ -105,11 +108,13 @@ def capacity_from_factor(T: int, n_experts: int, capacity_factor: float) -> int:
 
 
 def make_config(T, d_model, d_ff, n_experts, top_k, *, capacity=0, d_ff_shared=0, dtype="bf16",
-                aux_alpha=0.0) -> MoeConfig:
+                aux_alpha=0.0, weight_quant="none") -> MoeConfig:
     return MoeConfig(T=T, d_model=d_model, d_ff=d_ff, n_experts=n_experts, top_k=top_k,
                      capacity=capacity or 0, d_ff_shared=d_ff_shared,
                      dtype=MOE_F32 if dtype in ("f32", MOE_F32) else MOE_BF16,
-                     aux_alpha=float(aux_alpha))
+                     aux_alpha=float(aux_alpha),
+                     weight_quant=MOE_WQ_INT8 if weight_quant in ("int8", MOE_WQ_INT8)
+                     else MOE_WQ_NONE)
 
 
 def config_for(shape, T: Optional[int] = None) -> MoeConfig:
@@ -119,7 +124,8 @@ def config_for(shape, T: Optional[int] = None) -> MoeConfig:
     if shape.capacity_factor is not None:
         cap = capacity_from_factor(T, shape.n_experts, shape.capacity_factor)
     return make_config(T, shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, capacity=cap,
-                       d_ff_shared=shape.d_ff_shared, dtype=shape.dtype, aux_alpha=shape.aux_alpha)
+                       d_ff_shared=shape.d_ff_shared, dtype=shape.dtype, aux_alpha=shape.aux_alpha,
+                       weight_quant=getattr(shape, "weight_quant", "none"))
 
 
 def make_weights(t: Dict[str, object]) -> MoeWeights:
@@ -188,6 +194,32 @@ def moe_routing_stats(cfg, topk_idx, topk_w, counts_out, weight_mean_out, ws, st
     p, n = _ws(ws)
     _check(lib().moe_routing_stats(ctypes.byref(cfg), _p(topk_idx), _p(topk_w), _p(counts_out),
                                    _p(weight_mean_out), p, n, _stream(stream)))
+
+
+def moe_quantize_int8(w, q_out, scale_out, stream=None):
+    """Per-row INT8 codes and fp32 scales of a [rows, cols] bf16 or fp32 device
+    tensor (any leading shape; the last dimension is the row)."""
+    import torch
+    dt = MOE_F32 if w.dtype == torch.float32 else MOE_BF16
+    cols = int(w.shape[-1])
+    rows = int(w.numel() // cols)
+    _check(lib().moe_quantize_int8(_p(w), dt, rows, cols, _p(q_out), _p(scale_out),
+                                   _stream(stream)))
+
+
+def quantize_expert_weights(t: Dict[str, object]) -> Dict[str, object]:
+    """A copy of a weight dict whose routed w1 / w2 are INT8 codes with their
+    w1_scale / w2_scale, made on the device by moe_quantize_int8."""
+    import torch
+    out = dict(t)
+    for name in ("w1", "w2"):
+        w = t[name]
+        q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+        sc = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+        moe_quantize_int8(w, q, sc)
+        out[name] = q
+        out[name + "_scale"] = sc
+    return out
 
 
 def moe_layer_forward(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,

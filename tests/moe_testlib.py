@@ -27,19 +27,37 @@ def oracle_expert_source(inp):
     return get
 
 
+def oracle_expert_source_int8(inp):
+    """Experts as the oracle sees them with INT8 weights: its own quantisation
+    of the seeded bf16 weights, dequantised (s * q)."""
+    base = oracle_expert_source(inp)
+
+    def get(e):
+        w1, b1, w2, b2 = base(e)
+        q1, s1 = O.quantize_int8(w1)
+        q2, s2 = O.quantize_int8(w2)
+        return O.dequantize_int8(q1, s1), b1, O.dequantize_int8(q2, s2), b2
+    return get
+
+
 def oracle_run(inp, capacity, out_tokens=None):
     s = inp.shape
     shared = None
     if s.d_ff_shared:
         shared = (inp.f32("ws1"), inp.f32("ws2"))
-    return O.moe_forward(inp.f32("x"), inp.f32("w_router"), oracle_expert_source(inp), s.top_k,
+    src = oracle_expert_source_int8(inp) if getattr(s, "weight_quant", "none") == "int8" \
+        else oracle_expert_source(inp)
+    return O.moe_forward(inp.f32("x"), inp.f32("w_router"), src, s.top_k,
                          n_experts=s.n_experts, b_router=inp.b_router,
                          logit_offset=inp.logit_offset, sel_bias=inp.sel_bias, shared=shared,
                          capacity=capacity, aux_alpha=s.aux_alpha, out_tokens=out_tokens)
 
 
 def device_tensors(inp, device="cuda"):
-    return inputs.to_torch(inp, device)
+    t = inputs.to_torch(inp, device)
+    if getattr(inp.shape, "weight_quant", "none") == "int8":
+        t = moe.quantize_expert_weights(t)
+    return t
 
 
 def run_stages(cfg, t, device="cuda"):

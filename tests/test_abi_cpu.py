@@ -71,6 +71,33 @@ def test_bad_configs_are_rejected(kw, code):
     assert moe.lib().moe_workspace_size(ctypes.byref(cfg), 5) == ctypes.c_size_t(-1).value
 
 
+def test_weight_quant_checks():
+    cfg = _cfg()
+    cfg.weight_quant = 2
+    assert _route(cfg) == moe.MOE_ERR_INVALID_ARG
+    cfg = _cfg(dtype="f32")
+    cfg.weight_quant = moe.MOE_WQ_INT8
+    assert _route(cfg) == moe.MOE_ERR_UNSUPPORTED
+    assert b"INT8" in moe.lib().moe_last_error()
+    # INT8 experts need both scale arrays
+    cfg = _cfg(weight_quant="int8")
+    L = moe.lib()
+    W = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=FAKE, w1_scale=FAKE)
+    assert L.moe_expert_ffn(ctypes.byref(cfg), FAKE, FAKE, ctypes.byref(W), None, FAKE, None,
+                            FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"w2_scale" in L.moe_last_error()
+
+
+def test_quantize_rejects_bad_arguments():
+    L = moe.lib()
+    assert L.moe_quantize_int8(None, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int8(FAKE, moe.MOE_BF16, 0, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int8(FAKE, moe.MOE_BF16, 4, 100, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int8(FAKE, 5, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int8(FAKE, moe.MOE_F32, 4, 64, FAKE + 4, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"aligned" in L.moe_last_error()
+
+
 def test_bad_dtype_rejected():
     cfg = _cfg()
     cfg.dtype = 7

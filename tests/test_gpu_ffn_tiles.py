@@ -38,9 +38,10 @@ def _gpu():
     moe.lib()
 
 
+@pytest.mark.parametrize("quant", ["none", "int8"])
 @pytest.mark.parametrize("name", sorted(COUNTS))
 @pytest.mark.parametrize("d,f", [(320, 384), (256, 512)])
-def test_expert_blocks(name, d, f):
+def test_expert_blocks(name, d, f, quant):
     import torch
     counts = COUNTS[name]
     N = len(counts)
@@ -57,7 +58,7 @@ def test_expert_blocks(name, d, f):
     offs = np.zeros(N + 1, dtype=np.int32)
     offs[1:] = np.cumsum(counts)
 
-    cfg = moe.make_config(rows, d, f, N, 1, dtype="bf16")
+    cfg = moe.make_config(rows, d, f, N, 1, dtype="bf16", weight_quant=quant)
     dev = "cuda"
 
     def u16(a):
@@ -65,6 +66,8 @@ def test_expert_blocks(name, d, f):
 
     t = {"w_router": u16(w1[:, :1, :].copy()), "w1": u16(w1), "b1": u16(b1), "w2": u16(w2),
          "b2": u16(b2)}
+    if quant == "int8":
+        t = moe.quantize_expert_weights(t)
     W = moe.make_weights(t)
     xd = u16(x)
     y = torch.full((rows, d), 0, dtype=torch.int16, device=dev)
@@ -78,14 +81,19 @@ def test_expert_blocks(name, d, f):
 
     assert (yraw[M:] == SENTINEL).all(), "rows past the last expert block were written"
     xf = inputs.bf16_widen(x)
+    worst = 0.0
     for e in range(N):
         lo, hi = offs[e], offs[e + 1]
         if hi == lo:
             continue
-        ref = O.expert_ffn(xf[lo:hi], inputs.bf16_widen(w1[e]), inputs.bf16_widen(b1[e]),
-                           inputs.bf16_widen(w2[e]), inputs.bf16_widen(b2[e]))
+        W1, W2 = inputs.bf16_widen(w1[e]), inputs.bf16_widen(w2[e])
+        if quant == "int8":
+            W1 = O.dequantize_int8(*O.quantize_int8(W1))
+            W2 = O.dequantize_int8(*O.quantize_int8(W2))
+        ref = O.expert_ffn(xf[lo:hi], W1, inputs.bf16_widen(b1[e]), W2, inputs.bf16_widen(b2[e]))
         got = yh[lo:hi]
         assert np.isfinite(got).all(), f"expert {e}: rows left unwritten or non-finite"
         err = rel_l2(got, ref)
         assert err <= BF16_TOL, (e, counts[e], err)
-    say(f"  {N} expert blocks within {BF16_TOL} rel-L2; spare rows untouched")
+        worst = max(worst, err)
+    say(f"  {N} expert blocks, worst rel-L2 {worst:.2e} (tol {BF16_TOL}); spare rows untouched")

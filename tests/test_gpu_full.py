@@ -1,5 +1,6 @@
-"""GPU parity at the five workload sizes, in the launch configuration bench.py
-times (the same C-ABI stage calls).
+"""GPU parity at the five workload sizes (and the three weight-bound ones again
+with INT8 expert weights), in the launch configuration bench.py times (the
+same C-ABI stage calls).
 
 Routing, dispatch, aux loss, router z-loss and routing statistics are
 compared over every token (integers bit-exact).  The expert FFN and the layer output are compared on sampled rows
@@ -15,7 +16,8 @@ from mixture_experts_layer_prefix_amd import inputs, moe
 from oracle import moe_oracle as O
 
 from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, W_TOL, check_routing_and_dispatch,
-                         device_tensors, oracle_expert_source, oracle_run, rel_l2, run_stages, say)
+                         device_tensors, oracle_expert_source, oracle_expert_source_int8,
+                         oracle_run, rel_l2, run_stages, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +33,7 @@ def _sample_tokens(shape, o, n=10):
     return np.array(sorted(toks))
 
 
-@pytest.mark.parametrize("shape", C.ALL, ids=[s.name for s in C.ALL])
+@pytest.mark.parametrize("shape", C.ALL + C.INT8, ids=[s.name for s in C.ALL + C.INT8])
 def test_full_size(shape):
     import torch
     if not torch.cuda.is_available():
@@ -82,7 +84,8 @@ def test_full_size(shape):
     rows = np.unique(np.concatenate([np.random.default_rng(7).choice(M, size=min(8, M),
                                                                      replace=False),
                                      [0, M - 1]]))
-    get = oracle_expert_source(inp)
+    get = (oracle_expert_source_int8(inp) if shape.weight_quant == "int8"
+           else oracle_expert_source(inp))
     offs = g["expert_offsets"]
     yp = g["y_perm"][torch.from_numpy(rows).long().cuda()].float().cpu().numpy()
     ref = []
