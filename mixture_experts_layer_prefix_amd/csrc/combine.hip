@@ -11,8 +11,8 @@
 // output dtype.  Dropped slots contribute nothing.
 //
 // One wavefront per token; each lane moves 16-byte pieces of the rows, so a
-// wavefront reads 1 KiB of a row per instruction; no atomics, every output
-// element written exactly once.
+// wavefront reads 1 KiB of a row per instruction, and many such loads are in
+// flight per lane; no atomics, every output element written exactly once.
 #include "moe_internal.h"
 
 namespace moe {
@@ -54,7 +54,12 @@ struct Vec<uint16_t> {
   }
 };
 
-template <typename T>
+// One wavefront per token (its index made wave-uniform, so the slot rows and
+// weights are scalar loads).  The slots are taken in groups of KB; for each
+// group a lane first issues the loads of all the group's kept rows for U
+// 16-byte pieces, then adds them in slot order, so KB * U loads per lane are in
+// flight together instead of one row at a time.
+template <typename T, int KB, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y_perm,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ topk_w,
@@ -62,32 +67,87 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       uint4* __restrict__ out, int Ttok,
                                                       int nvec, int K) {
   constexpr int EV = Vec<T>::N;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   if (t >= Ttok) return;
   const int lane = threadIdx.x & 63;
   const int32_t* sr = slot_row + (int64_t)t * K;
   const float* wt = topk_w + (int64_t)t * K;
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[EV];
-#pragma unroll
-    for (int i = 0; i < EV; ++i) acc[i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int r = sr[k];
-      if (r < 0) continue;
-      const float w = wt[k];
-      float y[EV];
-      Vec<T>::unpack(y_perm[(int64_t)r * nvec + c], y);
-#pragma unroll
-      for (int i = 0; i < EV; ++i) acc[i] = fmaf(w, y[i], acc[i]);
-    }
+  for (int c0 = lane; c0 < nvec; c0 += 64 * U) {
+    // the shared expert's pieces are loaded with the first group of rows
+    uint4 vs[U];
     if (y_shared) {
-      float y[EV];
-      Vec<T>::unpack(y_shared[(int64_t)t * nvec + c], y);
 #pragma unroll
-      for (int i = 0; i < EV; ++i) acc[i] += y[i];
+      for (int u = 0; u < U; ++u)
+        if (c0 + 64 * u < nvec) vs[u] = y_shared[(int64_t)t * nvec + c0 + 64 * u];
     }
-    out[(int64_t)t * nvec + c] = Vec<T>::pack(acc);
+    float acc[U][EV];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < EV; ++i) acc[u][i] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+      int r[KB];
+      float w[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        r[j] = (k0 + j < K) ? sr[k0 + j] : -1;
+        w[j] = (r[j] >= 0) ? wt[k0 + j] : 0.f;
+      }
+      uint4 v[KB][U];
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (r[j] >= 0) {
+          const uint4* yr = y_perm + (int64_t)r[j] * nvec;
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (c0 + 64 * u < nvec) v[j][u] = yr[c0 + 64 * u];
+        }
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (r[j] >= 0) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            float y[EV];
+            Vec<T>::unpack(v[j][u], y);
+#pragma unroll
+            for (int i = 0; i < EV; ++i) acc[u][i] = fmaf(w[j], y[i], acc[u][i]);
+          }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= nvec) break;
+      if (y_shared) {
+        float y[EV];
+        Vec<T>::unpack(vs[u], y);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) acc[u][i] += y[i];
+      }
+      out[(int64_t)t * nvec + c] = Vec<T>::pack(acc[u]);
+    }
   }
+}
+
+template <typename T>
+void launch_combine_t(const void* y_perm, const int32_t* slot_row, const float* topk_w,
+                      const void* y_shared, void* out, int Ttok, int nvec, int K, hipStream_t s) {
+  const dim3 grid((Ttok + 3) / 4), block(256);
+  const uint4* y = static_cast<const uint4*>(y_perm);
+  const uint4* ys = static_cast<const uint4*>(y_shared);
+  uint4* o = static_cast<uint4*>(out);
+  if (K == 1)
+    hipLaunchKernelGGL((combine_kernel<T, 1, 2>), grid, block, 0, s, y, slot_row, topk_w, ys, o, Ttok,
+                       nvec, K);
+  else if (K <= 2)
+    hipLaunchKernelGGL((combine_kernel<T, 2, 4>), grid, block, 0, s, y, slot_row, topk_w, ys, o, Ttok,
+                       nvec, K);
+  else if (K <= 4)
+    hipLaunchKernelGGL((combine_kernel<T, 4, 4>), grid, block, 0, s, y, slot_row, topk_w, ys, o, Ttok,
+                       nvec, K);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, 8, 2>), grid, block, 0, s, y, slot_row, topk_w, ys, o, Ttok,
+                       nvec, K);
 }
 
 }  // namespace
@@ -96,15 +156,10 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* slot_row
                           const float* topk_w, const void* y_shared, void* out, int T, int d,
                           int K, hipStream_t s) {
   const int nvec = d * (dtype == 0 ? 4 : 2) / 16;
-  dim3 grid((T + 3) / 4);
   if (dtype == 0)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const uint4*>(y_perm), slot_row, topk_w,
-                       static_cast<const uint4*>(y_shared), static_cast<uint4*>(out), T, nvec, K);
+    launch_combine_t<float>(y_perm, slot_row, topk_w, y_shared, out, T, nvec, K, s);
   else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint4*>(y_perm), slot_row, topk_w,
-                       static_cast<const uint4*>(y_shared), static_cast<uint4*>(out), T, nvec, K);
+    launch_combine_t<uint16_t>(y_perm, slot_row, topk_w, y_shared, out, T, nvec, K, s);
   return hipGetLastError();
 }
 

@@ -17,8 +17,9 @@
 //   3. rank:    one wavefront per chunk walks its pairs in order, 64 at a
 //               time; lanes with equal experts are matched with ballots, so
 //               each pair's position is its chunk start + earlier matches.
-//   4. permute: one wavefront per token reads x[t] once (16-byte loads) and
-//               writes it to each of its kept rows.
+//   4. permute: one wavefront per token reads x[t] once (16-byte loads, the
+//               whole row in one batch for rows up to 16 KiB) and writes it to
+//               each of its kept rows.
 #include "moe_internal.h"
 
 namespace moe {
@@ -132,12 +133,15 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   }
 }
 
-// One wavefront per token; rows are copied as 16-byte units.
+// One wavefront per token (its index made wave-uniform, so the slot rows are
+// scalar loads); rows are copied as 16-byte units, up to U per lane loaded
+// together before they are stored to each kept row.
+template <int U>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x,
                                                       const int32_t* __restrict__ slot_row,
                                                       uint4* __restrict__ x_perm, int T, int K,
                                                       int row_vec) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   const int32_t* sr = slot_row + (int64_t)t * K;
@@ -145,23 +149,24 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
   for (int k = 0; k < K; ++k) any |= sr[k] >= 0;
   if (!any) return;
   const uint4* src = x + (int64_t)t * row_vec;
-  constexpr int U = 4;
-  for (int c0 = lane; c0 < row_vec; c0 += 64 * U) {
+  // this lane's pieces are c = lane + 64 i, i < n
+  const int n = (row_vec - lane + 63) / 64;
+  for (int i0 = 0; i0 < n; i0 += U) {
     uint4 v[U];
+    if (i0 + U <= n) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * 64;
-      if (c < row_vec) v[u] = src[c];
+      for (int u = 0; u < U; ++u) v[u] = src[lane + 64 * (i0 + u)];
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = (i0 + u < n) ? src[lane + 64 * (i0 + u)] : make_uint4(0, 0, 0, 0);
     }
     for (int k = 0; k < K; ++k) {
       const int r = sr[k];
       if (r < 0) continue;
-      uint4* dst = x_perm + (int64_t)r * row_vec;
+      uint4* dst = x_perm + (int64_t)r * row_vec + lane;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * 64;
-        if (c < row_vec) dst[c] = v[u];
-      }
+      for (int u = 0; u < U; ++u)
+        if (i0 + u < n) dst[64 * (i0 + u)] = v[u];
     }
   }
 }
@@ -257,9 +262,17 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
                      (int64_t)T * K, blkoff, counts, offsets, n_dropped);
   hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(64), 0, s, topk_idx, T, K, N, cap, blkoff,
                      offsets, slot_row, row_token);
-  hipLaunchKernelGGL(permute_kernel, dim3((T + 3) / 4), dim3(256), 0, s,
-                     static_cast<const uint4*>(x), slot_row, static_cast<uint4*>(x_perm), T, K,
-                     (int)(row_bytes / 16));
+  // the pieces a lane copies per row, all in one batch when they fit in 16
+  const int row_vec = (int)(row_bytes / 16), per_lane = (row_vec + 63) / 64;
+  const uint4* xs = static_cast<const uint4*>(x);
+  uint4* xd = static_cast<uint4*>(x_perm);
+  const dim3 pg((T + 3) / 4), pb(256);
+  if (per_lane <= 4)
+    hipLaunchKernelGGL(permute_kernel<4>, pg, pb, 0, s, xs, slot_row, xd, T, K, row_vec);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL(permute_kernel<8>, pg, pb, 0, s, xs, slot_row, xd, T, K, row_vec);
+  else
+    hipLaunchKernelGGL(permute_kernel<16>, pg, pb, 0, s, xs, slot_row, xd, T, K, row_vec);
   return hipGetLastError();
 }
 
