@@ -35,11 +35,16 @@ notes as well):
     ([yunthe] form, sum f = K), P_e the mean full-N softmax of the logits;
   * INT8 weight-only experts: symmetric, one fp32 scale per output row,
     s = maxabs / 127 and q = round-half-even(w / s) clamped to +-127, both
-    divisions in fp32; the expert then uses the weights s * q.
+    divisions in fp32; the expert then uses the weights s * q;
+  * backward: the gradient of the forward above with the Top-K choice and the
+    capacity drops held fixed, the logits' fp32 rounding taken as the
+    identity, selection bias, logit offsets and the aux loss's f constant.
 
-Pins: every function here is pinned by tests/test_oracle_pins.py against
-brute force, closed forms, the corrected worked example, special cases and
-textbook routines.  Absolute output values at the large workload sizes are
+Pins: every function here is pinned by tests/test_oracle_pins.py (the
+backward by tests/test_oracle_backward_pins.py: central finite differences of
+the forward, torch.autograd of an independently written forward, and
+invariants) against brute force, closed forms, the corrected worked example,
+special cases and textbook routines.  Absolute output values at the large workload sizes are
 "parity unpinned" beyond that: the pages print none, and the oracle runs the
 same code at every size.
 """
@@ -65,17 +70,20 @@ def _f64(a):
 # a1: router scoring.  [lmnt] §2.1: scores come from W_g . x, W_g being
 # d_model x N; [yunthe] reference forward: the router is a Linear layer
 # (with bias in nn.Linear's default form).
-def router_logits(x, w_router, b_router=None, logit_offset=None) -> np.ndarray:
+def router_logits(x, w_router, b_router=None, logit_offset=None,
+                  round_fp32: bool = True) -> np.ndarray:
     """logits[t, e] = fp32( sum_j x[t, j] * W_r[e, j] + b_r[e] + off[e] ).
 
     x: [T, d]; w_router: [N, d] (nn.Linear [out, in]); b_router, logit_offset: [N]
-    or None.  Products and sums in fp64; one rounding to fp32 at the end."""
+    or None.  Products and sums in fp64; one rounding to fp32 at the end
+    (round_fp32=False keeps the fp64 value: the gradient pins differentiate
+    the unrounded function)."""
     z = _f64(x) @ _f64(w_router).T
     if b_router is not None:
         z = z + _f64(b_router)[None, :]
     if logit_offset is not None:
         z = z + _f64(logit_offset)[None, :]
-    return z.astype(np.float32)
+    return z.astype(np.float32) if round_fp32 else z
 
 
 # --------------------------------------------------------------------------
@@ -267,7 +275,7 @@ ExpertSource = Union[Sequence, Callable[[int], tuple]]
 def moe_forward(x, w_router, experts: ExpertSource, top_k: int, *, n_experts: Optional[int] = None,
                 b_router=None, logit_offset=None, sel_bias=None, shared=None,
                 capacity: Optional[int] = None, aux_alpha: float = 0.0,
-                out_tokens: Optional[np.ndarray] = None) -> dict:
+                out_tokens: Optional[np.ndarray] = None, round_logits: bool = True) -> dict:
     """experts: sequence of (W1 [f, d], b1 [f] | None, W2 [d, f], b2 [d] | None)
     or a callable e -> that tuple.  shared: None or (Ws1 [f_s, d], Ws2 [d, f_s]).
     capacity: None or <= 0 for dropless, else C.  out_tokens: compute ``out``
@@ -278,8 +286,9 @@ def moe_forward(x, w_router, experts: ExpertSource, top_k: int, *, n_experts: Op
     N = n_experts if n_experts is not None else np.asarray(w_router).shape[0]
     get = experts if callable(experts) else (lambda e: experts[e])
 
-    logits = router_logits(x64, w_router, b_router, logit_offset)
-    scores = selection_scores(logits, sel_bias)
+    logits = router_logits(x64, w_router, b_router, logit_offset, round_fp32=round_logits)
+    scores = selection_scores(logits, sel_bias) if round_logits else (
+        logits if sel_bias is None else logits + _f64(sel_bias)[None, :])
     idx = topk_select(scores, top_k)
     w = topk_softmax(logits, idx)
     disp = dispatch(idx, N, capacity)
@@ -308,3 +317,140 @@ def moe_forward(x, w_router, experts: ExpertSource, top_k: int, *, n_experts: Op
     if aux_alpha:
         res["aux"] = aux_loss(logits, idx, N, aux_alpha)
     return res
+
+
+# --------------------------------------------------------------------------
+# Backward pass (training).  [lmnt] §2.2: in training the K routing weights
+# take part in back-propagation, which is how the gate learns its scores;
+# §5.1-5.2: the balance loss reaches the gate through the probabilities P;
+# §5.3: the z-loss constrains only the router scores; §4.1: under mixed
+# precision the gradients are kept in 16 bits like the weights; §6.2: an
+# expert that receives no tokens gets no gradient.
+#
+# What is differentiated is the forward defined above, with the Top-K choice
+# and the capacity drops held at their forward values (both are piecewise
+# constant in the inputs), the fp32 rounding of the logits taken as the
+# identity, the selection bias and logit offsets constants, and the aux
+# loss's f_e (a count) constant.  The scalar differentiated is
+#   L = <d_out, out> + g_aux * aux + g_z * zloss
+# so d_out is the upstream gradient of the layer output and g_aux, g_z those
+# of the two losses.
+def gelu_grad(z):
+    """d/dz GELU(z) = Phi(z) + z * phi(z) (erf form)."""
+    z = _f64(z)
+    return 0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+
+
+def expert_ffn_backward(x_rows, w1, b1, w2, g_y):
+    """Backward of E(x) = W2 . GELU(W1 . x + b1) + b2 for a block of rows.
+
+    g_y: [R, d] gradient of the rows' outputs.  Returns (g_x [R, d], dW1 [f, d],
+    db1 [f], dW2 [d, f], db2 [d]); every sum over rows in fp64."""
+    x64, g_y = _f64(x_rows), _f64(g_y)
+    z = x64 @ _f64(w1).T
+    if b1 is not None:
+        z = z + _f64(b1)[None, :]
+    h = gelu(z)
+    dW2 = g_y.T @ h
+    db2 = g_y.sum(axis=0)
+    g_h = g_y @ _f64(w2)
+    g_z = g_h * gelu_grad(z)
+    dW1 = g_z.T @ x64
+    db1 = g_z.sum(axis=0)
+    g_x = g_z @ _f64(w1)
+    return g_x, dW1, db1, dW2, db2
+
+
+def topk_softmax_backward(w: np.ndarray, d_w: np.ndarray) -> np.ndarray:
+    """Gradient of the K selected logits from that of w = softmax(selected):
+    d_l_j = w_j * (d_w_j - sum_k w_k d_w_k)."""
+    w, d_w = _f64(w), _f64(d_w)
+    return w * (d_w - (w * d_w).sum(axis=1, keepdims=True))
+
+
+def aux_loss_logit_grad(logits: np.ndarray, counts, alpha: float) -> np.ndarray:
+    """d aux / d logits[t, e] = alpha * N / T * p_te * (f_e - sum_e' f_e' p_te'),
+    p_t = softmax_N(logits_t), f_e = counts_e / T held constant."""
+    z = _f64(logits)
+    T, N = z.shape
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    f = _f64(counts) / T
+    return alpha * N / T * p * (f[None, :] - (p @ f)[:, None])
+
+
+def router_z_loss_logit_grad(logits: np.ndarray, beta: float) -> np.ndarray:
+    """d (beta * mean_t lse_t^2) / d logits[t, e] = 2 beta / T * lse_t * p_te."""
+    z = _f64(logits)
+    T = z.shape[0]
+    m = z.max(axis=1, keepdims=True)
+    s = np.exp(z - m).sum(axis=1, keepdims=True)
+    lse = m + np.log(s)
+    p = np.exp(z - m) / s
+    return 2.0 * beta / T * lse * p
+
+
+def moe_backward(x, w_router, experts: ExpertSource, top_k: int, d_out, *,
+                 n_experts: Optional[int] = None, b_router=None, logit_offset=None,
+                 sel_bias=None, shared=None, capacity: Optional[int] = None,
+                 aux_alpha: float = 0.0, aux_grad: float = 1.0, zloss_beta: float = 0.0,
+                 zloss_grad: float = 1.0, round_logits: bool = True) -> dict:
+    """Gradients of L = <d_out, out> + aux_grad * aux + zloss_grad * zloss.
+
+    Same arguments as moe_forward plus d_out [T, d].  Returns d_x [T, d],
+    d_w_router [N, d], d_b_router [N], d_w1 [N, f, d], d_b1 [N, f],
+    d_w2 [N, d, f], d_b2 [N, d], d_ws1, d_ws2 (shared, or None), d_topk_w [T, K]
+    (zero for dropped slots), d_logits [T, N] and the forward's routing."""
+    x64, g_out = _f64(x), _f64(d_out)
+    T, d = x64.shape
+    N = n_experts if n_experts is not None else np.asarray(w_router).shape[0]
+    get = experts if callable(experts) else (lambda e: experts[e])
+    logits = router_logits(x64, w_router, b_router, logit_offset, round_fp32=round_logits)
+    scores = selection_scores(logits, sel_bias) if round_logits else (
+        logits if sel_bias is None else logits + _f64(sel_bias)[None, :])
+    idx = topk_select(scores, top_k)
+    w = topk_softmax(logits, idx)
+    disp = dispatch(idx, N, capacity)
+    kept_pair = disp["slot_row"] >= 0
+
+    d_x = np.zeros_like(x64)
+    d_w = np.zeros((T, top_k))
+    e0 = get(0)
+    f = np.asarray(e0[0]).shape[0]
+    d_w1 = np.zeros((N, f, d))
+    d_b1 = np.zeros((N, f))
+    d_w2 = np.zeros((N, d, f))
+    d_b2 = np.zeros((N, d))
+    # the pages' loop over slots and experts; the rows of one (slot, expert)
+    # pair set go through the expert together
+    for k in range(top_k):
+        for e in range(N):
+            mask = (idx[:, k] == e) & kept_pair[:, k]
+            if not mask.any():
+                continue
+            w1, b1, w2, b2 = get(e)
+            y = expert_ffn(x64[mask], w1, b1, w2, b2)
+            d_w[mask, k] = (g_out[mask] * y).sum(axis=1)
+            g_y = w[mask, k][:, None] * g_out[mask]
+            g_x, dW1, db1, dW2, db2 = expert_ffn_backward(x64[mask], w1, b1, w2, g_y)
+            d_x[mask] += g_x
+            d_w1[e] += dW1
+            d_b1[e] += db1
+            d_w2[e] += dW2
+            d_b2[e] += db2
+    d_ws1 = d_ws2 = None
+    if shared is not None:
+        ws1, ws2 = shared
+        g_x, d_ws1, _, d_ws2, _ = expert_ffn_backward(x64, ws1, None, ws2, g_out)
+        d_x += g_x
+
+    d_logits = np.zeros((T, N))
+    np.put_along_axis(d_logits, idx.astype(np.int64), topk_softmax_backward(w, d_w), axis=1)
+    if aux_alpha:
+        d_logits += aux_grad * aux_loss_logit_grad(logits, disp["counts"], aux_alpha)
+    if zloss_beta:
+        d_logits += zloss_grad * router_z_loss_logit_grad(logits, zloss_beta)
+    d_x += d_logits @ _f64(w_router)
+    return dict(d_x=d_x, d_w_router=d_logits.T @ x64, d_b_router=d_logits.sum(axis=0),
+                d_w1=d_w1, d_b1=d_b1, d_w2=d_w2, d_b2=d_b2, d_ws1=d_ws1, d_ws2=d_ws2,
+                d_topk_w=d_w, d_logits=d_logits, logits=logits, idx=idx, w=w, **disp)
