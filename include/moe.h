@@ -1,6 +1,6 @@
 /*
  * moe.h -- C ABI of libmoe.so: the forward hot path of a Mixture-of-Experts
- * (MoE) layer on one AMD MI355X (gfx950) GPU.
+ * (MoE) layer on one AMD MI355X (gfx950) GPU, and its backward pass.
  *
  * The layer (per token x_t, N routed experts, top-K):
  *   logits = W_r . x_t (+ b_r) (+ offset)            router scoring
@@ -103,7 +103,12 @@ typedef enum {
   MOE_STAGE_EXPERT_FFN = 2,
   MOE_STAGE_COMBINE = 3,
   MOE_STAGE_AUX = 4,
-  MOE_STAGE_LAYER = 5
+  MOE_STAGE_LAYER = 5,
+  MOE_STAGE_EXPERT_FFN_TRAIN = 6,    /* moe_expert_ffn_train     */
+  MOE_STAGE_LAYER_TRAIN = 7,         /* moe_layer_forward_train  */
+  MOE_STAGE_EXPERT_FFN_BACKWARD = 8, /* moe_expert_ffn_backward  */
+  MOE_STAGE_ROUTE_BACKWARD = 9,      /* moe_route_backward       */
+  MOE_STAGE_LAYER_BACKWARD = 10      /* moe_layer_backward       */
 } moe_stage_t;
 
 /* Bytes of device workspace the entry point of `stage` needs for `cfg`
@@ -246,6 +251,158 @@ int moe_layer_forward(const moe_config_t *cfg, const void *x, const moe_weights_
  * not a positive multiple of 64, or an unknown dtype. */
 int moe_quantize_int8(const void *w, int32_t dtype, int64_t rows, int32_t cols, int8_t *q,
                       float *scale, hipStream_t stream);
+
+/* ------------------------------------------------------------------ training
+ * The backward pass (lmnt.cn MoE walkthrough §2.2: in training the K routing
+ * weights take part in back-propagation, which is how the gate learns its
+ * scores; §5.1-5.3: the balance loss and the z-loss act on the gate through
+ * its probabilities and logits; §4.1: under mixed precision the gradients are
+ * kept in 16 bits like the weights; §6.2: an expert that receives no tokens
+ * gets no gradient).
+ *
+ * What is differentiated: the forward above with the Top-K choice and the
+ * capacity drops held at their forward values (both are piecewise constant
+ * in the inputs), the fp32 rounding of the logits taken as the identity,
+ * sel_bias and logit_offset constants, and the aux loss's f_e (a count)
+ * constant.  The scalar is
+ *   L = <d_out, out> + aux_grad * aux + zloss_grad * zloss_beta * mean_t lse_t^2
+ * with aux = cfg->aux_alpha * N * sum_e f_e P_e as in moe_aux_loss.
+ *
+ * Precision: the expert GEMMs run on the forward's kernels (bf16 operands,
+ * fp32 accumulation, results rounded to dtype); d_h, d_z and the expert
+ * weight and bias gradients are stored in dtype; every sum over rows or
+ * tokens is fp32 with a fixed order (deterministic); the router gradients
+ * d_w_router, d_b_router and the router's share of d_x are fp32.
+ * INT8 experts are inference-only: every training entry point returns
+ * MOE_ERR_UNSUPPORTED for MOE_WQ_INT8, and for
+ * max(d_model, d_ff, d_ff_shared) * (T*K + 32*N) >= 2^31.
+ */
+
+/* Tensors the training forward keeps for the backward.  All [dev],
+ * caller-owned, 16-byte aligned; rows past expert_offsets[N] are unused. */
+typedef struct {
+  float *logits;            /* [T, N] fp32                                    */
+  int32_t *topk_idx;        /* [T, K]                                         */
+  float *topk_w;            /* [T, K] fp32                                    */
+  int32_t *counts;          /* [N] pre-drop selections                        */
+  int32_t *expert_offsets;  /* [N+1]                                          */
+  int32_t *slot_row;        /* [T, K]                                         */
+  int32_t *row_token;       /* [T*K]                                          */
+  int32_t *n_dropped;       /* [1]                                            */
+  void *x_perm;             /* [T*K, d] dtype                                 */
+  void *z;                  /* [T*K, f] dtype: W1 x + b1, before the GELU     */
+  void *h;                  /* [T*K, f] dtype: GELU(z)                        */
+  void *y_perm;             /* [T*K, d] dtype                                 */
+  void *zs;                 /* [T, f_s] dtype (shared expert), or NULL        */
+  void *hs;                 /* [T, f_s] dtype (shared expert), or NULL        */
+} moe_saved_t;
+
+/* Gradients.  All [dev], caller-owned, overwritten (not accumulated). */
+typedef struct {
+  float *d_w_router;        /* [N, d] fp32                                    */
+  float *d_b_router;        /* [N] fp32, or NULL: not written                 */
+  void *d_w1;               /* [N, f, d] dtype                                */
+  void *d_b1;               /* [N, f] dtype, or NULL: not written             */
+  void *d_w2;               /* [N, d, f] dtype                                */
+  void *d_b2;               /* [N, d] dtype, or NULL: not written             */
+  void *d_ws1;              /* [f_s, d] dtype (shared expert), or NULL        */
+  void *d_ws2;              /* [d, f_s] dtype (shared expert), or NULL        */
+} moe_grads_t;
+
+/* moe_expert_ffn that keeps its intermediates: GEMM1 writes z = W1 x + b1
+ * (no GELU), a GELU pass writes h = GELU(z), GEMM2 reads h.  Same arguments
+ * as moe_expert_ffn plus z, h [T*K, f] and, with a shared expert, zs, hs
+ * [T, f_s] (all [dev] dtype out).  The rounding of z to dtype before the GELU
+ * is the only difference from moe_expert_ffn.
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_EXPERT_FFN_TRAIN) bytes. */
+int moe_expert_ffn_train(const moe_config_t *cfg, const void *x_perm,
+                         const int32_t *expert_offsets, const moe_weights_t *w, const void *x,
+                         void *z, void *h, void *y_perm, void *zs, void *hs, void *y_shared,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward that fills `saved` (route, dispatch and
+ * moe_expert_ffn_train into the caller's buffers, then combine; the aux loss
+ * when aux_out != NULL).
+ *   x [dev] [T, d] dtype in;  out [dev] [T, d] dtype out;
+ *   aux_out [dev] [1] fp32 out or NULL;  saved: every pointer [dev] out;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_LAYER_TRAIN) bytes. */
+int moe_layer_forward_train(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
+                            void *out, float *aux_out, const moe_saved_t *saved, void *ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Combine backward (the transpose of lmnt.cn §3.2's weighted sum):
+ *   d_y_perm[slot_row[t,k]] = topk_w[t,k] * d_out[t]       (kept slots only)
+ *   d_topk_w[t,k] = <d_out[t], y_perm[slot_row[t,k]]>      (0 if dropped)
+ * dot products in fp32 with a fixed order.
+ *   d_out [dev] [T, d] dtype in;  y_perm [dev] [T*K, d] dtype in;
+ *   slot_row [dev] [T, K] int32 in;  topk_w [dev] [T, K] fp32 in;
+ *   d_y_perm [dev] [T*K, d] dtype out;  d_topk_w [dev] [T, K] fp32 out. */
+int moe_combine_backward(const moe_config_t *cfg, const void *d_out, const void *y_perm,
+                         const int32_t *slot_row, const float *topk_w, void *d_y_perm,
+                         float *d_topk_w, hipStream_t stream);
+
+/* Expert FFN backward, routed experts then the shared one (whose upstream
+ * gradient is d_out itself, weight 1):
+ *   d_h = d_y W2_e,  d_z = d_h * GELU'(z),  d_x_perm = d_z W1_e,
+ *   d_w2[e] = d_y_e^T h_e,  d_b2[e] = sum of d_y_e's rows,
+ *   d_w1[e] = d_z_e^T x_perm_e,  d_b1[e] = sum of d_z_e's rows;
+ * an expert with no rows gets zeros.
+ *   x_perm, expert_offsets, z, h: as saved by the training forward;
+ *   x [dev] [T, d], zs, hs [dev] [T, f_s]: shared expert (NULL without one);
+ *   d_y_perm [dev] [T*K, d] dtype in (moe_combine_backward);
+ *   d_out [dev] [T, d] dtype in (shared expert only; may be NULL without one);
+ *   d_x_perm [dev] [T*K, d] dtype out;  d_x_shared [dev] [T, d] dtype out, NULL
+ *   iff no shared expert;  grads: d_w1, d_w2 (+ d_b1, d_b2 if not NULL; d_ws1,
+ *   d_ws2 with a shared expert) written;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_EXPERT_FFN_BACKWARD) bytes
+ *   (transposed weights and activations). */
+int moe_expert_ffn_backward(const moe_config_t *cfg, const void *x_perm,
+                            const int32_t *expert_offsets, const moe_weights_t *w, const void *x,
+                            const void *z, const void *h, const void *zs, const void *hs,
+                            const void *d_y_perm, const void *d_out, void *d_x_perm,
+                            void *d_x_shared, const moe_grads_t *grads, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Router backward:
+ *   d_logits[t, sel_k] = w_k (d_w_k - sum_j w_j d_w_j)          (softmax over K)
+ *     + aux_grad * cfg->aux_alpha * N / T * p_te (f_e - sum_e' f_e' p_te')
+ *     + zloss_grad * 2 * zloss_beta / T * lse_t * p_te,
+ *   p_t = softmax_N(logits_t) (fp32), f_e = counts[e] / T;
+ *   d_w_router = d_logits^T x,  d_b_router = sum_t d_logits,
+ *   d_x_router = d_logits W_r   (all fp32, fixed-order sums).
+ *   x [dev] [T, d] dtype in;  logits, topk_idx, topk_w: from the forward;
+ *   d_topk_w [dev] [T, K] fp32 in (moe_combine_backward);
+ *   counts [dev] [N] int32 in (needed when aux_alpha * aux_grad != 0);
+ *   d_logits [dev] [T, N] fp32 out or NULL;  d_x_router [dev] [T, d] fp32 out
+ *   or NULL;  grads: d_w_router (+ d_b_router if not NULL) written;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_ROUTE_BACKWARD) bytes. */
+int moe_route_backward(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
+                       const float *logits, const int32_t *topk_idx, const float *topk_w,
+                       const float *d_topk_w, const int32_t *counts, float aux_grad,
+                       float zloss_beta, float zloss_grad, float *d_logits, float *d_x_router,
+                       const moe_grads_t *grads, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch backward (the transpose of lmnt.cn §3.1's permutation):
+ *   d_x[t] = sum over kept slots k of d_x_perm[slot_row[t,k]] (slot order)
+ *            + d_x_shared[t] + d_x_router[t],
+ * fp32 sums rounded once to dtype.
+ *   d_x_perm [dev] [T*K, d] dtype in;  slot_row [dev] [T, K] int32 in;
+ *   d_x_shared [dev] [T, d] dtype in or NULL;  d_x_router [dev] [T, d] fp32 in
+ *   or NULL;  d_x [dev] [T, d] dtype out. */
+int moe_dispatch_backward(const moe_config_t *cfg, const void *d_x_perm, const int32_t *slot_row,
+                          const void *d_x_shared, const float *d_x_router, void *d_x,
+                          hipStream_t stream);
+
+/* The whole backward: combine, expert FFN (+ shared), router and dispatch
+ * backward in that order, from the tensors moe_layer_forward_train saved.
+ *   x [dev] [T, d] dtype in (the forward's input);  d_out [dev] [T, d] dtype in;
+ *   aux_grad, zloss_beta, zloss_grad: finite (0 leaves that loss out);
+ *   d_x [dev] [T, d] dtype out;  grads: every non-NULL field written;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_LAYER_BACKWARD) bytes. */
+int moe_layer_backward(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
+                       const moe_saved_t *saved, const void *d_out, float aux_grad,
+                       float zloss_beta, float zloss_grad, void *d_x, const moe_grads_t *grads,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Thread-local text of the last non-OK return on this thread ("" if none). */
 const char *moe_last_error(void);

@@ -1,0 +1,758 @@
+// Backward pass of the layer: the bandwidth-bound kernels.
+//
+// What is computed (lmnt.cn MoE walkthrough §2.2: in training the K routing
+// weights take part in back-propagation, which is how the gate learns;
+// §5.1-5.3: the balance loss and the z-loss reach the gate through its
+// probabilities and logits; §4.1: gradients are kept in 16 bits like the
+// weights under mixed precision): the gradient of the forward with the Top-K
+// choice and the capacity drops held at their forward values.  With
+// g = d out (the upstream gradient of the layer output):
+//   combine:   d_y_perm[row(t,k)] = w[t,k] * g[t];  d_w[t,k] = <g[t], y_perm[row(t,k)]>
+//              (0 for a dropped slot)
+//   GELU:      d_z = d_h * GELU'(z),  GELU'(z) = Phi(z) + z phi(z)
+//   unpermute: d_x[t] = sum_{kept k} d_x_perm[row(t,k)] + d_x_shared[t] + d_x_router[t]
+//   router:    d_l[t, sel_k] += w_k (d_w_k - sum_j w_j d_w_j)
+//              d_l[t, e]     += g_aux * alpha N / T * p_te (f_e - sum_e' f_e' p_te')
+//              d_l[t, e]     += g_z * 2 beta / T * lse_t * p_te
+//              d_W_r = d_l^T x,  d_b_r = sum_t d_l,  d_x_router = d_l W_r
+// The grouped GEMMs of the expert backward run on the forward's GEMM kernels:
+// the input gradients on transposed weights (transpose_batched below), the
+// weight gradients in their k-segment mode on activations transposed per
+// expert into zero-padded segments (transpose_segments below, which also
+// forms the bias gradients as column sums).
+//
+// Every reduction has a fixed order, so results are deterministic.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// 16 bytes of T: 8 bf16 or 4 fp32
+template <typename T>
+struct V16;
+template <>
+struct V16<uint16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  static __device__ __forceinline__ float gelu(float z) { return gelu_as(z); }
+  static __device__ __forceinline__ float gelu_grad(float z) { return gelu_grad_as(z); }
+};
+template <>
+struct V16<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  static __device__ __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+  static __device__ __forceinline__ float gelu(float z) { return gelu_erf(z); }
+  static __device__ __forceinline__ float gelu_grad(float z) { return gelu_grad_erf(z); }
+};
+
+// ---------------------------------------------------------------- elementwise
+// Rows [0, *nrows) of a [*, width] matrix, as 16-byte pieces.  The GELU has
+// the form the forward's fused epilogue uses for the dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void gelu_fwd_kernel(const uint4* __restrict__ z,
+                                                       uint4* __restrict__ h,
+                                                       const int32_t* __restrict__ nrows,
+                                                       int rows_const, int width) {
+  const int rows = nrows ? *nrows : rows_const;
+  const int64_t n = (int64_t)rows * width / V16<T>::N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float v[V16<T>::N];
+    V16<T>::unpack(z[i], v);
+#pragma unroll
+    for (int q = 0; q < V16<T>::N; ++q) v[q] = V16<T>::gelu(v[q]);
+    h[i] = V16<T>::pack(v);
+  }
+}
+
+// d_z = d_h * GELU'(z), written over d_h.
+template <typename T>
+__global__ __launch_bounds__(256) void gelu_bwd_kernel(const uint4* __restrict__ z,
+                                                       uint4* __restrict__ dh,
+                                                       const int32_t* __restrict__ nrows,
+                                                       int rows_const, int width) {
+  const int rows = nrows ? *nrows : rows_const;
+  const int64_t n = (int64_t)rows * width / V16<T>::N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float zv[V16<T>::N], g[V16<T>::N];
+    V16<T>::unpack(z[i], zv);
+    V16<T>::unpack(dh[i], g);
+#pragma unroll
+    for (int q = 0; q < V16<T>::N; ++q) g[q] *= V16<T>::gelu_grad(zv[q]);
+    dh[i] = V16<T>::pack(g);
+  }
+}
+
+// ---------------------------------------------------------------- combine backward
+// One wavefront per token (wave-uniform index, so the slot rows and weights
+// are scalar loads); slots in groups of KB.  For each group, a lane walks its
+// 16-byte pieces of the row: it loads g[t] and the group's kept y_perm rows,
+// adds the products into one fp32 partial dot per slot and stores w * g to
+// each kept row of d_y_perm; the partials are then added across the lanes
+// by a fixed butterfly.
+template <typename T, int KB, int U>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const uint4* __restrict__ d_out, const uint4* __restrict__ y_perm,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ topk_w,
+    uint4* __restrict__ d_y_perm, float* __restrict__ d_topk_w, int Ttok, int nvec, int K) {
+  constexpr int EV = V16<T>::N;
+  const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  if (t >= Ttok) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t* sr = slot_row + (int64_t)t * K;
+  const float* wt = topk_w + (int64_t)t * K;
+  const uint4* g_row = d_out + (int64_t)t * nvec;
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    int r[KB];
+    float w[KB], dot[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      r[j] = (k0 + j < K) ? sr[k0 + j] : -1;
+      w[j] = (r[j] >= 0) ? wt[k0 + j] : 0.f;
+      dot[j] = 0.f;
+    }
+    for (int c0 = lane; c0 < nvec; c0 += 64 * U) {
+      uint4 gv[U];
+      uint4 v[KB][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + 64 * u < nvec) gv[u] = g_row[c0 + 64 * u];
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (r[j] >= 0) {
+          const uint4* yr = y_perm + (int64_t)r[j] * nvec;
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (c0 + 64 * u < nvec) v[j][u] = yr[c0 + 64 * u];
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 64 * u;
+        if (c >= nvec) break;
+        float g[EV];
+        V16<T>::unpack(gv[u], g);
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+          if (r[j] >= 0) {
+            float y[EV], o[EV];
+            V16<T>::unpack(v[j][u], y);
+#pragma unroll
+            for (int q = 0; q < EV; ++q) {
+              dot[j] = fmaf(g[q], y[q], dot[j]);
+              o[q] = w[j] * g[q];
+            }
+            d_y_perm[(int64_t)r[j] * nvec + c] = V16<T>::pack(o);
+          }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) dot[j] += __shfl_xor(dot[j], off, 64);
+      if (lane == 0 && k0 + j < K) d_topk_w[(int64_t)t * K + k0 + j] = r[j] >= 0 ? dot[j] : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- unpermute
+// d_x[t] = (sum over kept slots, in slot order, of d_x_perm[row]) + d_x_shared[t]
+// + d_x_router[t]; fp32 sums, one rounding.  Layout as the combine kernel.
+template <typename T, int KB, int U>
+__global__ __launch_bounds__(256) void unpermute_kernel(
+    const uint4* __restrict__ d_x_perm, const int32_t* __restrict__ slot_row,
+    const uint4* __restrict__ d_x_shared, const float4* __restrict__ d_x_router,
+    uint4* __restrict__ d_x, int Ttok, int nvec, int K) {
+  constexpr int EV = V16<T>::N;
+  const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  if (t >= Ttok) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t* sr = slot_row + (int64_t)t * K;
+  for (int c0 = lane; c0 < nvec; c0 += 64 * U) {
+    float acc[U][EV];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < EV; ++i) acc[u][i] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += KB) {
+      int r[KB];
+#pragma unroll
+      for (int j = 0; j < KB; ++j) r[j] = (k0 + j < K) ? sr[k0 + j] : -1;
+      uint4 v[KB][U];
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (r[j] >= 0) {
+          const uint4* src = d_x_perm + (int64_t)r[j] * nvec;
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (c0 + 64 * u < nvec) v[j][u] = src[c0 + 64 * u];
+        }
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (r[j] >= 0) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            float y[EV];
+            V16<T>::unpack(v[j][u], y);
+#pragma unroll
+            for (int i = 0; i < EV; ++i) acc[u][i] += y[i];
+          }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= nvec) break;
+      if (d_x_shared) {
+        float y[EV];
+        V16<T>::unpack(d_x_shared[(int64_t)t * nvec + c], y);
+#pragma unroll
+        for (int i = 0; i < EV; ++i) acc[u][i] += y[i];
+      }
+      if (d_x_router) {
+        // the EV fp32 values of this piece: EV / 4 float4 at element c * EV
+        const float4* rr = d_x_router + ((int64_t)t * nvec + c) * (EV / 4);
+#pragma unroll
+        for (int i = 0; i < EV / 4; ++i) {
+          const float4 q = rr[i];
+          acc[u][4 * i] += q.x;
+          acc[u][4 * i + 1] += q.y;
+          acc[u][4 * i + 2] += q.z;
+          acc[u][4 * i + 3] += q.w;
+        }
+      }
+      d_x[(int64_t)t * nvec + c] = V16<T>::pack(acc[u]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- transposes
+// 64 x 64 tiles through LDS: 16-byte loads of tile rows, 16-byte stores of
+// transposed rows (each gathers VEC elements down a column of the tile).
+constexpr int TD = 64;
+
+template <typename T>
+struct TileT {
+  static constexpr int VEC = 16 / (int)sizeof(T);
+  static constexpr int CPR = TD / VEC;               // 16-byte pieces per tile row
+  static constexpr int LD = TD + VEC;                // padded LDS row (16-byte aligned)
+};
+
+// out[b][c][r] = in[b][r][c] for a batch of R x C matrices; grid (C/64, R/64, B).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_batched_kernel(const T* __restrict__ in,
+                                                                T* __restrict__ out, int R,
+                                                                int C) {
+  using TT = TileT<T>;
+  __shared__ __attribute__((aligned(16))) T tile[TD * TT::LD];
+  const int c0 = blockIdx.x * TD, r0 = blockIdx.y * TD;
+  const T* src = in + (int64_t)blockIdx.z * R * C;
+  T* dst = out + (int64_t)blockIdx.z * R * C;
+  for (int i = threadIdx.x; i < TD * TT::CPR; i += 256) {
+    const int r = i / TT::CPR, cc = (i % TT::CPR) * TT::VEC;
+    *reinterpret_cast<uint4*>(tile + r * TT::LD + cc) =
+        *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * C + c0 + cc);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TD * TT::CPR; i += 256) {
+    const int oc = i / TT::CPR, rr = (i % TT::CPR) * TT::VEC;
+    alignas(16) T v[TT::VEC];
+#pragma unroll
+    for (int q = 0; q < TT::VEC; ++q) v[q] = tile[(rr + q) * TT::LD + oc];
+    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + oc) * R + r0 + rr) =
+        *reinterpret_cast<const uint4*>(v);
+  }
+}
+
+// Expert e's rows [off[e], off[e+1]) of in [*, C] become columns
+// [kseg[e], kseg[e+1]) of out [C, ldo]: out[c][kseg[e] + j] = in[off[e] + j][c]
+// for j < R_e and 0 in the padding up to kseg[e+1]; colsum[e][c] (if not null)
+// = sum over the expert's rows of in[.][c] (fp32, fixed order, stored as T).
+// grid (C/64, number of segments); a workgroup walks its segment 64 rows at a
+// time.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_segments_kernel(
+    const T* __restrict__ in, const int32_t* __restrict__ off, const int32_t* __restrict__ kseg,
+    int C, int ldo, T* __restrict__ out, T* __restrict__ colsum) {
+  using TT = TileT<T>;
+  constexpr int PER = TD * TT::CPR / 256;            // read-phase items per thread
+  __shared__ __attribute__((aligned(16))) T tile[TD * TT::LD];
+  const int e = blockIdx.y, c0 = blockIdx.x * TD;
+  const int row0 = off[e], R = off[e + 1] - row0;
+  const int k0 = kseg[e], KP = kseg[e + 1] - k0;
+  float part[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) part[p] = 0.f;
+  for (int j0 = 0; j0 < KP; j0 += TD) {
+    for (int i = threadIdx.x; i < TD * TT::CPR; i += 256) {
+      const int r = i / TT::CPR, cc = (i % TT::CPR) * TT::VEC;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j0 + r < R) v = *reinterpret_cast<const uint4*>(in + (int64_t)(row0 + j0 + r) * C + c0 + cc);
+      *reinterpret_cast<uint4*>(tile + r * TT::LD + cc) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int i = threadIdx.x + 256 * p;
+      const int oc = i / TT::CPR, rr = (i % TT::CPR) * TT::VEC;
+      alignas(16) T v[TT::VEC];
+#pragma unroll
+      for (int q = 0; q < TT::VEC; ++q) {
+        v[q] = tile[(rr + q) * TT::LD + oc];
+        part[p] += Elem<T>::load(v, q);
+      }
+      if (j0 + rr < KP)
+        *reinterpret_cast<uint4*>(out + (int64_t)(c0 + oc) * ldo + k0 + j0 + rr) =
+            *reinterpret_cast<const uint4*>(v);
+    }
+    __syncthreads();
+  }
+  if (colsum) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      // the CPR threads of one column are consecutive lanes
+#pragma unroll
+      for (int o = 1; o < TT::CPR; o <<= 1) part[p] += __shfl_xor(part[p], o, 64);
+      const int i = threadIdx.x + 256 * p;
+      if (i % TT::CPR == 0) Elem<T>::store(colsum, (int64_t)e * C + c0 + i / TT::CPR, part[p]);
+    }
+  }
+}
+
+// kseg[e] = sum over e' < e of round_up(off[e'+1] - off[e'], 32), e = 0..N;
+// wa[e] = e * ra, wb[e] = e * rb.  One workgroup of 256 threads (N <= 256).
+__global__ __launch_bounds__(256) void seg_offsets_kernel(const int32_t* __restrict__ off, int N,
+                                                          int ra, int rb,
+                                                          int32_t* __restrict__ kseg,
+                                                          int32_t* __restrict__ wa,
+                                                          int32_t* __restrict__ wb) {
+  __shared__ int wsum[4];
+  const int e = threadIdx.x;
+  const int n = e < N ? ((off[e + 1] - off[e] + 31) / 32) * 32 : 0;
+  const int lane = e & 63, wave = e >> 6;
+  int v = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  if (e < N) {
+    kseg[e] = base + v - n;
+    wa[e] = e * ra;
+    wb[e] = e * rb;
+  }
+  if (e == N - 1) {
+    kseg[N] = base + v;
+    wa[N] = N * ra;
+    wb[N] = N * rb;
+  }
+}
+
+// One dense segment of T rows: off = {0, T}, kseg = {0, round_up(T, 32)},
+// wa = {0, ra}, wb = {0, rb}.
+__global__ void dense_offsets_kernel(int T, int ra, int rb, int32_t* __restrict__ off,
+                                     int32_t* __restrict__ kseg, int32_t* __restrict__ wa,
+                                     int32_t* __restrict__ wb) {
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    off[1] = T;
+    kseg[0] = 0;
+    kseg[1] = ((T + 31) / 32) * 32;
+    wa[0] = 0;
+    wa[1] = ra;
+    wb[0] = 0;
+    wb[1] = rb;
+  }
+}
+
+// ---------------------------------------------------------------- router backward
+// d_l for one token per wavefront; lane = expert (e, e + 64, e + 128, e + 192).
+// The softmax over all N (for the aux loss and the z-loss) in fp32.
+__global__ __launch_bounds__(256) void route_bwd_logits_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ w, const float* __restrict__ dw,
+    const int32_t* __restrict__ counts, int Ttok, int N, int K, float aux_coef, float z_coef,
+    float* __restrict__ dl) {
+  const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  if (t >= Ttok) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t* it = idx + (int64_t)t * K;
+  const float* wtt = w + (int64_t)t * K;
+  const float* dwt = dw + (int64_t)t * K;
+  float s = 0.f;
+  for (int k = lane; k < K; k += 64) s = fmaf(wtt[k], dwt[k], s);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  float l[4], p[4];
+  float lse = 0.f, fp = 0.f;
+  const bool smx = aux_coef != 0.f || z_coef != 0.f;
+  if (smx) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = lane + 64 * v;
+      l[v] = e < N ? logits[(int64_t)t * N + e] : -INFINITY;
+      m = fmaxf(m, l[v]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    float S = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[v] = (lane + 64 * v < N) ? expf(l[v] - m) : 0.f;
+      S += p[v];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o, 64);
+    const float inv = 1.0f / S;
+    lse = m + logf(S);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      p[v] *= inv;
+      const int e = lane + 64 * v;
+      if (aux_coef != 0.f && e < N) fp = fmaf((float)counts[e] / (float)Ttok, p[v], fp);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) fp += __shfl_xor(fp, o, 64);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int e = lane + 64 * v;
+    if (e >= N) continue;
+    float g = 0.f;
+    for (int k = 0; k < K; ++k)
+      if (it[k] == e) g = wtt[k] * (dwt[k] - s);
+    if (aux_coef != 0.f) g = fmaf(aux_coef * p[v], (float)counts[e] / (float)Ttok - fp, g);
+    if (z_coef != 0.f) g = fmaf(z_coef * lse, p[v], g);
+    dl[(int64_t)t * N + e] = g;
+  }
+}
+
+// Partial router weight gradient over a slice of tokens:
+// part[s][e][j] = sum_{t in slice s} d_l[t][e] * x[t][j].  Workgroup: 32 experts
+// (8 groups of 4) x 256 columns (32 groups of 8); grid (ceil(d/256), ceil(N/32), S).
+template <typename T>
+__global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl,
+                                                        const T* __restrict__ x, int Ttok, int N,
+                                                        int d, int tslice,
+                                                        float* __restrict__ part) {
+  __shared__ float sdl[64][33];
+  const int cg = threadIdx.x & 31, eg = threadIdx.x >> 5;
+  const int j0 = blockIdx.x * 256 + cg * 8;
+  const int eb = blockIdx.y * 32;
+  const int tlo = blockIdx.z * tslice, thi = min(Ttok, tlo + tslice);
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
+  for (int tb = tlo; tb < thi; tb += 64) {
+    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+      const int tt = i / 32, ee = i % 32;
+      sdl[tt][ee] = (tb + tt < thi && eb + ee < N) ? dl[(int64_t)(tb + tt) * N + eb + ee] : 0.f;
+    }
+    __syncthreads();
+    const int nt = min(64, thi - tb);
+    if (j0 < d) {
+      for (int tt = 0; tt < nt; ++tt) {
+        float xv[8];
+        if constexpr (sizeof(T) == 2) {
+          V16<uint16_t>::unpack(*reinterpret_cast<const uint4*>(x + (int64_t)(tb + tt) * d + j0), xv);
+        } else {
+          V16<float>::unpack(*reinterpret_cast<const uint4*>(x + (int64_t)(tb + tt) * d + j0), xv);
+          V16<float>::unpack(*reinterpret_cast<const uint4*>(x + (int64_t)(tb + tt) * d + j0 + 4), xv + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = sdl[tt][eg * 4 + i];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, xv[q], acc[i][q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (j0 >= d) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = eb + eg * 4 + i;
+    if (e >= N) continue;
+    float* o = part + ((int64_t)blockIdx.z * N + e) * d + j0;
+    *reinterpret_cast<float4*>(o) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+  }
+}
+
+// d_W_r[e][j] = sum over slices, in slice order, of part[s][e][j].
+__global__ __launch_bounds__(256) void router_dw_reduce_kernel(const float* __restrict__ part,
+                                                               int S, int64_t n,
+                                                               float* __restrict__ dwr) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float a = 0.f;
+    for (int s = 0; s < S; ++s) a += part[(int64_t)s * n + i];
+    dwr[i] = a;
+  }
+}
+
+// d_b_r[e] = sum_t d_l[t][e]: one wavefront per expert, lanes stride over the
+// tokens, then a fixed butterfly.
+__global__ __launch_bounds__(64) void router_db_kernel(const float* __restrict__ dl, int Ttok,
+                                                       int N, float* __restrict__ dbr) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  float a = 0.f;
+  for (int t = lane; t < Ttok; t += 64) a += dl[(int64_t)t * N + e];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o, 64);
+  if (lane == 0) dbr[e] = a;
+}
+
+// d_x_router[t][j] = sum_e d_l[t][e] * W_r[e][j] (fp32).  Workgroup: 32 tokens
+// (8 groups of 4) x 256 columns (32 groups of 8); experts staged 64 at a time.
+template <typename T>
+__global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dl,
+                                                        const T* __restrict__ wr, int Ttok, int N,
+                                                        int d, float* __restrict__ dxr) {
+  __shared__ float sdl[32][65];
+  const int cg = threadIdx.x & 31, tg = threadIdx.x >> 5;
+  const int j0 = blockIdx.x * 256 + cg * 8;
+  const int tb = blockIdx.y * 32;
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
+  for (int e0 = 0; e0 < N; e0 += 64) {
+    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+      const int tt = i / 64, ee = i % 64;
+      sdl[tt][ee] = (tb + tt < Ttok && e0 + ee < N) ? dl[(int64_t)(tb + tt) * N + e0 + ee] : 0.f;
+    }
+    __syncthreads();
+    const int ne = min(64, N - e0);
+    if (j0 < d) {
+      for (int ee = 0; ee < ne; ++ee) {
+        float wv[8];
+        const T* wrow = wr + (int64_t)(e0 + ee) * d + j0;
+        if constexpr (sizeof(T) == 2) {
+          V16<uint16_t>::unpack(*reinterpret_cast<const uint4*>(wrow), wv);
+        } else {
+          V16<float>::unpack(*reinterpret_cast<const uint4*>(wrow), wv);
+          V16<float>::unpack(*reinterpret_cast<const uint4*>(wrow + 4), wv + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = sdl[tg * 4 + i][ee];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, wv[q], acc[i][q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (j0 >= d) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tb + tg * 4 + i;
+    if (t >= Ttok) continue;
+    float* o = dxr + (int64_t)t * d + j0;
+    *reinterpret_cast<float4*>(o) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+  }
+}
+
+inline unsigned ew_blocks(int64_t rows, int width, int vec) {
+  const int64_t n = rows * width / vec;
+  const int64_t b = (n + 255) / 256;
+  return (unsigned)(b < 1 ? 1 : (b > 65536 ? 65536 : b));
+}
+
+}  // namespace
+
+hipError_t launch_gelu_fwd(int dtype, const void* z, void* h, const int32_t* nrows, int rows_max,
+                           int width, hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(gelu_fwd_kernel<float>, dim3(ew_blocks(rows_max, width, 4)), dim3(256), 0,
+                       s, static_cast<const uint4*>(z), static_cast<uint4*>(h), nrows, rows_max,
+                       width);
+  else
+    hipLaunchKernelGGL(gelu_fwd_kernel<uint16_t>, dim3(ew_blocks(rows_max, width, 8)), dim3(256),
+                       0, s, static_cast<const uint4*>(z), static_cast<uint4*>(h), nrows,
+                       rows_max, width);
+  return hipGetLastError();
+}
+
+hipError_t launch_gelu_bwd(int dtype, const void* z, void* dh, const int32_t* nrows, int rows_max,
+                           int width, hipStream_t s) {
+  if (dtype == 0)
+    hipLaunchKernelGGL(gelu_bwd_kernel<float>, dim3(ew_blocks(rows_max, width, 4)), dim3(256), 0,
+                       s, static_cast<const uint4*>(z), static_cast<uint4*>(dh), nrows, rows_max,
+                       width);
+  else
+    hipLaunchKernelGGL(gelu_bwd_kernel<uint16_t>, dim3(ew_blocks(rows_max, width, 8)), dim3(256),
+                       0, s, static_cast<const uint4*>(z), static_cast<uint4*>(dh), nrows,
+                       rows_max, width);
+  return hipGetLastError();
+}
+
+template <typename T>
+static void combine_bwd_t(const void* d_out, const void* y_perm, const int32_t* slot_row,
+                          const float* topk_w, void* d_y_perm, float* d_topk_w, int Ttok,
+                          int nvec, int K, hipStream_t s) {
+  const dim3 grid((Ttok + 3) / 4), block(256);
+  const uint4* g = static_cast<const uint4*>(d_out);
+  const uint4* y = static_cast<const uint4*>(y_perm);
+  uint4* dy = static_cast<uint4*>(d_y_perm);
+  if (K <= 2)
+    hipLaunchKernelGGL((combine_bwd_kernel<T, 2, 2>), grid, block, 0, s, g, y, slot_row, topk_w,
+                       dy, d_topk_w, Ttok, nvec, K);
+  else
+    hipLaunchKernelGGL((combine_bwd_kernel<T, 8, 1>), grid, block, 0, s, g, y, slot_row, topk_w,
+                       dy, d_topk_w, Ttok, nvec, K);
+}
+
+hipError_t launch_combine_bwd(int dtype, const void* d_out, const void* y_perm,
+                              const int32_t* slot_row, const float* topk_w, void* d_y_perm,
+                              float* d_topk_w, int T, int d, int K, hipStream_t s) {
+  const int nvec = d * (dtype == 0 ? 4 : 2) / 16;
+  if (dtype == 0)
+    combine_bwd_t<float>(d_out, y_perm, slot_row, topk_w, d_y_perm, d_topk_w, T, nvec, K, s);
+  else
+    combine_bwd_t<uint16_t>(d_out, y_perm, slot_row, topk_w, d_y_perm, d_topk_w, T, nvec, K, s);
+  return hipGetLastError();
+}
+
+template <typename T>
+static void unpermute_t(const void* d_x_perm, const int32_t* slot_row, const void* d_x_shared,
+                        const float* d_x_router, void* d_x, int Ttok, int nvec, int K,
+                        hipStream_t s) {
+  const dim3 grid((Ttok + 3) / 4), block(256);
+  const uint4* a = static_cast<const uint4*>(d_x_perm);
+  const uint4* sh = static_cast<const uint4*>(d_x_shared);
+  const float4* rt = reinterpret_cast<const float4*>(d_x_router);
+  uint4* o = static_cast<uint4*>(d_x);
+  if (K <= 2)
+    hipLaunchKernelGGL((unpermute_kernel<T, 2, 4>), grid, block, 0, s, a, slot_row, sh, rt, o,
+                       Ttok, nvec, K);
+  else
+    hipLaunchKernelGGL((unpermute_kernel<T, 8, 2>), grid, block, 0, s, a, slot_row, sh, rt, o,
+                       Ttok, nvec, K);
+}
+
+hipError_t launch_unpermute(int dtype, const void* d_x_perm, const int32_t* slot_row,
+                            const void* d_x_shared, const float* d_x_router, void* d_x, int T,
+                            int d, int K, hipStream_t s) {
+  const int nvec = d * (dtype == 0 ? 4 : 2) / 16;
+  if (dtype == 0)
+    unpermute_t<float>(d_x_perm, slot_row, d_x_shared, d_x_router, d_x, T, nvec, K, s);
+  else
+    unpermute_t<uint16_t>(d_x_perm, slot_row, d_x_shared, d_x_router, d_x, T, nvec, K, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_batched(int dtype, const void* in, void* out, int B, int R, int C,
+                                    hipStream_t s) {
+  const dim3 grid(C / TD, R / TD, B);
+  if (dtype == 0)
+    hipLaunchKernelGGL(transpose_batched_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(in), static_cast<float*>(out), R, C);
+  else
+    hipLaunchKernelGGL(transpose_batched_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_segments(int dtype, const void* in, const int32_t* off,
+                                     const int32_t* kseg, int nseg, int C, int ldo, void* out,
+                                     void* colsum, hipStream_t s) {
+  const dim3 grid(C / TD, nseg);
+  if (dtype == 0)
+    hipLaunchKernelGGL(transpose_segments_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(in), off, kseg, C, ldo, static_cast<float*>(out),
+                       static_cast<float*>(colsum));
+  else
+    hipLaunchKernelGGL(transpose_segments_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(in), off, kseg, C, ldo,
+                       static_cast<uint16_t*>(out), static_cast<uint16_t*>(colsum));
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_offsets(const int32_t* off, int N, int ra, int rb, int32_t* kseg,
+                              int32_t* wa, int32_t* wb, hipStream_t s) {
+  hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(256), 0, s, off, N, ra, rb, kseg, wa, wb);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_offsets(int T, int ra, int rb, int32_t* off, int32_t* kseg, int32_t* wa,
+                                int32_t* wb, hipStream_t s) {
+  hipLaunchKernelGGL(dense_offsets_kernel, dim3(1), dim3(64), 0, s, T, ra, rb, off, kseg, wa, wb);
+  return hipGetLastError();
+}
+
+int router_dw_slices(int T, int N, int d) {
+  const int base = ((d + 255) / 256) * ((N + 31) / 32);
+  int S = (512 + base - 1) / base;
+  const int maxS = (T + 63) / 64;
+  if (S > maxS) S = maxS;
+  return S < 1 ? 1 : S;
+}
+
+hipError_t launch_route_bwd(int dtype, const void* x, const void* w_router, const float* logits,
+                            const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
+                            const int32_t* counts, float aux_coef, float z_coef, float* dl,
+                            float* part, float* d_w_router, float* d_b_router, float* d_x_router,
+                            int T, int d, int N, int K, hipStream_t s) {
+  hipLaunchKernelGGL(route_bwd_logits_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits,
+                     topk_idx, topk_w, d_topk_w, counts, T, N, K, aux_coef, z_coef, dl);
+  const int S = router_dw_slices(T, N, d);
+  const int tslice = (((T + S - 1) / S) + 63) / 64 * 64;
+  const dim3 g1((d + 255) / 256, (N + 31) / 32, S);
+  if (dtype == 0)
+    hipLaunchKernelGGL(router_dw_kernel<float>, g1, dim3(256), 0, s, dl,
+                       static_cast<const float*>(x), T, N, d, tslice, part);
+  else
+    hipLaunchKernelGGL(router_dw_kernel<uint16_t>, g1, dim3(256), 0, s, dl,
+                       static_cast<const uint16_t*>(x), T, N, d, tslice, part);
+  const int64_t n = (int64_t)N * d;
+  hipLaunchKernelGGL(router_dw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     part, S, n, d_w_router);
+  if (d_b_router)
+    hipLaunchKernelGGL(router_db_kernel, dim3(N), dim3(64), 0, s, dl, T, N, d_b_router);
+  if (d_x_router) {
+    const dim3 g2((d + 255) / 256, (T + 31) / 32);
+    if (dtype == 0)
+      hipLaunchKernelGGL(router_dx_kernel<float>, g2, dim3(256), 0, s, dl,
+                         static_cast<const float*>(w_router), T, N, d, d_x_router);
+    else
+      hipLaunchKernelGGL(router_dx_kernel<uint16_t>, g2, dim3(256), 0, s, dl,
+                         static_cast<const uint16_t*>(w_router), T, N, d, d_x_router);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

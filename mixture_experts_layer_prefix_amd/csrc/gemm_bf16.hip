@@ -116,7 +116,10 @@ constexpr int W4_CST = BN + 8;                // staged output row stride in bf1
 // codes travel to LDS as bytes (half the bytes of bf16), each fragment is
 // widened to bf16 in registers (exact: |q| <= 127) just before its MFMAs,
 // and the epilogue multiplies by the row scale before the bias.
-template <bool GELU, bool QW, int NS, int LAY>
+// WG: weight-gradient (k-segment) mode -- expert e's tile contracts over
+// columns [kseg[e], kseg[e+1]) of A [wg_rows, Kd] and W [Nd, Kd], both shared
+// by all experts; an empty segment leaves the accumulators at zero.
+template <bool GELU, bool QW, int NS, int LAY, bool WG>
 __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
   using Lay = W4Layout<LAY>;
@@ -133,7 +136,16 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   const uint16_t* bias = nullptr;
   const float* wsc = nullptr;
   uint16_t* C;
-  if (tr.shared) {
+  int arow0 = tr.row0;          // A row of the tile's first row
+  int kbeg = 0, KT = Kd / BK;   // contraction columns [kbeg, kbeg + KT * BK)
+  if constexpr (WG) {
+    A = static_cast<const uint16_t*>(a.A);
+    W = static_cast<const char*>(a.W);
+    C = static_cast<uint16_t*>(a.C);
+    kbeg = a.kseg[tr.e];
+    KT = (a.kseg[tr.e + 1] - kbeg) / BK;
+    arow0 = tr.row0 - tr.e * a.wg_rows;
+  } else if (tr.shared) {
     A = static_cast<const uint16_t*>(a.As);
     W = static_cast<const char*>(a.Ws);
     C = static_cast<uint16_t*>(a.Cs);
@@ -159,7 +171,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   for (int i = 0; i < NLA; ++i) {
     const int row = (wave * NLA + i) * RPI + r_in;
     const int lchunk = (lane % CH) ^ swz(row);
-    offA[i] = (uint32_t)(tr.row0 + min(row, rows - 1)) * (uint32_t)Kd + lchunk * 8;
+    offA[i] = (uint32_t)(arow0 + min(row, rows - 1)) * (uint32_t)Kd + lchunk * 8 + kbeg;
   }
   // (byte offsets of the W rows)
 #pragma unroll
@@ -171,7 +183,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     } else {
       const int row = (wave * NLB + i) * RPI + r_in;
       const int lchunk = (lane % CH) ^ swz(row);
-      offB[i] = ((uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8) * 2;
+      offB[i] = ((uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8 + kbeg) * 2;
     }
   }
   auto issue_a = [&](int buf, int k0) {
@@ -263,7 +275,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     static_assert(ND <= NM && NV <= ND, "every read and load sits between two MFMAs");
   };
 
-  const int KT = Kd / BK;
+  if (!WG || KT > 0) {
   // Prologue: stages 0 .. NS-2 in flight (chunks past the end re-read the
   // last chunk into buffers nobody reads again, so every k-step issues the
   // same number of loads and the wait counts are constants).
@@ -303,6 +315,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   }
   // no direct-to-LDS load may still be in flight past this point
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  }
 
   // Epilogue.  The 32x32 accumulator of (ni, mi) holds C^T: element v of lane l
   // is output row mi*32 + l%32, column ni*32 + (v/4)*8 + (l/32)*4 + v%4.
@@ -395,7 +408,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   }
 }
 
-template <bool GELU, bool QW, int NS>
+template <bool GELU, bool QW, int NS, bool WG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(GemmArgs a) {
   // the output tile is staged through the same LDS after the main loop
@@ -412,13 +425,13 @@ gemm_bf16_w4_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   const int rows = tr.row_end - tr.row0;
   if (rows > W4_TM)
-    w4_tile<GELU, QW, NS, 3>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 3, WG>(a, tr, lds, acc);
   else if (rows > 128)
-    w4_tile<GELU, QW, NS, 0>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 0, WG>(a, tr, lds, acc);
   else if (rows > 64)
-    w4_tile<GELU, QW, NS, 1>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 1, WG>(a, tr, lds, acc);
   else
-    w4_tile<GELU, QW, NS, 2>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 2, WG>(a, tr, lds, acc);
 }
 
 }  // namespace
@@ -430,16 +443,23 @@ int gemm_bf16_merge_rows() { return W4_MERGE; }
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
   const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
-  if (a.wscale) {
+  if (a.kseg) {
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, true>), dim3(grid), dim3(256), 0,
+                       s, a);
+  } else if (a.wscale) {
     if (gelu)
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, true, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, true, W4_NS, false>), dim3(grid), dim3(256), 0,
+                         s, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, true, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, true, W4_NS, false>), dim3(grid), dim3(256),
+                         0, s, a);
   } else {
     if (gelu)
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, false, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, false, W4_NS, false>), dim3(grid), dim3(256),
+                         0, s, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, false>), dim3(grid), dim3(256),
+                         0, s, a);
   }
   return hipGetLastError();
 }

@@ -4,7 +4,8 @@
 // per expert, yunthe.com "MoE混合专家模型实战" reference forward), in fp32
 // throughout.  64 x 64 workgroup tiles, BK = 16 staged in LDS k-major, each
 // of the 256 threads owning a 4 x 4 block of outputs.  Used for fp32 layers,
-// which are small; the products accumulate in k order with fma.
+// which are small; the products accumulate in k order with fma.  With
+// GemmArgs::kseg set it runs the weight-gradient (k-segment) form.
 #include "gemm_common.h"
 
 namespace moe {
@@ -24,7 +25,15 @@ __global__ __launch_bounds__(NTHR) void gemm_f32_kernel(GemmArgs a) {
   const float* W;
   const float* bias = nullptr;
   float* C;
-  if (tr.shared) {
+  int arow0 = tr.row0, kbeg = 0, kend = Kd;
+  if (a.kseg) {   // weight-gradient (k-segment) mode
+    A = static_cast<const float*>(a.A);
+    W = static_cast<const float*>(a.W);
+    C = static_cast<float*>(a.C);
+    kbeg = a.kseg[tr.e];
+    kend = a.kseg[tr.e + 1];
+    arow0 = tr.row0 - tr.e * a.wg_rows;
+  } else if (tr.shared) {
     A = static_cast<const float*>(a.As);
     W = static_cast<const float*>(a.Ws);
     C = static_cast<float*>(a.Cs);
@@ -39,10 +48,10 @@ __global__ __launch_bounds__(NTHR) void gemm_f32_kernel(GemmArgs a) {
   const int tx = tid % 16, ty = tid / 16;
 
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < Kd; k0 += BK) {
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
     for (int i = tid; i < BM * BK; i += NTHR) {
       const int r = i / BK, k = i % BK;
-      As[k][r] = (r < rows) ? A[(int64_t)(tr.row0 + r) * Kd + k0 + k] : 0.f;
+      As[k][r] = (r < rows) ? A[(int64_t)(arow0 + r) * Kd + k0 + k] : 0.f;
       const int n = tr.n0 + r;
       Bs[k][r] = (n < Nd) ? W[(int64_t)n * Kd + k0 + k] : 0.f;
     }

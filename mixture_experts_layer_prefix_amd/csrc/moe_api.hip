@@ -138,7 +138,7 @@ void carve_dispatch(Carver& cv, const moe_config_t* c, DispatchWs* w) {
   w->blkoff = cv.take<int32_t>(n);
 }
 
-void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w) {
+void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w, bool hidden = true) {
   const int64_t mmax = (int64_t)c->T * c->top_k;
   const size_t eb = elem_bytes(c->dtype);
   const int N = c->n_experts, bm = gemm_bm(c), bn = gemm_bn(c);
@@ -151,8 +151,9 @@ void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w) {
   for (int i = 0; i < 4; ++i)
     w->list[i] = cv.take<int4>((size_t)(w->bound[i] > 0 ? w->bound[i] : 1) * sizeof(int4));
   w->count = cv.take<int32_t>(4 * sizeof(int32_t));
-  w->h = cv.take<void>((size_t)mmax * c->d_ff * eb);
-  w->h_shared = c->d_ff_shared ? cv.take<void>((size_t)c->T * c->d_ff_shared * eb) : nullptr;
+  w->h = hidden ? cv.take<void>((size_t)mmax * c->d_ff * eb) : nullptr;
+  w->h_shared =
+      (hidden && c->d_ff_shared) ? cv.take<void>((size_t)c->T * c->d_ff_shared * eb) : nullptr;
 }
 
 void carve_aux(Carver& cv, const moe_config_t* c, AuxWs* w) {
@@ -183,6 +184,116 @@ void carve_layer(Carver& cv, const moe_config_t* c, LayerWs* w) {
   carve_aux(cv, c, &w->aux);
 }
 
+// ---------------------------------------------------------------- training workspaces
+// Backward GEMMs never take the decode-shaped kernel (it has no k-segment mode).
+bool bwd_f32(const moe_config_t* c) { return c->dtype == MOE_F32; }
+int bwd_bm(const moe_config_t* c) { return bwd_f32(c) ? moe::gemm_f32_bm() : moe::gemm_bf16_bm(); }
+int bwd_bn(const moe_config_t* c) { return bwd_f32(c) ? moe::gemm_f32_bn() : moe::gemm_bf16_bn(); }
+int bwd_merge(const moe_config_t* c) { return bwd_f32(c) ? 0 : moe::gemm_bf16_merge_rows(); }
+// Row stride of the per-expert transposed activations: every expert's rows
+// rounded up to 32 (at most T*K + 31 N in all), or the T rows of the shared
+// expert, rounded up to 64.
+int64_t bwd_ldt(const moe_config_t* c) {
+  const int64_t a = (int64_t)c->T * c->top_k + 32LL * c->n_experts, b = (int64_t)c->T + 32;
+  return ((a > b ? a : b) + 63) / 64 * 64;
+}
+int64_t bwd_maxw(const moe_config_t* c) {
+  int64_t m = c->d_model > c->d_ff ? c->d_model : c->d_ff;
+  return m > c->d_ff_shared ? m : c->d_ff_shared;
+}
+
+struct FfnBwdWs {
+  void *w1t, *w2t, *ws1t, *ws2t;   // transposed weights
+  void *dh, *dhs;                  // d_h, then d_z in place
+  void *tb1, *tb2;                 // transposed activations [maxw, ldt]
+  int32_t *kseg, *wr_d, *wr_f;     // routed k-segments and output-row offsets
+  int32_t *off2, *kseg2, *wr2_d, *wr2_s;   // the shared expert's single segment
+  int4* list[8];                   // dgrad1, dgrad2, wgrad2, wgrad1; the same for the shared expert
+  int64_t bound[8];
+  int32_t* count;
+};
+struct RouteBwdWs {
+  float* dl;                       // d_logits [T, N]
+  float* part;                     // router weight-gradient partials
+};
+struct LayerTrainWs {
+  RouteWs route;
+  DispatchWs disp;
+  FfnWs ffn;                       // tile lists only
+  void* y_shared;
+  AuxWs aux;
+};
+struct LayerBwdWs {
+  void* d_y_perm;
+  float* d_topk_w;
+  void* d_x_perm;
+  void* d_x_shared;
+  float* d_x_router;
+  FfnBwdWs ffn;
+  RouteBwdWs route;
+};
+
+void carve_ffn_bwd(Carver& cv, const moe_config_t* c, FfnBwdWs* w) {
+  const int64_t T = c->T, N = c->n_experts, d = c->d_model, f = c->d_ff, fs = c->d_ff_shared;
+  const int64_t M = T * c->top_k;
+  const size_t eb = elem_bytes(c->dtype);
+  w->w1t = cv.take<void>((size_t)(N * f * d) * eb);
+  w->w2t = cv.take<void>((size_t)(N * d * f) * eb);
+  w->ws1t = fs ? cv.take<void>((size_t)(fs * d) * eb) : nullptr;
+  w->ws2t = fs ? cv.take<void>((size_t)(fs * d) * eb) : nullptr;
+  w->dh = cv.take<void>((size_t)(M * f) * eb);
+  w->dhs = fs ? cv.take<void>((size_t)(T * fs) * eb) : nullptr;
+  const int64_t ldt = bwd_ldt(c), maxw = bwd_maxw(c);
+  w->tb1 = cv.take<void>((size_t)(maxw * ldt) * eb);
+  w->tb2 = cv.take<void>((size_t)(maxw * ldt) * eb);
+  w->kseg = cv.take<int32_t>((N + 1) * sizeof(int32_t));
+  w->wr_d = cv.take<int32_t>((N + 1) * sizeof(int32_t));
+  w->wr_f = cv.take<int32_t>((N + 1) * sizeof(int32_t));
+  w->off2 = cv.take<int32_t>(2 * sizeof(int32_t));
+  w->kseg2 = cv.take<int32_t>(2 * sizeof(int32_t));
+  w->wr2_d = cv.take<int32_t>(2 * sizeof(int32_t));
+  w->wr2_s = cv.take<int32_t>(2 * sizeof(int32_t));
+  const int bm = bwd_bm(c), bn = bwd_bn(c);
+  w->bound[0] = moe::max_tiles(M, (int)N, 0, bm, bn, f);
+  w->bound[1] = moe::max_tiles(M, (int)N, 0, bm, bn, d);
+  w->bound[2] = moe::max_tiles(N * d, (int)N, 0, bm, bn, f);
+  w->bound[3] = moe::max_tiles(N * f, (int)N, 0, bm, bn, d);
+  w->bound[4] = fs ? moe::max_tiles(0, 0, (int)T, bm, bn, fs) : 0;
+  w->bound[5] = fs ? moe::max_tiles(0, 0, (int)T, bm, bn, d) : 0;
+  w->bound[6] = fs ? moe::max_tiles(d, 1, 0, bm, bn, fs) : 0;
+  w->bound[7] = fs ? moe::max_tiles(fs, 1, 0, bm, bn, d) : 0;
+  for (int i = 0; i < 8; ++i)
+    w->list[i] = cv.take<int4>((size_t)(w->bound[i] > 0 ? w->bound[i] : 1) * sizeof(int4));
+  w->count = cv.take<int32_t>(8 * sizeof(int32_t));
+}
+
+void carve_route_bwd(Carver& cv, const moe_config_t* c, RouteBwdWs* w) {
+  w->dl = cv.take<float>((size_t)c->T * c->n_experts * sizeof(float));
+  w->part = cv.take<float>((size_t)moe::router_dw_slices(c->T, c->n_experts, c->d_model) *
+                           c->n_experts * c->d_model * sizeof(float));
+}
+
+void carve_layer_train(Carver& cv, const moe_config_t* c, LayerTrainWs* w) {
+  carve_route(cv, c, &w->route);
+  carve_dispatch(cv, c, &w->disp);
+  carve_ffn(cv, c, &w->ffn, false);
+  w->y_shared =
+      c->d_ff_shared ? cv.take<void>((size_t)c->T * c->d_model * elem_bytes(c->dtype)) : nullptr;
+  carve_aux(cv, c, &w->aux);
+}
+
+void carve_layer_bwd(Carver& cv, const moe_config_t* c, LayerBwdWs* w) {
+  const int64_t T = c->T, M = T * c->top_k, d = c->d_model;
+  const size_t eb = elem_bytes(c->dtype);
+  w->d_y_perm = cv.take<void>((size_t)(M * d) * eb);
+  w->d_topk_w = cv.take<float>((size_t)M * sizeof(float));
+  w->d_x_perm = cv.take<void>((size_t)(M * d) * eb);
+  w->d_x_shared = c->d_ff_shared ? cv.take<void>((size_t)(T * d) * eb) : nullptr;
+  w->d_x_router = cv.take<float>((size_t)(T * d) * sizeof(float));
+  carve_ffn_bwd(cv, c, &w->ffn);
+  carve_route_bwd(cv, c, &w->route);
+}
+
 size_t stage_bytes(const moe_config_t* c, moe_stage_t stage) {
   Carver cv{nullptr};
   switch (stage) {
@@ -211,6 +322,31 @@ size_t stage_bytes(const moe_config_t* c, moe_stage_t stage) {
     case MOE_STAGE_LAYER: {
       LayerWs w;
       carve_layer(cv, c, &w);
+      return cv.off;
+    }
+    case MOE_STAGE_EXPERT_FFN_TRAIN: {
+      FfnWs w;
+      carve_ffn(cv, c, &w, false);
+      return cv.off;
+    }
+    case MOE_STAGE_LAYER_TRAIN: {
+      LayerTrainWs w;
+      carve_layer_train(cv, c, &w);
+      return cv.off;
+    }
+    case MOE_STAGE_EXPERT_FFN_BACKWARD: {
+      FfnBwdWs w;
+      carve_ffn_bwd(cv, c, &w);
+      return cv.off;
+    }
+    case MOE_STAGE_ROUTE_BACKWARD: {
+      RouteBwdWs w;
+      carve_route_bwd(cv, c, &w);
+      return cv.off;
+    }
+    case MOE_STAGE_LAYER_BACKWARD: {
+      LayerBwdWs w;
+      carve_layer_bwd(cv, c, &w);
       return cv.off;
     }
   }
@@ -274,9 +410,13 @@ int do_dispatch(const moe_config_t* c, const int32_t* idx, const void* x, int32_
       "moe_dispatch launch");
 }
 
+// h / hs: the hidden activations GEMM2 reads.  Training mode (z != null):
+// GEMM1 writes the pre-activations z / zs without the GELU, and a GELU pass
+// writes h / hs from them, so the backward has both.
 int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
            const moe_weights_t* w, const void* x, void* y_perm, void* y_shared, const FfnWs& fw,
-           hipStream_t s) {
+           hipStream_t s, void* h, void* hs, void* z = nullptr, void* zs = nullptr) {
+  const bool train = z != nullptr;
   const GemmPath path = gemm_path(c);
   const int N = c->n_experts, T = c->T;
   const bool has_shared = c->d_ff_shared > 0;
@@ -309,7 +449,7 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
   g1.A = x_perm;
   g1.W = w->w1;
   g1.bias = w->b1;
-  g1.C = fw.h;
+  g1.C = train ? z : h;
   g1.offsets = offsets;
   g1.Kd = c->d_model;
   g1.Nd = c->d_ff;
@@ -317,7 +457,7 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
   const bool q8 = c->weight_quant == MOE_WQ_INT8;
   g1.wscale = q8 ? w->w1_scale : nullptr;
   moe::GemmArgs g2 = g1;
-  g2.A = fw.h;
+  g2.A = h;
   g2.W = w->w2;
   g2.wscale = q8 ? w->w2_scale : nullptr;
   g2.bias = w->b2;
@@ -328,12 +468,12 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
   if (has_shared) {
     s1.As = x;
     s1.Ws = w->ws1;
-    s1.Cs = fw.h_shared;
+    s1.Cs = train ? zs : hs;
     s1.Ts = T;
     s1.Kd = c->d_model;
     s1.Nd = c->d_ff_shared;
     s2 = s1;
-    s2.As = fw.h_shared;
+    s2.As = hs;
     s2.Ws = w->ws2;
     s2.Cs = y_shared;
     s2.Kd = c->d_ff_shared;
@@ -344,11 +484,21 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
     }
   }
   const int tsf = fused ? T : 0;
-  int r = gemm(g1, 0, offsets, N, tsf, true, "expert GEMM1 launch");
+  int r = gemm(g1, 0, offsets, N, tsf, !train, "expert GEMM1 launch");
   if (r != MOE_OK) return r;
   if (has_shared && !fused) {
-    r = gemm(s1, 2, nullptr, 0, T, true, "shared GEMM1 launch");
+    r = gemm(s1, 2, nullptr, 0, T, !train, "shared GEMM1 launch");
     if (r != MOE_OK) return r;
+  }
+  if (train) {
+    r = hip_status(moe::launch_gelu_fwd(c->dtype, z, h, offsets + N, T * c->top_k, c->d_ff, s),
+                   "GELU launch");
+    if (r != MOE_OK) return r;
+    if (has_shared) {
+      r = hip_status(moe::launch_gelu_fwd(c->dtype, zs, hs, nullptr, T, c->d_ff_shared, s),
+                     "shared GELU launch");
+      if (r != MOE_OK) return r;
+    }
   }
   r = gemm(g2, 1, offsets, N, tsf, false, "expert GEMM2 launch");
   if (r != MOE_OK) return r;
@@ -398,6 +548,221 @@ int check_weights(const moe_config_t* c, const moe_weights_t* w, bool router, bo
   return MOE_OK;
 }
 
+
+// ---------------------------------------------------------------- training (checked)
+// The training entry points: INT8 experts are inference-only, and the
+// transposed activations use 32-bit offsets in the GEMM kernels.
+std::string check_train(const moe_config_t* c, int* code) {
+  std::string why = check_config(c, code);
+  if (!why.empty()) return why;
+  *code = MOE_ERR_UNSUPPORTED;
+  if (c->weight_quant != MOE_WQ_NONE) return "training entry points need weight_quant MOE_WQ_NONE";
+  if (bwd_maxw(c) * bwd_ldt(c) >= (int64_t(1) << 31))
+    return "max(d_model, d_ff, d_ff_shared) * (T*K + 32N) must be < 2^31 for the backward";
+  *code = MOE_OK;
+  return "";
+}
+
+#define MOE_CHECK_TRAIN(c)                        \
+  do {                                            \
+    int code_;                                    \
+    std::string why_ = check_train((c), &code_);  \
+    if (code_ != MOE_OK) return fail(code_, why_); \
+  } while (0)
+
+// One backward GEMM: tile list, then the tiled (bf16) or fp32 kernel.
+int bwd_gemm(const moe_config_t* c, moe::GemmArgs g, int4* list, int32_t* count, int64_t bound,
+             const int32_t* offs, int Nr, int Ts, hipStream_t s, const char* what) {
+  hipError_t e = moe::launch_tile_list(offs, Nr, bwd_bm(c), bwd_bn(c), g.Nd, Ts, bwd_merge(c),
+                                       list, count, s);
+  if (e != hipSuccess) return hip_status(e, "tile list launch");
+  g.tile_list = list;
+  g.tile_count = count;
+  g.grid_tiles = bound;
+  e = bwd_f32(c) ? moe::launch_gemm_f32(g, false, s) : moe::launch_gemm_bf16(g, false, s);
+  return e == hipSuccess ? MOE_OK : hip_status(e, what);
+}
+
+int do_combine_bwd(const moe_config_t* c, const void* d_out, const void* y_perm,
+                   const int32_t* slot_row, const float* tw, void* d_y_perm, float* d_tw,
+                   hipStream_t s) {
+  return hip_status(moe::launch_combine_bwd(c->dtype, d_out, y_perm, slot_row, tw, d_y_perm, d_tw,
+                                            c->T, c->d_model, c->top_k, s),
+                    "moe_combine_backward launch");
+}
+
+// Expert FFN backward (routed experts, then the shared one):
+//   d_h = d_y . W2 (on W2^T), d_z = d_h * GELU'(z), d_x_perm = d_z . W1 (on W1^T),
+//   dW2_e = d_y_e^T h_e, db2_e = column sums of d_y_e, dW1_e = d_z_e^T x_e,
+//   db1_e = column sums of d_z_e (weight gradients in the k-segment mode).
+int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
+               const moe_weights_t* w, const void* x, const void* z, const void* h,
+               const void* zs, const void* hs, const void* d_y_perm, const void* d_out,
+               void* d_x_perm, void* d_x_shared, const moe_grads_t* g, const FfnBwdWs& fw,
+               hipStream_t s) {
+  const int dt = c->dtype, T = c->T, N = c->n_experts, d = c->d_model, f = c->d_ff;
+  const int fs = c->d_ff_shared;
+  const int M = T * c->top_k;
+  const int ldt = (int)bwd_ldt(c);
+  int r;
+#define MOE_TRY(expr, what)                           \
+  do {                                                \
+    r = hip_status((expr), what);                     \
+    if (r != MOE_OK) return r;                        \
+  } while (0)
+  MOE_TRY(moe::launch_seg_offsets(offsets, N, d, f, fw.kseg, fw.wr_d, fw.wr_f, s), "offsets launch");
+  MOE_TRY(moe::launch_transpose_batched(dt, w->w2, fw.w2t, N, d, f, s), "transpose launch");
+  MOE_TRY(moe::launch_transpose_batched(dt, w->w1, fw.w1t, N, f, d, s), "transpose launch");
+  moe::GemmArgs a{};
+  a.A = d_y_perm;                       // d_h [M, f] = d_y [M, d] . (W2^T)^T
+  a.W = fw.w2t;
+  a.C = fw.dh;
+  a.offsets = offsets;
+  a.Kd = d;
+  a.Nd = f;
+  a.E = N;
+  r = bwd_gemm(c, a, fw.list[0], fw.count + 0, fw.bound[0], offsets, N, 0, s, "dgrad GEMM launch");
+  if (r != MOE_OK) return r;
+  MOE_TRY(moe::launch_gelu_bwd(dt, z, fw.dh, offsets + N, M, f, s), "GELU backward launch");
+  a.A = fw.dh;                          // d_x_perm [M, d] = d_z [M, f] . (W1^T)^T
+  a.W = fw.w1t;
+  a.C = d_x_perm;
+  a.Kd = f;
+  a.Nd = d;
+  r = bwd_gemm(c, a, fw.list[1], fw.count + 1, fw.bound[1], offsets, N, 0, s, "dgrad GEMM launch");
+  if (r != MOE_OK) return r;
+  // dW2 [N, d, f]: A = d_y^T [d, ldt], W = h^T [f, ldt]
+  MOE_TRY(moe::launch_transpose_segments(dt, d_y_perm, offsets, fw.kseg, N, d, ldt, fw.tb1, g->d_b2, s),
+          "transpose launch");
+  MOE_TRY(moe::launch_transpose_segments(dt, h, offsets, fw.kseg, N, f, ldt, fw.tb2, nullptr, s),
+          "transpose launch");
+  moe::GemmArgs wg{};
+  wg.A = fw.tb1;
+  wg.W = fw.tb2;
+  wg.C = g->d_w2;
+  wg.Kd = ldt;
+  wg.Nd = f;
+  wg.E = N;
+  wg.kseg = fw.kseg;
+  wg.wg_rows = d;
+  r = bwd_gemm(c, wg, fw.list[2], fw.count + 2, fw.bound[2], fw.wr_d, N, 0, s, "wgrad GEMM launch");
+  if (r != MOE_OK) return r;
+  // dW1 [N, f, d]: A = d_z^T [f, ldt], W = x_perm^T [d, ldt]
+  MOE_TRY(moe::launch_transpose_segments(dt, fw.dh, offsets, fw.kseg, N, f, ldt, fw.tb1, g->d_b1, s),
+          "transpose launch");
+  MOE_TRY(moe::launch_transpose_segments(dt, x_perm, offsets, fw.kseg, N, d, ldt, fw.tb2, nullptr, s),
+          "transpose launch");
+  wg.C = g->d_w1;
+  wg.Nd = d;
+  wg.wg_rows = f;
+  r = bwd_gemm(c, wg, fw.list[3], fw.count + 3, fw.bound[3], fw.wr_f, N, 0, s, "wgrad GEMM launch");
+  if (r != MOE_OK) return r;
+  if (!fs) return MOE_OK;
+
+  // shared expert: upstream gradient d_out for every token, weight 1
+  MOE_TRY(moe::launch_dense_offsets(T, d, fs, fw.off2, fw.kseg2, fw.wr2_d, fw.wr2_s, s),
+          "offsets launch");
+  MOE_TRY(moe::launch_transpose_batched(dt, w->ws2, fw.ws2t, 1, d, fs, s), "transpose launch");
+  MOE_TRY(moe::launch_transpose_batched(dt, w->ws1, fw.ws1t, 1, fs, d, s), "transpose launch");
+  moe::GemmArgs sa{};
+  sa.As = d_out;                        // d_hs [T, fs]
+  sa.Ws = fw.ws2t;
+  sa.Cs = fw.dhs;
+  sa.Ts = T;
+  sa.Kd = d;
+  sa.Nd = fs;
+  r = bwd_gemm(c, sa, fw.list[4], fw.count + 4, fw.bound[4], nullptr, 0, T, s, "dgrad GEMM launch");
+  if (r != MOE_OK) return r;
+  MOE_TRY(moe::launch_gelu_bwd(dt, zs, fw.dhs, nullptr, T, fs, s), "GELU backward launch");
+  sa.As = fw.dhs;                       // d_x_shared [T, d]
+  sa.Ws = fw.ws1t;
+  sa.Cs = d_x_shared;
+  sa.Kd = fs;
+  sa.Nd = d;
+  r = bwd_gemm(c, sa, fw.list[5], fw.count + 5, fw.bound[5], nullptr, 0, T, s, "dgrad GEMM launch");
+  if (r != MOE_OK) return r;
+  MOE_TRY(moe::launch_transpose_segments(dt, d_out, fw.off2, fw.kseg2, 1, d, ldt, fw.tb1, nullptr, s),
+          "transpose launch");
+  MOE_TRY(moe::launch_transpose_segments(dt, hs, fw.off2, fw.kseg2, 1, fs, ldt, fw.tb2, nullptr, s),
+          "transpose launch");
+  moe::GemmArgs sw{};
+  sw.A = fw.tb1;                        // dWs2 [d, fs]
+  sw.W = fw.tb2;
+  sw.C = g->d_ws2;
+  sw.Kd = ldt;
+  sw.Nd = fs;
+  sw.E = 1;
+  sw.kseg = fw.kseg2;
+  sw.wg_rows = d;
+  r = bwd_gemm(c, sw, fw.list[6], fw.count + 6, fw.bound[6], fw.wr2_d, 1, 0, s, "wgrad GEMM launch");
+  if (r != MOE_OK) return r;
+  MOE_TRY(moe::launch_transpose_segments(dt, fw.dhs, fw.off2, fw.kseg2, 1, fs, ldt, fw.tb1, nullptr, s),
+          "transpose launch");
+  MOE_TRY(moe::launch_transpose_segments(dt, x, fw.off2, fw.kseg2, 1, d, ldt, fw.tb2, nullptr, s),
+          "transpose launch");
+  sw.C = g->d_ws1;                      // dWs1 [fs, d]
+  sw.Nd = d;
+  sw.wg_rows = fs;
+  r = bwd_gemm(c, sw, fw.list[7], fw.count + 7, fw.bound[7], fw.wr2_s, 1, 0, s, "wgrad GEMM launch");
+#undef MOE_TRY
+  return r;
+}
+
+int do_route_bwd(const moe_config_t* c, const void* x, const moe_weights_t* w, const float* logits,
+                 const int32_t* idx, const float* tw, const float* dtw, const int32_t* counts,
+                 float aux_grad, float zloss_beta, float zloss_grad, float* dl, float* d_x_router,
+                 const moe_grads_t* g, const RouteBwdWs& rw, hipStream_t s) {
+  const float aux_coef = (c->aux_alpha != 0.f && aux_grad != 0.f)
+                             ? (float)((double)aux_grad * c->aux_alpha * c->n_experts / c->T)
+                             : 0.f;
+  const float z_coef = (float)((double)zloss_grad * 2.0 * zloss_beta / c->T);
+  return hip_status(moe::launch_route_bwd(c->dtype, x, w->w_router, logits, idx, tw, dtw, counts,
+                                          aux_coef, z_coef, dl ? dl : rw.dl, rw.part,
+                                          g->d_w_router, g->d_b_router, d_x_router, c->T,
+                                          c->d_model, c->n_experts, c->top_k, s),
+                    "moe_route_backward launch");
+}
+
+int check_grads(const moe_config_t* c, const moe_grads_t* g, bool router, bool experts) {
+  if (!g) return fail(MOE_ERR_INVALID_ARG, "grads is NULL");
+  if (router) {
+    MOE_REQUIRE_PTR(g->d_w_router, "d_w_router");
+    MOE_OPTIONAL_PTR(g->d_b_router, "d_b_router");
+  }
+  if (experts) {
+    MOE_REQUIRE_PTR(g->d_w1, "d_w1");
+    MOE_REQUIRE_PTR(g->d_w2, "d_w2");
+    MOE_OPTIONAL_PTR(g->d_b1, "d_b1");
+    MOE_OPTIONAL_PTR(g->d_b2, "d_b2");
+    if (c->d_ff_shared) {
+      MOE_REQUIRE_PTR(g->d_ws1, "d_ws1");
+      MOE_REQUIRE_PTR(g->d_ws2, "d_ws2");
+    }
+  }
+  return MOE_OK;
+}
+
+int check_saved(const moe_config_t* c, const moe_saved_t* sv) {
+  if (!sv) return fail(MOE_ERR_INVALID_ARG, "saved is NULL");
+  MOE_REQUIRE_PTR(sv->logits, "saved.logits");
+  MOE_REQUIRE_PTR(sv->topk_idx, "saved.topk_idx");
+  MOE_REQUIRE_PTR(sv->topk_w, "saved.topk_w");
+  MOE_REQUIRE_PTR(sv->counts, "saved.counts");
+  MOE_REQUIRE_PTR(sv->expert_offsets, "saved.expert_offsets");
+  MOE_REQUIRE_PTR(sv->slot_row, "saved.slot_row");
+  MOE_REQUIRE_PTR(sv->row_token, "saved.row_token");
+  MOE_REQUIRE_PTR(sv->n_dropped, "saved.n_dropped");
+  MOE_REQUIRE_PTR(sv->x_perm, "saved.x_perm");
+  MOE_REQUIRE_PTR(sv->z, "saved.z");
+  MOE_REQUIRE_PTR(sv->h, "saved.h");
+  MOE_REQUIRE_PTR(sv->y_perm, "saved.y_perm");
+  if (c->d_ff_shared) {
+    MOE_REQUIRE_PTR(sv->zs, "saved.zs");
+    MOE_REQUIRE_PTR(sv->hs, "saved.hs");
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,7 +770,7 @@ extern "C" {
 size_t moe_workspace_size(const moe_config_t* cfg, moe_stage_t stage) {
   int code;
   if (!check_config(cfg, &code).empty()) return (size_t)-1;
-  if ((int)stage < MOE_STAGE_ROUTE || (int)stage > MOE_STAGE_LAYER) return (size_t)-1;
+  if ((int)stage < MOE_STAGE_ROUTE || (int)stage > MOE_STAGE_LAYER_BACKWARD) return (size_t)-1;
   return stage_bytes(cfg, stage);
 }
 
@@ -490,7 +855,7 @@ int moe_expert_ffn(const moe_config_t* cfg, const void* x_perm, const int32_t* e
   Carver cv{static_cast<char*>(ws)};
   FfnWs fw;
   carve_ffn(cv, cfg, &fw);
-  return do_ffn(cfg, x_perm, expert_offsets, w, x, y_perm, y_shared, fw, stream);
+  return do_ffn(cfg, x_perm, expert_offsets, w, x, y_perm, y_shared, fw, stream, fw.h, fw.h_shared);
 }
 
 int moe_combine(const moe_config_t* cfg, const void* y_perm, const int32_t* slot_row,
@@ -586,7 +951,8 @@ int moe_layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_
   r = do_dispatch(cfg, lw.idx, x, counts, lw.offsets, lw.slot_row, lw.row_token, lw.x_perm,
                   ndrop, lw.disp, stream);
   if (r != MOE_OK) return r;
-  r = do_ffn(cfg, lw.x_perm, lw.offsets, w, x, lw.y_perm, lw.y_shared, lw.ffn, stream);
+  r = do_ffn(cfg, lw.x_perm, lw.offsets, w, x, lw.y_perm, lw.y_shared, lw.ffn, stream, lw.ffn.h,
+             lw.ffn.h_shared);
   if (r != MOE_OK) return r;
   r = do_combine(cfg, lw.y_perm, lw.slot_row, lw.w, lw.y_shared, out, stream);
   if (r != MOE_OK) return r;
@@ -595,6 +961,193 @@ int moe_layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_
     if (r != MOE_OK) return r;
   }
   return MOE_OK;
+}
+
+// ---------------------------------------------------------------- training entry points
+int moe_expert_ffn_train(const moe_config_t* cfg, const void* x_perm,
+                         const int32_t* expert_offsets, const moe_weights_t* w, const void* x,
+                         void* z, void* h, void* y_perm, void* zs, void* hs, void* y_shared,
+                         void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_TRAIN(cfg);
+  MOE_REQUIRE_PTR(x_perm, "x_perm");
+  MOE_REQUIRE_PTR(expert_offsets, "expert_offsets");
+  int r = check_weights(cfg, w, false, true);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(z, "z");
+  MOE_REQUIRE_PTR(h, "h");
+  MOE_REQUIRE_PTR(y_perm, "y_perm");
+  if (cfg->d_ff_shared) {
+    MOE_REQUIRE_PTR(x, "x");
+    MOE_REQUIRE_PTR(zs, "zs");
+    MOE_REQUIRE_PTR(hs, "hs");
+    MOE_REQUIRE_PTR(y_shared, "y_shared");
+  } else if (y_shared || zs || hs) {
+    return fail(MOE_ERR_INVALID_ARG, "shared-expert buffers given but the layer has none");
+  }
+  r = check_ws(cfg, MOE_STAGE_EXPERT_FFN_TRAIN, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  FfnWs fw;
+  carve_ffn(cv, cfg, &fw, false);
+  return do_ffn(cfg, x_perm, expert_offsets, w, x, y_perm, y_shared, fw, stream, h, hs, z, zs);
+}
+
+int moe_layer_forward_train(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                            void* out, float* aux_out, const moe_saved_t* saved, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_TRAIN(cfg);
+  MOE_REQUIRE_PTR(x, "x");
+  int r = check_weights(cfg, w, true, true);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(out, "out");
+  r = check_saved(cfg, saved);
+  if (r != MOE_OK) return r;
+  r = check_ws(cfg, MOE_STAGE_LAYER_TRAIN, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  LayerTrainWs lw;
+  carve_layer_train(cv, cfg, &lw);
+  const moe_saved_t& sv = *saved;
+  r = do_route(cfg, x, w, sv.logits, sv.topk_idx, sv.topk_w, lw.route, stream);
+  if (r != MOE_OK) return r;
+  r = do_dispatch(cfg, sv.topk_idx, x, sv.counts, sv.expert_offsets, sv.slot_row, sv.row_token,
+                  sv.x_perm, sv.n_dropped, lw.disp, stream);
+  if (r != MOE_OK) return r;
+  r = do_ffn(cfg, sv.x_perm, sv.expert_offsets, w, x, sv.y_perm, lw.y_shared, lw.ffn, stream,
+             sv.h, sv.hs, sv.z, sv.zs);
+  if (r != MOE_OK) return r;
+  r = do_combine(cfg, sv.y_perm, sv.slot_row, sv.topk_w, lw.y_shared, out, stream);
+  if (r != MOE_OK) return r;
+  if (aux_out) return do_aux(cfg, sv.logits, sv.counts, aux_out, lw.aux, stream);
+  return MOE_OK;
+}
+
+int moe_combine_backward(const moe_config_t* cfg, const void* d_out, const void* y_perm,
+                         const int32_t* slot_row, const float* topk_w, void* d_y_perm,
+                         float* d_topk_w, hipStream_t stream) {
+  MOE_CHECK_TRAIN(cfg);
+  MOE_REQUIRE_PTR(d_out, "d_out");
+  MOE_REQUIRE_PTR(y_perm, "y_perm");
+  MOE_REQUIRE_PTR(slot_row, "slot_row");
+  MOE_REQUIRE_PTR(topk_w, "topk_w");
+  MOE_REQUIRE_PTR(d_y_perm, "d_y_perm");
+  MOE_REQUIRE_PTR(d_topk_w, "d_topk_w");
+  return do_combine_bwd(cfg, d_out, y_perm, slot_row, topk_w, d_y_perm, d_topk_w, stream);
+}
+
+int moe_expert_ffn_backward(const moe_config_t* cfg, const void* x_perm,
+                            const int32_t* expert_offsets, const moe_weights_t* w, const void* x,
+                            const void* z, const void* h, const void* zs, const void* hs,
+                            const void* d_y_perm, const void* d_out, void* d_x_perm,
+                            void* d_x_shared, const moe_grads_t* grads, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  MOE_CHECK_TRAIN(cfg);
+  MOE_REQUIRE_PTR(x_perm, "x_perm");
+  MOE_REQUIRE_PTR(expert_offsets, "expert_offsets");
+  int r = check_weights(cfg, w, false, true);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(z, "z");
+  MOE_REQUIRE_PTR(h, "h");
+  MOE_REQUIRE_PTR(d_y_perm, "d_y_perm");
+  MOE_REQUIRE_PTR(d_x_perm, "d_x_perm");
+  if (cfg->d_ff_shared) {
+    MOE_REQUIRE_PTR(x, "x");
+    MOE_REQUIRE_PTR(zs, "zs");
+    MOE_REQUIRE_PTR(hs, "hs");
+    MOE_REQUIRE_PTR(d_out, "d_out");
+    MOE_REQUIRE_PTR(d_x_shared, "d_x_shared");
+  } else if (d_x_shared) {
+    return fail(MOE_ERR_INVALID_ARG, "d_x_shared given but the layer has no shared expert");
+  }
+  r = check_grads(cfg, grads, false, true);
+  if (r != MOE_OK) return r;
+  r = check_ws(cfg, MOE_STAGE_EXPERT_FFN_BACKWARD, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  FfnBwdWs fw;
+  carve_ffn_bwd(cv, cfg, &fw);
+  return do_ffn_bwd(cfg, x_perm, expert_offsets, w, x, z, h, zs, hs, d_y_perm, d_out, d_x_perm,
+                    d_x_shared, grads, fw, stream);
+}
+
+int moe_route_backward(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                       const float* logits, const int32_t* topk_idx, const float* topk_w,
+                       const float* d_topk_w, const int32_t* counts, float aux_grad,
+                       float zloss_beta, float zloss_grad, float* d_logits, float* d_x_router,
+                       const moe_grads_t* grads, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_TRAIN(cfg);
+  MOE_REQUIRE_PTR(x, "x");
+  int r = check_weights(cfg, w, true, false);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(logits, "logits");
+  MOE_REQUIRE_PTR(topk_idx, "topk_idx");
+  MOE_REQUIRE_PTR(topk_w, "topk_w");
+  MOE_REQUIRE_PTR(d_topk_w, "d_topk_w");
+  if (!isfinite(aux_grad) || !isfinite(zloss_beta) || !isfinite(zloss_grad))
+    return fail(MOE_ERR_INVALID_ARG, "aux_grad, zloss_beta and zloss_grad must be finite");
+  if (cfg->aux_alpha != 0.f && aux_grad != 0.f) MOE_REQUIRE_PTR(counts, "counts");
+  MOE_OPTIONAL_PTR(d_logits, "d_logits");
+  MOE_OPTIONAL_PTR(d_x_router, "d_x_router");
+  r = check_grads(cfg, grads, true, false);
+  if (r != MOE_OK) return r;
+  r = check_ws(cfg, MOE_STAGE_ROUTE_BACKWARD, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  RouteBwdWs rw;
+  carve_route_bwd(cv, cfg, &rw);
+  return do_route_bwd(cfg, x, w, logits, topk_idx, topk_w, d_topk_w, counts, aux_grad, zloss_beta,
+                      zloss_grad, d_logits, d_x_router, grads, rw, stream);
+}
+
+int moe_dispatch_backward(const moe_config_t* cfg, const void* d_x_perm, const int32_t* slot_row,
+                          const void* d_x_shared, const float* d_x_router, void* d_x,
+                          hipStream_t stream) {
+  MOE_CHECK_TRAIN(cfg);
+  MOE_REQUIRE_PTR(d_x_perm, "d_x_perm");
+  MOE_REQUIRE_PTR(slot_row, "slot_row");
+  MOE_OPTIONAL_PTR(d_x_shared, "d_x_shared");
+  MOE_OPTIONAL_PTR(d_x_router, "d_x_router");
+  MOE_REQUIRE_PTR(d_x, "d_x");
+  return hip_status(moe::launch_unpermute(cfg->dtype, d_x_perm, slot_row, d_x_shared, d_x_router,
+                                          d_x, cfg->T, cfg->d_model, cfg->top_k, stream),
+                    "moe_dispatch_backward launch");
+}
+
+int moe_layer_backward(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                       const moe_saved_t* saved, const void* d_out, float aux_grad,
+                       float zloss_beta, float zloss_grad, void* d_x, const moe_grads_t* grads,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_CHECK_TRAIN(cfg);
+  MOE_REQUIRE_PTR(x, "x");
+  int r = check_weights(cfg, w, true, true);
+  if (r != MOE_OK) return r;
+  r = check_saved(cfg, saved);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(d_out, "d_out");
+  MOE_REQUIRE_PTR(d_x, "d_x");
+  if (!isfinite(aux_grad) || !isfinite(zloss_beta) || !isfinite(zloss_grad))
+    return fail(MOE_ERR_INVALID_ARG, "aux_grad, zloss_beta and zloss_grad must be finite");
+  r = check_grads(cfg, grads, true, true);
+  if (r != MOE_OK) return r;
+  r = check_ws(cfg, MOE_STAGE_LAYER_BACKWARD, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  LayerBwdWs lw;
+  carve_layer_bwd(cv, cfg, &lw);
+  const moe_saved_t& sv = *saved;
+  r = do_combine_bwd(cfg, d_out, sv.y_perm, sv.slot_row, sv.topk_w, lw.d_y_perm, lw.d_topk_w,
+                     stream);
+  if (r != MOE_OK) return r;
+  r = do_ffn_bwd(cfg, sv.x_perm, sv.expert_offsets, w, x, sv.z, sv.h, sv.zs, sv.hs, lw.d_y_perm,
+                 d_out, lw.d_x_perm, lw.d_x_shared, grads, lw.ffn, stream);
+  if (r != MOE_OK) return r;
+  r = do_route_bwd(cfg, x, w, sv.logits, sv.topk_idx, sv.topk_w, lw.d_topk_w, sv.counts, aux_grad,
+                   zloss_beta, zloss_grad, nullptr, lw.d_x_router, grads, lw.route, stream);
+  if (r != MOE_OK) return r;
+  return hip_status(moe::launch_unpermute(cfg->dtype, lw.d_x_perm, sv.slot_row, lw.d_x_shared,
+                                          lw.d_x_router, d_x, cfg->T, cfg->d_model, cfg->top_k,
+                                          stream),
+                    "unpermute launch");
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

@@ -51,6 +51,27 @@ __device__ __forceinline__ float gelu_as(float z) {
   return fmaf(az * t, q * e, relu);
 }
 
+// d/dz GELU(z) = Phi(z) + z phi(z), with the erf of gelu_as: for x = |z|/sqrt(2),
+// t q e = -erfc(x) / 2, so Phi(z) = 1 + t q e for z >= 0 and -t q e for z < 0.
+__device__ __forceinline__ float gelu_grad_as(float z) {
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189f, az, 1.0f));
+  float q = fmaf(-0.5307027145f, t, 0.7265760135f);
+  q = fmaf(q, t, -0.7107068705f);
+  q = fmaf(q, t, 0.1422483680f);
+  q = fmaf(q, t, -0.1274147960f);
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170368f);
+  const float tqe = t * q * e;
+  const float cdf = z >= 0.f ? 1.0f + tqe : -tqe;
+  return fmaf(z * e, 0.39894228040143267794f, cdf);   // 1 / sqrt(2 pi)
+}
+
+// The same derivative with the library erf (fp32 layers).
+__device__ __forceinline__ float gelu_grad_erf(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752440f)) +
+         z * expf(-0.5f * z * z) * 0.39894228040143267794f;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
@@ -114,6 +135,12 @@ struct GemmArgs {
   int Kd, Nd;
   int E;
   int64_t grid_tiles;   // upper bound on the tile count (grid size)
+  // Weight-gradient (k-segment) mode, tiled and fp32 kernels: when kseg is
+  // set, expert e's tiles contract over columns [kseg[e], kseg[e+1]) of
+  // A [wg_rows, Kd] and W [Nd, Kd] (both shared by all experts, row stride
+  // Kd), writing C rows e * wg_rows + i; kseg entries are multiples of 32.
+  const int32_t* kseg;
+  int wg_rows;
 };
 
 // Prefill-shaped grouped GEMM (bf16 MFMA): tiles of gemm_bf16_bm() x
@@ -166,6 +193,46 @@ constexpr int kStatsTokensPerBlock = 64;
 inline int stats_blocks(int T) { return (T + kStatsTokensPerBlock - 1) / kStatsTokensPerBlock; }
 hipError_t launch_stats(const int32_t* topk_idx, const float* topk_w, int T, int K, int N,
                         int32_t* pcnt, double* pw, int32_t* counts, float* wmean, hipStream_t s);
+// ---------------------------------------------------------------- backward
+// h = GELU(z) and d_z = d_h * GELU'(z) over rows [0, *nrows) (or rows_max
+// when nrows is null) of [*, width] matrices.
+hipError_t launch_gelu_fwd(int dtype, const void* z, void* h, const int32_t* nrows, int rows_max,
+                           int width, hipStream_t s);
+hipError_t launch_gelu_bwd(int dtype, const void* z, void* dh, const int32_t* nrows, int rows_max,
+                           int width, hipStream_t s);
+// d_y_perm rows of the kept slots and d_topk_w (0 for dropped slots).
+hipError_t launch_combine_bwd(int dtype, const void* d_out, const void* y_perm,
+                              const int32_t* slot_row, const float* topk_w, void* d_y_perm,
+                              float* d_topk_w, int T, int d, int K, hipStream_t s);
+// d_x[t] = sum of the kept d_x_perm rows + d_x_shared[t] + d_x_router[t].
+hipError_t launch_unpermute(int dtype, const void* d_x_perm, const int32_t* slot_row,
+                            const void* d_x_shared, const float* d_x_router, void* d_x, int T,
+                            int d, int K, hipStream_t s);
+// out[b] = in[b]^T for B matrices of R x C (R, C multiples of 64).
+hipError_t launch_transpose_batched(int dtype, const void* in, void* out, int B, int R, int C,
+                                    hipStream_t s);
+// Rows of segment e of in [*, C] -> columns [kseg[e], kseg[e+1]) of out
+// [C, ldo], zero padded; colsum [nseg, C] (or null) = per-segment column sums.
+hipError_t launch_transpose_segments(int dtype, const void* in, const int32_t* off,
+                                     const int32_t* kseg, int nseg, int C, int ldo, void* out,
+                                     void* colsum, hipStream_t s);
+// kseg = scan of the segment lengths rounded up to 32; wa[e] = e * ra,
+// wb[e] = e * rb (the output-row offsets of two weight-gradient GEMMs).
+hipError_t launch_seg_offsets(const int32_t* off, int N, int ra, int rb, int32_t* kseg,
+                              int32_t* wa, int32_t* wb, hipStream_t s);
+// One segment of T rows (off = {0, T}).
+hipError_t launch_dense_offsets(int T, int ra, int rb, int32_t* off, int32_t* kseg, int32_t* wa,
+                                int32_t* wb, hipStream_t s);
+// Router backward: d_logits, then d_w_router (part holds
+// router_dw_slices(T, N, d) * N * d floats), d_b_router (or null) and
+// d_x_router [T, d] fp32 (or null).
+int router_dw_slices(int T, int N, int d);
+hipError_t launch_route_bwd(int dtype, const void* x, const void* w_router, const float* logits,
+                            const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
+                            const int32_t* counts, float aux_coef, float z_coef, float* dl,
+                            float* part, float* d_w_router, float* d_b_router, float* d_x_router,
+                            int T, int d, int N, int K, hipStream_t s);
+
 // Router z-loss: beta * mean_t logsumexp(logits[t])^2 in fp64; zpart holds
 // aux_blocks(T) doubles.
 hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,

@@ -34,6 +34,7 @@ from .configs import MoEShape
 # tensor codes for the stream keys
 _ROUTER_W, _ROUTER_B, _OFFSET, _SEL_BIAS = 1, 2, 3, 4
 _W1, _B1, _W2, _B2, _WS1, _WS2, _X, _PERM = 5, 6, 7, 8, 9, 10, 11, 12
+_D_OUT = 13
 _X_BLOCK = 1024
 
 
@@ -186,6 +187,12 @@ def make_inputs(shape: MoEShape, seed: int = 0, materialize_experts: bool = True
     return MoEInputs(shape=shape, seed=seed, x=x, w_router=w_router, b_router=b_router,
                      logit_offset=logit_offset, sel_bias=sel_bias, w1=w1, b1=b1, w2=w2,
                      b2=b2, ws1=ws1, ws2=ws2)
+
+
+def upstream_grad(shape: MoEShape, seed: int = 0) -> np.ndarray:
+    """A seeded upstream gradient d_out [T, d_model] ~ N(0, 1) in the layer
+    dtype (bf16 bit patterns or fp32), for the backward pass."""
+    return _normal_block(_rng(seed, shape, _D_OUT), (shape.T, shape.d_model), 1.0, shape.dtype)
 
 
 def to_torch(inp: MoEInputs, device) -> Dict[str, "object"]:

@@ -17,10 +17,15 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WQ_NONE, MOE_WQ_INT8 = 0, 1
-STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5}
+STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5,
+          "expert_ffn_train": 6, "layer_train": 7, "expert_ffn_backward": 8,
+          "route_backward": 9, "layer_backward": 10}
 ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
                 "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_router_z_loss",
-                "moe_routing_stats", "moe_quantize_int8", "moe_layer_forward", "moe_last_error")
+                "moe_routing_stats", "moe_quantize_int8", "moe_layer_forward",
+                "moe_expert_ffn_train", "moe_layer_forward_train", "moe_combine_backward",
+                "moe_expert_ffn_backward", "moe_route_backward", "moe_dispatch_backward",
+                "moe_layer_backward", "moe_last_error")
 
 
 class MoeConfig(ctypes.Structure):
@@ -37,6 +42,19 @@ _WEIGHT_FIELDS = ("w_router", "b_router", "logit_offset", "sel_bias", "w1", "b1"
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _WEIGHT_FIELDS]
+
+
+SAVED_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "expert_offsets", "slot_row",
+                "row_token", "n_dropped", "x_perm", "z", "h", "y_perm", "zs", "hs")
+GRAD_FIELDS = ("d_w_router", "d_b_router", "d_w1", "d_b1", "d_w2", "d_b2", "d_ws1", "d_ws2")
+
+
+class MoeSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in SAVED_FIELDS]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
 class MoEError(RuntimeError):
@@ -72,9 +90,21 @@ def lib():
     L.moe_routing_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_quantize_int8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
+    svp, gp, f32 = ctypes.POINTER(MoeSaved), ctypes.POINTER(MoeGrads), ctypes.c_float
+    L.moe_expert_ffn_train.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_layer_forward_train.argtypes = [cfgp, vp, wp, vp, vp, svp, vp, sz, vp]
+    L.moe_combine_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_ffn_backward.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          gp, vp, sz, vp]
+    L.moe_route_backward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, gp,
+                                     vp, sz, vp]
+    L.moe_dispatch_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+    L.moe_layer_backward.argtypes = [cfgp, vp, wp, svp, vp, f32, f32, f32, vp, gp, vp, sz, vp]
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
                  "moe_router_z_loss", "moe_routing_stats", "moe_quantize_int8",
-                 "moe_layer_forward"):
+                 "moe_layer_forward", "moe_expert_ffn_train", "moe_layer_forward_train",
+                 "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward",
+                 "moe_dispatch_backward", "moe_layer_backward"):
         getattr(L, name).restype = ctypes.c_int
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
@@ -230,6 +260,114 @@ def moe_layer_forward(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,
                                    _stream(stream)))
 
 
+# ---------------------------------------------------------------- training entry points
+def make_saved(t: Dict[str, object]) -> MoeSaved:
+    return MoeSaved(**{n: _p(t.get(n)) for n in SAVED_FIELDS})
+
+
+def make_grads(t: Dict[str, object]) -> MoeGrads:
+    return MoeGrads(**{n: _p(t.get(n)) for n in GRAD_FIELDS})
+
+
+def moe_expert_ffn_train(cfg, x_perm, expert_offsets, w: MoeWeights, x, z, h, y_perm, zs, hs,
+                         y_shared, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_expert_ffn_train(ctypes.byref(cfg), _p(x_perm), _p(expert_offsets),
+                                      ctypes.byref(w), _p(x), _p(z), _p(h), _p(y_perm), _p(zs),
+                                      _p(hs), _p(y_shared), p, n, _stream(stream)))
+
+
+def moe_layer_forward_train(cfg, x, w: MoeWeights, out, aux_out, saved: MoeSaved, ws,
+                            stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_layer_forward_train(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(out),
+                                         _p(aux_out), ctypes.byref(saved), p, n,
+                                         _stream(stream)))
+
+
+def moe_combine_backward(cfg, d_out, y_perm, slot_row, topk_w, d_y_perm, d_topk_w, stream=None):
+    _check(lib().moe_combine_backward(ctypes.byref(cfg), _p(d_out), _p(y_perm), _p(slot_row),
+                                      _p(topk_w), _p(d_y_perm), _p(d_topk_w), _stream(stream)))
+
+
+def moe_expert_ffn_backward(cfg, x_perm, expert_offsets, w: MoeWeights, x, z, h, zs, hs,
+                            d_y_perm, d_out, d_x_perm, d_x_shared, grads: MoeGrads, ws,
+                            stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_expert_ffn_backward(ctypes.byref(cfg), _p(x_perm), _p(expert_offsets),
+                                         ctypes.byref(w), _p(x), _p(z), _p(h), _p(zs), _p(hs),
+                                         _p(d_y_perm), _p(d_out), _p(d_x_perm), _p(d_x_shared),
+                                         ctypes.byref(grads), p, n, _stream(stream)))
+
+
+def moe_route_backward(cfg, x, w: MoeWeights, logits, topk_idx, topk_w, d_topk_w, counts,
+                       aux_grad, zloss_beta, zloss_grad, d_logits, d_x_router, grads: MoeGrads,
+                       ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_route_backward(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(logits),
+                                    _p(topk_idx), _p(topk_w), _p(d_topk_w), _p(counts),
+                                    float(aux_grad), float(zloss_beta), float(zloss_grad),
+                                    _p(d_logits), _p(d_x_router), ctypes.byref(grads), p, n,
+                                    _stream(stream)))
+
+
+def moe_dispatch_backward(cfg, d_x_perm, slot_row, d_x_shared, d_x_router, d_x, stream=None):
+    _check(lib().moe_dispatch_backward(ctypes.byref(cfg), _p(d_x_perm), _p(slot_row),
+                                       _p(d_x_shared), _p(d_x_router), _p(d_x), _stream(stream)))
+
+
+def moe_layer_backward(cfg, x, w: MoeWeights, saved: MoeSaved, d_out, aux_grad, zloss_beta,
+                       zloss_grad, d_x, grads: MoeGrads, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_layer_backward(ctypes.byref(cfg), _p(x), ctypes.byref(w),
+                                    ctypes.byref(saved), _p(d_out), float(aux_grad),
+                                    float(zloss_beta), float(zloss_grad), _p(d_x),
+                                    ctypes.byref(grads), p, n, _stream(stream)))
+
+
+def alloc_saved(cfg: MoeConfig, device="cuda") -> Dict[str, object]:
+    """Device buffers for the tensors the training forward keeps."""
+    import torch
+    T, K, N, d, f, fs = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+    dt = torch.float32 if cfg.dtype == MOE_F32 else torch.bfloat16
+    i32, f32 = torch.int32, torch.float32
+    t = dict(logits=torch.empty(T, N, dtype=f32, device=device),
+             topk_idx=torch.empty(T, K, dtype=i32, device=device),
+             topk_w=torch.empty(T, K, dtype=f32, device=device),
+             counts=torch.empty(N, dtype=i32, device=device),
+             expert_offsets=torch.empty(N + 1, dtype=i32, device=device),
+             slot_row=torch.empty(T, K, dtype=i32, device=device),
+             row_token=torch.empty(T * K, dtype=i32, device=device),
+             n_dropped=torch.empty(1, dtype=i32, device=device),
+             x_perm=torch.empty(T * K, d, dtype=dt, device=device),
+             z=torch.empty(T * K, f, dtype=dt, device=device),
+             h=torch.empty(T * K, f, dtype=dt, device=device),
+             y_perm=torch.empty(T * K, d, dtype=dt, device=device))
+    if fs:
+        t["zs"] = torch.empty(T, fs, dtype=dt, device=device)
+        t["hs"] = torch.empty(T, fs, dtype=dt, device=device)
+    return t
+
+
+def alloc_grads(cfg: MoeConfig, biases: bool, router_bias: bool, device="cuda") -> Dict[str, object]:
+    """Device buffers for the gradients (expert biases and router bias optional)."""
+    import torch
+    N, d, f, fs = cfg.n_experts, cfg.d_model, cfg.d_ff, cfg.d_ff_shared
+    dt = torch.float32 if cfg.dtype == MOE_F32 else torch.bfloat16
+    g = dict(d_w_router=torch.empty(N, d, dtype=torch.float32, device=device),
+             d_w1=torch.empty(N, f, d, dtype=dt, device=device),
+             d_w2=torch.empty(N, d, f, dtype=dt, device=device))
+    if router_bias:
+        g["d_b_router"] = torch.empty(N, dtype=torch.float32, device=device)
+    if biases:
+        g["d_b1"] = torch.empty(N, f, dtype=dt, device=device)
+        g["d_b2"] = torch.empty(N, d, dtype=dt, device=device)
+    if fs:
+        g["d_ws1"] = torch.empty(fs, d, dtype=dt, device=device)
+        g["d_ws2"] = torch.empty(d, fs, dtype=dt, device=device)
+    return g
+
+
 # ---------------------------------------------------------------- convenience
 class MoELayer:
     """Holds a config, device weights and a workspace; ``forward`` enqueues
@@ -263,3 +401,35 @@ class MoELayer:
         ndrop = torch.empty(1, dtype=torch.int32, device=x.device)
         moe_layer_forward(self.cfg, x, self.w, out, aux_t, counts, ndrop, self.ws, stream)
         return out, aux_t, counts, ndrop
+
+
+class MoETrainLayer(MoELayer):
+    """MoELayer with a training step: ``forward`` keeps the tensors the
+    backward needs; ``backward`` fills the gradient buffers and returns d_x."""
+
+    def __init__(self, cfg: MoeConfig, tensors: Dict[str, object], device="cuda"):
+        super().__init__(cfg, tensors, device)
+        self.ws = alloc_workspace(cfg, "layer_train", device)
+        self.ws_bwd = alloc_workspace(cfg, "layer_backward", device)
+        self.saved_t = alloc_saved(cfg, device)
+        self.saved = make_saved(self.saved_t)
+        biases = tensors.get("b1") is not None or tensors.get("b2") is not None
+        self.grads_t = alloc_grads(cfg, biases, tensors.get("b_router") is not None, device)
+        self.grads = make_grads(self.grads_t)
+
+    def forward(self, x, aux: bool = False, out=None, stream=None):
+        import torch
+        if tuple(x.shape) != (self.cfg.T, self.cfg.d_model) or x.dtype != self.dtype:
+            raise ValueError("x must be [T, d_model] in the layer dtype")
+        out = torch.empty_like(x) if out is None else out
+        aux_t = torch.empty(1, dtype=torch.float32, device=x.device) if aux else None
+        moe_layer_forward_train(self.cfg, x, self.w, out, aux_t, self.saved, self.ws, stream)
+        return out, aux_t
+
+    def backward(self, x, d_out, aux_grad=0.0, zloss_beta=0.0, zloss_grad=0.0, d_x=None,
+                 stream=None):
+        import torch
+        d_x = torch.empty_like(x) if d_x is None else d_x
+        moe_layer_backward(self.cfg, x, self.w, self.saved, d_out, aux_grad, zloss_beta,
+                           zloss_grad, d_x, self.grads, self.ws_bwd, stream)
+        return d_x

@@ -175,3 +175,64 @@ def test_capacity_rejects_bad_arguments():
     assert L.moe_capacity_from_factor(8, 8, 0.0) == -1
     assert L.moe_capacity_from_factor(8, 8, float("nan")) == -1
     assert L.moe_capacity_from_factor(8, 8, float("inf")) == -1
+
+
+def test_training_entry_points_check_arguments():
+    L = moe.lib()
+    cfg = _cfg()
+    W = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=FAKE)
+    G = moe.MoeGrads(d_w_router=FAKE, d_w1=FAKE, d_w2=FAKE)
+    S = moe.MoeSaved(**{n: FAKE for n in moe.SAVED_FIELDS if n not in ("zs", "hs")})
+    for stage in ("expert_ffn_train", "layer_train", "expert_ffn_backward", "route_backward",
+                  "layer_backward"):
+        assert moe.workspace_size(cfg, stage) > 0
+    big = 1 << 40
+    # INT8 experts are inference-only
+    q8 = _cfg(weight_quant=moe.MOE_WQ_INT8)
+    assert L.moe_layer_backward(ctypes.byref(q8), FAKE, ctypes.byref(W), ctypes.byref(S), FAKE,
+                                0.0, 0.0, 0.0, FAKE, ctypes.byref(G), FAKE * 256, big,
+                                None) == moe.MOE_ERR_UNSUPPORTED
+    assert b"MOE_WQ_NONE" in L.moe_last_error()
+    assert L.moe_combine_backward(ctypes.byref(q8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None) == moe.MOE_ERR_UNSUPPORTED
+    # missing saved tensors, gradients, non-finite scalars, short workspace
+    S_missing = moe.MoeSaved(**{n: FAKE for n in moe.SAVED_FIELDS if n not in ("z", "zs", "hs")})
+    assert L.moe_layer_backward(ctypes.byref(cfg), FAKE, ctypes.byref(W), ctypes.byref(S_missing),
+                                FAKE, 0.0, 0.0, 0.0, FAKE, ctypes.byref(G), FAKE * 256, big,
+                                None) == moe.MOE_ERR_INVALID_ARG
+    assert b"saved.z" in L.moe_last_error()
+    G_missing = moe.MoeGrads(d_w_router=FAKE, d_w1=FAKE)
+    assert L.moe_layer_backward(ctypes.byref(cfg), FAKE, ctypes.byref(W), ctypes.byref(S), FAKE,
+                                0.0, 0.0, 0.0, FAKE, ctypes.byref(G_missing), FAKE * 256, big,
+                                None) == moe.MOE_ERR_INVALID_ARG
+    assert b"d_w2" in L.moe_last_error()
+    assert L.moe_layer_backward(ctypes.byref(cfg), FAKE, ctypes.byref(W), ctypes.byref(S), FAKE,
+                                float("inf"), 0.0, 0.0, FAKE, ctypes.byref(G), FAKE * 256, big,
+                                None) == moe.MOE_ERR_INVALID_ARG
+    need = moe.workspace_size(cfg, "layer_backward")
+    assert L.moe_layer_backward(ctypes.byref(cfg), FAKE, ctypes.byref(W), ctypes.byref(S), FAKE,
+                                0.0, 0.0, 0.0, FAKE, ctypes.byref(G), FAKE * 256, need - 1,
+                                None) == moe.MOE_ERR_WORKSPACE
+    # the shared expert needs its saved tensors and gradients
+    cfg_s = _cfg(d_ff_shared=64)
+    Ws = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=FAKE, ws1=FAKE, ws2=FAKE)
+    assert L.moe_layer_forward_train(ctypes.byref(cfg_s), FAKE, ctypes.byref(Ws), FAKE, None,
+                                     ctypes.byref(S), FAKE * 256, big,
+                                     None) == moe.MOE_ERR_INVALID_ARG
+    assert b"saved.zs" in L.moe_last_error()
+    assert L.moe_expert_ffn_backward(ctypes.byref(cfg_s), FAKE, FAKE, ctypes.byref(Ws), FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     ctypes.byref(G), FAKE * 256, big,
+                                     None) == moe.MOE_ERR_INVALID_ARG
+    assert b"d_ws1" in L.moe_last_error()
+    # router backward: aux needs counts; the optional outputs may be NULL
+    cfg_a = _cfg(aux_alpha=0.01)
+    assert L.moe_route_backward(ctypes.byref(cfg_a), FAKE, ctypes.byref(W), FAKE, FAKE, FAKE,
+                                FAKE, None, 1.0, 0.0, 0.0, None, None, ctypes.byref(G),
+                                FAKE * 256, big, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"counts" in L.moe_last_error()
+    assert L.moe_dispatch_backward(ctypes.byref(cfg), FAKE, FAKE, None, None, None,
+                                   None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_expert_ffn_train(ctypes.byref(cfg), FAKE, FAKE, ctypes.byref(W), None, FAKE,
+                                  FAKE, FAKE, FAKE, None, None, FAKE * 256, big,
+                                  None) == moe.MOE_ERR_INVALID_ARG
