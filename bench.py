@@ -9,7 +9,8 @@ on the launch stream around each stage, so the grouped-GEMM stage's own
 duration is measured live inside the timed region.
 
 Prints ONE JSON line.  Default workload: the Mixtral-8x7B-shaped prefill
-layer (T=4096, d=4096, f=14336, N=8, top-2, bf16).
+layer (T=4096, d=4096, f=14336, N=8, top-2, bf16).  --pass train times one
+training step instead (the training forward, then the backward's stages).
 """
 from __future__ import annotations
 
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=128)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy and exit (counter calibration)")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "train"), default="forward",
+                    help="forward: the forward hot path (default); train: one training step, "
+                         "the training forward and the whole backward")
     return ap.parse_args()
 
 
@@ -117,6 +121,189 @@ def cpu_baseline(shape, inp, n_tok):
                       f"one run, {dt:.1f} s, fp64 NumPy, BLAS threads {int(threads)}"}
 
 
+def algorithmic_backward(shape, counts, M):
+    """FLOPs and minimum HBM bytes of the expert FFN backward stage: four
+    GEMMs per expert (two input gradients, two weight gradients) of 2*M*d*f
+    each; bytes = weights read once, weight gradients written once, x_perm,
+    z, h, d_y read once, d_x_perm written once (the shared expert alike)."""
+    d, f, fs = shape.d_model, shape.d_ff, shape.d_ff_shared
+    T = shape.T
+    eb = 4 if shape.dtype == "f32" else 2
+    touched = int((counts > 0).sum())
+    flops = 4 * 2 * M * d * f + (4 * 2 * T * d * fs if fs else 0)
+    wbytes = 2 * (touched * 2 * d * f + (2 * d * fs if fs else 0)) * eb
+    abytes = (3 * M * d + 2 * M * f) * eb + ((3 * T * d + 2 * T * fs) * eb if fs else 0)
+    return flops, wbytes + abytes, touched
+
+
+def cpu_baseline_train(shape, inp, n_tok):
+    """The CPU oracle's forward + backward (moe_backward recomputes the
+    forward) on the first n tokens of the workload; the sample grows like
+    cpu_baseline's."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from mixture_experts_layer_prefix_amd import inputs
+    from oracle import moe_oracle as O
+
+    get = lambda e: tuple(None if a is None else (inputs.bf16_widen(a) if a.dtype == np.uint16 else a)
+                          for a in inp.expert(e))
+    shared = (inp.f32("ws1"), inp.f32("ws2")) if shape.d_ff_shared else None
+    x_all = inp.f32("x")
+    g_all = inputs.upstream_grad(shape, seed=inp.seed)
+    g_all = inputs.bf16_widen(g_all) if g_all.dtype == np.uint16 else g_all
+
+    def run(n):
+        cap = None
+        if shape.capacity_factor is not None:
+            cap = O.capacity_from_factor(n, shape.n_experts, shape.capacity_factor)
+        t0 = time.perf_counter()
+        O.moe_backward(x_all[:n], inp.f32("w_router"), get, shape.top_k, g_all[:n],
+                       n_experts=shape.n_experts, b_router=inp.b_router,
+                       logit_offset=inp.logit_offset, sel_bias=inp.sel_bias, shared=shared,
+                       capacity=cap, aux_alpha=shape.aux_alpha)
+        return time.perf_counter() - t0
+
+    n = min(n_tok, shape.T)
+    dt = run(n)
+    for _ in range(3):
+        if dt >= 10.0 or n >= shape.T:
+            break
+        n = min(shape.T, max(2 * n, int(n * 15.0 / max(dt, 1e-3))))
+        dt = run(n)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n} of {shape.T} tokens of {shape.name}: the oracle's "
+                      f"moe_backward (forward recomputed, then every gradient), one run, "
+                      f"{dt:.1f} s, fp64 NumPy, BLAS threads {int(threads)}"}
+
+
+def main_train(args, shape, inp, t):
+    """One training step: moe_layer_forward_train, then the backward's four
+    stage entry points (the kernels moe_layer_backward enqueues), with HIP
+    events on the launch stream around each."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_prefix_amd import inputs, moe
+
+    dev = "cuda:0"
+    cfg = moe.config_for(shape)
+    W = moe.make_weights(t)
+    T, N, K, d = cfg.T, cfg.n_experts, cfg.top_k, cfg.d_model
+    dt = torch.float32 if shape.dtype == "f32" else torch.bfloat16
+    sv_t = moe.alloc_saved(cfg, dev)
+    sv = moe.make_saved(sv_t)
+    biases = t.get("b1") is not None
+    g_t = moe.alloc_grads(cfg, biases, t.get("b_router") is not None, dev)
+    G = moe.make_grads(g_t)
+    g_np = inputs.upstream_grad(shape, seed=args.seed)
+    d_out = torch.from_numpy(g_np)
+    d_out = (d_out.view(torch.bfloat16) if g_np.dtype == np.uint16 else d_out).to(dev)
+    out = torch.empty(T, d, dtype=dt, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev) if cfg.aux_alpha else None
+    d_y_perm = torch.empty(T * K, d, dtype=dt, device=dev)
+    d_topk_w = torch.empty(T, K, dtype=torch.float32, device=dev)
+    d_x_perm = torch.empty(T * K, d, dtype=dt, device=dev)
+    d_x_shared = torch.empty(T, d, dtype=dt, device=dev) if cfg.d_ff_shared else None
+    d_x_router = torch.empty(T, d, dtype=torch.float32, device=dev)
+    d_x = torch.empty(T, d, dtype=dt, device=dev)
+    ws_t = moe.alloc_workspace(cfg, "layer_train", dev)
+    ws_f = moe.alloc_workspace(cfg, "expert_ffn_backward", dev)
+    ws_r = moe.alloc_workspace(cfg, "route_backward", dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    xs = t["x"]
+    names = ("forward_train", "combine_backward", "expert_ffn_backward", "route_backward",
+             "dispatch_backward")
+    g_aux = 1.0 if cfg.aux_alpha else 0.0
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        moe.moe_layer_forward_train(cfg, xs, W, out, aux, sv, ws_t, stream=sp)
+        if ev: ev[1].record(stream)
+        moe.moe_combine_backward(cfg, d_out, sv_t["y_perm"], sv_t["slot_row"], sv_t["topk_w"],
+                                 d_y_perm, d_topk_w, stream=sp)
+        if ev: ev[2].record(stream)
+        moe.moe_expert_ffn_backward(cfg, sv_t["x_perm"], sv_t["expert_offsets"], W,
+                                    xs if cfg.d_ff_shared else None, sv_t["z"], sv_t["h"],
+                                    sv_t.get("zs"), sv_t.get("hs"), d_y_perm, d_out, d_x_perm,
+                                    d_x_shared, G, ws_f, stream=sp)
+        if ev: ev[3].record(stream)
+        moe.moe_route_backward(cfg, xs, W, sv_t["logits"], sv_t["topk_idx"], sv_t["topk_w"],
+                               d_topk_w, sv_t["counts"], g_aux, 0.0, 0.0, None, d_x_router, G,
+                               ws_r, stream=sp)
+        if ev: ev[4].record(stream)
+        moe.moe_dispatch_backward(cfg, d_x_perm, sv_t["slot_row"], d_x_shared, d_x_router, d_x,
+                                  stream=sp)
+        if ev: ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # the staged backward must reproduce the whole-layer entry point bit for bit
+    d_x_layer = torch.empty_like(d_x)
+    g_l = {k: torch.empty_like(v) for k, v in g_t.items()}
+    moe.moe_layer_backward(cfg, xs, W, sv, d_out, g_aux, 0.0, 0.0, d_x_layer, moe.make_grads(g_l),
+                           moe.alloc_workspace(cfg, "layer_backward", dev), stream=sp)
+    torch.cuda.synchronize()
+    assert torch.equal(d_x_layer, d_x), "staged backward and moe_layer_backward differ"
+    for k in g_t:
+        assert torch.equal(g_l[k], g_t[k]), k
+    del d_x_layer, g_l
+    torch.cuda.empty_cache()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    stage_ms = {n: float(np.mean([evs[s_][i].elapsed_time(evs[s_][i + 1])
+                                  for s_ in range(args.steps)])) for i, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    counts_h = sv_t["counts"].cpu().numpy()
+    offs = sv_t["expert_offsets"].cpu().numpy()
+    M = int(offs[-1])
+    kept = np.diff(offs)
+    flops, nbytes, touched = algorithmic_backward(shape, kept, M)
+    st = stage_ms["expert_ffn_backward"] / 1e3
+    if shape.dtype == "f32":
+        roof = {"bound": "alu", "achieved": round(flops / st / 1e12, 2), "peak": PEAK_F32_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif flops / nbytes >= RIDGE:
+        roof = {"bound": "mfma", "achieved": round(flops / st / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nbytes / st / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = ("moe_expert_ffn_backward: weight transposes, input-gradient GEMMs, GELU "
+                      "backward, per-expert activation transposes and weight-gradient GEMMs")
+    roof["per_launch"] = {"flops": flops, "min_bytes": nbytes, "rows": M,
+                          "touched_experts": touched, "ms": round(stage_ms["expert_ffn_backward"], 4)}
+    res = {
+        "metric": "MoE-layer training-step tokens/s on 1 MI355X (training forward + backward)",
+        "value": round(T / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": shape.dtype, "data": "synthetic (seeded, N(0,1) x and d_out, N(0,1/fan_in) weights)",
+        "config": {"workload": shape.name, "pass": "train", "T": T, "d_model": d,
+                   "d_ff": cfg.d_ff, "n_experts": N, "top_k": K, "capacity": cfg.capacity,
+                   "d_ff_shared": cfg.d_ff_shared, "parallelism": "single GPU"},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle's backward on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline_train(shape, inp, args.cpu_sample_tokens)
+    print(json.dumps(res), flush=True)
+
+
 def traffic_from_profile(shape):
     """HBM bytes per launch of the grouped-GEMM stage from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the plain-copy
@@ -183,6 +370,13 @@ def main():
         t = moe.quantize_expert_weights(t)
         torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    if args.pass_ == "train":
+        if shape.weight_quant != "none":
+            print("the training pass needs unquantised expert weights", file=sys.stderr)
+            sys.exit(2)
+        main_train(args, shape, inp, t)
+        return
 
     cfg = moe.config_for(shape)
     W = moe.make_weights(t)
