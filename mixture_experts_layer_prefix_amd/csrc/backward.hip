@@ -16,10 +16,10 @@
 //              d_l[t, e]     += g_z * 2 beta / T * lse_t * p_te
 //              d_W_r = d_l^T x,  d_b_r = sum_t d_l,  d_x_router = d_l W_r
 // The grouped GEMMs of the expert backward run on the forward's GEMM kernels:
-// the input gradients on transposed weights (transpose_batched below), the
-// weight gradients in their k-segment mode on activations transposed per
-// expert into zero-padded segments (transpose_segments below, which also
-// forms the bias gradients as column sums).
+// the input gradients read the forward's weights k-major, the weight
+// gradients run in their k-segment mode on activations transposed per expert
+// into zero-padded segments (transpose_segments below, which also forms the
+// bias gradients as column sums).
 //
 // Every reduction has a fixed order, so results are deterministic.
 #include <math.h>
@@ -261,32 +261,6 @@ struct TileT {
   static constexpr int LD = TD + VEC;                // padded LDS row (16-byte aligned)
 };
 
-// out[b][c][r] = in[b][r][c] for a batch of R x C matrices; grid (C/64, R/64, B).
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_batched_kernel(const T* __restrict__ in,
-                                                                T* __restrict__ out, int R,
-                                                                int C) {
-  using TT = TileT<T>;
-  __shared__ __attribute__((aligned(16))) T tile[TD * TT::LD];
-  const int c0 = blockIdx.x * TD, r0 = blockIdx.y * TD;
-  const T* src = in + (int64_t)blockIdx.z * R * C;
-  T* dst = out + (int64_t)blockIdx.z * R * C;
-  for (int i = threadIdx.x; i < TD * TT::CPR; i += 256) {
-    const int r = i / TT::CPR, cc = (i % TT::CPR) * TT::VEC;
-    *reinterpret_cast<uint4*>(tile + r * TT::LD + cc) =
-        *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * C + c0 + cc);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < TD * TT::CPR; i += 256) {
-    const int oc = i / TT::CPR, rr = (i % TT::CPR) * TT::VEC;
-    alignas(16) T v[TT::VEC];
-#pragma unroll
-    for (int q = 0; q < TT::VEC; ++q) v[q] = tile[(rr + q) * TT::LD + oc];
-    *reinterpret_cast<uint4*>(dst + (int64_t)(c0 + oc) * R + r0 + rr) =
-        *reinterpret_cast<const uint4*>(v);
-  }
-}
-
 // Expert e's rows [off[e], off[e+1]) of in [*, C] become columns
 // [kseg[e], kseg[e+1]) of out [C, ldo]: out[c][kseg[e] + j] = in[off[e] + j][c]
 // for j < R_e and 0 in the padding up to kseg[e+1]; colsum[e][c] (if not null)
@@ -455,6 +429,25 @@ __global__ __launch_bounds__(256) void route_bwd_logits_kernel(
   }
 }
 
+// Eight consecutive values of a bf16 or fp32 row (16-byte aligned), kept
+// packed (R8) until they are widened to fp32 (unpack8).
+template <typename T>
+struct R8 {
+  uint4 v[sizeof(T) / 2];
+};
+template <typename T>
+__device__ __forceinline__ R8<T> load8(const T* p) {
+  R8<T> r;
+#pragma unroll
+  for (int i = 0; i < (int)sizeof(T) / 2; ++i) r.v[i] = reinterpret_cast<const uint4*>(p)[i];
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void unpack8(const R8<T>& r, float* f) {
+#pragma unroll
+  for (int i = 0; i < (int)sizeof(T) / 2; ++i) V16<T>::unpack(r.v[i], f + i * V16<T>::N);
+}
+
 // Partial router weight gradient over a slice of tokens:
 // part[s][e][j] = sum_{t in slice s} d_l[t][e] * x[t][j].  Workgroup: 32 experts
 // (8 groups of 4) x 256 columns (32 groups of 8); grid (ceil(d/256), ceil(N/32), S).
@@ -481,19 +474,23 @@ __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict_
     __syncthreads();
     const int nt = min(64, thi - tb);
     if (j0 < d) {
-      for (int tt = 0; tt < nt; ++tt) {
-        float xv[8];
-        if constexpr (sizeof(T) == 2) {
-          V16<uint16_t>::unpack(*reinterpret_cast<const uint4*>(x + (int64_t)(tb + tt) * d + j0), xv);
-        } else {
-          V16<float>::unpack(*reinterpret_cast<const uint4*>(x + (int64_t)(tb + tt) * d + j0), xv);
-          V16<float>::unpack(*reinterpret_cast<const uint4*>(x + (int64_t)(tb + tt) * d + j0 + 4), xv + 4);
-        }
+      // eight tokens' loads in flight before their FMAs
+      for (int t0 = 0; t0 < nt; t0 += 8) {
+        R8<T> xr[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float g = sdl[tt][eg * 4 + i];
+        for (int u = 0; u < 8; ++u)
+          if (t0 + u < nt) xr[u] = load8(x + (int64_t)(tb + t0 + u) * d + j0);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, xv[q], acc[i][q]);
+        for (int u = 0; u < 8; ++u) {
+          if (t0 + u >= nt) break;
+          float xv[8];
+          unpack8(xr[u], xv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float g = sdl[t0 + u][eg * 4 + i];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, xv[q], acc[i][q]);
+          }
         }
       }
     }
@@ -556,20 +553,23 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict_
     __syncthreads();
     const int ne = min(64, N - e0);
     if (j0 < d) {
-      for (int ee = 0; ee < ne; ++ee) {
-        float wv[8];
-        const T* wrow = wr + (int64_t)(e0 + ee) * d + j0;
-        if constexpr (sizeof(T) == 2) {
-          V16<uint16_t>::unpack(*reinterpret_cast<const uint4*>(wrow), wv);
-        } else {
-          V16<float>::unpack(*reinterpret_cast<const uint4*>(wrow), wv);
-          V16<float>::unpack(*reinterpret_cast<const uint4*>(wrow + 4), wv + 4);
-        }
+      // eight experts' loads in flight before their FMAs
+      for (int b0 = 0; b0 < ne; b0 += 8) {
+        R8<T> wraw[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float g = sdl[tg * 4 + i][ee];
+        for (int u = 0; u < 8; ++u)
+          if (b0 + u < ne) wraw[u] = load8(wr + (int64_t)(e0 + b0 + u) * d + j0);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, wv[q], acc[i][q]);
+        for (int u = 0; u < 8; ++u) {
+          if (b0 + u >= ne) break;
+          float wv[8];
+          unpack8(wraw[u], wv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float g = sdl[tg * 4 + i][b0 + u];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, wv[q], acc[i][q]);
+          }
         }
       }
     }
@@ -672,18 +672,6 @@ hipError_t launch_unpermute(int dtype, const void* d_x_perm, const int32_t* slot
     unpermute_t<float>(d_x_perm, slot_row, d_x_shared, d_x_router, d_x, T, nvec, K, s);
   else
     unpermute_t<uint16_t>(d_x_perm, slot_row, d_x_shared, d_x_router, d_x, T, nvec, K, s);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_batched(int dtype, const void* in, void* out, int B, int R, int C,
-                                    hipStream_t s) {
-  const dim3 grid(C / TD, R / TD, B);
-  if (dtype == 0)
-    hipLaunchKernelGGL(transpose_batched_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(in), static_cast<float*>(out), R, C);
-  else
-    hipLaunchKernelGGL(transpose_batched_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C);
   return hipGetLastError();
 }
 

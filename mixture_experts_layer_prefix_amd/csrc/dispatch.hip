@@ -197,6 +197,8 @@ __device__ __forceinline__ int m_tiles(int rows, int BM, int merge) {
   return (mt >= 2 && rows - (mt - 1) * BM <= merge) ? mt - 1 : mt;
 }
 
+constexpr int TL_PER_WG = 2048;   // routed tiles written per workgroup
+
 __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restrict__ offsets, int N,
                                                         int BM, int BN, int Nd, int Ts, int merge,
                                                         int4* __restrict__ list,
@@ -235,8 +237,11 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
   if (e == 0) s_base[N] = total;
   __syncthreads();
   // every thread writes tiles: find the expert owning routed tile j (the last
-  // expert whose first tile is <= j; experts without tiles share the next base)
-  for (int j = threadIdx.x; j < total; j += blockDim.x) {
+  // expert whose first tile is <= j; experts without tiles share the next base).
+  // Workgroup b writes tiles [b * TL_PER_WG, (b + 1) * TL_PER_WG); each
+  // workgroup repeats the per-expert scan above (N <= 256 values).
+  const int jend = min(total, (int)(blockIdx.x + 1) * TL_PER_WG);
+  for (int j = blockIdx.x * TL_PER_WG + threadIdx.x; j < jend; j += blockDim.x) {
     int lo = 0, hi = N - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -244,9 +249,11 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
     }
     list[shared_tiles + j] = band_tile(j - s_base[lo], s_mt[lo], ntn, BN, lo, s_o0[lo], s_o1[lo], BM);
   }
-  for (int j = threadIdx.x; j < shared_tiles; j += blockDim.x)
-    list[j] = band_tile(j, ms, ntn, BN, -1, 0, Ts, BM);
-  if (threadIdx.x == 0) count[0] = shared_tiles + total;
+  if (blockIdx.x == 0) {
+    for (int j = threadIdx.x; j < shared_tiles; j += blockDim.x)
+      list[j] = band_tile(j, ms, ntn, BN, -1, 0, Ts, BM);
+    if (threadIdx.x == 0) count[0] = shared_tiles + total;
+  }
 }
 
 }  // namespace
@@ -277,9 +284,11 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
 }
 
 hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
-                            int merge, int4* list, int32_t* count, hipStream_t s) {
-  hipLaunchKernelGGL(tile_list_kernel, dim3(1), dim3(256), 0, s, offsets, N, BM, BN, Nd, Ts, merge,
-                     list, count);
+                            int merge, int64_t max_tiles, int4* list, int32_t* count,
+                            hipStream_t s) {
+  const unsigned nwg = (unsigned)((max_tiles + TL_PER_WG - 1) / TL_PER_WG);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(nwg < 1 ? 1 : nwg), dim3(256), 0, s, offsets, N, BM,
+                     BN, Nd, Ts, merge, list, count);
   return hipGetLastError();
 }
 

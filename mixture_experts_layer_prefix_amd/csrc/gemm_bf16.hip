@@ -53,6 +53,24 @@ __device__ __forceinline__ void lds_load16(const void* g, void* l) {
 // banks (a 2-way conflict remains between r and r + 16).
 __device__ __forceinline__ int swzq(int r) { return (r >> 3) & 1; }
 
+// k-major weights (KM): a stage holds 32 k-rows of 256 bf16 (512 bytes, 32
+// chunks of 16 bytes); chunk c of k-row r sits at chunk c ^ (4 (r mod 4)).  A
+// fragment is two ds_read_b64_tr_b16: in each group of 16 lanes, result lane
+// m receives element m mod 4 of the 8 bytes addressed by source lanes m/4,
+// m/4 + 4, m/4 + 8, m/4 + 12 -- i.e. 4 consecutive k of one n column when
+// source lane 4q + u points at k-row q, columns 4u .. 4u + 3.  The 16 lanes
+// of a half-group read 4 k-rows x 8 chunks that the swizzle spreads over all
+// 64 banks.
+__device__ __forceinline__ int kswz(int r) { return 4 * (r & 3); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_lds;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  return __builtin_bit_cast(
+      bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (__attribute__((address_space(3))) bf16x4_lds*)(p)));
+}
+
 // s_barrier with a compiler memory fence: no LDS access moves across it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -119,7 +137,9 @@ constexpr int W4_CST = BN + 8;                // staged output row stride in bf1
 // WG: weight-gradient (k-segment) mode -- expert e's tile contracts over
 // columns [kseg[e], kseg[e+1]) of A [wg_rows, Kd] and W [Nd, Kd], both shared
 // by all experts; an empty segment leaves the accumulators at zero.
-template <bool GELU, bool QW, int NS, int LAY, bool WG>
+// KM: k-major weights, W_e stored [Kd, Nd] (the input gradients of the
+// backward read the forward's weights as they are).
+template <bool GELU, bool QW, int NS, int LAY, bool WG, bool KM>
 __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
   using Lay = W4Layout<LAY>;
@@ -180,6 +200,12 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       const int row = (wave * NLB + i) * 32 + (lane >> 1);
       const int lchunk = (lane & 1) ^ swzq(row);
       offB[i] = (uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 16;
+    } else if constexpr (KM) {
+      // instruction i fills k-rows 2 (w NLB + i) and + 1, 32 lanes per row;
+      // columns past Nd (partial tiles) read a valid chunk and are not stored
+      const int row = (wave * NLB + i) * 2 + (lane >> 5);
+      const int lchunk = (lane & 31) ^ kswz(row);
+      offB[i] = ((uint32_t)row * (uint32_t)Nd + (uint32_t)min(tr.n0 + lchunk * 8, Nd - 8)) * 2;
     } else {
       const int row = (wave * NLB + i) * RPI + r_in;
       const int lchunk = (lane % CH) ^ swz(row);
@@ -194,7 +220,9 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   auto issue_b = [&](int buf, int k0) {
     char* base = reinterpret_cast<char*>(lds + buf * W4_STAGE + W4_AR * BK) + wave * NLB * 1024;
 #pragma unroll
-    for (int i = 0; i < NLB; ++i) lds_load16(W + offB[i] + k0 * (QW ? 1 : 2), base + i * 1024);
+    for (int i = 0; i < NLB; ++i)
+      lds_load16(W + offB[i] + (KM ? (uint32_t)k0 * (uint32_t)Nd * 2 : k0 * (QW ? 1 : 2)),
+                 base + i * 1024);
   };
 
   const int sw = swz(lane & 31);   // the same for every fragment row this lane reads
@@ -206,6 +234,11 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   using BF = typename std::conditional<QW, uint2, bf16x8>::type;
   const int browq = (wn * WCOLS + (lane & 31)) * 32 + (lane >> 5) * 8;   // bytes (INT8)
   const int swq = swzq(lane & 31);
+  // KM: this lane's byte offset inside a stage's weight region (source role:
+  // group g = lane / 16, q = (lane mod 16) / 4, u = lane mod 4), without the
+  // half, the second read's 4 k-rows and the fragment's 32-column group
+  const int kg = lane >> 4, kq = (lane & 15) >> 2, ku = lane & 3;
+  const int kmb = (8 * (kg >> 1) + kq) * 512 + (2 * (kg & 1) + (ku >> 1)) * 16 + (ku & 1) * 8;
   bf16x8 fa0[MX], fa1[MX];
   BF fb0[NI], fb1[NI];
   f32x16 accx[EX ? NI : 1];
@@ -225,11 +258,17 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     if constexpr (EX) fa[MI] = *reinterpret_cast<const bf16x8*>(As + xrow + pc);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      if constexpr (QW)
+      if constexpr (QW) {
         fb[i] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(Bs) + browq +
                                                 i * 32 * 32 + ((kk ^ swq) * 16));
-      else
+      } else if constexpr (KM) {
+        const char* p = reinterpret_cast<const char*>(Bs) + kk * 8192 + kmb +
+                        ((((wn * WCOLS + i * 32) >> 3) ^ (4 * kq)) << 4);
+        const bf16x4 lo = lds_read_tr(p), hi = lds_read_tr(p + 2048);
+        fb[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
         fb[i] = *reinterpret_cast<const bf16x8*>(Bs + brow + i * 32 * BK + pc);
+      }
     }
   };
   auto wfrag = [&](const BF& f) -> bf16x8 {
@@ -261,18 +300,20 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
             : "v"(fb), "v"(fa[MI]));
     }
   };
-  // one half: MI*NI MFMAs interleaved with MI+NI fragment reads and `nv`
-  // direct loads
+  // one half: MI*NI MFMAs interleaved with the fragment reads (MX + NI, or
+  // MX + 2 NI with KM) and `nv` direct loads; RPS reads follow each MFMA
   auto interleave = [&](auto nv_tag) {
     constexpr int NV = decltype(nv_tag)::value;
-    constexpr int NM = MX * NI, ND = MX + NI;
+    constexpr int NM = MX * NI, ND = MX + (KM ? 2 : 1) * NI;
+    constexpr int RPS = (ND + NM - 1) / NM, NSL = (ND + RPS - 1) / RPS;
+    constexpr int VS = NSL >= NV ? NSL - NV : 0;    // first slot with a direct load
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i >= ND - NV && i < ND) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i < NSL) __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+      if (i >= VS && i < VS + NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    static_assert(ND <= NM && NV <= ND, "every read and load sits between two MFMAs");
+    static_assert(VS + NV <= NM, "every load sits between two MFMAs");
   };
 
   if (!WG || KT > 0) {
@@ -408,7 +449,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   }
 }
 
-template <bool GELU, bool QW, int NS, bool WG>
+template <bool GELU, bool QW, int NS, bool WG, bool KM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(GemmArgs a) {
   // the output tile is staged through the same LDS after the main loop
@@ -425,13 +466,13 @@ gemm_bf16_w4_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   const int rows = tr.row_end - tr.row0;
   if (rows > W4_TM)
-    w4_tile<GELU, QW, NS, 3, WG>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 3, WG, KM>(a, tr, lds, acc);
   else if (rows > 128)
-    w4_tile<GELU, QW, NS, 0, WG>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 0, WG, KM>(a, tr, lds, acc);
   else if (rows > 64)
-    w4_tile<GELU, QW, NS, 1, WG>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 1, WG, KM>(a, tr, lds, acc);
   else
-    w4_tile<GELU, QW, NS, 2, WG>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 2, WG, KM>(a, tr, lds, acc);
 }
 
 }  // namespace
@@ -444,22 +485,25 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
   const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
   if (a.kseg) {
-    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, true>), dim3(grid), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, true, false>), dim3(grid),
+                       dim3(256), 0, s, a);
+  } else if (a.wkmaj) {
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, false, true>), dim3(grid),
+                       dim3(256), 0, s, a);
   } else if (a.wscale) {
     if (gelu)
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, true, W4_NS, false>), dim3(grid), dim3(256), 0,
-                         s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, true, W4_NS, false, false>), dim3(grid),
+                         dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, true, W4_NS, false>), dim3(grid), dim3(256),
-                         0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, true, W4_NS, false, false>), dim3(grid),
+                         dim3(256), 0, s, a);
   } else {
     if (gelu)
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, false, W4_NS, false>), dim3(grid), dim3(256),
-                         0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, false, W4_NS, false, false>), dim3(grid),
+                         dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, false>), dim3(grid), dim3(256),
-                         0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, false, false>), dim3(grid),
+                         dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

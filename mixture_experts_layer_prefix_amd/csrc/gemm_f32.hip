@@ -5,7 +5,8 @@
 // throughout.  64 x 64 workgroup tiles, BK = 16 staged in LDS k-major, each
 // of the 256 threads owning a 4 x 4 block of outputs.  Used for fp32 layers,
 // which are small; the products accumulate in k order with fma.  With
-// GemmArgs::kseg set it runs the weight-gradient (k-segment) form.
+// GemmArgs::kseg set it runs the weight-gradient (k-segment) form; with
+// GemmArgs::wkmaj it reads k-major weights.
 #include "gemm_common.h"
 
 namespace moe {
@@ -53,7 +54,8 @@ __global__ __launch_bounds__(NTHR) void gemm_f32_kernel(GemmArgs a) {
       const int r = i / BK, k = i % BK;
       As[k][r] = (r < rows) ? A[(int64_t)(arow0 + r) * Kd + k0 + k] : 0.f;
       const int n = tr.n0 + r;
-      Bs[k][r] = (n < Nd) ? W[(int64_t)n * Kd + k0 + k] : 0.f;
+      Bs[k][r] = (n >= Nd) ? 0.f
+                 : a.wkmaj ? W[(int64_t)(k0 + k) * Nd + n] : W[(int64_t)n * Kd + k0 + k];
     }
     __syncthreads();
 #pragma unroll

@@ -203,7 +203,6 @@ int64_t bwd_maxw(const moe_config_t* c) {
 }
 
 struct FfnBwdWs {
-  void *w1t, *w2t, *ws1t, *ws2t;   // transposed weights
   void *dh, *dhs;                  // d_h, then d_z in place
   void *tb1, *tb2;                 // transposed activations [maxw, ldt]
   int32_t *kseg, *wr_d, *wr_f;     // routed k-segments and output-row offsets
@@ -237,10 +236,6 @@ void carve_ffn_bwd(Carver& cv, const moe_config_t* c, FfnBwdWs* w) {
   const int64_t T = c->T, N = c->n_experts, d = c->d_model, f = c->d_ff, fs = c->d_ff_shared;
   const int64_t M = T * c->top_k;
   const size_t eb = elem_bytes(c->dtype);
-  w->w1t = cv.take<void>((size_t)(N * f * d) * eb);
-  w->w2t = cv.take<void>((size_t)(N * d * f) * eb);
-  w->ws1t = fs ? cv.take<void>((size_t)(fs * d) * eb) : nullptr;
-  w->ws2t = fs ? cv.take<void>((size_t)(fs * d) * eb) : nullptr;
   w->dh = cv.take<void>((size_t)(M * f) * eb);
   w->dhs = fs ? cv.take<void>((size_t)(T * fs) * eb) : nullptr;
   const int64_t ldt = bwd_ldt(c), maxw = bwd_maxw(c);
@@ -429,8 +424,8 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
     hipError_t e = hipSuccess;
     if (path != PATH_SKINNY) {
       const int merge = path == PATH_TILED ? moe::gemm_bf16_merge_rows() : 0;
-      e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.list[list],
-                                fw.count + list, s);
+      e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.bound[list],
+                                fw.list[list], fw.count + list, s);
       if (e != hipSuccess) return hip_status(e, "tile list launch");
       g.tile_list = fw.list[list];
       g.tile_count = fw.count + list;
@@ -574,7 +569,7 @@ std::string check_train(const moe_config_t* c, int* code) {
 int bwd_gemm(const moe_config_t* c, moe::GemmArgs g, int4* list, int32_t* count, int64_t bound,
              const int32_t* offs, int Nr, int Ts, hipStream_t s, const char* what) {
   hipError_t e = moe::launch_tile_list(offs, Nr, bwd_bm(c), bwd_bn(c), g.Nd, Ts, bwd_merge(c),
-                                       list, count, s);
+                                       bound, list, count, s);
   if (e != hipSuccess) return hip_status(e, "tile list launch");
   g.tile_list = list;
   g.tile_count = count;
@@ -592,7 +587,8 @@ int do_combine_bwd(const moe_config_t* c, const void* d_out, const void* y_perm,
 }
 
 // Expert FFN backward (routed experts, then the shared one):
-//   d_h = d_y . W2 (on W2^T), d_z = d_h * GELU'(z), d_x_perm = d_z . W1 (on W1^T),
+//   d_h = d_y . W2, d_z = d_h * GELU'(z), d_x_perm = d_z . W1 (the GEMMs read
+//   the forward's weights k-major),
 //   dW2_e = d_y_e^T h_e, db2_e = column sums of d_y_e, dW1_e = d_z_e^T x_e,
 //   db1_e = column sums of d_z_e (weight gradients in the k-segment mode).
 int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
@@ -611,11 +607,10 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
     if (r != MOE_OK) return r;                        \
   } while (0)
   MOE_TRY(moe::launch_seg_offsets(offsets, N, d, f, fw.kseg, fw.wr_d, fw.wr_f, s), "offsets launch");
-  MOE_TRY(moe::launch_transpose_batched(dt, w->w2, fw.w2t, N, d, f, s), "transpose launch");
-  MOE_TRY(moe::launch_transpose_batched(dt, w->w1, fw.w1t, N, f, d, s), "transpose launch");
   moe::GemmArgs a{};
-  a.A = d_y_perm;                       // d_h [M, f] = d_y [M, d] . (W2^T)^T
-  a.W = fw.w2t;
+  a.A = d_y_perm;                       // d_h [M, f] = d_y [M, d] . W2_e [d, f]
+  a.W = w->w2;
+  a.wkmaj = true;
   a.C = fw.dh;
   a.offsets = offsets;
   a.Kd = d;
@@ -624,8 +619,8 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   r = bwd_gemm(c, a, fw.list[0], fw.count + 0, fw.bound[0], offsets, N, 0, s, "dgrad GEMM launch");
   if (r != MOE_OK) return r;
   MOE_TRY(moe::launch_gelu_bwd(dt, z, fw.dh, offsets + N, M, f, s), "GELU backward launch");
-  a.A = fw.dh;                          // d_x_perm [M, d] = d_z [M, f] . (W1^T)^T
-  a.W = fw.w1t;
+  a.A = fw.dh;                          // d_x_perm [M, d] = d_z [M, f] . W1_e [f, d]
+  a.W = w->w1;
   a.C = d_x_perm;
   a.Kd = f;
   a.Nd = d;
@@ -662,11 +657,10 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   // shared expert: upstream gradient d_out for every token, weight 1
   MOE_TRY(moe::launch_dense_offsets(T, d, fs, fw.off2, fw.kseg2, fw.wr2_d, fw.wr2_s, s),
           "offsets launch");
-  MOE_TRY(moe::launch_transpose_batched(dt, w->ws2, fw.ws2t, 1, d, fs, s), "transpose launch");
-  MOE_TRY(moe::launch_transpose_batched(dt, w->ws1, fw.ws1t, 1, fs, d, s), "transpose launch");
   moe::GemmArgs sa{};
-  sa.As = d_out;                        // d_hs [T, fs]
-  sa.Ws = fw.ws2t;
+  sa.As = d_out;                        // d_hs [T, fs] = d_out . Ws2 [d, fs]
+  sa.Ws = w->ws2;
+  sa.wkmaj = true;
   sa.Cs = fw.dhs;
   sa.Ts = T;
   sa.Kd = d;
@@ -674,8 +668,8 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   r = bwd_gemm(c, sa, fw.list[4], fw.count + 4, fw.bound[4], nullptr, 0, T, s, "dgrad GEMM launch");
   if (r != MOE_OK) return r;
   MOE_TRY(moe::launch_gelu_bwd(dt, zs, fw.dhs, nullptr, T, fs, s), "GELU backward launch");
-  sa.As = fw.dhs;                       // d_x_shared [T, d]
-  sa.Ws = fw.ws1t;
+  sa.As = fw.dhs;                       // d_x_shared [T, d] = d_zs . Ws1 [fs, d]
+  sa.Ws = w->ws1;
   sa.Cs = d_x_shared;
   sa.Kd = fs;
   sa.Nd = d;

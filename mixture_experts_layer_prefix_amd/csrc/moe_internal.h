@@ -108,8 +108,10 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
 // receives the number of tiles.  A block's last remainder of at most `merge`
 // rows (when the block has a full tile) is folded into its last full tile,
 // which then spans up to BM + merge rows.
+// max_tiles bounds the list (it sizes the launch: one workgroup per 2048 tiles).
 hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
-                            int merge, int4* list, int32_t* count, hipStream_t s);
+                            int merge, int64_t max_tiles, int4* list, int32_t* count,
+                            hipStream_t s);
 inline int max_m_tiles(int64_t M_max, int N, int BM) {
   return static_cast<int>((M_max + BM - 1) / BM) + N;
 }
@@ -141,6 +143,9 @@ struct GemmArgs {
   // Kd), writing C rows e * wg_rows + i; kseg entries are multiples of 32.
   const int32_t* kseg;
   int wg_rows;
+  // k-major weights (tiled and fp32 kernels): W_e is stored [Kd, Nd], Nd
+  // contiguous, instead of [Nd, Kd] (the backward's input gradients).
+  bool wkmaj;
 };
 
 // Prefill-shaped grouped GEMM (bf16 MFMA): tiles of gemm_bf16_bm() x
@@ -208,9 +213,6 @@ hipError_t launch_combine_bwd(int dtype, const void* d_out, const void* y_perm,
 hipError_t launch_unpermute(int dtype, const void* d_x_perm, const int32_t* slot_row,
                             const void* d_x_shared, const float* d_x_router, void* d_x, int T,
                             int d, int K, hipStream_t s);
-// out[b] = in[b]^T for B matrices of R x C (R, C multiples of 64).
-hipError_t launch_transpose_batched(int dtype, const void* in, void* out, int B, int R, int C,
-                                    hipStream_t s);
 // Rows of segment e of in [*, C] -> columns [kseg[e], kseg[e+1]) of out
 // [C, ldo], zero padded; colsum [nseg, C] (or null) = per-segment column sums.
 hipError_t launch_transpose_segments(int dtype, const void* in, const int32_t* off,
