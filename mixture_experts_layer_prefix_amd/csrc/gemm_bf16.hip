@@ -100,34 +100,62 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // before it every lane has its own loads of the next stage landed and its
 // reads of the current stage done, so after it the next stage is whole and
 // the current one may be refilled.
-template <int L>
-struct W4Layout;
-template <>
-struct W4Layout<0> {   // 128 < R <= 256
-  static constexpr int WN = 2, MI = 4, NI = 4, AROWS = 256;
-  static constexpr bool EXTRA = false;
-};
-template <>
-struct W4Layout<1> {   // 64 < R <= 128
-  static constexpr int WN = 4, MI = 4, NI = 2, AROWS = 128;
-  static constexpr bool EXTRA = false;
-};
-template <>
-struct W4Layout<2> {   // R <= 64
-  static constexpr int WN = 4, MI = 2, NI = 2, AROWS = 64;
-  static constexpr bool EXTRA = false;
-};
-template <>
-struct W4Layout<3> {   // 256 < R <= 320
-  static constexpr int WN = 2, MI = 4, NI = 4, AROWS = 320;
-  static constexpr bool EXTRA = true;
-};
-
+//
+// Eight-wavefront workgroups (layouts 4, 5, 7; two wavefronts per SIMD, 128
+// accumulators each) serve the backward's routed GEMMs when experts have few
+// rows: one workgroup of four wavefronts per CU streams direct-to-LDS loads
+// at about 4.9 TB/s over the chip whatever the pipeline depth, eight
+// wavefronts at about 5.7 TB/s (a plain streaming probe), and a second
+// wavefront per SIMD overlaps the many short tiles of the weight gradients.
+//   256 < R <= 320: 2 x 4 wavefronts of 128 x 64 plus 32 folded rows each,
+//   128 < R <= 256: 2 x 4 wavefronts of 128 x 64,
+//   R <= 128:       2 x 4 wavefronts of  64 x 64.
 constexpr int W4_TM = 256;
 constexpr int W4_MERGE = 64;                  // remainder rows folded into the previous tile
 constexpr int W4_AR = W4_TM + W4_MERGE;       // A rows held per LDS stage
 constexpr int W4_STAGE = (W4_AR + BN) * BK;   // bf16 elements per LDS stage (36 KiB)
 constexpr int W4_CST = BN + 8;                // staged output row stride in bf16 (528 bytes)
+constexpr int W8_AR = 384;                    // eight wavefronts, folded tiles: 3 loads per wave
+constexpr int W8_STAGE = (W8_AR + BN) * BK;   // 40 KiB: four stages fill the 160 KiB of LDS
+
+template <int L>
+struct W4Layout;
+template <>
+struct W4Layout<0> {   // 128 < R <= 256
+  static constexpr int NW = 4, WN = 2, MI = 4, NI = 4, AROWS = 256, AR = W4_AR;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<1> {   // 64 < R <= 128
+  static constexpr int NW = 4, WN = 4, MI = 4, NI = 2, AROWS = 128, AR = W4_AR;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<2> {   // R <= 64
+  static constexpr int NW = 4, WN = 4, MI = 2, NI = 2, AROWS = 64, AR = W4_AR;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<3> {   // 256 < R <= 320
+  static constexpr int NW = 4, WN = 2, MI = 4, NI = 4, AROWS = 320, AR = W4_AR;
+  static constexpr bool EXTRA = true;
+};
+template <>
+struct W4Layout<4> {   // eight wavefronts, 128 < R <= 256
+  static constexpr int NW = 8, WN = 4, MI = 4, NI = 2, AROWS = 256, AR = W4_AR;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<5> {   // eight wavefronts, R <= 128
+  static constexpr int NW = 8, WN = 4, MI = 2, NI = 2, AROWS = 128, AR = W4_AR;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<7> {   // eight wavefronts, 256 < R <= 320 (384 A rows loaded, the last clamped)
+  static constexpr int NW = 8, WN = 4, MI = 4, NI = 2, AROWS = W8_AR, AR = W8_AR;
+  static constexpr bool EXTRA = true;
+};
+
 
 // QW: the routed weights are INT8 codes with one fp32 scale per output row
 // (a.wscale); launches with INT8 weights carry no shared-problem tiles.  The
@@ -145,10 +173,12 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   using Lay = W4Layout<LAY>;
   constexpr int MI = Lay::MI, NI = Lay::NI, WN = Lay::WN;
   constexpr bool EX = Lay::EXTRA;
-  constexpr int NLA = Lay::AROWS / RPI / 4;   // direct loads per wavefront per stage, A rows
+  constexpr int NW = Lay::NW;
+  constexpr int NLA = Lay::AROWS / RPI / NW;   // direct loads per wavefront per stage, A rows
   // W rows: 16 rows of 64 bytes per wave instruction (bf16), 32 rows of 32
   // bytes (INT8)
-  constexpr int NLB = QW ? W4_TM / 32 / 4 : W4_TM / RPI / 4;
+  constexpr int NLB = QW ? W4_TM / 32 / NW : W4_TM / RPI / NW;
+  static_assert(NLA * RPI * NW == Lay::AROWS && NLB > 0, "loads split evenly over the waves");
   constexpr int NLS = NLA + NLB;
   const int Kd = a.Kd, Nd = a.Nd;
   const uint16_t* A;
@@ -212,13 +242,14 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       offB[i] = ((uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8 + kbeg) * 2;
     }
   }
+  constexpr int STG = (Lay::AR + BN) * BK;   // bf16 elements per LDS stage
   auto issue_a = [&](int buf, int k0) {
-    uint16_t* base = lds + buf * W4_STAGE + wave * NLA * RPI * BK;
+    uint16_t* base = lds + buf * STG + wave * NLA * RPI * BK;
 #pragma unroll
     for (int i = 0; i < NLA; ++i) lds_load16(A + offA[i] + k0, base + i * RPI * BK);
   };
   auto issue_b = [&](int buf, int k0) {
-    char* base = reinterpret_cast<char*>(lds + buf * W4_STAGE + W4_AR * BK) + wave * NLB * 1024;
+    char* base = reinterpret_cast<char*>(lds + buf * STG + Lay::AR * BK) + wave * NLB * 1024;
 #pragma unroll
     for (int i = 0; i < NLB; ++i)
       lds_load16(W + offB[i] + (KM ? (uint32_t)k0 * (uint32_t)Nd * 2 : k0 * (QW ? 1 : 2)),
@@ -249,8 +280,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       for (int v = 0; v < 16; ++v) accx[i][v] = 0.f;
   }
   auto read_half = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int kk) {
-    const uint16_t* As = lds + buf * W4_STAGE;
-    const uint16_t* Bs = As + W4_AR * BK;
+    const uint16_t* As = lds + buf * STG;
+    const uint16_t* Bs = As + Lay::AR * BK;
     const int pc = ((kk * 2 + (lane >> 5)) ^ sw) * 8;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -398,11 +429,11 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     }
   }
   __syncthreads();
-  // 256 threads x 16 bytes = 8 rows of 256 columns per pass
+  // 64 NW threads x 16 bytes = 2 NW rows of 256 columns per pass
   const int cc = (threadIdx.x & 31) * 8;
   const int ncol = tr.n0 + cc;
   const int nrow = min(rows, W4_TM);
-  for (int ml = threadIdx.x >> 5; ml < nrow; ml += 8)
+  for (int ml = threadIdx.x >> 5; ml < nrow; ml += 2 * NW)
     if (ncol < Nd)
       *reinterpret_cast<uint4*>(C + (int64_t)(tr.row0 + ml) * Nd + ncol) =
           *reinterpret_cast<const uint4*>(lds + ml * W4_CST + cc);
@@ -410,8 +441,11 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     // the folded remainder: rows 256 .. R-1, staged as LDS rows 0 .. 63.
     // 24 wait states between the last MFMA writing accx and its first VALU
     // read (the tie to accx keeps the pad after those MFMAs)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+v"(accx[0]), "+v"(accx[1]), "+v"(accx[2]), "+v"(accx[3]));
+    if constexpr (NI == 4)
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+v"(accx[0]), "+v"(accx[1]), "+v"(accx[2]), "+v"(accx[3]));
+    else
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(accx[0]), "+v"(accx[1]));
     __syncthreads();
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
@@ -442,7 +476,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       }
     }
     __syncthreads();
-    for (int ml = threadIdx.x >> 5; ml < rows - W4_TM; ml += 8)
+    for (int ml = threadIdx.x >> 5; ml < rows - W4_TM; ml += 2 * NW)
       if (ncol < Nd)
         *reinterpret_cast<uint4*>(C + (int64_t)(tr.row0 + W4_TM + ml) * Nd + ncol) =
             *reinterpret_cast<const uint4*>(lds + ml * W4_CST + cc);
@@ -475,6 +509,41 @@ gemm_bf16_w4_kernel(GemmArgs a) {
     w4_tile<GELU, QW, NS, 2, WG, KM>(a, tr, lds, acc);
 }
 
+// The same tiles with eight wavefronts (two per SIMD, at most 256 registers
+// each; only acc[0..1][0..3] are live).
+template <bool GELU, bool QW, int NS, bool WG, bool KM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+gemm_bf16_w8_kernel(GemmArgs a) {
+  constexpr int LDS_ELEMS = NS * W8_STAGE > W4_TM * W4_CST ? NS * W8_STAGE : W4_TM * W4_CST;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+  const TileRef tr = map_tile(a);
+  if (!tr.valid) return;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int rows = tr.row_end - tr.row0;
+  if (rows > W4_TM)
+    w4_tile<GELU, QW, NS, 7, WG, KM>(a, tr, lds, acc);
+  else if (rows > 128)
+    w4_tile<GELU, QW, NS, 4, WG, KM>(a, tr, lds, acc);
+  else
+    w4_tile<GELU, QW, NS, 5, WG, KM>(a, tr, lds, acc);
+}
+
+template <bool GELU, bool QW, bool WG, bool KM>
+void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
+  if (a.waves8)
+    hipLaunchKernelGGL((gemm_bf16_w8_kernel<GELU, QW, W4_NS, WG, KM>), dim3(grid), dim3(512), 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<GELU, QW, W4_NS, WG, KM>), dim3(grid), dim3(256), 0, s,
+                       a);
+}
+
 }  // namespace
 
 int gemm_bf16_bm() { return W4_TM; }
@@ -484,27 +553,16 @@ int gemm_bf16_merge_rows() { return W4_MERGE; }
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
   const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
-  if (a.kseg) {
-    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, true, false>), dim3(grid),
-                       dim3(256), 0, s, a);
-  } else if (a.wkmaj) {
-    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, false, true>), dim3(grid),
-                       dim3(256), 0, s, a);
-  } else if (a.wscale) {
-    if (gelu)
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, true, W4_NS, false, false>), dim3(grid),
-                         dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, true, W4_NS, false, false>), dim3(grid),
-                         dim3(256), 0, s, a);
-  } else {
-    if (gelu)
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<true, false, W4_NS, false, false>), dim3(grid),
-                         dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_w4_kernel<false, false, W4_NS, false, false>), dim3(grid),
-                         dim3(256), 0, s, a);
-  }
+  if (a.kseg)
+    launch_w<false, false, true, false>(a, grid, s);
+  else if (a.wkmaj)
+    launch_w<false, false, false, true>(a, grid, s);
+  else if (a.wscale)
+    gelu ? launch_w<true, true, false, false>(a, grid, s)
+         : launch_w<false, true, false, false>(a, grid, s);
+  else
+    gelu ? launch_w<true, false, false, false>(a, grid, s)
+         : launch_w<false, false, false, false>(a, grid, s);
   return hipGetLastError();
 }
 

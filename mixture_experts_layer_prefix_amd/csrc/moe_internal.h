@@ -146,6 +146,9 @@ struct GemmArgs {
   // k-major weights (tiled and fp32 kernels): W_e is stored [Kd, Nd], Nd
   // contiguous, instead of [Nd, Kd] (the backward's input gradients).
   bool wkmaj;
+  // tiled kernel: eight-wavefront workgroups (launches bound by the weight
+  // stream: few rows per expert, or short weight-gradient k-segments)
+  bool waves8;
 };
 
 // Prefill-shaped grouped GEMM (bf16 MFMA): tiles of gemm_bf16_bm() x

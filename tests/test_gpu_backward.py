@@ -34,6 +34,8 @@ CASES = {
     "fine_shared_wide": C.DEEPSEEK_FINE.with_(T=200, d_model=192, d_ff=128, n_experts=32,
                                               top_k=4, d_ff_shared=320),
     "decode": C.DECODE.with_(T=8, d_model=256, d_ff=512, n_experts=16),
+    # few rows per expert (eight-wavefront tiles) and 320-row weight-gradient tiles
+    "folded_waves8": C.MIXTRAL_PREFILL.with_(T=256, d_model=320, d_ff=256, n_experts=16),
 }
 
 
