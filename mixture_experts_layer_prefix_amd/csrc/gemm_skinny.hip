@@ -13,6 +13,12 @@
 // per 16 outputs; experts with no rows exit at once.  Expert index E stands
 // for the dense shared problem when one is present (its weights are always
 // in the activation dtype; launches with INT8 routed weights carry none).
+// KS = 4 (long reductions, Kd > Nd): a workgroup takes 16 outputs and its
+// four wavefronts split the model dimension in quarters; the four partial
+// sums are added in wavefront order through LDS.  Four times as many,
+// shorter workgroups keep every CU streaming: with one wavefront per 16
+// outputs the decode shape's second GEMM has about 4 workgroups per CU of
+// the 5 that fit, so some CUs idle while the rest run their long loops.
 #include "gemm_common.h"
 
 namespace moe {
@@ -31,7 +37,7 @@ constexpr int U = 8;                    // k-steps of 32 in flight
 // with the first and second 8; the activations use the same permutation of
 // k inside the block (the dot product does not depend on it).  The row
 // scale multiplies the result before the bias.
-template <bool GELU, bool QW>
+template <bool GELU, bool QW, int KS>
 __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   const int e = blockIdx.y;
   const int Kd = a.Kd, Nd = a.Nd;
@@ -56,8 +62,34 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   }
   if (r1 <= r0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * NPB + wave * NPW;
+  // KS > 1: one n0 for the whole workgroup, so the exit below is uniform
+  // and every wavefront reaches the barriers of the reduction
+  const int n0 = KS == 1 ? blockIdx.x * NPB + wave * NPW : blockIdx.x * NPW;
   if (n0 >= Nd) return;
+  int kb = 0, ke = Kd;   // this wavefront's part of the model dimension
+  if constexpr (KS > 1) {
+    const int kq = ((Kd + KS - 1) / KS + 63) / 64 * 64;
+    kb = min(Kd, wave * kq);
+    ke = min(Kd, kb + kq);
+  }
+  __shared__ f32x4 red[KS][64];
+  // the KS partial sums of a row group in wavefront order; wavefront 0
+  // stores the result
+  auto reduce = [&](f32x4& acc) -> bool {
+    if constexpr (KS == 1) {
+      return true;
+    } else {
+      red[wave][lane] = acc;
+      __syncthreads();
+      if (wave == 0) {
+        acc = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) acc += red[w][lane];
+      }
+      __syncthreads();
+      return wave == 0;
+    }
+  };
   const int kq = (lane >> 4) * 8;      // this lane's 8-element slice of each 32-wide k-step
   const uint16_t* wrow = W + (int64_t)(n0 + (lane & 15)) * Kd + kq;
   const float bv = bias ? bf16_to_f32(bias[n0 + (lane & 15)]) : 0.f;
@@ -71,8 +103,8 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
       const bool arow_ok = ar < r1;
       const uint16_t* arow = A + (int64_t)(arow_ok ? ar : r0) * Kd + (lane >> 4) * 16;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < Kd; k0 += 64 * U8) {
-        const int nb = min(U8, (Kd - k0) / 64);
+      for (int k0 = kb; k0 < ke; k0 += 64 * U8) {
+        const int nb = min(U8, (ke - k0) / 64);
         uint4 wv[U8], av[U8][2];
 #pragma unroll
         for (int u = 0; u < U8; ++u)
@@ -95,6 +127,7 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
                                                           acc, 0, 0, 0);
           }
       }
+      if (!reduce(acc)) continue;
       const int col = n0 + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -114,8 +147,8 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
     const bool arow_ok = ar < r1;
     const uint16_t* arow = A + (int64_t)(arow_ok ? ar : r0) * Kd + kq;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int k0 = 0;
-    for (; k0 + 32 * U <= Kd; k0 += 32 * U) {
+    int k0 = kb;
+    for (; k0 + 32 * U <= ke; k0 += 32 * U) {
       uint4 wv[U], av[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) wv[u] = *reinterpret_cast<const uint4*>(wrow + k0 + u * 32);
@@ -130,13 +163,14 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
                                                       __builtin_bit_cast(bf16x8, wv[u]), acc, 0,
                                                       0, 0);
     }
-    for (; k0 < Kd; k0 += 32) {
+    for (; k0 < ke; k0 += 32) {
       uint4 wv = *reinterpret_cast<const uint4*>(wrow + k0);
       uint4 av = *reinterpret_cast<const uint4*>(arow + k0);
       if (!arow_ok) av = make_uint4(0, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                     __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
     }
+    if (!reduce(acc)) continue;
     // 16x16 accumulator layout: element v of lane l holds row (l/16)*4 + v, column l%16.
     const int col = n0 + (lane & 15);
 #pragma unroll
@@ -157,17 +191,28 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_
                                    hipStream_t s) {
   const int E = a.E + (a.As ? 1 : 0);
   if (E == 0) return hipSuccess;
-  dim3 grid((a.Nd + NPB - 1) / NPB, E);
-  if (a.wscale) {
-    if (gelu)
-      hipLaunchKernelGGL((gemm_skinny_kernel<true, true>), grid, dim3(NTHR), 0, s, a);
+  // long reductions: the four wavefronts of a workgroup split the model dimension
+  const bool ks = a.Kd > a.Nd && a.Kd >= 4096;
+  const dim3 grid(ks ? (a.Nd + NPW - 1) / NPW : (a.Nd + NPB - 1) / NPB, E);
+  if (ks) {
+    if (a.wscale && gelu)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, true, 4>), grid, dim3(NTHR), 0, s, a);
+    else if (a.wscale)
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, true, 4>), grid, dim3(NTHR), 0, s, a);
+    else if (gelu)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, false, 4>), grid, dim3(NTHR), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<false, true>), grid, dim3(NTHR), 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, false, 4>), grid, dim3(NTHR), 0, s, a);
+  } else if (a.wscale) {
+    if (gelu)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, true, 1>), grid, dim3(NTHR), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, true, 1>), grid, dim3(NTHR), 0, s, a);
   } else {
     if (gelu)
-      hipLaunchKernelGGL((gemm_skinny_kernel<true, false>), grid, dim3(NTHR), 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, false, 1>), grid, dim3(NTHR), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_skinny_kernel<false, false>), grid, dim3(NTHR), 0, s, a);
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, false, 1>), grid, dim3(NTHR), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -73,6 +73,8 @@ CASES = {
                                                  top_k=4, d_ff_shared=320, weight_quant="int8"),
     "skinny_decode_w8": C.DECODE.with_(T=8, d_model=256, d_ff=512, n_experts=16,
                                        weight_quant="int8"),
+    "skinny_ksplit_w8": C.DECODE.with_(T=12, d_model=256, d_ff=4096, n_experts=16,
+                                       weight_quant="int8"),
     "skinny_shared_w8": C.DEEPSEEK_FINE.with_(T=6, d_model=128, d_ff=192, n_experts=64, top_k=8,
                                               d_ff_shared=128, weight_quant="int8"),
 }

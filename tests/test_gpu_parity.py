@@ -34,6 +34,8 @@ CASES = {
     "tiled_shared_unfused": C.DEEPSEEK_FINE.with_(T=200, d_model=192, d_ff=128, n_experts=32,
                                                   top_k=4, d_ff_shared=320),
     "skinny_decode": C.DECODE.with_(T=8, d_model=256, d_ff=512, n_experts=16),
+    # second GEMM with Kd = 4096 > Nd: the workgroup's four wavefronts split Kd
+    "skinny_ksplit": C.DECODE.with_(T=12, d_model=256, d_ff=4096, n_experts=16),
     "skinny_shared_unfused": C.DEEPSEEK_FINE.with_(T=6, d_model=128, d_ff=192, n_experts=64,
                                                    top_k=8, d_ff_shared=128),
     "skinny_shared_fused": C.DEEPSEEK_FINE.with_(T=5, d_model=128, d_ff=128, n_experts=64,
@@ -124,8 +126,11 @@ def test_all_tokens_one_expert_with_capacity():
     assert (g["out"][100:] == 0).all()
 
 
-def test_skinny_expert_with_more_than_16_rows():
-    shape = C.DECODE.with_(T=40, d_model=128, d_ff=256, n_experts=8, top_k=1)
+@pytest.mark.parametrize("d_ff", [256, 4096])
+def test_skinny_expert_with_more_than_16_rows(d_ff):
+    # d_ff = 4096: the second GEMM splits Kd over the wavefronts, with a
+    # reduction per 16-row group
+    shape = C.DECODE.with_(T=40, d_model=128, d_ff=d_ff, n_experts=8, top_k=1)
     inp = inputs.make_inputs(shape)
     off = np.zeros(8, np.float32)
     off[0] = 1e4
