@@ -65,6 +65,10 @@ CASES = {
     "tiled_ragged_w8": C.MIXTRAL_PREFILL.with_(T=300, d_model=256, d_ff=384, weight_quant="int8"),
     "tiled_bm256_w8": C.MIXTRAL_PREFILL.with_(T=1000, d_model=256, d_ff=384, n_experts=4,
                                               weight_quant="int8"),
+    # 290 rows per expert (a folded 320-row tile) and Kd = 64 (two k-steps,
+    # one pair of INT8 code rows)
+    "folded_k64_w8": C.MIXTRAL_PREFILL.with_(T=290, d_model=64, d_ff=192, n_experts=2,
+                                             weight_quant="int8"),
     "capacity_aux_w8": C.SWITCH_CAPACITY.with_(T=512, d_model=128, d_ff=256, n_experts=16,
                                                weight_quant="int8"),
     "fine_shared_w8": C.DEEPSEEK_FINE.with_(T=256, d_model=256, d_ff=128, n_experts=32, top_k=4,
