@@ -161,10 +161,11 @@ struct W4Layout<7> {   // eight wavefronts, 256 < R <= 320 (384 A rows loaded, t
 
 
 // QW: the routed weights are INT8 codes with one fp32 scale per output row
-// (a.wscale); launches with INT8 weights carry no shared-problem tiles.  The
-// codes travel to LDS as bytes (half the bytes of bf16), each fragment is
-// widened to bf16 in registers (exact: |q| <= 127) just before its MFMAs,
-// and the epilogue multiplies by the row scale before the bias.
+// (a.wscale); the shared problem's tiles keep bf16 weights and take the
+// kernel's bf16 path.  The codes travel to LDS as bytes (half the bytes of
+// bf16), each fragment is widened to bf16 in registers (exact: |q| <= 127)
+// just before its MFMAs, and the epilogue multiplies by the row scale before
+// the bias.
 // WG: weight-gradient (k-segment) mode -- expert e's tile contracts over
 // columns [kseg[e], kseg[e+1]) of A [wg_rows, Kd] and W [Nd, Kd], both shared
 // by all experts; an empty segment leaves the accumulators at zero.
@@ -528,6 +529,21 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   }
 }
 
+// Four-wavefront tile: the wave arrangement from the tile's row count.
+template <bool GELU, bool QW, int NS, bool WG, bool KM>
+__device__ __forceinline__ void w4_rows(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
+                                        f32x16 (&acc)[4][4]) {
+  const int rows = tr.row_end - tr.row0;
+  if (rows > W4_TM)
+    w4_tile<GELU, QW, NS, 3, WG, KM>(a, tr, lds, acc);
+  else if (rows > 128)
+    w4_tile<GELU, QW, NS, 0, WG, KM>(a, tr, lds, acc);
+  else if (rows > 64)
+    w4_tile<GELU, QW, NS, 1, WG, KM>(a, tr, lds, acc);
+  else
+    w4_tile<GELU, QW, NS, 2, WG, KM>(a, tr, lds, acc);
+}
+
 template <bool GELU, bool QW, int NS, bool WG, bool KM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(GemmArgs a) {
@@ -543,15 +559,10 @@ gemm_bf16_w4_kernel(GemmArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  const int rows = tr.row_end - tr.row0;
-  if (rows > W4_TM)
-    w4_tile<GELU, QW, NS, 3, WG, KM>(a, tr, lds, acc);
-  else if (rows > 128)
-    w4_tile<GELU, QW, NS, 0, WG, KM>(a, tr, lds, acc);
-  else if (rows > 64)
-    w4_tile<GELU, QW, NS, 1, WG, KM>(a, tr, lds, acc);
+  if (QW && tr.shared)
+    w4_rows<GELU, false, NS, WG, KM>(a, tr, lds, acc);
   else
-    w4_tile<GELU, QW, NS, 2, WG, KM>(a, tr, lds, acc);
+    w4_rows<GELU, QW, NS, WG, KM>(a, tr, lds, acc);
 }
 
 // The same tiles with eight wavefronts (two per SIMD, at most 256 registers
@@ -579,14 +590,18 @@ gemm_bf16_w8_kernel(GemmArgs a) {
     w4_tile<GELU, QW, NS, 5, WG, KM>(a, tr, lds, acc);
 }
 
+// Eight wavefronts serve the backward's GEMMs, which never have INT8 weights.
 template <bool GELU, bool QW, bool WG, bool KM>
 void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
-  if (a.waves8)
-    hipLaunchKernelGGL((gemm_bf16_w8_kernel<GELU, QW, W4_NS, WG, KM>), dim3(grid), dim3(512), 0, s,
-                       a);
-  else
-    hipLaunchKernelGGL((gemm_bf16_w4_kernel<GELU, QW, W4_NS, WG, KM>), dim3(grid), dim3(256), 0, s,
-                       a);
+  if constexpr (!QW) {
+    if (a.waves8) {
+      hipLaunchKernelGGL((gemm_bf16_w8_kernel<GELU, false, W4_NS, WG, KM>), dim3(grid), dim3(512),
+                         0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_w4_kernel<GELU, QW, W4_NS, WG, KM>), dim3(grid), dim3(256), 0, s,
+                     a);
 }
 
 }  // namespace

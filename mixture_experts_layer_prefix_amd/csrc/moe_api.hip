@@ -72,7 +72,9 @@ int gemm_bn(const moe_config_t* c) {
   return gemm_path(c) == PATH_F32 ? moe::gemm_f32_bn() : moe::gemm_bf16_bn();
 }
 // The shared expert rides in the routed launches when its width matches.
-// (Not with INT8 routed weights: the shared expert keeps bf16 weights.)
+// Its weights stay bf16 under INT8 routed weights: the tiled kernel runs the
+// shared tiles through its bf16 path, the decode kernel leaves them to
+// launches of their own.
 // Few rows per expert (at most 320 on average): the backward's routed GEMMs
 // run eight-wavefront workgroups (measured on the same GPU: the Switch-shaped
 // backward 7% and the DeepSeek-shaped one 3.5% faster, from the
@@ -83,7 +85,8 @@ bool weight_bound(const moe_config_t* c) {
 }
 
 bool fuse_shared(const moe_config_t* c) {
-  return c->d_ff_shared > 0 && c->d_ff_shared == c->d_ff && c->weight_quant == MOE_WQ_NONE;
+  return c->d_ff_shared > 0 && c->d_ff_shared == c->d_ff &&
+         (c->weight_quant == MOE_WQ_NONE || gemm_path(c) == PATH_TILED);
 }
 
 struct Carver {
