@@ -83,10 +83,13 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 //                   more rows x 128 columns held in ordinary VGPRs: the tile
 //                   list folds a remainder of up to 64 rows into an expert's
 //                   last full tile, which streams the weight rows anyway,
-//   128 < R <= 256: 2 x 2 wavefronts of 128 x 128 (4 x 4 MFMA tiles of 32 x 32),
-//   64 < R <= 128:  1 x 4 wavefronts of 128 x 64,
+//   192 < R <= 256: 2 x 2 wavefronts of 128 x 128 (4 x 4 MFMA tiles of 32 x 32),
+//   128 < R <= 192: 2 x 2 wavefronts of  96 x 128,
+//   96 < R <= 128:  1 x 4 wavefronts of 128 x 64,
+//   64 < R <= 96:   1 x 4 wavefronts of  96 x 64 (128 A rows loaded),
 //   R <= 64:        1 x 4 wavefronts of  64 x 64;
-// A rows past the arrangement's height are neither loaded nor multiplied.
+// A rows past the arrangement's height are neither loaded nor multiplied, so
+// a tile multiplies fewer than 32 rows past its end (fewer than 64 below 64).
 // The loads of this kernel run at the L2's pace (an expert's weight panel
 // is streamed once per m-tile), so a separate tile for a short remainder
 // would cost nearly as much as a full one.
@@ -142,6 +145,16 @@ template <>
 struct W4Layout<3> {   // 256 < R <= 320
   static constexpr int NW = 4, WN = 2, MI = 4, NI = 4, AROWS = 320, AR = W4_AR;
   static constexpr bool EXTRA = true;
+};
+template <>
+struct W4Layout<8> {   // 128 < R <= 192
+  static constexpr int NW = 4, WN = 2, MI = 3, NI = 4, AROWS = 192, AR = W4_AR;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<9> {   // 64 < R <= 96 (the load split needs a multiple of 64 A rows)
+  static constexpr int NW = 4, WN = 4, MI = 3, NI = 2, AROWS = 128, AR = W4_AR;
+  static constexpr bool EXTRA = false;
 };
 template <>
 struct W4Layout<4> {   // eight wavefronts, 128 < R <= 256
@@ -536,10 +549,14 @@ __device__ __forceinline__ void w4_rows(const GemmArgs& a, const TileRef& tr, ui
   const int rows = tr.row_end - tr.row0;
   if (rows > W4_TM)
     w4_tile<GELU, QW, NS, 3, WG, KM>(a, tr, lds, acc);
-  else if (rows > 128)
+  else if (rows > 192)
     w4_tile<GELU, QW, NS, 0, WG, KM>(a, tr, lds, acc);
-  else if (rows > 64)
+  else if (rows > 128)
+    w4_tile<GELU, QW, NS, 8, WG, KM>(a, tr, lds, acc);
+  else if (rows > 96)
     w4_tile<GELU, QW, NS, 1, WG, KM>(a, tr, lds, acc);
+  else if (rows > 64)
+    w4_tile<GELU, QW, NS, 9, WG, KM>(a, tr, lds, acc);
   else
     w4_tile<GELU, QW, NS, 2, WG, KM>(a, tr, lds, acc);
 }
