@@ -201,24 +201,28 @@ constexpr int TL_PER_WG = 2048;   // routed tiles written per workgroup
 
 __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restrict__ offsets, int N,
                                                         int BM, int BN, int Nd, int Ts, int merge,
-                                                        int4* __restrict__ list,
+                                                        int wide_rows, int4* __restrict__ list,
                                                         int32_t* __restrict__ count) {
   __shared__ int wsum[4];
-  __shared__ int s_base[MAXN + 1], s_mt[MAXN], s_o0[MAXN], s_o1[MAXN];
+  __shared__ int s_base[MAXN + 1], s_mt[MAXN], s_o0[MAXN], s_o1[MAXN], s_wide[MAXN];
   const int e = threadIdx.x;
   const int ntn = (Nd + BN - 1) / BN;
   const int ms = m_tiles(Ts, BM, merge);
   const int shared_tiles = ms * ntn;
-  int o0 = 0, o1 = 0, mt = 0;
+  int o0 = 0, o1 = 0, mt = 0, ntn_e = ntn;
   if (e < N) {
     o0 = offsets[e];
     o1 = offsets[e + 1];
     mt = m_tiles(o1 - o0, BM, merge);
+    // a block of at most wide_rows rows: tiles of 2 BN columns
+    const int wide = wide_rows > 0 && o1 - o0 <= wide_rows;
+    if (wide) ntn_e = (Nd + 2 * BN - 1) / (2 * BN);
     s_mt[e] = mt;
     s_o0[e] = o0;
     s_o1[e] = o1;
+    s_wide[e] = wide;
   }
-  const int n = mt * ntn;
+  const int n = mt * ntn_e;
   const int lane = e & 63, wave = e >> 6;
   int v = n;
 #pragma unroll
@@ -247,7 +251,9 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
       const int mid = (lo + hi + 1) >> 1;
       if (s_base[mid] <= j) lo = mid; else hi = mid - 1;
     }
-    list[shared_tiles + j] = band_tile(j - s_base[lo], s_mt[lo], ntn, BN, lo, s_o0[lo], s_o1[lo], BM);
+    const int wd = s_wide[lo];
+    list[shared_tiles + j] = band_tile(j - s_base[lo], s_mt[lo], ntn, wd ? 2 * BN : BN,
+                                       lo | (wd ? kWideTile : 0), s_o0[lo], s_o1[lo], BM);
   }
   if (blockIdx.x == 0) {
     for (int j = threadIdx.x; j < shared_tiles; j += blockDim.x)
@@ -285,10 +291,10 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
 
 hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
                             int merge, int64_t max_tiles, int4* list, int32_t* count,
-                            hipStream_t s) {
+                            hipStream_t s, int wide_rows) {
   const unsigned nwg = (unsigned)((max_tiles + TL_PER_WG - 1) / TL_PER_WG);
   hipLaunchKernelGGL(tile_list_kernel, dim3(nwg < 1 ? 1 : nwg), dim3(256), 0, s, offsets, N, BM,
-                     BN, Nd, Ts, merge, list, count);
+                     BN, Nd, Ts, merge, wide_rows, list, count);
   return hipGetLastError();
 }
 

@@ -116,6 +116,7 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 //   256 < R <= 320: 2 x 4 wavefronts of 128 x 64 plus 32 folded rows each,
 //   128 < R <= 256: 2 x 4 wavefronts of 128 x 64,
 //   R <= 128:       2 x 4 wavefronts of  64 x 64.
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int W4_TM = 256;
 constexpr int W4_MERGE = 64;                  // remainder rows folded into the previous tile
 constexpr int W4_AR = W4_TM + W4_MERGE;       // A rows held per LDS stage
@@ -124,50 +125,71 @@ constexpr int W4_CST = BN + 8;                // staged output row stride in bf1
 constexpr int W8_AR = 384;                    // eight wavefronts, folded tiles: 3 loads per wave
 constexpr int W8_STAGE = (W8_AR + BN) * BK;   // 40 KiB: four stages fill the 160 KiB of LDS
 
+// Wide tiles (tile lists built with wide_rows = 128): an expert block of at
+// most 128 rows takes 512 columns per tile, 1 x 4 wavefronts of 128 x 128.
+// Per k-step the tile loads 8 KiB of A rows and 32 KiB of weight rows for
+// twice the MFMAs of a 128 x 256 tile (which loads 8 + 16 KiB), and each
+// wavefront reads 16 KiB of fragments from LDS per 32 MFMAs instead of 12
+// KiB per 16: the short tiles of the fine-grained shapes are bound by these
+// two rates.
+constexpr int WIDE_BN = 2 * BN, WIDE_AR = 128;
+constexpr int WIDE_STAGE = (WIDE_AR + WIDE_BN) * BK;   // 40 KiB
+constexpr int WIDE_CST = WIDE_BN + 8;
+
+// Per layout: BNL columns per tile, CST = staged output row stride (bf16).
+struct W4Cols {
+  static constexpr int BNL = BN, CST = W4_CST;
+};
 template <int L>
 struct W4Layout;
 template <>
-struct W4Layout<0> {   // 128 < R <= 256
+struct W4Layout<0> : W4Cols {   // 128 < R <= 256
   static constexpr int NW = 4, WN = 2, MI = 4, NI = 4, AROWS = 256, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<1> {   // 64 < R <= 128
+struct W4Layout<1> : W4Cols {   // 64 < R <= 128
   static constexpr int NW = 4, WN = 4, MI = 4, NI = 2, AROWS = 128, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<2> {   // R <= 64
+struct W4Layout<2> : W4Cols {   // R <= 64
   static constexpr int NW = 4, WN = 4, MI = 2, NI = 2, AROWS = 64, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<3> {   // 256 < R <= 320
+struct W4Layout<3> : W4Cols {   // 256 < R <= 320
   static constexpr int NW = 4, WN = 2, MI = 4, NI = 4, AROWS = 320, AR = W4_AR;
   static constexpr bool EXTRA = true;
 };
 template <>
-struct W4Layout<8> {   // 128 < R <= 192
+struct W4Layout<8> : W4Cols {   // 128 < R <= 192
   static constexpr int NW = 4, WN = 2, MI = 3, NI = 4, AROWS = 192, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<9> {   // 64 < R <= 96 (the load split needs a multiple of 64 A rows)
+struct W4Layout<9> : W4Cols {   // 64 < R <= 96 (the load split needs a multiple of 64 A rows)
   static constexpr int NW = 4, WN = 4, MI = 3, NI = 2, AROWS = 128, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<4> {   // eight wavefronts, 128 < R <= 256
+struct W4Layout<10> {   // wide tiles: R <= 128, 512 columns
+  static constexpr int NW = 4, WN = 4, MI = 4, NI = 4, AROWS = WIDE_AR, AR = WIDE_AR;
+  static constexpr int BNL = WIDE_BN, CST = WIDE_CST;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<4> : W4Cols {   // eight wavefronts, 128 < R <= 256
   static constexpr int NW = 8, WN = 4, MI = 4, NI = 2, AROWS = 256, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<5> {   // eight wavefronts, R <= 128
+struct W4Layout<5> : W4Cols {   // eight wavefronts, R <= 128
   static constexpr int NW = 8, WN = 4, MI = 2, NI = 2, AROWS = 128, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<7> {   // eight wavefronts, 256 < R <= 320 (384 A rows loaded, the last clamped)
+struct W4Layout<7> : W4Cols {   // eight wavefronts, 256 < R <= 320 (384 A rows loaded, the last clamped)
   static constexpr int NW = 8, WN = 4, MI = 4, NI = 2, AROWS = W8_AR, AR = W8_AR;
   static constexpr bool EXTRA = true;
 };
@@ -194,7 +216,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   constexpr int NLA = Lay::AROWS / RPI / NW;   // direct loads per wavefront per stage, A rows
   // W rows: 16 rows of 64 bytes per wave instruction (bf16 rows of one
   // k-step, INT8 rows of two)
-  constexpr int NLB = W4_TM / RPI / NW;
+  constexpr int NLB = Lay::BNL / RPI / NW;
+  static_assert(!KM || Lay::BNL == BN, "k-major weight stages hold 256 columns");
   static_assert(!QW || NS == 4, "the INT8 wait counts below assume four stages");
   static_assert(NLA * RPI * NW == Lay::AROWS && NLB > 0, "loads split evenly over the waves");
   constexpr int NLS = NLA + NLB;
@@ -260,7 +283,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       offB[i] = ((uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 8 + kbeg) * 2;
     }
   }
-  constexpr int STG = (Lay::AR + BN) * BK;   // bf16 elements per LDS stage
+  constexpr int STG = (Lay::AR + Lay::BNL) * BK;   // bf16 elements per LDS stage
   auto issue_a = [&](int buf, int k0) {
     uint16_t* base = lds + buf * STG + wave * NLA * RPI * BK;
 #pragma unroll
@@ -483,19 +506,20 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
         }
         // v_cvt_pk_bf16_f32: round to nearest even, two values per instruction
         const bf16x4 pk = __builtin_convertvector((f32x4){z[0], z[1], z[2], z[3]}, bf16x4);
-        *reinterpret_cast<bf16x4*>(lds + ml * W4_CST + nl) = pk;
+        *reinterpret_cast<bf16x4*>(lds + ml * Lay::CST + nl) = pk;
       }
     }
   }
   __syncthreads();
-  // 64 NW threads x 16 bytes = 2 NW rows of 256 columns per pass
-  const int cc = (threadIdx.x & 31) * 8;
+  // TPR threads x 16 bytes per staged row; 64 NW / TPR rows per pass
+  constexpr int TPR = Lay::BNL / 8;
+  const int cc = (threadIdx.x % TPR) * 8;
   const int ncol = tr.n0 + cc;
   const int nrow = min(rows, W4_TM);
-  for (int ml = threadIdx.x >> 5; ml < nrow; ml += 2 * NW)
+  for (int ml = threadIdx.x / TPR; ml < nrow; ml += 64 * NW / TPR)
     if (ncol < Nd)
       *reinterpret_cast<uint4*>(C + (int64_t)(tr.row0 + ml) * Nd + ncol) =
-          *reinterpret_cast<const uint4*>(lds + ml * W4_CST + cc);
+          *reinterpret_cast<const uint4*>(lds + ml * Lay::CST + cc);
   if constexpr (EX) {
     // the folded remainder: rows 256 .. R-1, staged as LDS rows 0 .. 63.
     // 24 wait states between the last MFMA writing accx and its first VALU
@@ -531,14 +555,14 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
           if (GELU) z[q] = gelu_as(z[q]);
         }
         const bf16x4 pk = __builtin_convertvector((f32x4){z[0], z[1], z[2], z[3]}, bf16x4);
-        *reinterpret_cast<bf16x4*>(lds + (wm * 32 + (lane & 31)) * W4_CST + nl) = pk;
+        *reinterpret_cast<bf16x4*>(lds + (wm * 32 + (lane & 31)) * Lay::CST + nl) = pk;
       }
     }
     __syncthreads();
-    for (int ml = threadIdx.x >> 5; ml < rows - W4_TM; ml += 2 * NW)
+    for (int ml = threadIdx.x / TPR; ml < rows - W4_TM; ml += 64 * NW / TPR)
       if (ncol < Nd)
         *reinterpret_cast<uint4*>(C + (int64_t)(tr.row0 + W4_TM + ml) * Nd + ncol) =
-            *reinterpret_cast<const uint4*>(lds + ml * W4_CST + cc);
+            *reinterpret_cast<const uint4*>(lds + ml * Lay::CST + cc);
   }
 }
 
@@ -565,7 +589,9 @@ template <bool GELU, bool QW, int NS, bool WG, bool KM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(GemmArgs a) {
   // the output tile is staged through the same LDS after the main loop
-  constexpr int LDS_ELEMS = NS * W4_STAGE > W4_TM * W4_CST ? NS * W4_STAGE : W4_TM * W4_CST;
+  // (wide tiles: four 40 KiB stages, the whole 160 KiB)
+  constexpr int LDS_ELEMS = cmax(cmax(NS * W4_STAGE, W4_TM * W4_CST),
+                                 KM || WG ? 0 : cmax(NS * WIDE_STAGE, WIDE_AR * WIDE_CST));
   __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
   const TileRef tr = map_tile(a);
   if (!tr.valid) return;
@@ -576,6 +602,12 @@ gemm_bf16_w4_kernel(GemmArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if constexpr (!KM && !WG) {
+    if (tr.wide) {   // routed tiles only
+      w4_tile<GELU, QW, NS, 10, WG, KM>(a, tr, lds, acc);
+      return;
+    }
+  }
   if (QW && tr.shared)
     w4_rows<GELU, false, NS, WG, KM>(a, tr, lds, acc);
   else
@@ -607,11 +639,12 @@ gemm_bf16_w8_kernel(GemmArgs a) {
     w4_tile<GELU, QW, NS, 5, WG, KM>(a, tr, lds, acc);
 }
 
-// Eight wavefronts serve the backward's GEMMs, which never have INT8 weights.
+// Eight wavefronts serve the backward's GEMMs, which never have INT8 weights
+// or wide tiles.
 template <bool GELU, bool QW, bool WG, bool KM>
 void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
   if constexpr (!QW) {
-    if (a.waves8) {
+    if (a.waves8 && a.wide_rows == 0) {
       hipLaunchKernelGGL((gemm_bf16_w8_kernel<GELU, false, W4_NS, WG, KM>), dim3(grid), dim3(512),
                          0, s, a);
       return;
@@ -625,6 +658,7 @@ void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
 
 int gemm_bf16_bm() { return W4_TM; }
 int gemm_bf16_bn() { return BN; }
+int gemm_bf16_wide_rows() { return WIDE_AR; }
 int gemm_bf16_merge_rows() { return W4_MERGE; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {

@@ -21,6 +21,7 @@ namespace moe {
 struct TileRef {
   bool valid;
   bool shared;
+  bool wide;    // 2 BN columns (tile lists built with wide_rows)
   int e;        // expert (routed tiles)
   int row0;     // first row of the tile
   int row_end;  // one past the last valid row
@@ -31,6 +32,7 @@ __device__ __forceinline__ TileRef map_tile(const GemmArgs& a) {
   TileRef r;
   r.valid = false;
   r.shared = false;
+  r.wide = false;
   r.e = 0;
   r.row0 = r.row_end = r.n0 = 0;
   const int total = a.tile_count[0];
@@ -42,7 +44,8 @@ __device__ __forceinline__ TileRef map_tile(const GemmArgs& a) {
   const int4 t = a.tile_list[L];
   r.valid = true;
   r.shared = t.x < 0;
-  r.e = t.x < 0 ? 0 : t.x;
+  r.wide = t.x >= 0 && (t.x & kWideTile);
+  r.e = t.x < 0 ? 0 : (t.x & (kWideTile - 1));
   r.row0 = t.y;
   r.row_end = t.z;
   r.n0 = t.w;

@@ -436,8 +436,17 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
     hipError_t e = hipSuccess;
     if (path != PATH_SKINNY) {
       const int merge = path == PATH_TILED ? moe::gemm_bf16_merge_rows() : 0;
+      // Wide tiles for small blocks: with INT8 weights, whose A rows are half
+      // of a short tile's load bytes (same-GPU: Switch-shaped INT8 stage 5%
+      // faster; with bf16 weights the Switch-shaped first GEMM lost 4%), and
+      // only where there are rounds of tiles to spare (about four of the
+      // chip's 256 CUs' worth), so that halving the tiles of the small blocks
+      // (each twice as long) does not unbalance the last round.
+      g.wide_rows = path == PATH_TILED && g.wscale &&
+                            (int64_t)Nr * ((g.Nd + bn - 1) / bn) >= 1024
+                        ? moe::gemm_bf16_wide_rows() : 0;
       e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.bound[list],
-                                fw.list[list], fw.count + list, s);
+                                fw.list[list], fw.count + list, s, g.wide_rows);
       if (e != hipSuccess) return hip_status(e, "tile list launch");
       g.tile_list = fw.list[list];
       g.tile_count = fw.count + list;

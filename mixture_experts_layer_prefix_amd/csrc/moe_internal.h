@@ -109,9 +109,13 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
 // rows (when the block has a full tile) is folded into its last full tile,
 // which then spans up to BM + merge rows.
 // max_tiles bounds the list (it sizes the launch: one workgroup per 2048 tiles).
+// wide_rows > 0: an expert block of at most wide_rows rows gets one row of
+// tiles 2 BN columns wide, marked by kWideTile in the expert field (never
+// more tiles than with BN, so max_tiles still bounds the list).
+constexpr int kWideTile = 1 << 16;
 hipError_t launch_tile_list(const int32_t* offsets, int N, int BM, int BN, int Nd, int Ts,
                             int merge, int64_t max_tiles, int4* list, int32_t* count,
-                            hipStream_t s);
+                            hipStream_t s, int wide_rows = 0);
 inline int max_m_tiles(int64_t M_max, int N, int BM) {
   return static_cast<int>((M_max + BM - 1) / BM) + N;
 }
@@ -149,6 +153,9 @@ struct GemmArgs {
   // tiled kernel: eight-wavefront workgroups (launches bound by the weight
   // stream: few rows per expert, or short weight-gradient k-segments)
   bool waves8;
+  // tiled kernel: the tile list was built with this wide_rows (routed blocks
+  // of at most wide_rows rows have tiles 2 BN wide); 0 = none
+  int wide_rows;
 };
 
 // Prefill-shaped grouped GEMM (bf16 MFMA): tiles of gemm_bf16_bm() x
@@ -156,6 +163,7 @@ struct GemmArgs {
 // gemm_bf16_merge_rows() rows is folded into its last full tile.
 int gemm_bf16_bm();
 int gemm_bf16_bn();
+int gemm_bf16_wide_rows();   // the largest block that takes wide tiles
 int gemm_bf16_merge_rows();
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s);
 // fp32 grouped GEMM (VALU), BM rows per tile.

@@ -45,8 +45,23 @@ def _gpu():
 @pytest.mark.parametrize("name", sorted(COUNTS))
 @pytest.mark.parametrize("d,f", [(320, 384), (256, 512)])
 def test_expert_blocks(name, d, f, quant):
+    _check_blocks(name, COUNTS[name], d, f, quant)
+
+
+def test_wide_tiles_int8():
+    """With INT8 weights and at least 1024 expert x 256-column tiles per
+    launch, blocks of at most 128 rows take 512-column tiles.  256 experts,
+    d = 832 and f = 1216: both GEMMs qualify and both end in a partial wide
+    tile (320 and 192 columns); the counts put blocks on both sides of 128
+    rows (wide and ordinary tiles in one launch) and of the other layout
+    boundaries."""
+    pattern = [0, 1, 5, 33, 64, 65, 96, 97, 127, 128, 2, 17, 129, 40, 200, 257]
+    counts = [pattern[(e * 7) % len(pattern)] for e in range(256)]
+    _check_blocks("wide_int8", counts, 832, 1216, "int8")
+
+
+def _check_blocks(name, counts, d, f, quant):
     import torch
-    counts = COUNTS[name]
     N = len(counts)
     M = int(sum(counts))
     spare = 37                         # rows of x_perm / y_perm past the last block
