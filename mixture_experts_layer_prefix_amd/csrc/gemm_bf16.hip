@@ -178,6 +178,21 @@ struct W4Layout<10> {   // wide tiles: R <= 128, 512 columns
   static constexpr int BNL = WIDE_BN, CST = WIDE_CST;
   static constexpr bool EXTRA = false;
 };
+// Weight gradients of launches bound by the weight stream (few rows per
+// expert, so k-segments of a few k-steps): tiles of 256 x 128, 2 x 2
+// wavefronts of 128 x 64 (128 accumulators each), three 24 KiB stages.  Two
+// workgroups fit on a CU (at most 256 registers per lane and 72 KiB of LDS
+// each), so one's epilogue stores and prologue loads overlap the other's
+// MFMAs; a 256 x 256 tile holds half of a CU's registers and all its LDS.
+constexpr int WG2_BN = BN / 2, WG2_NS = 3;
+constexpr int WG2_STAGE = (W4_TM + WG2_BN) * BK;   // 24 KiB
+constexpr int WG2_CST = WG2_BN + 8;
+template <>
+struct W4Layout<11> {   // weight gradients, 256 x 128 tiles, no folded rows
+  static constexpr int NW = 4, WN = 2, MI = 4, NI = 2, AROWS = W4_TM, AR = W4_TM;
+  static constexpr int BNL = WG2_BN, CST = WG2_CST;
+  static constexpr bool EXTRA = false;
+};
 template <>
 struct W4Layout<4> : W4Cols {   // eight wavefronts, 128 < R <= 256
   static constexpr int NW = 8, WN = 4, MI = 4, NI = 2, AROWS = 256, AR = W4_AR;
@@ -639,6 +654,23 @@ gemm_bf16_w8_kernel(GemmArgs a) {
     w4_tile<GELU, QW, NS, 5, WG, KM>(a, tr, lds, acc);
 }
 
+template <int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+gemm_bf16_wg2_kernel(GemmArgs a) {
+  constexpr int LDS_ELEMS = cmax(NS * WG2_STAGE, W4_TM * WG2_CST);
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[LDS_ELEMS];
+  const TileRef tr = map_tile(a);
+  if (!tr.valid) return;
+  f32x16 acc[4][4];   // acc[0..1][0..3] live
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  w4_tile<false, false, NS, 11, true, false>(a, tr, lds, acc);
+}
+
 // Eight wavefronts serve the backward's GEMMs, which never have INT8 weights
 // or wide tiles.
 template <bool GELU, bool QW, bool WG, bool KM>
@@ -659,12 +691,15 @@ void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
 int gemm_bf16_bm() { return W4_TM; }
 int gemm_bf16_bn() { return BN; }
 int gemm_bf16_wide_rows() { return WIDE_AR; }
+int gemm_bf16_wg_narrow_bn() { return WG2_BN; }
 int gemm_bf16_merge_rows() { return W4_MERGE; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
   const int grid = gemm_grid(a);
   if (grid == 0) return hipSuccess;
-  if (a.kseg)
+  if (a.kseg && a.wg_narrow)
+    hipLaunchKernelGGL((gemm_bf16_wg2_kernel<WG2_NS>), dim3(grid), dim3(256), 0, s, a);
+  else if (a.kseg)
     launch_w<false, false, true, false>(a, grid, s);
   else if (a.wkmaj)
     launch_w<false, false, false, true>(a, grid, s);

@@ -202,6 +202,12 @@ bool bwd_f32(const moe_config_t* c) { return c->dtype == MOE_F32; }
 int bwd_bm(const moe_config_t* c) { return bwd_f32(c) ? moe::gemm_f32_bm() : moe::gemm_bf16_bm(); }
 int bwd_bn(const moe_config_t* c) { return bwd_f32(c) ? moe::gemm_f32_bn() : moe::gemm_bf16_bn(); }
 int bwd_merge(const moe_config_t* c) { return bwd_f32(c) ? 0 : moe::gemm_bf16_merge_rows(); }
+// The routed weight-gradient GEMMs of launches bound by the weight stream run
+// narrow tiles, two workgroups per CU (their k-segments are a few k-steps).
+bool wg_narrow(const moe_config_t* c) { return !bwd_f32(c) && weight_bound(c); }
+int wg_bn(const moe_config_t* c) {
+  return wg_narrow(c) ? moe::gemm_bf16_wg_narrow_bn() : bwd_bn(c);
+}
 // Row stride of the per-expert transposed activations: every expert's rows
 // rounded up to 32 (at most T*K + 31 N in all), or the T rows of the shared
 // expert, rounded up to 64.
@@ -263,8 +269,8 @@ void carve_ffn_bwd(Carver& cv, const moe_config_t* c, FfnBwdWs* w) {
   const int bm = bwd_bm(c), bn = bwd_bn(c);
   w->bound[0] = moe::max_tiles(M, (int)N, 0, bm, bn, f);
   w->bound[1] = moe::max_tiles(M, (int)N, 0, bm, bn, d);
-  w->bound[2] = moe::max_tiles(N * d, (int)N, 0, bm, bn, f);
-  w->bound[3] = moe::max_tiles(N * f, (int)N, 0, bm, bn, d);
+  w->bound[2] = moe::max_tiles(N * d, (int)N, 0, bm, wg_bn(c), f);
+  w->bound[3] = moe::max_tiles(N * f, (int)N, 0, bm, wg_bn(c), d);
   w->bound[4] = fs ? moe::max_tiles(0, 0, (int)T, bm, bn, fs) : 0;
   w->bound[5] = fs ? moe::max_tiles(0, 0, (int)T, bm, bn, d) : 0;
   w->bound[6] = fs ? moe::max_tiles(d, 1, 0, bm, bn, fs) : 0;
@@ -589,8 +595,9 @@ std::string check_train(const moe_config_t* c, int* code) {
 // One backward GEMM: tile list, then the tiled (bf16) or fp32 kernel.
 int bwd_gemm(const moe_config_t* c, moe::GemmArgs g, int4* list, int32_t* count, int64_t bound,
              const int32_t* offs, int Nr, int Ts, hipStream_t s, const char* what) {
-  hipError_t e = moe::launch_tile_list(offs, Nr, bwd_bm(c), bwd_bn(c), g.Nd, Ts, bwd_merge(c),
-                                       bound, list, count, s);
+  hipError_t e = moe::launch_tile_list(offs, Nr, bwd_bm(c), g.wg_narrow ? wg_bn(c) : bwd_bn(c),
+                                       g.Nd, Ts, g.wg_narrow ? 0 : bwd_merge(c), bound, list,
+                                       count, s);
   if (e != hipSuccess) return hip_status(e, "tile list launch");
   g.tile_list = list;
   g.tile_count = count;
@@ -663,6 +670,7 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   wg.kseg = fw.kseg;
   wg.wg_rows = d;
   wg.waves8 = weight_bound(c);
+  wg.wg_narrow = wg_narrow(c);
   r = bwd_gemm(c, wg, fw.list[2], fw.count + 2, fw.bound[2], fw.wr_d, N, 0, s, "wgrad GEMM launch");
   if (r != MOE_OK) return r;
   // dW1 [N, f, d]: A = d_z^T [f, ldt], W = x_perm^T [d, ldt]

@@ -156,6 +156,9 @@ struct GemmArgs {
   // tiled kernel: the tile list was built with this wide_rows (routed blocks
   // of at most wide_rows rows have tiles 2 BN wide); 0 = none
   int wide_rows;
+  // tiled kernel, weight-gradient mode: tiles of 256 x gemm_bf16_wg_narrow_bn()
+  // columns, two workgroups per CU (tile list without folded remainders)
+  bool wg_narrow;
 };
 
 // Prefill-shaped grouped GEMM (bf16 MFMA): tiles of gemm_bf16_bm() x
@@ -164,6 +167,7 @@ struct GemmArgs {
 int gemm_bf16_bm();
 int gemm_bf16_bn();
 int gemm_bf16_wide_rows();   // the largest block that takes wide tiles
+int gemm_bf16_wg_narrow_bn();   // tile width of the narrow weight-gradient tiles
 int gemm_bf16_merge_rows();
 hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s);
 // fp32 grouped GEMM (VALU), BM rows per tile.
