@@ -304,6 +304,12 @@ def main_train(args, shape, inp, t):
     print(json.dumps(res), flush=True)
 
 
+# the sources that decide the grouped-GEMM stage's memory traffic (kernels,
+# tile lists, launch parameters)
+GEMM_SOURCES = ("gemm_bf16.hip", "gemm_skinny.hip", "gemm_common.h", "moe_internal.h",
+                "dispatch.hip", "moe_api.hip")
+
+
 def traffic_from_profile(shape):
     """HBM bytes per launch of the grouped-GEMM stage from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the plain-copy
@@ -318,7 +324,7 @@ def traffic_from_profile(shape):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in ("gemm_bf16.hip", "gemm_common.h", "moe_api.hip"):
+    for f in GEMM_SOURCES:
         h.update(open(os.path.join(ROOT, "mixture_experts_layer_prefix_amd", "csrc", f), "rb").read())
     if vals.get("gemm_source_sha256") != h.hexdigest():
         return None
