@@ -282,7 +282,7 @@ def main_train(args, shape, inp, t):
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = None
-    roof["kernel"] = ("moe_expert_ffn_backward: weight transposes, input-gradient GEMMs, GELU "
+    roof["kernel"] = ("moe_expert_ffn_backward: input-gradient GEMMs (weights read k-major), GELU "
                       "backward, per-expert activation transposes and weight-gradient GEMMs")
     roof["per_launch"] = {"flops": flops, "min_bytes": nbytes, "rows": M,
                           "touched_experts": touched, "ms": round(stage_ms["expert_ffn_backward"], 4)}
