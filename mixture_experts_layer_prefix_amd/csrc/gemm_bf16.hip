@@ -43,6 +43,16 @@ constexpr int RPI = 64 / CH;               // LDS rows filled by one wave instru
 // each span the 256 bytes once, so the chunk is XORed with the group index.
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
+// k-pairs (bf16 forward tiles): LDS rows of 128 bytes hold two 32-wide
+// k-steps (8 chunks of 16 bytes); chunk c of row r sits at c ^ swz8(r).  A
+// ds_read_b128 serves 16 lanes = 16 consecutive rows: rows of equal parity
+// share a 32-bank half, and the XOR spreads each half's 8 rows over its 8
+// chunks, so the 16 reads cover the 64 banks once.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+#ifndef MOE_KPAIRS
+#define MOE_KPAIRS 1
+#endif
+
 __device__ __forceinline__ void lds_load16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
 }
@@ -312,7 +322,40 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
                  base + i * 1024);
   };
 
+  // k-pairs: one direct load moves 8 rows x 128 bytes (two k-steps of a
+  // row), into two pair buffers of (AR + BNL) rows x 128 bytes each
+  constexpr bool P2 = MOE_KPAIRS && !QW && !WG && !KM;
+  constexpr int NLA2 = Lay::AROWS / 8 / NW, NLB2 = Lay::BNL / 8 / NW;
+  static_assert(!P2 || (NLA2 * 8 * NW == Lay::AROWS && NLB2 % 2 == 0), "pair loads split evenly");
+  constexpr int PST = (Lay::AR + Lay::BNL) * 2 * BK;   // bf16 elements per pair buffer
+  static_assert(!P2 || NS == 4, "the pair buffers take the four stages' LDS");
+  uint32_t oA2[P2 ? NLA2 : 1], oB2[P2 ? NLB2 : 1];
+  if constexpr (P2) {
+#pragma unroll
+    for (int i = 0; i < NLA2; ++i) {
+      const int row = (wave * NLA2 + i) * 8 + (lane >> 3);
+      oA2[i] = (uint32_t)(arow0 + min(row, rows - 1)) * (uint32_t)Kd + ((lane & 7) ^ swz8(row)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < NLB2; ++i) {
+      const int row = (wave * NLB2 + i) * 8 + (lane >> 3);
+      oB2[i] = ((uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + ((lane & 7) ^ swz8(row)) * 8) * 2;
+    }
+  }
+  auto issue_a2 = [&](int buf, int k0) {
+    uint16_t* base = lds + buf * PST + wave * NLA2 * 8 * 2 * BK;
+#pragma unroll
+    for (int i = 0; i < NLA2; ++i) lds_load16(A + oA2[i] + k0, base + i * 8 * 2 * BK);
+  };
+  auto issue_b2 = [&](int buf, int k0, auto i0_tag, auto i1_tag) {
+    char* base = reinterpret_cast<char*>(lds + buf * PST + Lay::AR * 2 * BK) + wave * NLB2 * 1024;
+#pragma unroll
+    for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
+      lds_load16(W + oB2[i] + (uint32_t)k0 * 2, base + i * 1024);
+  };
+
   const int sw = swz(lane & 31);   // the same for every fragment row this lane reads
+  const int sw8 = swz8(lane & 31);   // (k-pairs; fragment rows start at multiples of 16)
   const int arow = (wm * WROWS + (lane & 31)) * BK, brow = (wn * WCOLS + (lane & 31)) * BK;
   // rows 256 + 32*wm .. +32 of a 320-row tile (EX only)
   const int xrow = (W4_TM + wm * 32 + (lane & 31)) * BK;
@@ -370,6 +413,23 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       }
     }
   };
+  // k-pairs: fragments of half kk of k-step ks (0, 1) of the pair in buffer buf
+  auto read_q = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int ks, int kk) {
+    const uint16_t* As = lds + buf * PST;
+    const uint16_t* Bs = As + Lay::AR * 2 * BK;
+    const int pc = ((ks * 4 + kk * 2 + (lane >> 5)) ^ sw8) * 8;
+    const int ar = (wm * WROWS + (lane & 31)) * 2 * BK, br = (wn * WCOLS + (lane & 31)) * 2 * BK;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(As + ar + i * 32 * 2 * BK + pc);
+    if constexpr (EX)
+      fa[MI] = *reinterpret_cast<const bf16x8*>(As + (W4_TM + wm * 32 + (lane & 31)) * 2 * BK + pc);
+    if constexpr (!QW) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        fb[i] = *reinterpret_cast<const bf16x8*>(Bs + br + i * 32 * 2 * BK + pc);
+    }
+  };
   auto wfrag = [&](const BF& f) -> bf16x8 {
     if constexpr (QW)
       return __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(f));
@@ -416,7 +476,50 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     static_assert(VS + NV <= NM, "every load sits between two MFMAs");
   };
 
-  if (!WG || KT > 0) {
+  if constexpr (P2) {
+  // k-pairs: pair p covers k-steps 2p, 2p+1 (KT is even: Kd is a multiple of
+  // 64) in buffer p mod 2, four halves per pair.  The weight rows of pair
+  // p+1 are issued in the first two halves of pair p into the other buffer
+  // (its reads ended before the previous pair's barrier); one barrier after
+  // the third half, once every lane has its own loads of pair p+1 landed and
+  // its reads of pair p done; the fourth half reads pair p+1's first
+  // fragments and issues the A rows of pair p+2 into the buffer just freed.
+  const int NP = KT / 2;
+  issue_a2(0, 0);
+  issue_b2(0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, NLB2>{});
+  issue_a2(1, min(1, NP - 1) * 2 * BK);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLA2) : "memory");
+  barrier();
+  read_q(fa0, fb0, 0, 0, 0);
+  for (int p = 0; p < NP; ++p) {
+    const int buf = p & 1, nb = buf ^ 1;
+    const int kn = min(p + 1, NP - 1) * 2 * BK, kn2 = min(p + 2, NP - 1) * 2 * BK;
+    __builtin_amdgcn_sched_barrier(0);
+    read_q(fa1, fb1, buf, 0, 1);
+    issue_b2(nb, kn, std::integral_constant<int, 0>{}, std::integral_constant<int, NLB2 / 2>{});
+    mfma_half(fa0, fb0);
+    interleave(std::integral_constant<int, NLB2 / 2>{}, std::integral_constant<int, NI>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_q(fa0, fb0, buf, 1, 0);
+    issue_b2(nb, kn, std::integral_constant<int, NLB2 / 2>{}, std::integral_constant<int, NLB2>{});
+    mfma_half(fa1, fb1);
+    interleave(std::integral_constant<int, NLB2 - NLB2 / 2>{}, std::integral_constant<int, NI>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read_q(fa1, fb1, buf, 1, 1);
+    mfma_half(fa0, fb0);
+    interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, NI>{});
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_q(fa0, fb0, nb, 0, 0);
+    issue_a2(buf, kn2);
+    mfma_half(fa1, fb1);
+    interleave(std::integral_constant<int, NLA2>{}, std::integral_constant<int, NI>{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  } else if (!WG || KT > 0) {
   // Prologue: stages 0 .. NS-2 in flight (chunks past the end re-read the
   // last chunk into buffers nobody reads again, so every k-step issues the
   // same number of loads and the wait counts are constants).  INT8: the even
