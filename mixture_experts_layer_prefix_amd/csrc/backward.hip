@@ -258,7 +258,17 @@ template <typename T>
 struct TileT {
   static constexpr int VEC = 16 / (int)sizeof(T);
   static constexpr int CPR = TD / VEC;               // 16-byte pieces per tile row
-  static constexpr int LD = TD + VEC;                // padded LDS row (16-byte aligned)
+  // bf16: unpadded 128-byte rows, piece p of row r stored at p ^ ((r / 8) mod 8).
+  // A read-phase instruction has its 64 lanes read element q of 8 rows r0 + 8i
+  // (one per lane group) in 8 columns of one piece: the XOR puts the 8 rows'
+  // pieces in 8 different 16-byte bank groups of the same 128-byte half, and
+  // the 8 columns of a piece fall on 4 dwords, so no bank serves two dwords.
+  // fp32: rows padded by one piece.
+  static constexpr bool SWZ = sizeof(T) == 2;
+  static constexpr int LD = SWZ ? TD : TD + VEC;     // LDS row (16-byte aligned)
+  static __device__ __forceinline__ int at(int r, int c) {   // element (r, c) of the tile
+    return SWZ ? r * LD + ((((c / VEC) ^ ((r >> 3) & (CPR - 1)))) * VEC) + c % VEC : r * LD + c;
+  }
 };
 
 // Expert e's rows [off[e], off[e+1]) of in [*, C] become columns
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(256) void transpose_segments_kernel(
       const int r = i / TT::CPR, cc = (i % TT::CPR) * TT::VEC;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (j0 + r < R) v = *reinterpret_cast<const uint4*>(in + (int64_t)(row0 + j0 + r) * C + c0 + cc);
-      *reinterpret_cast<uint4*>(tile + r * TT::LD + cc) = v;
+      *reinterpret_cast<uint4*>(tile + TT::at(r, cc)) = v;
     }
     __syncthreads();
 #pragma unroll
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(256) void transpose_segments_kernel(
       alignas(16) T v[TT::VEC];
 #pragma unroll
       for (int q = 0; q < TT::VEC; ++q) {
-        v[q] = tile[(rr + q) * TT::LD + oc];
+        v[q] = tile[TT::at(rr + q, oc)];
         part[p] += Elem<T>::load(v, q);
       }
       if (j0 + rr < KP)
