@@ -152,8 +152,17 @@ __global__ __launch_bounds__(256) void select_kernel(
     sc[v] = -INFINITY;
     taken[v] = false;
     if (e < N) {
+      // the slices in order; eight loads in flight before their adds
       double z = part[(int64_t)t * N + e];
-      for (int s = 1; s < S; ++s) z += part[((int64_t)s * Ttok + t) * N + e];
+      int s = 1;
+      for (; s + 8 <= S; s += 8) {
+        double q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = part[((int64_t)(s + u) * Ttok + t) * N + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) z += q[u];
+      }
+      for (; s < S; ++s) z += part[((int64_t)s * Ttok + t) * N + e];
       if (b_router) z += (double)b_router[e];
       if (logit_offset) z += (double)logit_offset[e];
       lg[v] = (float)z;
