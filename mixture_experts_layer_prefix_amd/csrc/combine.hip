@@ -45,13 +45,7 @@ struct Vec<uint16_t> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
-  static __device__ __forceinline__ uint4 pack(const float* f) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
-  }
+  static __device__ __forceinline__ uint4 pack(const float* f) { return pack_bf16x8(f); }
 };
 
 // One wavefront per token (its index made wave-uniform, so the slot rows and

@@ -12,14 +12,21 @@
 //     wave arrangement is picked per tile from its row count, and a short
 //     remainder of an expert's rows rides in its last full tile;
 //   - operands move global -> LDS with 16-byte direct-to-LDS loads (no VGPR
-//     staging; one wave instruction fills 16 LDS rows of 64 bytes), BK = 32,
-//     four LDS stages; the 16-byte chunks of each LDS row are XOR-swizzled
-//     (swz below) so fragment reads hit every bank once per 16 lanes;
+//     staging), 32-wide k-steps.  bf16 forward tiles load k-pairs: one wave
+//     instruction fills 8 LDS rows of 128 bytes (two k-steps of a row) into
+//     two pair buffers; INT8, weight-gradient and k-major tiles fill 16 rows
+//     of 64 bytes per instruction into four stages.  The 16-byte chunks of
+//     each LDS row are XOR-swizzled (swz, swz8) so fragment reads hit every
+//     bank once per 16 lanes;
 //   - the MFMA takes the weight fragment as its first operand, so each lane
 //     ends up with 4 consecutive output columns of one row; the output tile
 //     is staged through LDS and written as whole rows;
 //   - rows past an expert's end read a clamped valid row and are not stored;
-//     the GELU epilogue uses the Abramowitz-Stegun 7.1.26 erf (gelu_as).
+//     the GELU epilogue uses the Abramowitz-Stegun 7.1.26 erf (gelu_as);
+//   - variants: INT8 weights (codes widened in registers), weight gradients
+//     over per-expert k-segments (and a two-workgroups-per-CU kernel of 256 x
+//     128 tiles for short segments), k-major weights for input gradients.
+// MOE_KPAIRS=0 builds the four-stage loop for the bf16 forward tiles too.
 #include <type_traits>
 
 #include "gemm_common.h"

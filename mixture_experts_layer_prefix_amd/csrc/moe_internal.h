@@ -22,6 +22,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Eight fp32 values rounded to bf16 and packed into 16 bytes: v_cvt_pk_bf16_f32
+// rounds to nearest even like f32_to_bf16 (equal on every finite input,
+// ties included), two values per instruction.
+__device__ __forceinline__ uint4 pack_bf16x8(const float* f) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = __builtin_bit_cast(uint32_t,
+                              __builtin_convertvector((f32x2_t){f[2 * i], f[2 * i + 1]}, bf16x2_t));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Exact GELU, z/2 * (1 + erf(z / sqrt(2))).
 __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.70710678118654752440f));
