@@ -6,14 +6,16 @@
 // With a handful of tokens per expert the work is a weight stream: every
 // weight byte is used for only rows_e multiply-adds.  The weights of each
 // touched expert are therefore split over many workgroups along the output
-// dimension, and each wavefront streams 16 weight rows through
-// v_mfma_f32_16x16x32_bf16 with the expert's (up to 16) token rows as the
-// other operand, eight 16-byte loads per lane in flight per step.
-// Workgroup (bx, e): outputs [64*bx, 64*bx + 64) of expert e, one wavefront
-// per 16 outputs; experts with no rows exit at once.  Expert index E stands
-// for the dense shared problem when one is present (its weights are always
-// in the activation dtype; launches with INT8 routed weights carry none).
-// KS = 4 (long reductions, Kd > Nd): a workgroup takes 16 outputs and its
+// dimension, and each wavefront streams 16 NR weight rows (NR = 1 for bf16,
+// 2 for INT8 weights) through v_mfma_f32_16x16x32_bf16 with the expert's
+// (up to 16) token rows as the other operand, eight 16-byte loads per lane
+// and row tile in flight per step (four per tile for INT8: 128 codes each).
+// Workgroup (bx, e): outputs [64 NR bx, 64 NR (bx + 1)) of expert e, one
+// wavefront per 16 NR outputs; experts with no rows exit at once.  Expert
+// index E stands for the dense shared problem when one is present (its
+// weights are always in the activation dtype; launches with INT8 routed
+// weights carry none).
+// KS = 4 (long reductions, Kd > Nd): a workgroup takes 16 NR outputs and its
 // four wavefronts split the model dimension in quarters; the four partial
 // sums are added in wavefront order through LDS.  Four times as many,
 // shorter workgroups keep every CU streaming: with one wavefront per 16
@@ -28,9 +30,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NTHR = 256;
-constexpr int NPW = 16;                 // output features per wavefront
-constexpr int NPB = NPW * NTHR / 64;    // per workgroup
-constexpr int U = 8;                    // k-steps of 32 in flight
+constexpr int U = 8;                    // k-steps of 32 in flight (bf16 weights)
+// NR 16-row MFMA tiles per wavefront: 16 * NR output features per
+// wavefront, 4x that per workgroup (KS = 1).  The tiles share each
+// activation fragment: INT8 weights take NR = 2, since a wavefront's
+// activation loads are two thirds of its load instructions there (same-GPU:
+// the decode-shaped INT8 stage 10% faster); with bf16 weights NR = 2
+// measured 5% slower and NR = 1 stays.
+template <bool QW>
+constexpr int skinny_nr() { return QW ? 2 : 1; }
 
 // INT8 weights (QW): a lane loads 16 codes = one 16-byte load per 64-wide
 // k-block (its slice is k = 64j + 16*(lane/16) .. +16) and feeds two MFMAs
@@ -39,6 +47,8 @@ constexpr int U = 8;                    // k-steps of 32 in flight
 // scale multiplies the result before the bias.
 template <bool GELU, bool QW, int KS>
 __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
+  constexpr int NR = skinny_nr<QW>();
+  constexpr int NPW = 16 * NR, NPB = NPW * NTHR / 64;
   const int e = blockIdx.y;
   const int Kd = a.Kd, Nd = a.Nd;
   const uint16_t* A;
@@ -63,7 +73,8 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   if (r1 <= r0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // KS > 1: one n0 for the whole workgroup, so the exit below is uniform
-  // and every wavefront reaches the barriers of the reduction
+  // and every wavefront reaches the barriers of the reduction.  Nd is a
+  // multiple of 64, so the NR row tiles of a wavefront lie inside it.
   const int n0 = KS == 1 ? blockIdx.x * NPB + wave * NPW : blockIdx.x * NPW;
   if (n0 >= Nd) return;
   int kb = 0, ke = Kd;   // this wavefront's part of the model dimension
@@ -72,43 +83,72 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
     kb = min(Kd, wave * kq);
     ke = min(Kd, kb + kq);
   }
-  __shared__ f32x4 red[KS][64];
+  __shared__ f32x4 red[KS][NR][64];
   // the KS partial sums of a row group in wavefront order; wavefront 0
   // stores the result
-  auto reduce = [&](f32x4& acc) -> bool {
+  auto reduce = [&](f32x4 (&acc)[NR]) -> bool {
     if constexpr (KS == 1) {
       return true;
     } else {
-      red[wave][lane] = acc;
+#pragma unroll
+      for (int j = 0; j < NR; ++j) red[wave][j][lane] = acc[j];
       __syncthreads();
       if (wave == 0) {
-        acc = red[0][lane];
 #pragma unroll
-        for (int w = 1; w < KS; ++w) acc += red[w][lane];
+        for (int j = 0; j < NR; ++j) {
+          acc[j] = red[0][j][lane];
+#pragma unroll
+          for (int w = 1; w < KS; ++w) acc[j] += red[w][j][lane];
+        }
       }
       __syncthreads();
       return wave == 0;
     }
   };
-  const int kq = (lane >> 4) * 8;      // this lane's 8-element slice of each 32-wide k-step
-  const uint16_t* wrow = W + (int64_t)(n0 + (lane & 15)) * Kd + kq;
-  const float bv = bias ? bf16_to_f32(bias[n0 + (lane & 15)]) : 0.f;
+  // 16x16 accumulator layout: element v of lane l holds row (l/16)*4 + v,
+  // column l%16 of its row tile
+  auto store = [&](const f32x4 (&acc)[NR], int g0, const float* sc, const float* bv) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int col = n0 + 16 * j + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = g0 + (lane >> 4) * 4 + v;
+        if (r < r1) {
+          float z = QW ? fmaf(acc[j][v], sc[j], bv[j]) : acc[j][v] + bv[j];
+          if (GELU) z = gelu_erf(z);
+          C[(int64_t)r * Nd + col] = f32_to_bf16(z);
+        }
+      }
+    }
+  };
+  float bv[NR], sc[NR];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    bv[j] = bias ? bf16_to_f32(bias[n0 + 16 * j + (lane & 15)]) : 0.f;
+    sc[j] = QW ? a.wscale[(int64_t)e * Nd + n0 + 16 * j + (lane & 15)] : 1.f;
+  }
   if constexpr (QW) {
     const int8_t* w8 = static_cast<const int8_t*>(a.W) + (int64_t)e * Nd * Kd +
                        (int64_t)(n0 + (lane & 15)) * Kd + (lane >> 4) * 16;
-    const float sc = a.wscale[(int64_t)e * Nd + n0 + (lane & 15)];
-    constexpr int U8 = 8;             // 64-wide k-blocks in flight
+    constexpr int U8 = 8 / NR;        // 64-wide k-blocks in flight
     for (int g0 = r0; g0 < r1; g0 += 16) {
       const int ar = g0 + (lane & 15);
       const bool arow_ok = ar < r1;
       const uint16_t* arow = A + (int64_t)(arow_ok ? ar : r0) * Kd + (lane >> 4) * 16;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[NR];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int k0 = kb; k0 < ke; k0 += 64 * U8) {
         const int nb = min(U8, (ke - k0) / 64);
-        uint4 wv[U8], av[U8][2];
+        uint4 wv[NR][U8], av[U8][2];
 #pragma unroll
         for (int u = 0; u < U8; ++u)
-          if (u < nb) wv[u] = *reinterpret_cast<const uint4*>(w8 + k0 + u * 64);
+          if (u < nb) {
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+              wv[j][u] = *reinterpret_cast<const uint4*>(w8 + (int64_t)16 * j * Kd + k0 + u * 64);
+          }
 #pragma unroll
         for (int u = 0; u < U8; ++u)
           if (u < nb) {
@@ -119,39 +159,42 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
         for (int u = 0; u < U8; ++u)
           if (u < nb) {
-            const bf16x8 w0 = __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(make_uint2(wv[u].x, wv[u].y)));
-            const bf16x8 w1 = __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(make_uint2(wv[u].z, wv[u].w)));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][0]), w0,
-                                                          acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][1]), w1,
-                                                          acc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+              const bf16x8 w0 =
+                  __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(make_uint2(wv[j][u].x, wv[j][u].y)));
+              const bf16x8 w1 =
+                  __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(make_uint2(wv[j][u].z, wv[j][u].w)));
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][0]),
+                                                               w0, acc[j], 0, 0, 0);
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u][1]),
+                                                               w1, acc[j], 0, 0, 0);
+            }
           }
       }
       if (!reduce(acc)) continue;
-      const int col = n0 + (lane & 15);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = g0 + (lane >> 4) * 4 + v;
-        if (r < r1) {
-          float z = fmaf(acc[v], sc, bv);
-          if (GELU) z = gelu_erf(z);
-          C[(int64_t)r * Nd + col] = f32_to_bf16(z);
-        }
-      }
+      store(acc, g0, sc, bv);
     }
     return;
   }
 
+  const int kq = (lane >> 4) * 8;      // this lane's 8-element slice of each 32-wide k-step
+  const uint16_t* wrow = W + (int64_t)(n0 + (lane & 15)) * Kd + kq;
   for (int g0 = r0; g0 < r1; g0 += 16) {
     const int ar = g0 + (lane & 15);
     const bool arow_ok = ar < r1;
     const uint16_t* arow = A + (int64_t)(arow_ok ? ar : r0) * Kd + kq;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     int k0 = kb;
     for (; k0 + 32 * U <= ke; k0 += 32 * U) {
-      uint4 wv[U], av[U];
+      uint4 wv[NR][U], av[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) wv[u] = *reinterpret_cast<const uint4*>(wrow + k0 + u * 32);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+          wv[j][u] = *reinterpret_cast<const uint4*>(wrow + (int64_t)16 * j * Kd + k0 + u * 32);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         av[u] = *reinterpret_cast<const uint4*>(arow + k0 + u * 32);
@@ -159,29 +202,25 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
-                                                      __builtin_bit_cast(bf16x8, wv[u]), acc, 0,
-                                                      0, 0);
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[u]),
+                                                           __builtin_bit_cast(bf16x8, wv[j][u]),
+                                                           acc[j], 0, 0, 0);
     }
     for (; k0 < ke; k0 += 32) {
-      uint4 wv = *reinterpret_cast<const uint4*>(wrow + k0);
       uint4 av = *reinterpret_cast<const uint4*>(arow + k0);
       if (!arow_ok) av = make_uint4(0, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
-                                                    __builtin_bit_cast(bf16x8, wv), acc, 0, 0, 0);
-    }
-    if (!reduce(acc)) continue;
-    // 16x16 accumulator layout: element v of lane l holds row (l/16)*4 + v, column l%16.
-    const int col = n0 + (lane & 15);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = g0 + (lane >> 4) * 4 + v;
-      if (r < r1) {
-        float z = acc[v] + bv;
-        if (GELU) z = gelu_erf(z);
-        C[(int64_t)r * Nd + col] = f32_to_bf16(z);
+      for (int j = 0; j < NR; ++j) {
+        const uint4 wv = *reinterpret_cast<const uint4*>(wrow + (int64_t)16 * j * Kd + k0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                         __builtin_bit_cast(bf16x8, wv), acc[j], 0,
+                                                         0, 0);
       }
     }
+    if (!reduce(acc)) continue;
+    store(acc, g0, sc, bv);
   }
 }
 
@@ -193,7 +232,9 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_
   if (E == 0) return hipSuccess;
   // long reductions: the four wavefronts of a workgroup split the model dimension
   const bool ks = a.Kd > a.Nd && a.Kd >= 4096;
-  const dim3 grid(ks ? (a.Nd + NPW - 1) / NPW : (a.Nd + NPB - 1) / NPB, E);
+  const int npw = 16 * (a.wscale ? skinny_nr<true>() : skinny_nr<false>());   // per wavefront
+  const int per_wg = ks ? npw : npw * NTHR / 64;
+  const dim3 grid((a.Nd + per_wg - 1) / per_wg, E);
   if (ks) {
     if (a.wscale && gelu)
       hipLaunchKernelGGL((gemm_skinny_kernel<true, true, 4>), grid, dim3(NTHR), 0, s, a);

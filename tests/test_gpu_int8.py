@@ -112,3 +112,26 @@ def test_layer_int8(name):
     lay = run_layer(cfg, t, aux=bool(shape.aux_alpha))
     assert torch.equal(lay["out"].float().cpu(), torch.from_numpy(g["out"]))
     assert (lay["counts"] == g["counts"]).all() and lay["n_dropped"] == g["n_dropped"]
+
+
+@pytest.mark.parametrize("d_ff", [256, 4096])
+def test_skinny_int8_expert_with_more_than_16_rows(d_ff):
+    """Decode kernel with INT8 weights (two 16-row tiles per wavefront): one
+    expert receives all 40 tokens, i.e. three row groups (16, 16, 8); with
+    d_ff = 4096 the second GEMM also splits Kd over the wavefronts."""
+    shape = C.DECODE.with_(T=40, d_model=128, d_ff=d_ff, n_experts=8, top_k=1,
+                           weight_quant="int8")
+    inp = inputs.make_inputs(shape, seed=0)
+    off = np.zeros(8, np.float32)
+    off[0] = 1e4
+    inp.logit_offset = off
+    cfg = moe.config_for(shape)
+    say(f"case skinny_int8_40_rows: f={d_ff}")
+    t = device_tensors(inp)
+    g = run_stages(cfg, t)
+    o = oracle_run(inp, None)
+    check_routing_and_dispatch(g, o, inp, None)
+    assert g["counts"][0] == 40
+    err = rel_l2(g["out"], o["out"])
+    say(f"  out rel-L2 {err:.3e} (tol {BF16_TOL})")
+    assert err <= BF16_TOL
