@@ -28,6 +28,9 @@ CASES = {
     "fp32_capacity_aux": C.TINY_FP32.with_(T=100, capacity_factor=1.0, aux_alpha=0.01),
     "tiled_bf16_ragged": C.MIXTRAL_PREFILL.with_(T=300, d_model=256, d_ff=384),
     "tiled_bm256_ragged": C.MIXTRAL_PREFILL.with_(T=1000, d_model=256, d_ff=384, n_experts=4),
+    # 290 rows per expert (folded 320-row tiles); the first GEMM's k-loop is a
+    # single pair of k-steps (d_model = 64), the second's three
+    "tiled_folded_k64": C.MIXTRAL_PREFILL.with_(T=290, d_model=64, d_ff=192, n_experts=2),
     "tiled_capacity_zipf": C.SWITCH_CAPACITY.with_(T=512, d_model=128, d_ff=256, n_experts=16),
     "tiled_shared_selbias": C.DEEPSEEK_FINE.with_(T=256, d_model=256, d_ff=128, n_experts=32,
                                                   top_k=4, d_ff_shared=128),
