@@ -433,81 +433,113 @@ __global__ __launch_bounds__(256) void route_bwd_logits_kernel(
   }
 }
 
-// Eight consecutive values of a bf16 or fp32 row (16-byte aligned), kept
-// packed (R8) until they are widened to fp32 (unpack8).
+// Four consecutive elements of a bf16 or fp32 row (aligned to four
+// elements), kept packed until each is widened to fp32 (at).
 template <typename T>
-struct R8 {
-  uint4 v[sizeof(T) / 2];
+struct R4;
+template <>
+struct R4<uint16_t> {
+  uint2 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ float at(int q) const {
+    const uint32_t w = q < 2 ? v.x : v.y;
+    return __uint_as_float((q & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
 };
-template <typename T>
-__device__ __forceinline__ R8<T> load8(const T* p) {
-  R8<T> r;
-#pragma unroll
-  for (int i = 0; i < (int)sizeof(T) / 2; ++i) r.v[i] = reinterpret_cast<const uint4*>(p)[i];
-  return r;
-}
-template <typename T>
-__device__ __forceinline__ void unpack8(const R8<T>& r, float* f) {
-#pragma unroll
-  for (int i = 0; i < (int)sizeof(T) / 2; ++i) V16<T>::unpack(r.v[i], f + i * V16<T>::N);
+template <>
+struct R4<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ float at(int q) const {
+    return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+  }
+};
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The router's two gradient products run on the fp32 matrix cores
+// (v_mfma_f32_32x32x2f32: a 32x32 block, two k per instruction; the bf16
+// operands widen to fp32 exactly).  A workgroup tile is 32 rows x 512
+// columns; wavefront w owns columns [128w, 128w + 128) as four 32-column
+// blocks, column n of block q being tile column 4n + q, so each lane loads
+// and stores four consecutive columns.  In the instruction's layout lane l
+// supplies row l%32 and column l%32 of the two operands at k = l/32, and its
+// result register v holds row (v/4)*8 + (l/32)*4 + v%4, column l%32.
+//
+// Workgroup b runs on XCD b mod 8; it takes the b/8-th tile of that XCD's
+// contiguous share of the tile space, so workgroups running together on one
+// XCD take neighbouring tiles and share their operands in its L2.
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+  const int xcd = b & 7, slot = b >> 3, per = total >> 3, extra = total & 7;
+  return xcd * per + min(xcd, extra) + slot;
 }
 
 // Partial router weight gradient over a slice of tokens:
-// part[s][e][j] = sum_{t in slice s} d_l[t][e] * x[t][j].  Workgroup: 32 experts
-// (8 groups of 4) x 256 columns (32 groups of 8); grid (ceil(d/256), ceil(N/32), S).
+// part[s][e][j] = sum_{t in slice s} d_l[t][e] * x[t][j].  Tile: 32 experts x
+// 512 columns x one slice, ordered expert block fastest (the tiles an XCD runs
+// together read the same x panel), then column block, then slice.  The k-loop
+// runs 16 tokens (8 instructions per block) at a time, the loads of the next
+// 16 in flight during the products of these.
 template <typename T>
 __global__ __launch_bounds__(256) void router_dw_kernel(const float* __restrict__ dl,
                                                         const T* __restrict__ x, int Ttok, int N,
-                                                        int d, int tslice,
+                                                        int d, int tslice, int nS,
                                                         float* __restrict__ part) {
-  __shared__ float sdl[64][33];
-  const int cg = threadIdx.x & 31, eg = threadIdx.x >> 5;
-  const int j0 = blockIdx.x * 256 + cg * 8;
-  const int eb = blockIdx.y * 32;
-  const int tlo = blockIdx.z * tslice, thi = min(Ttok, tlo + tslice);
-  float acc[4][8];
+  const int nE = (N + 31) / 32, nC = (d + 511) / 512;
+  const int L = xcd_tile(blockIdx.x, nE * nC * nS);
+  const int eb = (L % nE) * 32, cb = (L / nE) % nC, s = L / (nE * nC);
+  const int lane = threadIdx.x & 63, n = lane & 31, kh = lane >> 5;
+  const int j = cb * 512 + (threadIdx.x >> 6) * 128 + 4 * n;
+  const bool jv = j < d;
+  const int jc = jv ? j : 0, ec = min(eb + n, N - 1);
+  const int tlo = s * tslice, thi = min(Ttok, tlo + tslice);
+  f32x16 acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
-  for (int tb = tlo; tb < thi; tb += 64) {
-    for (int i = threadIdx.x; i < 64 * 32; i += 256) {
-      const int tt = i / 32, ee = i % 32;
-      sdl[tt][ee] = (tb + tt < thi && eb + ee < N) ? dl[(int64_t)(tb + tt) * N + eb + ee] : 0.f;
+    for (int v = 0; v < 16; ++v) acc[q][v] = 0.f;
+  // a token past the slice reads the last token's row and weighs it 0; rows
+  // and columns past N and d are computed from clamped addresses and not stored
+  auto load = [&](int t0, float* a, R4<T>* b) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tc = min(t0 + 2 * u + kh, thi - 1);
+      a[u] = dl[(int64_t)tc * N + ec];
+      b[u].load(x + (int64_t)tc * d + jc);
     }
-    __syncthreads();
-    const int nt = min(64, thi - tb);
-    if (j0 < d) {
-      // eight tokens' loads in flight before their FMAs
-      for (int t0 = 0; t0 < nt; t0 += 8) {
-        R8<T> xr[8];
+  };
+  auto mma = [&](int t0, const float* a, const R4<T>* b) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (t0 + u < nt) xr[u] = load8(x + (int64_t)(tb + t0 + u) * d + j0);
+    for (int u = 0; u < 8; ++u) {
+      const float av = a[u] * (t0 + 2 * u + kh < thi ? 1.f : 0.f);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (t0 + u >= nt) break;
-          float xv[8];
-          unpack8(xr[u], xv);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float g = sdl[t0 + u][eg * 4 + i];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, xv[q], acc[i][q]);
-          }
-        }
-      }
+      for (int q = 0; q < 4; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[u].at(q), acc[q], 0, 0, 0);
     }
-    __syncthreads();
+  };
+  const int nch = (thi - tlo + 15) / 16;
+  float a0[8], a1[8];
+  R4<T> b0[8], b1[8];
+  load(tlo, a0, b0);
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    load(tlo + 16 * (c + 1), a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(tlo + 16 * c, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(tlo + 16 * (c + 2), a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(tlo + 16 * (c + 1), a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (j0 >= d) return;
+  if (c < nch) mma(tlo + 16 * c, a0, b0);
+  if (!jv) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = eb + eg * 4 + i;
-    if (e >= N) continue;
-    float* o = part + ((int64_t)blockIdx.z * N + e) * d + j0;
-    *reinterpret_cast<float4*>(o) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    *reinterpret_cast<float4*>(o + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+  for (int v = 0; v < 16; ++v) {
+    const int e = eb + (v >> 2) * 8 + kh * 4 + (v & 3);
+    if (e < N)
+      *reinterpret_cast<float4*>(part + ((int64_t)s * N + e) * d + j) =
+          make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
   }
 }
 
@@ -534,59 +566,72 @@ __global__ __launch_bounds__(64) void router_db_kernel(const float* __restrict__
   if (lane == 0) dbr[e] = a;
 }
 
-// d_x_router[t][j] = sum_e d_l[t][e] * W_r[e][j] (fp32).  Workgroup: 32 tokens
-// (8 groups of 4) x 256 columns (32 groups of 8); experts staged 64 at a time.
+// d_x_router[t][j] = sum_e d_l[t][e] * W_r[e][j] (fp32).  Tile: 32 tokens x
+// 512 columns, ordered token block fastest (the tiles an XCD runs together
+// read the same W_r panel).  d_l of the 32 tokens is staged in LDS whole
+// (N <= 256, zero-padded to a multiple of 16 experts); W_r is read straight
+// from memory, 16 experts at a time with the next 16 in flight.
 template <typename T>
 __global__ __launch_bounds__(256) void router_dx_kernel(const float* __restrict__ dl,
                                                         const T* __restrict__ wr, int Ttok, int N,
                                                         int d, float* __restrict__ dxr) {
-  __shared__ float sdl[32][65];
-  const int cg = threadIdx.x & 31, tg = threadIdx.x >> 5;
-  const int j0 = blockIdx.x * 256 + cg * 8;
-  const int tb = blockIdx.y * 32;
-  float acc[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[i][q] = 0.f;
-  for (int e0 = 0; e0 < N; e0 += 64) {
-    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
-      const int tt = i / 64, ee = i % 64;
-      sdl[tt][ee] = (tb + tt < Ttok && e0 + ee < N) ? dl[(int64_t)(tb + tt) * N + e0 + ee] : 0.f;
-    }
-    __syncthreads();
-    const int ne = min(64, N - e0);
-    if (j0 < d) {
-      // eight experts' loads in flight before their FMAs
-      for (int b0 = 0; b0 < ne; b0 += 8) {
-        R8<T> wraw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (b0 + u < ne) wraw[u] = load8(wr + (int64_t)(e0 + b0 + u) * d + j0);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (b0 + u >= ne) break;
-          float wv[8];
-          unpack8(wraw[u], wv);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float g = sdl[tg * 4 + i][b0 + u];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[i][q] = fmaf(g, wv[q], acc[i][q]);
-          }
-        }
-      }
-    }
-    __syncthreads();
+  __shared__ float sdl[32][257];
+  const int nT = (Ttok + 31) / 32, nC = (d + 511) / 512;
+  const int L = xcd_tile(blockIdx.x, nT * nC);
+  const int tb = (L % nT) * 32, cb = L / nT;
+  const int lane = threadIdx.x & 63, n = lane & 31, kh = lane >> 5;
+  const int j = cb * 512 + (threadIdx.x >> 6) * 128 + 4 * n;
+  const bool jv = j < d;
+  const int jc = jv ? j : 0;
+  const int Np = (N + 15) / 16 * 16;
+  for (int i = threadIdx.x; i < 32 * Np; i += 256) {
+    const int tt = i / Np, ee = i % Np;
+    sdl[tt][ee] = (tb + tt < Ttok && ee < N) ? dl[(int64_t)(tb + tt) * N + ee] : 0.f;
   }
-  if (j0 >= d) return;
+  __syncthreads();
+  f32x16 acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = tb + tg * 4 + i;
-    if (t >= Ttok) continue;
-    float* o = dxr + (int64_t)t * d + j0;
-    *reinterpret_cast<float4*>(o) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    *reinterpret_cast<float4*>(o + 4) = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[q][v] = 0.f;
+  // an expert past N reads W_r's last row against a staged 0; columns past d
+  // are computed from clamped addresses and not stored
+  auto load = [&](int k0, R4<T>* b) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      b[u].load(wr + (int64_t)min(k0 + 2 * u + kh, N - 1) * d + jc);
+  };
+  auto mma = [&](int k0, const R4<T>* b) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float a = sdl[n][k0 + 2 * u + kh];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[u].at(q), acc[q], 0, 0, 0);
+    }
+  };
+  const int nch = Np / 16;
+  R4<T> b0[8], b1[8];
+  load(0, b0);
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    load(16 * (c + 1), b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(16 * c, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(16 * (c + 2), b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(16 * (c + 1), b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (c < nch) mma(16 * c, b0);
+  if (!jv) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int t = tb + (v >> 2) * 8 + kh * 4 + (v & 3);
+    if (t < Ttok)
+      *reinterpret_cast<float4*>(dxr + (int64_t)t * d + j) =
+          make_float4(acc[0][v], acc[1][v], acc[2][v], acc[3][v]);
   }
 }
 
@@ -706,13 +751,21 @@ hipError_t launch_dense_offsets(int T, int ra, int rb, int32_t* off, int32_t* ks
   return hipGetLastError();
 }
 
-int router_dw_slices(int T, int N, int d) {
-  const int base = ((d + 255) / 256) * ((N + 31) / 32);
-  int S = (512 + base - 1) / base;
+// Token slices of the router weight gradient: about 2048 wavefronts in all
+// (4 per tile and slice), at least 64 tokens a slice, each slice a multiple
+// of 16 tokens.  Returns the slice count; *tslice gets the slice length.
+int router_dw_split(int T, int N, int d, int* tslice) {
+  const int tiles = ((N + 31) / 32) * ((d + 511) / 512);
+  int S = (512 + tiles - 1) / tiles;
   const int maxS = (T + 63) / 64;
   if (S > maxS) S = maxS;
-  return S < 1 ? 1 : S;
+  if (S < 1) S = 1;
+  const int ts = ((T + S - 1) / S + 15) / 16 * 16;
+  if (tslice) *tslice = ts;
+  return (T + ts - 1) / ts;
 }
+
+int router_dw_slices(int T, int N, int d) { return router_dw_split(T, N, d, nullptr); }
 
 hipError_t launch_route_bwd(int dtype, const void* x, const void* w_router, const float* logits,
                             const int32_t* topk_idx, const float* topk_w, const float* d_topk_w,
@@ -721,22 +774,23 @@ hipError_t launch_route_bwd(int dtype, const void* x, const void* w_router, cons
                             int T, int d, int N, int K, hipStream_t s) {
   hipLaunchKernelGGL(route_bwd_logits_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits,
                      topk_idx, topk_w, d_topk_w, counts, T, N, K, aux_coef, z_coef, dl);
-  const int S = router_dw_slices(T, N, d);
-  const int tslice = (((T + S - 1) / S) + 63) / 64 * 64;
-  const dim3 g1((d + 255) / 256, (N + 31) / 32, S);
+  int tslice = 0;
+  const int S = router_dw_split(T, N, d, &tslice);
+  const int nC = (d + 511) / 512;
+  const dim3 g1((unsigned)(((N + 31) / 32) * nC * S));
   if (dtype == 0)
     hipLaunchKernelGGL(router_dw_kernel<float>, g1, dim3(256), 0, s, dl,
-                       static_cast<const float*>(x), T, N, d, tslice, part);
+                       static_cast<const float*>(x), T, N, d, tslice, S, part);
   else
     hipLaunchKernelGGL(router_dw_kernel<uint16_t>, g1, dim3(256), 0, s, dl,
-                       static_cast<const uint16_t*>(x), T, N, d, tslice, part);
+                       static_cast<const uint16_t*>(x), T, N, d, tslice, S, part);
   const int64_t n = (int64_t)N * d;
   hipLaunchKernelGGL(router_dw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                      part, S, n, d_w_router);
   if (d_b_router)
     hipLaunchKernelGGL(router_db_kernel, dim3(N), dim3(64), 0, s, dl, T, N, d_b_router);
   if (d_x_router) {
-    const dim3 g2((d + 255) / 256, (T + 31) / 32);
+    const dim3 g2((unsigned)(((T + 31) / 32) * nC));
     if (dtype == 0)
       hipLaunchKernelGGL(router_dx_kernel<float>, g2, dim3(256), 0, s, dl,
                          static_cast<const float*>(w_router), T, N, d, d_x_router);
