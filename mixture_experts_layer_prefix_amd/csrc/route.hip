@@ -94,12 +94,17 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const T* __restrict__ 
 #pragma unroll
     for (int j = 0; j < WE; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  for (int k0 = kb; k0 < ke; k0 += KC) {
-    Row16<T> xa[WT], wb[WE];
+  // chunk c of the slice; the loads of chunk c+1 are in flight during the
+  // products of chunk c (a chunk past the slice re-reads its last one)
+  const int nch = (ke - kb) / KC;
+  auto load = [&](int c, Row16<T>* xa, Row16<T>* wb) {
+    const int k0 = kb + min(c, nch - 1) * KC;
 #pragma unroll
     for (int i = 0; i < WT; ++i) xa[i].load(xrow[i] + k0);
 #pragma unroll
     for (int j = 0; j < WE; ++j) wb[j].load(wrow[j] + k0);
+  };
+  auto mma = [&](const Row16<T>* xa, const Row16<T>* wb) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       double a[WT], b[WE];
@@ -113,7 +118,21 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const T* __restrict__ 
         for (int j = 0; j < WE; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+  };
+  Row16<T> xa0[WT], wb0[WE], xa1[WT], wb1[WE];
+  load(0, xa0, wb0);
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    load(c + 1, xa1, wb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xa0, wb0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(c + 2, xa0, wb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xa1, wb1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (c < nch) mma(xa0, wb0);
   // 16x16 fp64 accumulator: element v of lane l is row 4*v + l/16, column l%16.
   double* out = part + (int64_t)blockIdx.z * Ttok * N;
 #pragma unroll

@@ -36,6 +36,11 @@ CASES = {
     "decode": C.DECODE.with_(T=8, d_model=256, d_ff=512, n_experts=16),
     # few rows per expert (eight-wavefront tiles) and 320-row weight-gradient tiles
     "folded_waves8": C.MIXTRAL_PREFILL.with_(T=256, d_model=320, d_ff=256, n_experts=16),
+    # router gradients with ragged tails everywhere: 200 experts (a partial
+    # 32-expert block, 208 staged), two 512-column blocks (the second
+    # partial), six token slices of 64 with a 13-token last one
+    "router_tails": C.DEEPSEEK_FINE.with_(T=333, d_model=640, d_ff=128, n_experts=200, top_k=3,
+                                          d_ff_shared=0),
 }
 
 
