@@ -238,10 +238,14 @@ struct W4Layout<7> : W4Cols {   // eight wavefronts, 256 < R <= 320 (384 A rows 
 // by all experts; an empty segment leaves the accumulators at zero.
 // KM: k-major weights, W_e stored [Kd, Nd] (the input gradients of the
 // backward read the forward's weights as they are).
-// 16 output bytes staged in LDS to memory.  Weight gradients (NT) go out as
-// non-temporal stores: nothing later in the pass reads them, and with ~128-row
-// k-segments their kernels are bound by these stores (the expert backward of
-// the Switch- and DeepSeek-shaped layers ran 8% and 4% faster with them).
+// 16 output bytes staged in LDS to memory, as non-temporal stores (NT) for
+// the weight gradients and the first GEMM's GELU output.  Nothing later in
+// the pass reads the gradients, and with ~128-row k-segments their kernels
+// are bound by these stores (the expert backward of the Switch- and
+// DeepSeek-shaped layers ran 8% and 4% faster with them).  The GELU output
+// is read once more, by the second GEMM; the forward expert stage still ran
+// 0.6-0.8% faster on the three prefill shapes (the second GEMM's output,
+// which the combine reads right away, measured better without).
 template <bool NT>
 __device__ __forceinline__ void store_out(uint16_t* dst, const uint16_t* src) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -657,7 +661,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   const int nrow = min(rows, W4_TM);
   for (int ml = threadIdx.x / TPR; ml < nrow; ml += 64 * NW / TPR)
     if (ncol < Nd)
-      store_out<WG>(C + (int64_t)(tr.row0 + ml) * Nd + ncol, lds + ml * Lay::CST + cc);
+      store_out<WG || GELU>(C + (int64_t)(tr.row0 + ml) * Nd + ncol, lds + ml * Lay::CST + cc);
   if constexpr (EX) {
     // the folded remainder: rows 256 .. R-1, staged as LDS rows 0 .. 63.
     // 24 wait states between the last MFMA writing accx and its first VALU
@@ -699,7 +703,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     __syncthreads();
     for (int ml = threadIdx.x / TPR; ml < rows - W4_TM; ml += 64 * NW / TPR)
       if (ncol < Nd)
-        store_out<WG>(C + (int64_t)(tr.row0 + W4_TM + ml) * Nd + ncol, lds + ml * Lay::CST + cc);
+        store_out<WG || GELU>(C + (int64_t)(tr.row0 + W4_TM + ml) * Nd + ncol, lds + ml * Lay::CST + cc);
   }
 }
 
