@@ -60,8 +60,11 @@ __device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 #define MOE_KPAIRS 1
 #endif
 
+// AUX = 2: non-temporal (nt), for bf16 weights streamed once
+// (GemmArgs::w_stream; the kernels' NTW instantiations)
+template <int AUX = 0>
 __device__ __forceinline__ void lds_load16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, AUX);
 }
 
 // INT8 weights: the weight region of an even stage (16 KiB, sized for bf16)
@@ -256,7 +259,7 @@ __device__ __forceinline__ void store_out(uint16_t* dst, const uint16_t* src) {
     *reinterpret_cast<u32x4*>(dst) = v;
 }
 
-template <bool GELU, bool QW, int NS, int LAY, bool WG, bool KM>
+template <bool GELU, bool QW, int NS, int LAY, bool WG, bool KM, bool NTW = false>
 __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
   using Lay = W4Layout<LAY>;
@@ -341,10 +344,14 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   };
   auto issue_b = [&](int buf, int k0) {
     char* base = reinterpret_cast<char*>(lds + buf * STG + Lay::AR * BK) + wave * NLB * 1024;
+    const uint32_t kb = KM ? (uint32_t)k0 * (uint32_t)Nd * 2 : k0 * (QW ? 1 : 2);
+    if constexpr (NTW) {
 #pragma unroll
-    for (int i = 0; i < NLB; ++i)
-      lds_load16(W + offB[i] + (KM ? (uint32_t)k0 * (uint32_t)Nd * 2 : k0 * (QW ? 1 : 2)),
-                 base + i * 1024);
+      for (int i = 0; i < NLB; ++i) lds_load16<2>(W + offB[i] + kb, base + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLB; ++i) lds_load16(W + offB[i] + kb, base + i * 1024);
+    }
   };
 
   // k-pairs: one direct load moves 8 rows x 128 bytes (two k-steps of a
@@ -374,9 +381,15 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   };
   auto issue_b2 = [&](int buf, int k0, auto i0_tag, auto i1_tag) {
     char* base = reinterpret_cast<char*>(lds + buf * PST + Lay::AR * 2 * BK) + wave * NLB2 * 1024;
+    if constexpr (NTW) {
 #pragma unroll
-    for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
-      lds_load16(W + oB2[i] + (uint32_t)k0 * 2, base + i * 1024);
+      for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
+        lds_load16<2>(W + oB2[i] + (uint32_t)k0 * 2, base + i * 1024);
+    } else {
+#pragma unroll
+      for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
+        lds_load16(W + oB2[i] + (uint32_t)k0 * 2, base + i * 1024);
+    }
   };
 
   const int sw = swz(lane & 31);   // the same for every fragment row this lane reads
@@ -708,25 +721,25 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
 }
 
 // Four-wavefront tile: the wave arrangement from the tile's row count.
-template <bool GELU, bool QW, int NS, bool WG, bool KM>
+template <bool GELU, bool QW, int NS, bool WG, bool KM, bool NTW = false>
 __device__ __forceinline__ void w4_rows(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
   const int rows = tr.row_end - tr.row0;
   if (rows > W4_TM)
-    w4_tile<GELU, QW, NS, 3, WG, KM>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 3, WG, KM, NTW>(a, tr, lds, acc);
   else if (rows > 192)
-    w4_tile<GELU, QW, NS, 0, WG, KM>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 0, WG, KM, NTW>(a, tr, lds, acc);
   else if (rows > 128)
-    w4_tile<GELU, QW, NS, 8, WG, KM>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 8, WG, KM, NTW>(a, tr, lds, acc);
   else if (rows > 96)
-    w4_tile<GELU, QW, NS, 1, WG, KM>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 1, WG, KM, NTW>(a, tr, lds, acc);
   else if (rows > 64)
-    w4_tile<GELU, QW, NS, 9, WG, KM>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 9, WG, KM, NTW>(a, tr, lds, acc);
   else
-    w4_tile<GELU, QW, NS, 2, WG, KM>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 2, WG, KM, NTW>(a, tr, lds, acc);
 }
 
-template <bool GELU, bool QW, int NS, bool WG, bool KM>
+template <bool GELU, bool QW, int NS, bool WG, bool KM, bool NTW = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(GemmArgs a) {
   // the output tile is staged through the same LDS after the main loop
@@ -752,7 +765,7 @@ gemm_bf16_w4_kernel(GemmArgs a) {
   if (QW && tr.shared)
     w4_rows<GELU, false, NS, WG, KM>(a, tr, lds, acc);
   else
-    w4_rows<GELU, QW, NS, WG, KM>(a, tr, lds, acc);
+    w4_rows<GELU, QW, NS, WG, KM, NTW>(a, tr, lds, acc);
 }
 
 // The same tiles with eight wavefronts (two per SIMD, at most 256 registers
@@ -799,7 +812,7 @@ gemm_bf16_wg2_kernel(GemmArgs a) {
 
 // Eight wavefronts serve the backward's GEMMs, which never have INT8 weights
 // or wide tiles.
-template <bool GELU, bool QW, bool WG, bool KM>
+template <bool GELU, bool QW, bool WG, bool KM, bool NTW = false>
 void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
   if constexpr (!QW) {
     if (a.waves8 && a.wide_rows == 0) {
@@ -808,7 +821,7 @@ void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
       return;
     }
   }
-  hipLaunchKernelGGL((gemm_bf16_w4_kernel<GELU, QW, W4_NS, WG, KM>), dim3(grid), dim3(256), 0, s,
+  hipLaunchKernelGGL((gemm_bf16_w4_kernel<GELU, QW, W4_NS, WG, KM, NTW>), dim3(grid), dim3(256), 0, s,
                      a);
 }
 
@@ -833,8 +846,10 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
     gelu ? launch_w<true, true, false, false>(a, grid, s)
          : launch_w<false, true, false, false>(a, grid, s);
   else
-    gelu ? launch_w<true, false, false, false>(a, grid, s)
-         : launch_w<false, false, false, false>(a, grid, s);
+    a.w_stream ? (gelu ? launch_w<true, false, false, false, true>(a, grid, s)
+                       : launch_w<false, false, false, false, true>(a, grid, s))
+               : (gelu ? launch_w<true, false, false, false>(a, grid, s)
+                       : launch_w<false, false, false, false>(a, grid, s));
   return hipGetLastError();
 }
 

@@ -451,6 +451,17 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
       g.wide_rows = path == PATH_TILED && g.wscale &&
                             (int64_t)Nr * ((g.Nd + bn - 1) / bn) >= 1024
                         ? moe::gemm_bf16_wide_rows() : 0;
+      // Non-temporal loads of bf16 weights where each expert's weights are
+      // streamed once (few rows per expert) and the permuted activations are
+      // small enough to stay in the 256 MB MALL (same-GPU: the Switch-shaped
+      // forward 3.6% faster, its combine 10%; with the DeepSeek shape's
+      // 470 MB of activations no gain, Mixtral's weights, re-read per
+      // m-tile, 5% slower, and INT8 codes, whose 64-byte rows fill a cache
+      // line over two k-steps, 12% slower).  Not with a shared expert in the
+      // launch: its weights are re-read by every m-tile of the T tokens.
+      g.w_stream = path == PATH_TILED && !g.wscale && Ts == 0 && weight_bound(c) &&
+                   (int64_t)c->T * c->top_k * c->d_model * (int64_t)elem_bytes(c->dtype) <=
+                       (int64_t(128) << 20);
       e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.bound[list],
                                 fw.list[list], fw.count + list, s, g.wide_rows);
       if (e != hipSuccess) return hip_status(e, "tile list launch");

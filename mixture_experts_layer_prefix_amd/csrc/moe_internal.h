@@ -173,6 +173,9 @@ struct GemmArgs {
   // tiled kernel, weight-gradient mode: tiles of 256 x gemm_bf16_wg_narrow_bn()
   // columns, two workgroups per CU (tile list without folded remainders)
   bool wg_narrow;
+  // tiled kernel: load the weights non-temporally (each weight panel is read
+  // once, so it need not displace the activations from L2 and the MALL)
+  bool w_stream;
 };
 
 // Prefill-shaped grouped GEMM (bf16 MFMA): tiles of gemm_bf16_bm() x
