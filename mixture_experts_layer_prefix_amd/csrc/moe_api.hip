@@ -458,8 +458,10 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
       // 470 MB of activations no gain, Mixtral's weights, re-read per
       // m-tile, 5% slower, and INT8 codes, whose 64-byte rows fill a cache
       // line over two k-steps, 12% slower).  Not with a shared expert in the
-      // launch: its weights are re-read by every m-tile of the T tokens.
-      g.w_stream = path == PATH_TILED && !g.wscale && Ts == 0 && weight_bound(c) &&
+      // launch: its weights are re-read by every m-tile of the T tokens.  Not
+      // in the training forward either, which keeps z and runs the GELU as a
+      // kernel of its own (there the Switch-shaped forward ran 5% slower).
+      g.w_stream = path == PATH_TILED && !train && !g.wscale && Ts == 0 && weight_bound(c) &&
                    (int64_t)c->T * c->top_k * c->d_model * (int64_t)elem_bytes(c->dtype) <=
                        (int64_t(128) << 20);
       e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.bound[list],
