@@ -772,6 +772,8 @@ hipError_t launch_route_bwd(int dtype, const void* x, const void* w_router, cons
                             const int32_t* counts, float aux_coef, float z_coef, float* dl,
                             float* part, float* d_w_router, float* d_b_router, float* d_x_router,
                             int T, int d, int N, int K, hipStream_t s) {
+  // the d_x share stages a token block's d_l (at most 256 experts) in LDS
+  if (N > 256 || d % 64 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(route_bwd_logits_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits,
                      topk_idx, topk_w, d_topk_w, counts, T, N, K, aux_coef, z_coef, dl);
   int tslice = 0;
