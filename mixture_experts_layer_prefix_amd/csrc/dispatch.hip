@@ -54,7 +54,19 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ b
   const int e = threadIdx.x;
   int run = 0;
   if (e < N) {
-    for (int b = 0; b < nblk; ++b) {
+    // eight blocks' counts loaded together, then added in block order
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = blkcnt[(int64_t)(b + u) * N + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        blkoff[(int64_t)(b + u) * N + e] = run;
+        run += c[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       blkoff[(int64_t)b * N + e] = run;
       run += blkcnt[(int64_t)b * N + e];
     }
@@ -99,37 +111,51 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
   const int64_t p0 = (int64_t)blockIdx.x * DB * K;
   const int64_t p1 = min((int64_t)(blockIdx.x + 1) * DB, (int64_t)T) * K;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t pb = p0; pb < p1; pb += 64) {
-    const int64_t p = pb + lane;
-    const bool inb = p < p1;
-    const int e = inb ? idx[p] : -1;
-    const bool valid = inb && e >= 0 && e < N;
-    // lanes holding the same valid expert: AND of per-bit ballots
-    uint64_t match = __ballot(valid);
+  // the expert indices of RB 64-slot steps are loaded together, then the
+  // steps run in slot order
+  constexpr int RB = 8;
+  for (int64_t pc = p0; pc < p1; pc += 64 * RB) {
+    int ev[RB];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t ones = __ballot(bit);
-      match &= bit ? ones : ~ones;
+    for (int u = 0; u < RB; ++u) {
+      const int64_t p = pc + 64 * u + lane;
+      ev[u] = p < p1 ? idx[p] : -1;
     }
-    if (!valid) match = 0;
-    int pos = 0;
-    if (valid) {
-      const int rank = __popcll(match & below);
-      const int start = run[e];
-      pos = start + rank;
-      const uint64_t above = (lane == 63) ? 0ull : (match >> (lane + 1));
-      if (above == 0) run[e] = start + __popcll(match);   // last lane of its group
-    }
-    if (inb) {
-      int r = -1;
-      if (valid && pos < cap) {
-        r = off_s[e] + pos;
-        row_token[r] = (int32_t)(p / K);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int64_t pb = pc + 64 * u;
+      if (pb >= p1) break;   // wave-uniform
+      const int64_t p = pb + lane;
+      const bool inb = p < p1;
+      const int e = ev[u];
+      const bool valid = inb && e >= 0 && e < N;
+      // lanes holding the same valid expert: AND of per-bit ballots
+      uint64_t match = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t ones = __ballot(bit);
+        match &= bit ? ones : ~ones;
       }
-      slot_row[p] = r;
+      if (!valid) match = 0;
+      int pos = 0;
+      if (valid) {
+        const int rank = __popcll(match & below);
+        const int start = run[e];
+        pos = start + rank;
+        const uint64_t above = (lane == 63) ? 0ull : (match >> (lane + 1));
+        if (above == 0) run[e] = start + __popcll(match);   // last lane of its group
+      }
+      if (inb) {
+        int r = -1;
+        if (valid && pos < cap) {
+          r = off_s[e] + pos;
+          row_token[r] = (int32_t)(p / K);
+        }
+        slot_row[p] = r;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
