@@ -41,6 +41,9 @@ CASES = {
     # partial), six token slices of 64 with a 13-token last one
     "router_tails": C.DEEPSEEK_FINE.with_(T=333, d_model=640, d_ff=128, n_experts=200, top_k=3,
                                           d_ff_shared=0),
+    # one token: 14 of 16 experts empty (zero weight gradients from empty
+    # k-segments), one-token router slices and d_x tile
+    "t1_empty_experts": C.MIXTRAL_PREFILL.with_(T=1, d_model=128, d_ff=192, n_experts=16),
 }
 
 
