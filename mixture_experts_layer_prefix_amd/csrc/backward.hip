@@ -102,13 +102,29 @@ __global__ __launch_bounds__(256) void gelu_bwd_kernel(const uint4* __restrict__
 }
 
 // ---------------------------------------------------------------- combine backward
+// A 16-byte piece of a permuted row; NT: a non-temporal load, for rows read
+// once from arrays too large for the MALL (the per-slot rows of the
+// DeepSeek-shaped layer, 470 MB), where cached loads only evict each other.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 ld_row16(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(q[0], q[1], q[2], q[3]);
+  } else {
+    return *p;
+  }
+}
+// Per-slot rows of T*K rows x nvec pieces: non-temporal beyond half the MALL.
+inline bool rows_nt(int64_t rows, int nvec) { return rows * nvec * 16 > (int64_t(128) << 20); }
+
 // One wavefront per token (wave-uniform index, so the slot rows and weights
 // are scalar loads); slots in groups of KB.  For each group, a lane walks its
 // 16-byte pieces of the row: it loads g[t] and the group's kept y_perm rows,
 // adds the products into one fp32 partial dot per slot and stores w * g to
 // each kept row of d_y_perm; the partials are then added across the lanes
 // by a fixed butterfly.
-template <typename T, int KB, int U>
+template <typename T, int KB, int U, bool NT>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const uint4* __restrict__ d_out, const uint4* __restrict__ y_perm,
     const int32_t* __restrict__ slot_row, const float* __restrict__ topk_w,
@@ -141,7 +157,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
           const uint4* yr = y_perm + (int64_t)r[j] * nvec;
 #pragma unroll
           for (int u = 0; u < U; ++u)
-            if (c0 + 64 * u < nvec) v[j][u] = yr[c0 + 64 * u];
+            if (c0 + 64 * u < nvec) v[j][u] = ld_row16<NT>(yr + c0 + 64 * u);
         }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -175,7 +191,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 // ---------------------------------------------------------------- unpermute
 // d_x[t] = (sum over kept slots, in slot order, of d_x_perm[row]) + d_x_shared[t]
 // + d_x_router[t]; fp32 sums, one rounding.  Layout as the combine kernel.
-template <typename T, int KB, int U>
+template <typename T, int KB, int U, bool NT>
 __global__ __launch_bounds__(256) void unpermute_kernel(
     const uint4* __restrict__ d_x_perm, const int32_t* __restrict__ slot_row,
     const uint4* __restrict__ d_x_shared, const float4* __restrict__ d_x_router,
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(
           const uint4* src = d_x_perm + (int64_t)r[j] * nvec;
 #pragma unroll
           for (int u = 0; u < U; ++u)
-            if (c0 + 64 * u < nvec) v[j][u] = src[c0 + 64 * u];
+            if (c0 + 64 * u < nvec) v[j][u] = ld_row16<NT>(src + c0 + 64 * u);
         }
 #pragma unroll
       for (int j = 0; j < KB; ++j)
@@ -677,12 +693,16 @@ static void combine_bwd_t(const void* d_out, const void* y_perm, const int32_t* 
   const uint4* g = static_cast<const uint4*>(d_out);
   const uint4* y = static_cast<const uint4*>(y_perm);
   uint4* dy = static_cast<uint4*>(d_y_perm);
+  const bool nt = rows_nt((int64_t)Ttok * K, nvec);
   if (K <= 2)
-    hipLaunchKernelGGL((combine_bwd_kernel<T, 2, 2>), grid, block, 0, s, g, y, slot_row, topk_w,
-                       dy, d_topk_w, Ttok, nvec, K);
+    hipLaunchKernelGGL((combine_bwd_kernel<T, 2, 2, false>), grid, block, 0, s, g, y, slot_row,
+                       topk_w, dy, d_topk_w, Ttok, nvec, K);
+  else if (nt)
+    hipLaunchKernelGGL((combine_bwd_kernel<T, 8, 1, true>), grid, block, 0, s, g, y, slot_row,
+                       topk_w, dy, d_topk_w, Ttok, nvec, K);
   else
-    hipLaunchKernelGGL((combine_bwd_kernel<T, 8, 1>), grid, block, 0, s, g, y, slot_row, topk_w,
-                       dy, d_topk_w, Ttok, nvec, K);
+    hipLaunchKernelGGL((combine_bwd_kernel<T, 8, 1, false>), grid, block, 0, s, g, y, slot_row,
+                       topk_w, dy, d_topk_w, Ttok, nvec, K);
 }
 
 hipError_t launch_combine_bwd(int dtype, const void* d_out, const void* y_perm,
@@ -705,12 +725,16 @@ static void unpermute_t(const void* d_x_perm, const int32_t* slot_row, const voi
   const uint4* sh = static_cast<const uint4*>(d_x_shared);
   const float4* rt = reinterpret_cast<const float4*>(d_x_router);
   uint4* o = static_cast<uint4*>(d_x);
+  const bool nt = rows_nt((int64_t)Ttok * K, nvec);
   if (K <= 2)
-    hipLaunchKernelGGL((unpermute_kernel<T, 2, 4>), grid, block, 0, s, a, slot_row, sh, rt, o,
-                       Ttok, nvec, K);
+    hipLaunchKernelGGL((unpermute_kernel<T, 2, 4, false>), grid, block, 0, s, a, slot_row, sh, rt,
+                       o, Ttok, nvec, K);
+  else if (nt)
+    hipLaunchKernelGGL((unpermute_kernel<T, 8, 2, true>), grid, block, 0, s, a, slot_row, sh, rt,
+                       o, Ttok, nvec, K);
   else
-    hipLaunchKernelGGL((unpermute_kernel<T, 8, 2>), grid, block, 0, s, a, slot_row, sh, rt, o,
-                       Ttok, nvec, K);
+    hipLaunchKernelGGL((unpermute_kernel<T, 8, 2, false>), grid, block, 0, s, a, slot_row, sh, rt,
+                       o, Ttok, nvec, K);
 }
 
 hipError_t launch_unpermute(int dtype, const void* d_x_perm, const int32_t* slot_row,
