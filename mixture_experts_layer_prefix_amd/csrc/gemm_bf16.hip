@@ -230,17 +230,6 @@ struct W4Layout<7> : W4Cols {   // eight wavefronts, 256 < R <= 320 (384 A rows 
 };
 
 
-// QW: the routed weights are INT8 codes with one fp32 scale per output row
-// (a.wscale); the shared problem's tiles keep bf16 weights and take the
-// kernel's bf16 path.  The codes travel to LDS as bytes (half the bytes of
-// bf16), each fragment is widened to bf16 in registers (exact: |q| <= 127)
-// just before its MFMAs, and the epilogue multiplies by the row scale before
-// the bias.
-// WG: weight-gradient (k-segment) mode -- expert e's tile contracts over
-// columns [kseg[e], kseg[e+1]) of A [wg_rows, Kd] and W [Nd, Kd], both shared
-// by all experts; an empty segment leaves the accumulators at zero.
-// KM: k-major weights, W_e stored [Kd, Nd] (the input gradients of the
-// backward read the forward's weights as they are).
 // 16 output bytes staged in LDS to memory, as non-temporal stores (NT) for
 // the weight gradients and the first GEMM's GELU output.  Nothing later in
 // the pass reads the gradients, and with ~128-row k-segments their kernels
@@ -259,6 +248,18 @@ __device__ __forceinline__ void store_out(uint16_t* dst, const uint16_t* src) {
     *reinterpret_cast<u32x4*>(dst) = v;
 }
 
+// QW: the routed weights are INT8 codes with one fp32 scale per output row
+// (a.wscale); the shared problem's tiles keep bf16 weights and take the
+// kernel's bf16 path.  The codes travel to LDS as bytes (half the bytes of
+// bf16), each fragment is widened to bf16 in registers (exact: |q| <= 127)
+// just before its MFMAs, and the epilogue multiplies by the row scale before
+// the bias.
+// WG: weight-gradient (k-segment) mode -- expert e's tile contracts over
+// columns [kseg[e], kseg[e+1]) of A [wg_rows, Kd] and W [Nd, Kd], both shared
+// by all experts; an empty segment leaves the accumulators at zero.
+// KM: k-major weights, W_e stored [Kd, Nd] (the input gradients of the
+// backward read the forward's weights as they are).
+// NTW: the weights' direct loads are non-temporal (lds_load16<2>).
 template <bool GELU, bool QW, int NS, int LAY, bool WG, bool KM, bool NTW = false>
 __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
