@@ -246,15 +246,12 @@ def routing_stats(idx: np.ndarray, w: np.ndarray, n_experts: int):
 def quantize_int8(w: np.ndarray):
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows = w.reshape(-1, w.shape[-1])
-    q = np.zeros(rows.shape, dtype=np.int8)
-    s = np.zeros(rows.shape[0], dtype=np.float32)
-    for r in range(rows.shape[0]):
-        m = np.float32(np.abs(rows[r]).max())
-        if m == 0:
-            continue
-        s[r] = np.float32(m / np.float32(127.0))
-        v = np.rint(rows[r] / s[r])                  # fp32 division, half to even
-        q[r] = np.clip(v, -127, 127).astype(np.int8)
+    m = np.abs(rows).max(axis=1)                           # exact in fp32
+    s = (m / np.float32(127.0)).astype(np.float32)         # fp32 division
+    div = np.where(s > 0, s, np.float32(1.0))
+    v = np.rint(rows / div[:, None])                       # fp32 division, half to even
+    v[s == 0] = 0                                          # a row of zeros: s = 0, q = 0
+    q = np.clip(v, -127, 127).astype(np.int8)
     return q.reshape(w.shape), s.reshape(w.shape[:-1])
 
 
@@ -262,25 +259,35 @@ def dequantize_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return _f64(s)[..., None] * q.astype(np.float64)
 
 
+
 # --------------------------------------------------------------------------
-# The whole layer.  Structure follows [yunthe]'s reference forward: a loop
-# over the K slots and, inside it, over the experts, adding w * E_e(x) into the
-# rows of the tokens that chose expert e in that slot ([lmnt] §3.2 combine
-# equation: output[t] = sum over selected e of weight[t, e] * E_e(x_t)); the
+# The whole layer.  [lmnt] §3.2 combine equation: output[t] = sum over the
+# experts e selected for t of weight[t, e] * E_e(x_t).  Each expert runs once
+# on the batch of all tokens routed to it ([yunthe] reference forward: the
+# rows that chose expert e are gathered with a boolean mask and passed
+# through E_e together; the note after it: production code batches the tokens
+# of one expert), and w * E_e(x) is added into those tokens' rows; the
 # capacity mask of [lmnt] §3.3 removes dropped pairs; a shared expert
-# ([wiblog], shared-expert isolation) is added for every token.
+# ([wiblog], shared-expert isolation) is added for every token.  A token
+# selects an expert at most once, so within one expert every token appears in
+# at most one row.  The K terms of a token are added in expert order (in
+# fp64; in exact arithmetic the sum does not depend on the order).
 ExpertSource = Union[Sequence, Callable[[int], tuple]]
 
 
 def moe_forward(x, w_router, experts: ExpertSource, top_k: int, *, n_experts: Optional[int] = None,
                 b_router=None, logit_offset=None, sel_bias=None, shared=None,
                 capacity: Optional[int] = None, aux_alpha: float = 0.0,
-                out_tokens: Optional[np.ndarray] = None, round_logits: bool = True) -> dict:
+                out_tokens: Optional[np.ndarray] = None, round_logits: bool = True,
+                return_y_perm: bool = False) -> dict:
     """experts: sequence of (W1 [f, d], b1 [f] | None, W2 [d, f], b2 [d] | None)
     or a callable e -> that tuple.  shared: None or (Ws1 [f_s, d], Ws2 [d, f_s]).
     capacity: None or <= 0 for dropless, else C.  out_tokens: compute ``out``
     only for these token indices (other rows stay 0); routing, dispatch and the
-    aux loss always cover every token."""
+    aux loss always cover every token.  return_y_perm: also return
+    ``y_perm`` [M, d], the expert output of every kept pair at its dispatch
+    row (y_perm[slot_row[t, k]] = E_{idx[t, k]}(x_t); rows of tokens outside
+    out_tokens stay 0)."""
     x64 = _f64(x)
     T = x64.shape[0]
     N = n_experts if n_experts is not None else np.asarray(w_router).shape[0]
@@ -301,19 +308,24 @@ def moe_forward(x, w_router, experts: ExpertSource, top_k: int, *, n_experts: Op
         active[np.asarray(out_tokens)] = True
 
     out = np.zeros_like(x64)
-    for k in range(top_k):
-        expert_of = idx[:, k]
-        for e in range(N):
-            mask = (expert_of == e) & kept_pair[:, k] & active
-            if not mask.any():
-                continue
-            w1, b1, w2, b2 = get(e)
-            out[mask] += w[mask, k][:, None] * expert_ffn(x64[mask], w1, b1, w2, b2)
+    y_perm = np.zeros((int(disp["expert_offsets"][-1]), x64.shape[1])) if return_y_perm else None
+    for e in range(N):
+        # the (token, slot) pairs routed to e, kept, and of an active token
+        tok, slot = np.nonzero((idx == e) & kept_pair & active[:, None])
+        if tok.size == 0:
+            continue
+        w1, b1, w2, b2 = get(e)
+        y = expert_ffn(x64[tok], w1, b1, w2, b2)
+        out[tok] += w[tok, slot][:, None] * y
+        if y_perm is not None:
+            y_perm[disp["slot_row"][tok, slot]] = y
     if shared is not None:
         ws1, ws2 = shared
         out[active] += expert_ffn(x64[active], ws1, None, ws2, None)
 
     res = dict(logits=logits, scores=scores, idx=idx, w=w, out=out, **disp)
+    if y_perm is not None:
+        res["y_perm"] = y_perm
     if aux_alpha:
         res["aux"] = aux_loss(logits, idx, N, aux_alpha)
     return res
@@ -394,13 +406,18 @@ def moe_backward(x, w_router, experts: ExpertSource, top_k: int, d_out, *,
                  n_experts: Optional[int] = None, b_router=None, logit_offset=None,
                  sel_bias=None, shared=None, capacity: Optional[int] = None,
                  aux_alpha: float = 0.0, aux_grad: float = 1.0, zloss_beta: float = 0.0,
-                 zloss_grad: float = 1.0, round_logits: bool = True) -> dict:
+                 zloss_grad: float = 1.0, round_logits: bool = True,
+                 expert_grad_sink: Optional[Callable] = None) -> dict:
     """Gradients of L = <d_out, out> + aux_grad * aux + zloss_grad * zloss.
 
     Same arguments as moe_forward plus d_out [T, d].  Returns d_x [T, d],
     d_w_router [N, d], d_b_router [N], d_w1 [N, f, d], d_b1 [N, f],
     d_w2 [N, d, f], d_b2 [N, d], d_ws1, d_ws2 (shared, or None), d_topk_w [T, K]
-    (zero for dropped slots), d_logits [T, N] and the forward's routing."""
+    (zero for dropped slots), d_logits [T, N] and the forward's routing.
+    expert_grad_sink: when given, called as sink(e, dW1, db1, dW2, db2) with
+    each routed expert's gradients (an expert without rows gets zeros), and
+    d_w1, d_b1, d_w2, d_b2 are not returned (the large layers' [N, f, d]
+    stacks need not be held at once)."""
     x64, g_out = _f64(x), _f64(d_out)
     T, d = x64.shape
     N = n_experts if n_experts is not None else np.asarray(w_router).shape[0]
@@ -417,27 +434,32 @@ def moe_backward(x, w_router, experts: ExpertSource, top_k: int, d_out, *,
     d_w = np.zeros((T, top_k))
     e0 = get(0)
     f = np.asarray(e0[0]).shape[0]
-    d_w1 = np.zeros((N, f, d))
-    d_b1 = np.zeros((N, f))
-    d_w2 = np.zeros((N, d, f))
-    d_b2 = np.zeros((N, d))
-    # the pages' loop over slots and experts; the rows of one (slot, expert)
-    # pair set go through the expert together
-    for k in range(top_k):
-        for e in range(N):
-            mask = (idx[:, k] == e) & kept_pair[:, k]
-            if not mask.any():
-                continue
-            w1, b1, w2, b2 = get(e)
-            y = expert_ffn(x64[mask], w1, b1, w2, b2)
-            d_w[mask, k] = (g_out[mask] * y).sum(axis=1)
-            g_y = w[mask, k][:, None] * g_out[mask]
-            g_x, dW1, db1, dW2, db2 = expert_ffn_backward(x64[mask], w1, b1, w2, g_y)
-            d_x[mask] += g_x
-            d_w1[e] += dW1
-            d_b1[e] += db1
-            d_w2[e] += dW2
-            d_b2[e] += db2
+    if expert_grad_sink is None:
+        d_w1 = np.zeros((N, f, d))
+        d_b1 = np.zeros((N, f))
+        d_w2 = np.zeros((N, d, f))
+        d_b2 = np.zeros((N, d))
+    # as in the forward, each expert takes the batch of all (kept) rows routed
+    # to it; a token appears at most once per expert
+    for e in range(N):
+        tok, slot = np.nonzero((idx == e) & kept_pair)
+        if tok.size == 0:
+            if expert_grad_sink is not None:
+                expert_grad_sink(e, np.zeros((f, d)), np.zeros(f), np.zeros((d, f)), np.zeros(d))
+            continue
+        w1, b1, w2, b2 = get(e)
+        y = expert_ffn(x64[tok], w1, b1, w2, b2)
+        d_w[tok, slot] = (g_out[tok] * y).sum(axis=1)
+        g_y = w[tok, slot][:, None] * g_out[tok]
+        g_x, dW1, db1, dW2, db2 = expert_ffn_backward(x64[tok], w1, b1, w2, g_y)
+        d_x[tok] += g_x
+        if expert_grad_sink is not None:
+            expert_grad_sink(e, dW1, db1, dW2, db2)
+        else:
+            d_w1[e] = dW1
+            d_b1[e] = db1
+            d_w2[e] = dW2
+            d_b2[e] = db2
     d_ws1 = d_ws2 = None
     if shared is not None:
         ws1, ws2 = shared
@@ -451,6 +473,9 @@ def moe_backward(x, w_router, experts: ExpertSource, top_k: int, d_out, *,
     if zloss_beta:
         d_logits += zloss_grad * router_z_loss_logit_grad(logits, zloss_beta)
     d_x += d_logits @ _f64(w_router)
-    return dict(d_x=d_x, d_w_router=d_logits.T @ x64, d_b_router=d_logits.sum(axis=0),
-                d_w1=d_w1, d_b1=d_b1, d_w2=d_w2, d_b2=d_b2, d_ws1=d_ws1, d_ws2=d_ws2,
-                d_topk_w=d_w, d_logits=d_logits, logits=logits, idx=idx, w=w, **disp)
+    res = dict(d_x=d_x, d_w_router=d_logits.T @ x64, d_b_router=d_logits.sum(axis=0),
+               d_ws1=d_ws1, d_ws2=d_ws2, d_topk_w=d_w, d_logits=d_logits, logits=logits,
+               idx=idx, w=w, **disp)
+    if expert_grad_sink is None:
+        res.update(d_w1=d_w1, d_b1=d_b1, d_w2=d_w2, d_b2=d_b2)
+    return res

@@ -40,17 +40,48 @@ def oracle_expert_source_int8(inp):
     return get
 
 
-def oracle_run(inp, capacity, out_tokens=None):
+def prefetching_source(get, n, window=8, workers=8):
+    """An expert source that prepares experts e+1 .. e+window (widened to
+    fp64) in worker threads while the caller works on expert e.  The oracle
+    walks the experts in increasing order, so the conversions of the large
+    layers' weights overlap its products.  Serves the same values as get."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def prep(e):
+        return tuple(None if a is None else np.asarray(a, dtype=np.float64) for a in get(e))
+
+    ex = ThreadPoolExecutor(workers)
+    futs = {}
+
+    def fetch(e):
+        for j in range(e, min(n, e + window + 1)):
+            if j not in futs:
+                futs[j] = ex.submit(prep, j)
+        r = futs.pop(e).result()
+        if e % 64 == 63:
+            say(f"    oracle at expert {e + 1} of {n}")
+        for j in [j for j in futs if j < e]:
+            futs.pop(j).cancel()
+        if e == n - 1:
+            ex.shutdown(wait=False)
+        return r
+    return fetch
+
+
+def oracle_run(inp, capacity, out_tokens=None, return_y_perm=False):
     s = inp.shape
     shared = None
     if s.d_ff_shared:
         shared = (inp.f32("ws1"), inp.f32("ws2"))
     src = oracle_expert_source_int8(inp) if getattr(s, "weight_quant", "none") == "int8" \
         else oracle_expert_source(inp)
+    if s.n_experts * s.d_model * s.d_ff >= (1 << 26):
+        src = prefetching_source(src, s.n_experts)
     return O.moe_forward(inp.f32("x"), inp.f32("w_router"), src, s.top_k,
                          n_experts=s.n_experts, b_router=inp.b_router,
                          logit_offset=inp.logit_offset, sel_bias=inp.sel_bias, shared=shared,
-                         capacity=capacity, aux_alpha=s.aux_alpha, out_tokens=out_tokens)
+                         capacity=capacity, aux_alpha=s.aux_alpha, out_tokens=out_tokens,
+                         return_y_perm=return_y_perm)
 
 
 def device_tensors(inp, device="cuda"):

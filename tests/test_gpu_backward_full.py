@@ -3,18 +3,14 @@
 moe_layer_backward; aux-loss multiplier 1 where the workload has an aux
 loss, no z-loss).
 
-A full fp64 backward of the large layers is too slow for the oracle, so it
-checks what it can compute exactly:
-  - routing over every token, bit-exact;
-  - the complete weight and bias gradients of two experts (the busiest and
-    the least loaded one with rows), from the oracle's expert_ffn_backward
-    on exactly the rows the oracle routes to them; experts without rows get
-    exactly zero gradients;
-  - d_x on sampled tokens (each from its own experts, the shared expert and
-    its router row);
-  - the router weight gradient over every token (the oracle's forward of
-    every kept row gives every d_topk_w).
-The tiny fp32 layer is compared whole against moe_backward."""
+Every gradient is compared whole against the oracle's moe_backward run over
+the whole batch: d_x [T, d_model], d_w_router, and every routed expert's
+d_w1 / d_w2 (passed expert by expert to a sink, so the large layers' [N, f, d]
+stacks are never held on the host at once; the relative L2 is taken over the
+whole stack), the shared expert's d_ws1 / d_ws2; experts without rows must get
+exactly zero gradients.  Routing over every token is bit-exact."""
+import gc
+
 import numpy as np
 import pytest
 
@@ -22,13 +18,10 @@ from mixture_experts_layer_prefix_amd import configs as C
 from mixture_experts_layer_prefix_amd import inputs, moe
 from oracle import moe_oracle as O
 
-from moe_testlib import BF16_TOL, F32_TOL, device_tensors, oracle_expert_source, rel_l2, say
+from moe_testlib import (BF16_TOL, F32_TOL, device_tensors, oracle_expert_source,
+                         prefetching_source, rel_l2, say)
 
 pytestmark = pytest.mark.gpu
-
-
-def _f64(a):
-    return None if a is None else np.asarray(a, dtype=np.float64)
 
 
 @pytest.mark.parametrize("shape", C.ALL, ids=[s.name for s in C.ALL])
@@ -51,96 +44,69 @@ def test_backward_full_size(shape):
     d_out = (d_out.view(torch.bfloat16) if g_np.dtype == np.uint16 else d_out).cuda()
     d_x = layer.backward(t["x"], d_out, aux_grad=g_aux)
     torch.cuda.synchronize()
-    G = {k: v.float().cpu().numpy() for k, v in layer.grads_t.items()}
     gdx = d_x.float().cpu().numpy()
     sv = {k: layer.saved_t[k].cpu().numpy() for k in ("topk_idx", "slot_row", "counts")}
-    del layer
-    torch.cuda.empty_cache()
-    say("  gpu done")
+    G = layer.grads_t            # stays on the device; pulled expert by expert
+    small = {k: G[k].float().cpu().numpy() for k in ("d_w_router", "d_b_router", "d_b1", "d_b2",
+                                                     "d_ws1", "d_ws2") if G.get(k) is not None}
+    del d_x, d_out
+    say("  gpu done; oracle backward over the whole batch ...")
 
     get = oracle_expert_source(inp)
+    if shape.n_experts * shape.d_model * shape.d_ff >= (1 << 26):
+        get = prefetching_source(get, shape.n_experts)
     x = inp.f32("x").astype(np.float64)
     g_out = (inputs.bf16_widen(g_np) if g_np.dtype == np.uint16 else g_np).astype(np.float64)
     shared = (inp.f32("ws1"), inp.f32("ws2")) if shape.d_ff_shared else None
 
-    if shape.T * shape.d_model <= 64 * 64:
-        o = O.moe_backward(x, inp.f32("w_router"), get, shape.top_k, g_out,
-                           n_experts=shape.n_experts, b_router=inp.b_router,
-                           logit_offset=inp.logit_offset, sel_bias=inp.sel_bias, shared=shared,
-                           capacity=cap, aux_alpha=shape.aux_alpha, aux_grad=g_aux)
-        for key in ("d_x", "d_w_router", "d_w1", "d_w2"):
-            got = gdx if key == "d_x" else G[key]
-            e = rel_l2(got, o[key])
-            say(f"  {key} rel-L2 {e:.2e}")
-            assert e <= tol, key
-        return
+    acc = {"d_w1": [0.0, 0.0], "d_w2": [0.0, 0.0], "d_b1": [0.0, 0.0], "d_b2": [0.0, 0.0]}
+    worst = {"d_w1": 0.0, "d_w2": 0.0}
+    empty = []
 
-    # routing over every token
-    logits = O.router_logits(x, inp.f32("w_router"), inp.b_router, inp.logit_offset)
-    idx = O.topk_select(O.selection_scores(logits, inp.sel_bias), shape.top_k)
-    w = O.topk_softmax(logits, idx)
-    disp = O.dispatch(idx, shape.n_experts, cap)
-    assert (sv["topk_idx"] == idx).all() and (sv["slot_row"] == disp["slot_row"]).all()
-    assert (sv["counts"] == disp["counts"]).all()
-    kept = disp["slot_row"] >= 0
-    say(f"  routing bit-exact; dropped {disp['n_dropped']}")
+    def sink(e, dW1, db1, dW2, db2):
+        g1 = G["d_w1"][e].float().cpu().numpy().astype(np.float64)
+        g2 = G["d_w2"][e].float().cpu().numpy().astype(np.float64)
+        if not dW1.any() and not dW2.any():
+            empty.append(e)
+            assert not g1.any() and not g2.any(), f"expert {e} has no rows: gradients must be 0"
+            return
+        for key, got, ref in (("d_w1", g1, dW1), ("d_w2", g2, dW2)):
+            num, den = float(np.sum((got - ref) ** 2)), float(np.sum(ref ** 2))
+            acc[key][0] += num
+            acc[key][1] += den
+            worst[key] = max(worst[key], (num / den) ** 0.5 if den > 0 else 0.0)
+        if "d_b1" in small:
+            for key, got, ref in (("d_b1", small["d_b1"][e], db1), ("d_b2", small["d_b2"][e], db2)):
+                acc[key][0] += float(np.sum((got - ref) ** 2))
+                acc[key][1] += float(np.sum(ref ** 2))
 
-    # the oracle's forward of every kept row gives every d_topk_w
-    d_w = np.zeros(idx.shape)
-    for e in range(shape.n_experts):
-        sel = (idx == e) & kept
-        if not sel.any():
-            continue
-        tok, slot = np.nonzero(sel)
-        w1, b1, w2, b2 = get(e)
-        y = O.expert_ffn(x[tok], w1, b1, w2, b2)
-        d_w[tok, slot] = (g_out[tok] * y).sum(axis=1)
-    d_logits = np.zeros(logits.shape)
-    np.put_along_axis(d_logits, idx.astype(np.int64), O.topk_softmax_backward(w, d_w), axis=1)
-    if shape.aux_alpha:
-        d_logits += g_aux * O.aux_loss_logit_grad(logits, disp["counts"], shape.aux_alpha)
-    e_r = rel_l2(G["d_w_router"], d_logits.T @ x)
-    say(f"  d_w_router rel-L2 {e_r:.2e} (every token)")
-    assert e_r <= tol
+    o = O.moe_backward(x, inp.f32("w_router"), get, shape.top_k, g_out,
+                       n_experts=shape.n_experts, b_router=inp.b_router,
+                       logit_offset=inp.logit_offset, sel_bias=inp.sel_bias, shared=shared,
+                       capacity=cap, aux_alpha=shape.aux_alpha, aux_grad=g_aux,
+                       expert_grad_sink=sink)
+    assert (sv["topk_idx"] == o["idx"]).all() and (sv["slot_row"] == o["slot_row"]).all()
+    assert (sv["counts"] == o["counts"]).all()
+    say(f"  routing bit-exact; dropped {o['n_dropped']}; {len(empty)} experts without rows "
+        f"(gradients exactly zero)")
 
-    # two experts' complete gradients
-    kept_e = np.diff(disp["expert_offsets"]).astype(np.int64)
-    busy = int(np.argmax(kept_e))
-    light = int(np.argmin(np.where(kept_e > 0, kept_e, 1 << 40)))
-    empty = np.nonzero(kept_e == 0)[0]
-    for e in empty:
-        assert not G["d_w1"][e].any() and not G["d_w2"][e].any(), f"expert {e} has no rows"
-    if len(empty):
-        say(f"  {len(empty)} experts without rows: gradients exactly zero")
-    for e in sorted({busy, light}):
-        tok, slot = np.nonzero((idx == e) & kept)
-        order = np.argsort(tok, kind="stable")
-        tok, slot = tok[order], slot[order]
-        w1, b1, w2, b2 = get(e)
-        g_y = w[tok, slot][:, None] * g_out[tok]
-        _, dW1, db1, dW2, db2 = O.expert_ffn_backward(x[tok], w1, b1, w2, g_y)
-        e1, e2 = rel_l2(G["d_w1"][e], dW1), rel_l2(G["d_w2"][e], dW2)
-        say(f"  expert {e} ({len(tok)} rows): d_w1 rel-L2 {e1:.2e}, d_w2 rel-L2 {e2:.2e}")
-        assert e1 <= tol and e2 <= tol
-
-    # d_x on sampled tokens
-    rng = np.random.default_rng(7)
-    toks = np.unique(np.concatenate([rng.choice(shape.T, size=min(12, shape.T), replace=False),
-                                     [0, shape.T - 1],
-                                     np.nonzero(~kept.all(axis=1))[0][:2]]))
-    ref = np.zeros((len(toks), shape.d_model))
-    for i, tt in enumerate(toks):
-        for k in range(shape.top_k):
-            if not kept[tt, k]:
-                continue
-            w1, b1, w2, b2 = get(int(idx[tt, k]))
-            gx, *_ = O.expert_ffn_backward(x[tt:tt + 1], w1, b1, w2, w[tt, k] * g_out[tt:tt + 1])
-            ref[i] += gx[0]
-        if shared is not None:
-            gx, *_ = O.expert_ffn_backward(x[tt:tt + 1], shared[0], None, shared[1],
-                                           g_out[tt:tt + 1])
-            ref[i] += gx[0]
-        ref[i] += d_logits[tt] @ _f64(inp.f32("w_router"))
-    e_x = rel_l2(gdx[toks], ref)
-    say(f"  sampled {len(toks)} tokens: d_x rel-L2 {e_x:.2e} (tol {tol})")
-    assert e_x <= tol
+    errs = {}
+    for key in ("d_w1", "d_w2", "d_b1", "d_b2"):
+        num, den = acc[key]
+        if den > 0:
+            errs[key] = (num / den) ** 0.5
+    errs["d_x"] = rel_l2(gdx, o["d_x"])
+    errs["d_w_router"] = rel_l2(small["d_w_router"], o["d_w_router"])
+    if "d_b_router" in small:
+        errs["d_b_router"] = rel_l2(small["d_b_router"], o["d_b_router"])
+    if shared is not None:
+        errs["d_ws1"] = rel_l2(small["d_ws1"], o["d_ws1"])
+        errs["d_ws2"] = rel_l2(small["d_ws2"], o["d_ws2"])
+    say("  whole-tensor rel-L2: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) +
+        f"; worst expert d_w1 {worst['d_w1']:.2e}, d_w2 {worst['d_w2']:.2e} (tol {tol})")
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    assert worst["d_w1"] <= 4 * tol and worst["d_w2"] <= 4 * tol
+    del layer, G, t, o, inp
+    gc.collect()
+    torch.cuda.empty_cache()
