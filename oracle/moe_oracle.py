@@ -9,7 +9,7 @@ Pages (by site and title):
   [lmnt]   lmnt.cn MoE walkthrough (news/351908): §1.2 per-token flow,
            §2.1 gate scoring equation, §2.2 TopK, §3.1 dispatch, §3.2 combine
            equation, §3.3 capacity equation, §4.3 weight quantisation for
-           inference, §5.2 load-balance code, §5.3 router z-loss equation,
+           inference (INT8 or INT4), §5.2 load-balance code, §5.3 router z-loss equation,
            §8.2 routing statistics.
   [csdn]   "MoE逐token路由与活跃参数率实战解析": §3.1 worked top-2 example,
            §4.2 MoELayer code.
@@ -36,6 +36,8 @@ notes as well):
   * INT8 weight-only experts: symmetric, one fp32 scale per output row,
     s = maxabs / 127 and q = round-half-even(w / s) clamped to +-127, both
     divisions in fp32; the expert then uses the weights s * q;
+  * INT4 weight-only experts: the same with 7 for 127 (codes in [-7, 7]),
+    stored two per byte (element 2i in the low nibble of byte i);
   * backward: the gradient of the forward above with the Top-K choice and the
     capacity drops held fixed, the logits' fp32 rounding taken as the
     identity, selection bias, logit offsets and the aux loss's f constant.
@@ -258,6 +260,52 @@ def quantize_int8(w: np.ndarray):
 def dequantize_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     return _f64(s)[..., None] * q.astype(np.float64)
 
+
+# [lmnt] §4.3 names INT4 beside INT8 for the expert weights (a quarter of the
+# 16-bit memory and bandwidth); [yunthe] deployment section cites 4-bit
+# weight-only formats.  The pages fix no scheme; the reading here is the INT8
+# one above with 4-bit codes, decided in fp32:
+#   s[r] = fp32(maxabs_k |w[r, k]| / 7),  q[r, k] = rint(fp32(w[r, k] / s[r]))
+# clamped to [-7, 7]; a row of zeros gets s = 0 and q = 0.  The expert uses
+# the weights s * q.
+def quantize_int4(w: np.ndarray):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows = w.reshape(-1, w.shape[-1])
+    m = np.abs(rows).max(axis=1)                           # exact in fp32
+    s = (m / np.float32(7.0)).astype(np.float32)           # fp32 division
+    div = np.where(s > 0, s, np.float32(1.0))
+    v = np.rint(rows / div[:, None])                       # fp32 division, half to even
+    v[s == 0] = 0
+    q = np.clip(v, -7, 7).astype(np.int8)
+    return q.reshape(w.shape), s.reshape(w.shape[:-1])
+
+
+def dequantize_int4(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    return _f64(s)[..., None] * q.astype(np.float64)
+
+
+# Storage of 4-bit codes: two per byte along the row, element 2i in the low
+# nibble and element 2i+1 in the high nibble of byte i, each as a 4-bit two's
+# complement number.
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    q = np.asarray(q, dtype=np.int8)
+    if q.shape[-1] % 2:
+        raise ValueError("the row length must be even")
+    lo = q[..., 0::2].astype(np.uint8) & np.uint8(0x0F)
+    hi = q[..., 1::2].astype(np.uint8) & np.uint8(0x0F)
+    return (lo | (hi << np.uint8(4))).astype(np.uint8)
+
+
+def unpack_int4(p: np.ndarray) -> np.ndarray:
+    p = np.asarray(p, dtype=np.uint8)
+    lo = (p & np.uint8(0x0F)).astype(np.int8)
+    hi = (p >> np.uint8(4)).astype(np.int8)
+    lo = np.where(lo >= 8, lo - 16, lo).astype(np.int8)
+    hi = np.where(hi >= 8, hi - 16, hi).astype(np.int8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -334,6 +334,115 @@ def test_int8_expert_equals_dense_ffn_on_dequantized_weights():
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------- INT4 weights
+def test_quantize_int4_scalar_brute_force():
+    # every decision re-derived in exact rational arithmetic: s = fp32(m / 7),
+    # q = clamp(rint_half_even(fp32(w / s)), -7, 7)
+    from fractions import Fraction
+    rng = np.random.default_rng(41)
+    w = (rng.standard_normal((6, 40)) * rng.choice([1e-3, 1.0, 50.0], size=(6, 1))).astype(
+        np.float32)
+    q, s = O.quantize_int4(w)
+    for r in range(w.shape[0]):
+        m = max(abs(Fraction(float(v))) for v in w[r])
+        assert s[r] == _nearest_f32(m / 7)
+        for k in range(w.shape[1]):
+            quot = _nearest_f32(Fraction(float(w[r, k])) / Fraction(float(s[r])))
+            assert int(q[r, k]) == max(-7, min(7, _rint_half_even(quot)))
+
+
+def test_quantize_int4_properties():
+    rng = np.random.default_rng(42)
+    w = rng.standard_normal((16, 64)).astype(np.float32)
+    w[3] = 0.0                                      # zero row
+    w[5, 7] = -np.abs(w[5]).max() * 2               # negative extreme
+    q, s = O.quantize_int4(w)
+    assert s[3] == 0 and (q[3] == 0).all()
+    for r in range(16):
+        if r == 3:
+            continue
+        k = int(np.abs(w[r]).argmax())
+        assert abs(int(q[r, k])) == 7 and np.sign(q[r, k]) == np.sign(w[r, k])
+        # round trip within half a step plus the fp32 rounding of w / s
+        err = np.abs(O.dequantize_int4(q[r:r + 1], s[r:r + 1])[0] - w[r].astype(np.float64))
+        assert err.max() <= float(s[r]) * (0.5 + 7 * 2.0 ** -23)
+    assert q.min() >= -7 and q.max() <= 7
+    # a long normal row uses every level from -6 to 6, and +-7 at its extreme
+    q2, _ = O.quantize_int4(rng.standard_normal((1, 4096)).astype(np.float32))
+    used = set(q2[0].tolist())
+    assert set(range(-6, 7)) <= used and (7 in used or -7 in used)
+
+
+def test_quantize_int4_divides_in_fp32():
+    # values whose exact quotient w / s lies just past k + 1/2 while the fp32
+    # quotient rounds onto k + 1/2 exactly (then half-to-even goes down): the
+    # decision is the fp32 one, found by search over fp32 neighbours
+    from fractions import Fraction
+    rng = np.random.default_rng(44)
+    found = 0
+    for _ in range(4000):
+        m = np.float32(rng.uniform(0.5, 2.0))
+        s = np.float32(m / np.float32(7.0))
+        k = 2 * int(rng.integers(0, 3))            # even k: half-to-even goes down to k
+        w = np.float32((k + 0.5) * float(s))
+        for _ in range(3):
+            w = np.nextafter(w, np.float32(np.inf))
+            exact = Fraction(float(w)) / Fraction(float(s))
+            fq = np.float32(w / s)
+            if exact > Fraction(2 * k + 1, 2) and fq == np.float32(k + 0.5) and abs(w) < m:
+                q, sc = O.quantize_int4(np.array([[m, w]], dtype=np.float32))
+                assert sc[0] == s
+                assert int(q[0, 1]) == k == _rint_half_even(fq)  # fp32 quotient, half to even
+                # (the exact quotient, past k + 1/2, would give k + 1)
+                found += 1
+                break
+        if found >= 5:
+            break
+    assert found >= 5
+
+
+def test_quantize_int4_ties_to_even():
+    s = np.float32(0.25)
+    w = np.array([[7 * s, 2.5 * s, 3.5 * s, -2.5 * s, -3.5 * s, 0.5 * s, -0.5 * s, 6.5 * s]],
+                 dtype=np.float32)
+    q, sc = O.quantize_int4(w)
+    assert sc[0] == s
+    assert q[0].tolist() == [7, 2, 4, -2, -4, 0, 0, 6]
+
+
+def test_int4_packing_bytes():
+    # element 2i in the low nibble, 2i+1 in the high nibble, 4-bit two's
+    # complement: byte = (q_even mod 16) + 16 * (q_odd mod 16)
+    q = np.array([[1, -1, -7, 7, 0, 3, -2, 0]], dtype=np.int8)
+    expect = [1 + 16 * 15, 9 + 16 * 7, 0 + 16 * 3, 14 + 16 * 0]
+    assert O.pack_int4(q)[0].tolist() == expect
+    # every pair of codes survives the round trip
+    a, b = np.meshgrid(np.arange(-7, 8), np.arange(-7, 8))
+    pairs = np.stack([a.ravel(), b.ravel()], axis=1).reshape(1, -1).astype(np.int8)
+    p = O.pack_int4(pairs)
+    assert p.dtype == np.uint8 and p.shape == (1, pairs.shape[1] // 2)
+    assert (O.unpack_int4(p) == pairs).all()
+    for i in range(p.shape[1]):
+        lo, hi = int(pairs[0, 2 * i]), int(pairs[0, 2 * i + 1])
+        assert int(p[0, i]) == (lo % 16) + 16 * (hi % 16)
+
+
+def test_int4_expert_equals_dense_ffn_on_dequantized_weights():
+    rng = np.random.default_rng(43)
+    d, f = 16, 24
+    x = rng.standard_normal((5, d))
+    w1 = rng.standard_normal((f, d)).astype(np.float32)
+    w2 = rng.standard_normal((d, f)).astype(np.float32)
+    q1, s1 = O.quantize_int4(w1)
+    q2, s2 = O.quantize_int4(w2)
+    W1 = s1.astype(np.float64)[:, None] * q1
+    W2 = s2.astype(np.float64)[:, None] * q2
+    h = x @ W1.T
+    ref = np.array([[0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in row] for row in h]) @ W2.T
+    got = O.expert_ffn(x, O.dequantize_int4(q1, s1), None, O.dequantize_int4(q2, s2), None)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- whole layer
 def _tiny_problem(rng, T, d, f, N, *, biases=True, fs=0):
     x = _bf16_values(rng, (T, d))
