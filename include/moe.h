@@ -25,8 +25,10 @@
  *
  * Conventions for every entry point:
  *   - Ownership: the caller owns every buffer.  The library never allocates
- *     device memory, never frees, and never synchronises the stream; every
- *     call only enqueues kernels on `stream` and returns.
+ *     device memory (beyond the fixed scratch array of
+ *     moe_layer_forward_noalloc, which exists once per GPU), never frees,
+ *     and never synchronises the stream; every call only enqueues kernels on
+ *     `stream` and returns.
  *   - Pointers marked [dev] are device pointers, 16-byte aligned; [host]
  *     pointers are read during the call only.
  *   - Layout: row-major; weight matrices use the nn.Linear [out, in] layout,
@@ -236,6 +238,27 @@ int moe_router_z_loss(const moe_config_t *cfg, const float *logits, float beta, 
 int moe_layer_forward(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
                       void *out, float *aux_out, int32_t *counts_out, int32_t *n_dropped_out,
                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The same layer as moe_layer_forward, for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is a device array the
+ * library holds itself (MOE_NOALLOC_SCRATCH_BYTES per GPU, from the first
+ * call on that GPU until the process ends), so the call allocates nothing and
+ * takes no workspace argument; results are those of moe_layer_forward,
+ * bit for bit.
+ *   Arguments as moe_layer_forward without ws / ws_bytes.
+ *   Limit: moe_workspace_size(cfg, MOE_STAGE_LAYER) must not exceed
+ *   MOE_NOALLOC_SCRATCH_BYTES (decode-shaped and small-batch layers fit);
+ *   otherwise MOE_ERR_WORKSPACE and nothing is enqueued.
+ *   Concurrency: every call on one GPU uses that GPU's one scratch array;
+ *   calls that overlap on one GPU (other streams or threads, without an
+ *   ordering between them) race and give undefined results.
+ *   Errors: as moe_layer_forward; MOE_ERR_HIP if the scratch address cannot
+ *   be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int moe_layer_forward_noalloc(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
+                              void *out, float *aux_out, int32_t *counts_out,
+                              int32_t *n_dropped_out, hipStream_t stream);
 
 /* Weight-only INT8 quantisation of a weight matrix, one fp32 scale per row
  * (lmnt.cn §4.3: expert weights compressed to INT8 for inference; the pages

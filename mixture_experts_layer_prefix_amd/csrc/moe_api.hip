@@ -3,10 +3,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/moe.h"
 #include "moe_internal.h"
+
+// The workspace of moe_layer_forward_noalloc: a file-scope device array, so
+// that call needs no allocation.  Each GPU the library runs on holds its own
+// copy (MOE_NOALLOC_SCRATCH_BYTES) until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: kernels and
+// copies get the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -801,6 +809,71 @@ int check_saved(const moe_config_t* c, const moe_saved_t* sv) {
   return MOE_OK;
 }
 
+// The whole layer on a caller-sized workspace (moe_layer_forward and
+// moe_layer_forward_noalloc).
+int layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_t* w, void* out,
+                  float* aux_out, int32_t* counts_out, int32_t* n_dropped_out, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  int r = check_ws(cfg, MOE_STAGE_LAYER, ws, ws_bytes);
+  if (r != MOE_OK) return r;
+  Carver cv{static_cast<char*>(ws)};
+  LayerWs lw;
+  carve_layer(cv, cfg, &lw);
+  int32_t* counts = counts_out ? counts_out : lw.counts;
+  int32_t* ndrop = n_dropped_out ? n_dropped_out : lw.n_dropped;
+
+  r = do_route(cfg, x, w, lw.logits, lw.idx, lw.w, lw.route, stream);
+  if (r != MOE_OK) return r;
+  r = do_dispatch(cfg, lw.idx, x, counts, lw.offsets, lw.slot_row, lw.row_token, lw.x_perm,
+                  ndrop, lw.disp, stream);
+  if (r != MOE_OK) return r;
+  r = do_ffn(cfg, lw.x_perm, lw.offsets, w, x, lw.y_perm, lw.y_shared, lw.ffn, stream, lw.ffn.h,
+             lw.ffn.h_shared);
+  if (r != MOE_OK) return r;
+  r = do_combine(cfg, lw.y_perm, lw.slot_row, lw.w, lw.y_shared, out, stream);
+  if (r != MOE_OK) return r;
+  if (aux_out) {
+    r = do_aux(cfg, lw.logits, counts, aux_out, lw.aux, stream);
+    if (r != MOE_OK) return r;
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- allocation-free layer
+// The address of `scratch` (above) on each device, taken once per device on
+// moe_layer_forward_noalloc's first call there.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (nullptr with the error recorded
+// on failure).
+void* scratch_for_current_device(int* code) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *code = fail(MOE_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *code = fail(MOE_ERR_UNSUPPORTED, "device index beyond the library's scratch table");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *code = fail(MOE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                    (e != hipSuccess ? hipGetErrorString(e) : "null address"));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -976,29 +1049,29 @@ int moe_layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_
   if (r != MOE_OK) return r;
   MOE_REQUIRE_PTR(out, "out");
   MOE_OPTIONAL_PTR(counts_out, "counts_out");
-  r = check_ws(cfg, MOE_STAGE_LAYER, ws, ws_bytes);
-  if (r != MOE_OK) return r;
-  Carver cv{static_cast<char*>(ws)};
-  LayerWs lw;
-  carve_layer(cv, cfg, &lw);
-  int32_t* counts = counts_out ? counts_out : lw.counts;
-  int32_t* ndrop = n_dropped_out ? n_dropped_out : lw.n_dropped;
+  return layer_forward(cfg, x, w, out, aux_out, counts_out, n_dropped_out, ws, ws_bytes, stream);
+}
 
-  r = do_route(cfg, x, w, lw.logits, lw.idx, lw.w, lw.route, stream);
+int moe_layer_forward_noalloc(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                              void* out, float* aux_out, int32_t* counts_out,
+                              int32_t* n_dropped_out, hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(x, "x");
+  int r = check_weights(cfg, w, true, true);
   if (r != MOE_OK) return r;
-  r = do_dispatch(cfg, lw.idx, x, counts, lw.offsets, lw.slot_row, lw.row_token, lw.x_perm,
-                  ndrop, lw.disp, stream);
-  if (r != MOE_OK) return r;
-  r = do_ffn(cfg, lw.x_perm, lw.offsets, w, x, lw.y_perm, lw.y_shared, lw.ffn, stream, lw.ffn.h,
-             lw.ffn.h_shared);
-  if (r != MOE_OK) return r;
-  r = do_combine(cfg, lw.y_perm, lw.slot_row, lw.w, lw.y_shared, out, stream);
-  if (r != MOE_OK) return r;
-  if (aux_out) {
-    r = do_aux(cfg, lw.logits, counts, aux_out, lw.aux, stream);
-    if (r != MOE_OK) return r;
-  }
-  return MOE_OK;
+  MOE_REQUIRE_PTR(out, "out");
+  MOE_OPTIONAL_PTR(counts_out, "counts_out");
+  const size_t need = stage_bytes(cfg, MOE_STAGE_LAYER);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_layer_forward_noalloc: this layer needs " + std::to_string(need) +
+                    " bytes of workspace, more than the " + std::to_string(kScratchBytes) +
+                    " bytes of device scratch the library holds (use moe_layer_forward)");
+  int code = MOE_OK;
+  void* ptr = scratch_for_current_device(&code);
+  if (!ptr) return code;
+  return layer_forward(cfg, x, w, out, aux_out, counts_out, n_dropped_out, ptr, kScratchBytes,
+                       stream);
 }
 
 // ---------------------------------------------------------------- training entry points

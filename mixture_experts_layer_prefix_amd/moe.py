@@ -25,7 +25,8 @@ ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "
                 "moe_routing_stats", "moe_quantize_int8", "moe_layer_forward",
                 "moe_expert_ffn_train", "moe_layer_forward_train", "moe_combine_backward",
                 "moe_expert_ffn_backward", "moe_route_backward", "moe_dispatch_backward",
-                "moe_layer_backward", "moe_last_error")
+                "moe_layer_backward", "moe_layer_forward_noalloc", "moe_last_error")
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeConfig(ctypes.Structure):
@@ -90,6 +91,7 @@ def lib():
     L.moe_routing_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_quantize_int8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_layer_forward_noalloc.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp]
     svp, gp, f32 = ctypes.POINTER(MoeSaved), ctypes.POINTER(MoeGrads), ctypes.c_float
     L.moe_expert_ffn_train.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward_train.argtypes = [cfgp, vp, wp, vp, vp, svp, vp, sz, vp]
@@ -102,7 +104,8 @@ def lib():
     L.moe_layer_backward.argtypes = [cfgp, vp, wp, svp, vp, f32, f32, f32, vp, gp, vp, sz, vp]
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
                  "moe_router_z_loss", "moe_routing_stats", "moe_quantize_int8",
-                 "moe_layer_forward", "moe_expert_ffn_train", "moe_layer_forward_train",
+                 "moe_layer_forward", "moe_layer_forward_noalloc", "moe_expert_ffn_train",
+                 "moe_layer_forward_train",
                  "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward",
                  "moe_dispatch_backward", "moe_layer_backward"):
         getattr(L, name).restype = ctypes.c_int
@@ -258,6 +261,13 @@ def moe_layer_forward(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,
     _check(lib().moe_layer_forward(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(out),
                                    _p(aux_out), _p(counts_out), _p(n_dropped_out), p, n,
                                    _stream(stream)))
+
+
+def moe_layer_forward_noalloc(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,
+                              n_dropped_out=None, stream=None):
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(out),
+                                           _p(aux_out), _p(counts_out), _p(n_dropped_out),
+                                           _stream(stream)))
 
 
 # ---------------------------------------------------------------- training entry points

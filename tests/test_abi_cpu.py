@@ -236,3 +236,22 @@ def test_training_entry_points_check_arguments():
     assert L.moe_expert_ffn_train(ctypes.byref(cfg), FAKE, FAKE, ctypes.byref(W), None, FAKE,
                                   FAKE, FAKE, FAKE, None, None, FAKE * 256, big,
                                   None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_layer_rejects_layers_beyond_its_scratch():
+    """moe_layer_forward_noalloc refuses, on the host and before any HIP call,
+    a layer whose workspace exceeds the fixed per-GPU scratch."""
+    big = _cfg(T=4096, d_model=4096, d_ff=14336, n_experts=8, top_k=2)
+    assert moe.workspace_size(big, "layer") > moe.NOALLOC_SCRATCH_BYTES
+    W = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=FAKE)
+    r = moe.lib().moe_layer_forward_noalloc(ctypes.byref(big), FAKE, ctypes.byref(W), FAKE, None,
+                                            None, None, None)
+    assert r == moe.MOE_ERR_WORKSPACE
+    assert b"scratch" in moe.lib().moe_last_error()
+    # argument checks come first, as for moe_layer_forward
+    small = _cfg()
+    assert moe.workspace_size(small, "layer") <= moe.NOALLOC_SCRATCH_BYTES
+    assert moe.lib().moe_layer_forward_noalloc(ctypes.byref(small), None, ctypes.byref(W), FAKE,
+                                               None, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_layer_forward_noalloc(ctypes.byref(small), FAKE, ctypes.byref(W), FAKE,
+                                               None, FAKE + 4, None, None) == moe.MOE_ERR_INVALID_ARG
