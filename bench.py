@@ -59,9 +59,12 @@ def algorithmic(shape, counts, M):
     eb = 4 if shape.dtype == "f32" else 2
     touched = int((counts > 0).sum())
     flops = 2 * 2 * M * d * f + (2 * 2 * T * d * fs if fs else 0)
-    if getattr(shape, "weight_quant", "none") == "int8":
-        # INT8 codes plus one fp32 scale per output row of w1 and w2
-        wbytes = touched * (2 * d * f + 4 * (f + d)) + (2 * d * fs * eb if fs else 0)
+    wq = getattr(shape, "weight_quant", "none")
+    if wq in ("int8", "int4"):
+        # INT8 (1 byte) or packed INT4 (half a byte) codes plus one fp32 scale
+        # per output row of w1 and w2
+        cb = 1 if wq == "int8" else 2
+        wbytes = touched * (2 * d * f // cb + 4 * (f + d)) + (2 * d * fs * eb if fs else 0)
     else:
         wbytes = touched * 2 * d * f * eb + (2 * d * fs * eb if fs else 0)
     # x_perm read, h written and read back, y_perm written (+ shared x, h_s, y_s)
@@ -85,13 +88,15 @@ def cpu_baseline(shape, inp, n_tok):
 
     get = lambda e: tuple(None if a is None else (inputs.bf16_widen(a) if a.dtype == np.uint16 else a)
                           for a in inp.expert(e))
-    if getattr(shape, "weight_quant", "none") == "int8":
+    wq = getattr(shape, "weight_quant", "none")
+    if wq in ("int8", "int4"):
         base = get
+        qz, dq = ((O.quantize_int8, O.dequantize_int8) if wq == "int8"
+                  else (O.quantize_int4, O.dequantize_int4))
 
         def get(e):
             w1, b1, w2, b2 = base(e)
-            return (O.dequantize_int8(*O.quantize_int8(w1)), b1,
-                    O.dequantize_int8(*O.quantize_int8(w2)), b2)
+            return dq(*qz(w1)), b1, dq(*qz(w2)), b2
     shared = (inp.f32("ws1"), inp.f32("ws2")) if shape.d_ff_shared else None
     x_all = inp.f32("x")
 
@@ -371,9 +376,9 @@ def main():
     t0 = time.time()
     inp = inputs.make_inputs(shape, seed=args.seed)
     t = inputs.to_torch(inp, dev)
-    if shape.weight_quant == "int8":
+    if shape.weight_quant in ("int8", "int4"):
         # weight preprocessing, once, outside the timed region
-        t = moe.quantize_expert_weights(t)
+        t = moe.quantize_expert_weights(t, bits=8 if shape.weight_quant == "int8" else 4)
         torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 

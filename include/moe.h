@@ -21,7 +21,7 @@
  *     capacity drop).
  *   wiblog.cn "MoE 专家路由如何实现稀疏激活": fine-grained and shared experts.
  *   lmnt.cn §4.3 and yunthe.com's deployment section: expert weights stored
- *     as INT8 for inference (weight-only quantisation).
+ *     as INT8 or INT4 for inference (weight-only quantisation).
  *
  * Conventions for every entry point:
  *   - Ownership: the caller owns every buffer.  The library never allocates
@@ -67,9 +67,14 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
 /* Storage of the routed experts' weights w1 / w2.  MOE_WQ_INT8: int8 codes q
  * with one fp32 scale per output row (w1_scale [N, f], w2_scale [N, d]); the
- * expert uses the weights scale * q (moe_quantize_int8 makes them).  Only
- * with dtype MOE_BF16; the shared expert and the router stay in dtype. */
-typedef enum { MOE_WQ_NONE = 0, MOE_WQ_INT8 = 1 } moe_weight_quant_t;
+ * expert uses the weights scale * q (moe_quantize_int8 makes them).
+ * MOE_WQ_INT4: 4-bit codes q in [-7, 7], two per byte along the row (element
+ * 2i in the low nibble of byte i, 4-bit two's complement), so w1 is
+ * [N, f, d/2] bytes and w2 [N, d, f/2] bytes, with the same fp32 row scales
+ * (moe_quantize_int4 makes them); needs d_model and d_ff multiples of 128.
+ * Quantised weights need dtype MOE_BF16; the shared expert and the router
+ * stay in dtype. */
+typedef enum { MOE_WQ_NONE = 0, MOE_WQ_INT8 = 1, MOE_WQ_INT4 = 2 } moe_weight_quant_t;
 
 typedef struct {
   int32_t T;           /* tokens in the batch                                  */
@@ -89,14 +94,14 @@ typedef struct {
   const float *b_router;    /* [dev] [N] fp32 or NULL: added to the logits         */
   const float *logit_offset;/* [dev] [N] fp32 or NULL: added to the logits         */
   const float *sel_bias;    /* [dev] [N] fp32 or NULL: added for selection only    */
-  const void *w1;           /* [dev] [N, f, d] dtype                               */
+  const void *w1;           /* [dev] [N, f, d] dtype (codes: see moe_weight_quant_t) */
   const void *b1;           /* [dev] [N, f] dtype or NULL                          */
-  const void *w2;           /* [dev] [N, d, f] dtype                               */
+  const void *w2;           /* [dev] [N, d, f] dtype (codes: see moe_weight_quant_t) */
   const void *b2;           /* [dev] [N, d] dtype or NULL                          */
   const void *ws1;          /* [dev] [f_s, d] dtype (shared expert) or NULL        */
   const void *ws2;          /* [dev] [d, f_s] dtype (shared expert) or NULL        */
-  const float *w1_scale;    /* [dev] [N, f] fp32 with MOE_WQ_INT8, else ignored    */
-  const float *w2_scale;    /* [dev] [N, d] fp32 with MOE_WQ_INT8, else ignored    */
+  const float *w1_scale;    /* [dev] [N, f] fp32 with quantised weights, else ignored */
+  const float *w2_scale;    /* [dev] [N, d] fp32 with quantised weights, else ignored */
 } moe_weights_t;
 
 typedef enum {
@@ -275,6 +280,23 @@ int moe_layer_forward_noalloc(const moe_config_t *cfg, const void *x, const moe_
 int moe_quantize_int8(const void *w, int32_t dtype, int64_t rows, int32_t cols, int8_t *q,
                       float *scale, hipStream_t stream);
 
+/* Weight-only INT4 quantisation, one fp32 scale per row (lmnt.cn §4.3 names
+ * INT4 beside INT8 for the expert weights, a quarter of their 16-bit memory
+ * and bandwidth; the scheme is moe_quantize_int8's with 4-bit codes):
+ *   scale[r] = fp32(max_c |w[r, c]| / 7)
+ *   q[r, c]  = clamp(round_half_even(fp32(w[r, c] / scale[r])), -7, 7)
+ * IEEE fp32 divisions (codes reproducible bit for bit); a row of zeros gets
+ * scale 0 and codes 0.  Codes are packed two per byte: element 2i of a row in
+ * the low nibble of byte i, element 2i+1 in the high nibble (4-bit two's
+ * complement).  For w1 [N, f, d]: rows = N*f, cols = d (w2: rows = N*d,
+ * cols = f).
+ *   w     [dev] [rows, cols] dtype (MOE_BF16 or MOE_F32) in;
+ *   q     [dev] [rows, cols/2] bytes out;  scale [dev] [rows] fp32 out.
+ * Errors: MOE_ERR_INVALID_ARG for NULL or misaligned pointers, rows < 1, cols
+ * not a positive multiple of 64, or an unknown dtype. */
+int moe_quantize_int4(const void *w, int32_t dtype, int64_t rows, int32_t cols, uint8_t *q,
+                      float *scale, hipStream_t stream);
+
 /* ------------------------------------------------------------------ training
  * The backward pass (lmnt.cn MoE walkthrough §2.2: in training the K routing
  * weights take part in back-propagation, which is how the gate learns its
@@ -296,8 +318,8 @@ int moe_quantize_int8(const void *w, int32_t dtype, int64_t rows, int32_t cols, 
  * weight and bias gradients are stored in dtype; every sum over rows or
  * tokens is fp32 with a fixed order (deterministic); the router gradients
  * d_w_router, d_b_router and the router's share of d_x are fp32.
- * INT8 experts are inference-only: every training entry point returns
- * MOE_ERR_UNSUPPORTED for MOE_WQ_INT8, and for
+ * Quantised experts are inference-only: every training entry point returns
+ * MOE_ERR_UNSUPPORTED for MOE_WQ_INT8 and MOE_WQ_INT4, and for
  * max(d_model, d_ff, d_ff_shared) * (T*K + 32*N) >= 2^31.
  */
 

@@ -36,7 +36,7 @@ class MoEShape:
     sel_bias: bool = False         # per-expert selection-only bias ~ U(-0.5, 0.5)
     aux_alpha: float = 0.0         # >0: also compute alpha*N*sum(f*P)
     index: int = 0                 # position in the list below; keys the input streams
-    weight_quant: str = "none"     # "int8": routed w1 / w2 quantised per output row
+    weight_quant: str = "none"     # "int8" / "int4": routed w1 / w2 quantised per output row
 
     @property
     def M_max(self) -> int:
@@ -77,4 +77,11 @@ INT8 = [DECODE.with_(name="decode_t32_e64_w8", weight_quant="int8"),
         SWITCH_CAPACITY.with_(name="switch_top1_capacity_w8", weight_quant="int8"),
         DEEPSEEK_FINE.with_(name="deepseek_v3_fine_grained_w8", weight_quant="int8")]
 
-BY_NAME = {c.name: c for c in ALL + INT8}
+# The same three again with INT4 routed expert weights (lmnt.cn walkthrough
+# §4.3 names INT4 beside INT8; yunthe.com's deployment section cites 4-bit
+# weight-only formats).
+INT4 = [DECODE.with_(name="decode_t32_e64_w4", weight_quant="int4"),
+        SWITCH_CAPACITY.with_(name="switch_top1_capacity_w4", weight_quant="int4"),
+        DEEPSEEK_FINE.with_(name="deepseek_v3_fine_grained_w4", weight_quant="int4")]
+
+BY_NAME = {c.name: c for c in ALL + INT8 + INT4}

@@ -23,7 +23,7 @@
 //     is staged through LDS and written as whole rows;
 //   - rows past an expert's end read a clamped valid row and are not stored;
 //     the GELU epilogue uses the Abramowitz-Stegun 7.1.26 erf (gelu_as);
-//   - variants: INT8 weights (codes widened in registers), weight gradients
+//   - variants: INT8 and INT4 weights (codes widened in registers), weight gradients
 //     over per-expert k-segments (and a two-workgroups-per-CU kernel of 256 x
 //     128 tiles for short segments), k-major weights for input gradients.
 // MOE_KPAIRS=0 builds the four-stage loop for the bf16 forward tiles too.
@@ -260,7 +260,8 @@ __device__ __forceinline__ void store_out(uint16_t* dst, const uint16_t* src) {
 // KM: k-major weights, W_e stored [Kd, Nd] (the input gradients of the
 // backward read the forward's weights as they are).
 // NTW: the weights' direct loads are non-temporal (lds_load16<2>).
-template <bool GELU, bool QW, int NS, int LAY, bool WG, bool KM, bool NTW = false>
+template <bool GELU, bool QW, int NS, int LAY, bool WG, bool KM, bool NTW = false,
+          bool Q4 = false>
 __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
   using Lay = W4Layout<LAY>;
@@ -272,7 +273,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   // k-step, INT8 rows of two)
   constexpr int NLB = Lay::BNL / RPI / NW;
   static_assert(!KM || Lay::BNL == BN, "k-major weight stages hold 256 columns");
-  static_assert(!QW || NS == 4, "the INT8 wait counts below assume four stages");
+  static_assert(!QW || NS == 4, "the INT8 / INT4 wait counts below assume four stages");
+  static_assert(!Q4 || QW, "INT4 codes are a form of quantised weights");
   static_assert(NLA * RPI * NW == Lay::AROWS && NLB > 0, "loads split evenly over the waves");
   constexpr int NLS = NLA + NLB;
   const int Kd = a.Kd, Nd = a.Nd;
@@ -296,7 +298,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     C = static_cast<uint16_t*>(a.Cs);
   } else {
     A = static_cast<const uint16_t*>(a.A);
-    W = static_cast<const char*>(a.W) + (int64_t)tr.e * Nd * Kd * (QW ? 1 : 2);
+    W = static_cast<const char*>(a.W) + (Q4 ? (int64_t)tr.e * Nd * (Kd / 2)
+                                            : (int64_t)tr.e * Nd * Kd * (QW ? 1 : 2));
     if (a.bias) bias = static_cast<const uint16_t*>(a.bias) + (int64_t)tr.e * Nd;
     if (QW) wsc = a.wscale + (int64_t)tr.e * Nd;
     C = static_cast<uint16_t*>(a.C);
@@ -324,7 +327,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     if constexpr (QW) {
       const int row = (wave * NLB + i) * RPI + r_in;
       const int lchunk = (lane % CH) ^ swz(row);
-      offB[i] = (uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)Kd + lchunk * 16;
+      offB[i] = (uint32_t)min(tr.n0 + row, Nd - 1) * (uint32_t)(Q4 ? Kd / 2 : Kd) + lchunk * 16;
     } else if constexpr (KM) {
       // instruction i fills k-rows 2 (w NLB + i) and + 1, 32 lanes per row;
       // columns past Nd (partial tiles) read a valid chunk and are not stored
@@ -345,7 +348,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   };
   auto issue_b = [&](int buf, int k0) {
     char* base = reinterpret_cast<char*>(lds + buf * STG + Lay::AR * BK) + wave * NLB * 1024;
-    const uint32_t kb = KM ? (uint32_t)k0 * (uint32_t)Nd * 2 : k0 * (QW ? 1 : 2);
+    const uint32_t kb = KM ? (uint32_t)k0 * (uint32_t)Nd * 2 : (Q4 ? k0 / 2 : k0 * (QW ? 1 : 2));
     if constexpr (NTW) {
 #pragma unroll
       for (int i = 0; i < NLB; ++i) lds_load16<2>(W + offB[i] + kb, base + i * 1024);
@@ -400,7 +403,9 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   const int xrow = (W4_TM + wm * 32 + (lane & 31)) * BK;
   constexpr int MX = MI + (EX ? 1 : 0);   // A fragments per half
   // W fragments: bf16x8, or 8 INT8 codes widened just before their MFMAs
-  using BF = typename std::conditional<QW, uint2, bf16x8>::type;
+  // (INT4: one 32-bit word of 8 codes)
+  using BF = typename std::conditional<Q4, uint32_t,
+                                       typename std::conditional<QW, uint2, bf16x8>::type>::type;
   // INT8: byte offset of this lane's row (n = lane mod 32) in a pair region
   const int browq = (wn * WCOLS + (lane & 31)) * 64;
   // KM: this lane's byte offset inside a stage's weight region (source role:
@@ -410,7 +415,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   const int kmb = (8 * (kg >> 1) + kq) * 512 + (2 * (kg & 1) + (ku >> 1)) * 16 + (ku & 1) * 8;
   bf16x8 fa0[MX], fa1[MX];
   BF fb0[NI], fb1[NI];
-  uint2 fbq[QW ? NI : 1];   // INT8: the second half's codes, read with the first's
+  BF fbq[QW ? NI : 1];   // INT8 / INT4: the second half's codes, read with the first's
   f32x16 accx[EX ? NI : 1];
   if constexpr (EX) {
 #pragma unroll
@@ -421,7 +426,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   // Fragments of half kk: lane half h = lane / 32 holds k = 16 kk + 8 h + 0..7
   // of the step (bf16 weights), or k = 16 h + 8 kk + 0..7 (INT8 weights, so
   // that one 16-byte chunk of codes serves both halves).
-  auto read_half = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int kk) {
+  // kabs: the k-step's index (INT4: which of the two code regions holds it)
+  auto read_half = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int kk, int kabs) {
     const uint16_t* As = lds + buf * STG;
     const uint16_t* Bs = As + Lay::AR * BK;
     const int pc = ((QW ? (lane >> 5) * 2 + kk : kk * 2 + (lane >> 5)) ^ sw) * 8;
@@ -431,7 +437,20 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     if constexpr (EX) fa[MI] = *reinterpret_cast<const bf16x8*>(As + xrow + pc);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      if constexpr (QW) {
+      if constexpr (Q4) {
+        if (kk == 0) {
+          // INT4: chunk buf (= k-step mod 4) of the region of stage 0 or 2
+          // holding this group of four k-steps; lane half h reads its 8 bytes
+          const char* Bq = reinterpret_cast<const char*>(lds + ((kabs >> 2) & 1) * 2 * STG +
+                                                         Lay::AR * BK);
+          const uint2 q = *reinterpret_cast<const uint2*>(
+              Bq + browq + i * 32 * 64 + ((buf ^ sw) * 16) + (lane >> 5) * 8);
+          fb[i] = q.x;
+          fbq[i] = q.y;
+        } else {
+          fb[i] = fbq[i];
+        }
+      } else if constexpr (QW) {
         if (kk == 0) {
           // chunk 2 (buf mod 2) + lane / 32 of the pair region of the even stage
           const char* Bq = reinterpret_cast<const char*>(lds + (buf & ~1) * STG + Lay::AR * BK);
@@ -470,7 +489,9 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     }
   };
   auto wfrag = [&](const BF& f) -> bf16x8 {
-    if constexpr (QW)
+    if constexpr (Q4)
+      return __builtin_bit_cast(bf16x8, int4x8_to_bf16x8(f));
+    else if constexpr (QW)
       return __builtin_bit_cast(bf16x8, int8x8_to_bf16x8(f));
     else
       return f;
@@ -565,28 +586,39 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   // stages load the codes of their pair (Kd is a multiple of 64, so KT is
   // even), and a k-step waits for fewer younger loads when the stage it
   // waits for is even (no codes were issued with the stage after it).
+  // INT4: stages 4g load the codes of k-steps 4g .. 4g+3 (64 bytes a row,
+  // Kd a multiple of 128) into the weight region of stage 0 (g even) or 2 (g
+  // odd); with codes issued at one step in four, the k-step of phase 2 is
+  // the one that waits for fewer younger loads.
+  constexpr int CPL = Q4 ? 4 : 2;   // quantised: k-steps per code load
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) {
     issue_a(st, min(st, KT - 1) * BK);
     if (!QW)
       issue_b(st, min(st, KT - 1) * BK);
-    else if ((st & 1) == 0)
-      issue_b(st, min(st, KT - 2) * BK);
+    else if (st % CPL == 0)
+      issue_b(st, min(st, KT - CPL) * BK);
   }
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QW ? 2 * NLA + NLB : NLS * (NS - 2)) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Q4 ? 2 * NLA : QW ? 2 * NLA + NLB : NLS * (NS - 2))
+               : "memory");
   barrier();
-  read_half(fa0, fb0, 0, 0);
+  read_half(fa0, fb0, 0, 0, 0);
 
-  // one k-step; ODD (INT8 only): kt is odd.  The INT8 loop runs two steps
-  // per iteration so that the parity is known at compile time.
-  auto step = [&](int kt, auto odd_tag) {
-    constexpr bool ODD = decltype(odd_tag)::value;
+  // one k-step; PH (quantised weights only): kt mod CPL.  The quantised loops
+  // run CPL steps per iteration so that the phase is known at compile time.
+  auto step = [&](int kt, auto ph_tag) {
+    constexpr int PH = decltype(ph_tag)::value;
+    // the step whose second half issues the codes of stage kt+NS-1, and the
+    // step that then waits for one code load fewer (INT8: PH 1 and 0; INT4:
+    // PH 1 and 2)
+    constexpr bool CODES = QW && PH == 1;
+    constexpr bool WAIT_B = QW && PH == (Q4 ? 2 : 0);
     const int buf = kt % NS, nbuf = (kt + NS - 1) % NS;
     const int nk = min(kt + NS - 1, KT - 1) * BK;
     // first half: MFMAs on set 0; set 1 <- second half of this stage; A rows
     // of stage kt+NS-1 into the buffer last read before the previous barrier
     __builtin_amdgcn_sched_barrier(0);
-    read_half(fa1, fb1, buf, 1);
+    read_half(fa1, fb1, buf, 1, kt);
     issue_a(nbuf, nk);
     mfma_half(fa0, fb0);
     interleave(std::integral_constant<int, NLA>{},
@@ -594,7 +626,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     __builtin_amdgcn_sched_barrier(0);
     // own loads of stage kt+1 landed (younger: NS-3 whole stages and this
     // step's A rows), own reads of stage kt done
-    if constexpr (QW && ODD)
+    if constexpr (QW && !WAIT_B)
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * NLA) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(QW ? 2 * NLA + NLB : NLS * (NS - 3) + NLA)
@@ -602,27 +634,38 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     barrier();
     // second half: MFMAs on set 1; set 0 <- first half of stage kt+1 (in the
     // last step this reads a stale buffer that nobody uses); W rows of stage
-    // kt+NS-1 (INT8: only when that stage is even)
+    // kt+NS-1 (quantised: only when that stage starts a code load, into the
+    // region of its group)
     __builtin_amdgcn_sched_barrier(0);
-    read_half(fa0, fb0, (kt + 1) % NS, 0);
-    if constexpr (QW && !ODD) {
+    read_half(fa0, fb0, (kt + 1) % NS, 0, kt + 1);
+    if constexpr (QW && !CODES) {
       mfma_half(fa1, fb1);
       interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, NI>{});
     } else {
-      issue_b(nbuf, QW ? min(kt + NS - 1, KT - 2) * BK : nk);
+      if constexpr (Q4)
+        issue_b((((kt + NS - 1) >> 2) & 1) * 2, min(kt + NS - 1, KT - CPL) * BK);
+      else
+        issue_b(nbuf, QW ? min(kt + NS - 1, KT - CPL) * BK : nk);
       mfma_half(fa1, fb1);
       interleave(std::integral_constant<int, NLB>{},
                  std::integral_constant<int, (KM ? 2 : 1) * NI>{});
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  if constexpr (QW) {
+  if constexpr (Q4) {
+    for (int kt = 0; kt < KT; kt += 4) {
+      step(kt, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+      step(kt + 2, std::integral_constant<int, 2>{});
+      step(kt + 3, std::integral_constant<int, 3>{});
+    }
+  } else if constexpr (QW) {
     for (int kt = 0; kt < KT; kt += 2) {
-      step(kt, std::false_type{});
-      step(kt + 1, std::true_type{});
+      step(kt, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
     }
   } else {
-    for (int kt = 0; kt < KT; ++kt) step(kt, std::false_type{});
+    for (int kt = 0; kt < KT; ++kt) step(kt, std::integral_constant<int, 0>{});
   }
   // no direct-to-LDS load may still be in flight past this point
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -722,25 +765,25 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
 }
 
 // Four-wavefront tile: the wave arrangement from the tile's row count.
-template <bool GELU, bool QW, int NS, bool WG, bool KM, bool NTW = false>
+template <bool GELU, bool QW, int NS, bool WG, bool KM, bool NTW = false, bool Q4 = false>
 __device__ __forceinline__ void w4_rows(const GemmArgs& a, const TileRef& tr, uint16_t* lds,
                                         f32x16 (&acc)[4][4]) {
   const int rows = tr.row_end - tr.row0;
   if (rows > W4_TM)
-    w4_tile<GELU, QW, NS, 3, WG, KM, NTW>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 3, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else if (rows > 192)
-    w4_tile<GELU, QW, NS, 0, WG, KM, NTW>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 0, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else if (rows > 128)
-    w4_tile<GELU, QW, NS, 8, WG, KM, NTW>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 8, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else if (rows > 96)
-    w4_tile<GELU, QW, NS, 1, WG, KM, NTW>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 1, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else if (rows > 64)
-    w4_tile<GELU, QW, NS, 9, WG, KM, NTW>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 9, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else
-    w4_tile<GELU, QW, NS, 2, WG, KM, NTW>(a, tr, lds, acc);
+    w4_tile<GELU, QW, NS, 2, WG, KM, NTW, Q4>(a, tr, lds, acc);
 }
 
-template <bool GELU, bool QW, int NS, bool WG, bool KM, bool NTW = false>
+template <bool GELU, bool QW, int NS, bool WG, bool KM, bool NTW = false, bool Q4 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 gemm_bf16_w4_kernel(GemmArgs a) {
   // the output tile is staged through the same LDS after the main loop
@@ -759,14 +802,14 @@ gemm_bf16_w4_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   if constexpr (!KM && !WG) {
     if (tr.wide) {   // routed tiles only
-      w4_tile<GELU, QW, NS, 10, WG, KM>(a, tr, lds, acc);
+      w4_tile<GELU, QW, NS, 10, WG, KM, false, Q4>(a, tr, lds, acc);
       return;
     }
   }
   if (QW && tr.shared)
     w4_rows<GELU, false, NS, WG, KM>(a, tr, lds, acc);
   else
-    w4_rows<GELU, QW, NS, WG, KM, NTW>(a, tr, lds, acc);
+    w4_rows<GELU, QW, NS, WG, KM, NTW, Q4>(a, tr, lds, acc);
 }
 
 // The same tiles with eight wavefronts (two per SIMD, at most 256 registers
@@ -813,7 +856,7 @@ gemm_bf16_wg2_kernel(GemmArgs a) {
 
 // Eight wavefronts serve the backward's GEMMs, which never have INT8 weights
 // or wide tiles.
-template <bool GELU, bool QW, bool WG, bool KM, bool NTW = false>
+template <bool GELU, bool QW, bool WG, bool KM, bool NTW = false, bool Q4 = false>
 void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
   if constexpr (!QW) {
     if (a.waves8 && a.wide_rows == 0) {
@@ -822,8 +865,8 @@ void launch_w(const GemmArgs& a, int grid, hipStream_t s) {
       return;
     }
   }
-  hipLaunchKernelGGL((gemm_bf16_w4_kernel<GELU, QW, W4_NS, WG, KM, NTW>), dim3(grid), dim3(256), 0, s,
-                     a);
+  hipLaunchKernelGGL((gemm_bf16_w4_kernel<GELU, QW, W4_NS, WG, KM, NTW, Q4>), dim3(grid),
+                     dim3(256), 0, s, a);
 }
 
 }  // namespace
@@ -843,6 +886,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, bool gelu, hipStream_t s) {
     launch_w<false, false, true, false>(a, grid, s);
   else if (a.wkmaj)
     launch_w<false, false, false, true>(a, grid, s);
+  else if (a.wscale && a.w4)
+    gelu ? launch_w<true, true, false, false, false, true>(a, grid, s)
+         : launch_w<false, true, false, false, false, true>(a, grid, s);
   else if (a.wscale)
     gelu ? launch_w<true, true, false, false>(a, grid, s)
          : launch_w<false, true, false, false>(a, grid, s);

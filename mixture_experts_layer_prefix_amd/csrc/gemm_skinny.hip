@@ -37,17 +37,21 @@ constexpr int U = 8;                    // k-steps of 32 in flight (bf16 weights
 // activation loads are two thirds of its load instructions there (same-GPU:
 // the decode-shaped INT8 stage 10% faster); with bf16 weights NR = 2
 // measured 5% slower and NR = 1 stays.
-template <bool QW>
-constexpr int skinny_nr() { return QW ? 2 : 1; }
+template <bool QW, bool Q4 = false>
+constexpr int skinny_nr() { return Q4 ? 4 : (QW ? 2 : 1); }
 
 // INT8 weights (QW): a lane loads 16 codes = one 16-byte load per 64-wide
 // k-block (its slice is k = 64j + 16*(lane/16) .. +16) and feeds two MFMAs
 // with the first and second 8; the activations use the same permutation of
 // k inside the block (the dot product does not depend on it).  The row
 // scale multiplies the result before the bias.
-template <bool GELU, bool QW, int KS>
+// INT4 weights (Q4, with QW): a lane loads 16 bytes = 32 codes per 128-wide
+// k-block (its slice is k = 128j + 32*(lane/16) .. +32) and feeds four MFMAs
+// with 8 codes each, activations in the same order of k; four 16-row tiles
+// per wavefront share each activation load (64 outputs per wavefront).
+template <bool GELU, bool QW, int KS, bool Q4 = false>
 __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
-  constexpr int NR = skinny_nr<QW>();
+  constexpr int NR = skinny_nr<QW, Q4>();
   constexpr int NPW = 16 * NR, NPB = NPW * NTHR / 64;
   const int e = blockIdx.y;
   const int Kd = a.Kd, Nd = a.Nd;
@@ -79,7 +83,8 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   if (n0 >= Nd) return;
   int kb = 0, ke = Kd;   // this wavefront's part of the model dimension
   if constexpr (KS > 1) {
-    const int kq = ((Kd + KS - 1) / KS + 63) / 64 * 64;
+    constexpr int KA = Q4 ? 128 : 64;   // k-block of one load step
+    const int kq = ((Kd + KS - 1) / KS + KA - 1) / KA * KA;
     kb = min(Kd, wave * kq);
     ke = min(Kd, kb + kq);
   }
@@ -128,7 +133,59 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
     bv[j] = bias ? bf16_to_f32(bias[n0 + 16 * j + (lane & 15)]) : 0.f;
     sc[j] = QW ? a.wscale[(int64_t)e * Nd + n0 + 16 * j + (lane & 15)] : 1.f;
   }
-  if constexpr (QW) {
+  if constexpr (Q4) {
+    const int Kb = Kd / 2;             // bytes per row of codes
+    const uint8_t* w4 = static_cast<const uint8_t*>(a.W) + (int64_t)e * Nd * Kb +
+                        (int64_t)(n0 + (lane & 15)) * Kb + (lane >> 4) * 16;
+    constexpr int U4 = 2;              // 128-wide k-blocks in flight
+    for (int g0 = r0; g0 < r1; g0 += 16) {
+      const int ar = g0 + (lane & 15);
+      const bool arow_ok = ar < r1;
+      const uint16_t* arow = A + (int64_t)(arow_ok ? ar : r0) * Kd + (lane >> 4) * 32;
+      f32x4 acc[NR];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = kb; k0 < ke; k0 += 128 * U4) {
+        const int nb = min(U4, (ke - k0) / 128);
+        uint4 wv[NR][U4], av[U4][4];
+#pragma unroll
+        for (int u = 0; u < U4; ++u)
+          if (u < nb) {
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+              wv[j][u] = *reinterpret_cast<const uint4*>(w4 + (int64_t)16 * j * Kb +
+                                                         (k0 + u * 128) / 2);
+          }
+#pragma unroll
+        for (int u = 0; u < U4; ++u)
+          if (u < nb) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              av[u][m] = *reinterpret_cast<const uint4*>(arow + k0 + u * 128 + 8 * m);
+              if (!arow_ok) av[u][m] = make_uint4(0, 0, 0, 0);
+            }
+          }
+#pragma unroll
+        for (int u = 0; u < U4; ++u)
+          if (u < nb) {
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                const uint32_t wd = m == 0 ? wv[j][u].x
+                                  : m == 1 ? wv[j][u].y
+                                  : m == 2 ? wv[j][u].z : wv[j][u].w;
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, av[u][m]),
+                    __builtin_bit_cast(bf16x8, int4x8_to_bf16x8(wd)), acc[j], 0, 0, 0);
+              }
+          }
+      }
+      if (!reduce(acc)) continue;
+      store(acc, g0, sc, bv);
+    }
+    return;
+  } else if constexpr (QW) {
     const int8_t* w8 = static_cast<const int8_t*>(a.W) + (int64_t)e * Nd * Kd +
                        (int64_t)(n0 + (lane & 15)) * Kd + (lane >> 4) * 16;
     constexpr int U8 = 8 / NR;        // 64-wide k-blocks in flight
@@ -232,10 +289,21 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_
   if (E == 0) return hipSuccess;
   // long reductions: the four wavefronts of a workgroup split the model dimension
   const bool ks = a.Kd > a.Nd && a.Kd >= 4096;
-  const int npw = 16 * (a.wscale ? skinny_nr<true>() : skinny_nr<false>());   // per wavefront
+  const bool q4 = a.wscale && a.w4;
+  const int npw = 16 * (q4 ? skinny_nr<true, true>()
+                           : (a.wscale ? skinny_nr<true>() : skinny_nr<false>()));   // per wavefront
   const int per_wg = ks ? npw : npw * NTHR / 64;
   const dim3 grid((a.Nd + per_wg - 1) / per_wg, E);
-  if (ks) {
+  if (q4) {
+    if (ks && gelu)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, true, 4, true>), grid, dim3(NTHR), 0, s, a);
+    else if (ks)
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, true, 4, true>), grid, dim3(NTHR), 0, s, a);
+    else if (gelu)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, true, 1, true>), grid, dim3(NTHR), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, true, 1, true>), grid, dim3(NTHR), 0, s, a);
+  } else if (ks) {
     if (a.wscale && gelu)
       hipLaunchKernelGGL((gemm_skinny_kernel<true, true, 4>), grid, dim3(NTHR), 0, s, a);
     else if (a.wscale)

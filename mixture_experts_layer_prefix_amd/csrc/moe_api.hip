@@ -43,11 +43,14 @@ std::string check_config(const moe_config_t* c, int* code) {
   if (c->d_ff_shared < 0) return "d_ff_shared must be >= 0";
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return "dtype must be MOE_F32 or MOE_BF16";
   if (!isfinite(c->aux_alpha)) return "aux_alpha must be finite";
-  if (c->weight_quant != MOE_WQ_NONE && c->weight_quant != MOE_WQ_INT8)
-    return "weight_quant must be MOE_WQ_NONE or MOE_WQ_INT8";
+  if (c->weight_quant != MOE_WQ_NONE && c->weight_quant != MOE_WQ_INT8 &&
+      c->weight_quant != MOE_WQ_INT4)
+    return "weight_quant must be MOE_WQ_NONE, MOE_WQ_INT8 or MOE_WQ_INT4";
   *code = MOE_ERR_UNSUPPORTED;
-  if (c->weight_quant == MOE_WQ_INT8 && c->dtype != MOE_BF16)
-    return "INT8 expert weights need dtype MOE_BF16";
+  if (c->weight_quant != MOE_WQ_NONE && c->dtype != MOE_BF16)
+    return "INT8 and INT4 expert weights need dtype MOE_BF16";
+  if (c->weight_quant == MOE_WQ_INT4 && (c->d_model % 128 || c->d_ff % 128))
+    return "INT4 expert weights need d_model and d_ff multiples of 128";
   if (c->n_experts > 256) return "n_experts > 256 is not supported";
   if (c->top_k > 64) return "top_k > 64 is not supported";
   if (c->d_model % 64 || c->d_ff % 64 || c->d_ff_shared % 64)
@@ -497,12 +500,13 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
   g1.Kd = c->d_model;
   g1.Nd = c->d_ff;
   g1.E = N;
-  const bool q8 = c->weight_quant == MOE_WQ_INT8;
-  g1.wscale = q8 ? w->w1_scale : nullptr;
+  const bool quant = c->weight_quant != MOE_WQ_NONE;
+  g1.wscale = quant ? w->w1_scale : nullptr;
+  g1.w4 = c->weight_quant == MOE_WQ_INT4;
   moe::GemmArgs g2 = g1;
   g2.A = h;
   g2.W = w->w2;
-  g2.wscale = q8 ? w->w2_scale : nullptr;
+  g2.wscale = quant ? w->w2_scale : nullptr;
   g2.bias = w->b2;
   g2.C = y_perm;
   g2.Kd = c->d_ff;
@@ -577,7 +581,7 @@ int check_weights(const moe_config_t* c, const moe_weights_t* w, bool router, bo
   if (experts) {
     MOE_REQUIRE_PTR(w->w1, "w1");
     MOE_REQUIRE_PTR(w->w2, "w2");
-    if (c->weight_quant == MOE_WQ_INT8) {
+    if (c->weight_quant != MOE_WQ_NONE) {
       MOE_REQUIRE_PTR(w->w1_scale, "w1_scale");
       MOE_REQUIRE_PTR(w->w2_scale, "w2_scale");
     }
@@ -1004,6 +1008,18 @@ int moe_quantize_int8(const void* w, int32_t dtype, int64_t rows, int32_t cols, 
   if (cols < 64 || cols % 64) return fail(MOE_ERR_INVALID_ARG, "cols must be a positive multiple of 64");
   return hip_status(moe::launch_quantize_int8(w, dtype, rows, cols, q, scale, stream),
                     "moe_quantize_int8 launch");
+}
+
+int moe_quantize_int4(const void* w, int32_t dtype, int64_t rows, int32_t cols, uint8_t* q,
+                      float* scale, hipStream_t stream) {
+  MOE_REQUIRE_PTR(w, "w");
+  MOE_REQUIRE_PTR(q, "q");
+  MOE_REQUIRE_PTR(scale, "scale");
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32 or MOE_BF16");
+  if (rows < 1) return fail(MOE_ERR_INVALID_ARG, "rows must be >= 1");
+  if (cols < 64 || cols % 64) return fail(MOE_ERR_INVALID_ARG, "cols must be a positive multiple of 64");
+  return hip_status(moe::launch_quantize_int4(w, dtype, rows, cols, q, scale, stream),
+                    "moe_quantize_int4 launch");
 }
 
 int moe_routing_stats(const moe_config_t* cfg, const int32_t* topk_idx, const float* topk_w,

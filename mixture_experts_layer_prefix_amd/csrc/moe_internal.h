@@ -147,7 +147,9 @@ struct GemmArgs {
   const int32_t* offsets;   // [E+1] (skinny and fp32 kernels)
   const int4* tile_list;    // tiled kernels: tiles in execution order
   const int32_t* tile_count;
-  const float* wscale;  // INT8 weights: [E, Nd] fp32 row scales (W is int8); null: W is bf16
+  const float* wscale;  // INT8 / INT4 weights: [E, Nd] fp32 row scales (W holds the codes);
+                        // null: W is bf16
+  bool w4;              // with wscale: INT4 codes, two per byte ([E, Nd, Kd / 2] bytes)
   const void* As;       // shared problem: [Ts, Kd] (null if none)
   const void* Ws;       // [Nd, Kd]
   void* Cs;             // [Ts, Nd]
@@ -224,6 +226,21 @@ __device__ __forceinline__ uint4 int8x8_to_bf16x8(uint2 v) {
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
+// int4 -> bf16 of the 8 codes of a 32-bit word (element i in bits 4i .. 4i+3,
+// 4-bit two's complement; exact: |q| <= 8), two per output word.
+__device__ __forceinline__ uint4 int4x8_to_bf16x8(uint32_t v) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // arithmetic shifts sign-extend nibbles 2j and 2j + 1 (v_bfe_i32)
+    const float f0 = (float)(static_cast<int32_t>(v << (28 - 8 * j)) >> 28);
+    const float f1 = (float)(static_cast<int32_t>(v << (24 - 8 * j)) >> 28);
+    o[j] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+hipError_t launch_quantize_int4(const void* w, int dtype, int64_t rows, int cols, uint8_t* q,
+                                float* scale, hipStream_t s);
 // Routing statistics: per-expert selection counts and mean routing weight
 // (pcnt / pw hold stats_blocks(T) * N partials each).
 constexpr int kStatsTokensPerBlock = 64;

@@ -16,13 +16,14 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_WQ_NONE, MOE_WQ_INT8 = 0, 1
+MOE_WQ_NONE, MOE_WQ_INT8, MOE_WQ_INT4 = 0, 1, 2
+_WQ = {"none": MOE_WQ_NONE, "int8": MOE_WQ_INT8, "int4": MOE_WQ_INT4}
 STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5,
           "expert_ffn_train": 6, "layer_train": 7, "expert_ffn_backward": 8,
           "route_backward": 9, "layer_backward": 10}
 ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
                 "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_router_z_loss",
-                "moe_routing_stats", "moe_quantize_int8", "moe_layer_forward",
+                "moe_routing_stats", "moe_quantize_int8", "moe_quantize_int4", "moe_layer_forward",
                 "moe_expert_ffn_train", "moe_layer_forward_train", "moe_combine_backward",
                 "moe_expert_ffn_backward", "moe_route_backward", "moe_dispatch_backward",
                 "moe_layer_backward", "moe_layer_forward_noalloc", "moe_last_error")
@@ -90,6 +91,7 @@ def lib():
     L.moe_router_z_loss.argtypes = [cfgp, vp, ctypes.c_float, vp, vp, sz, vp]
     L.moe_routing_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_quantize_int8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
+    L.moe_quantize_int4.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward_noalloc.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp]
     svp, gp, f32 = ctypes.POINTER(MoeSaved), ctypes.POINTER(MoeGrads), ctypes.c_float
@@ -103,7 +105,7 @@ def lib():
     L.moe_dispatch_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     L.moe_layer_backward.argtypes = [cfgp, vp, wp, svp, vp, f32, f32, f32, vp, gp, vp, sz, vp]
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
-                 "moe_router_z_loss", "moe_routing_stats", "moe_quantize_int8",
+                 "moe_router_z_loss", "moe_routing_stats", "moe_quantize_int8", "moe_quantize_int4",
                  "moe_layer_forward", "moe_layer_forward_noalloc", "moe_expert_ffn_train",
                  "moe_layer_forward_train",
                  "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward",
@@ -146,8 +148,7 @@ def make_config(T, d_model, d_ff, n_experts, top_k, *, capacity=0, d_ff_shared=0
                      capacity=capacity or 0, d_ff_shared=d_ff_shared,
                      dtype=MOE_F32 if dtype in ("f32", MOE_F32) else MOE_BF16,
                      aux_alpha=float(aux_alpha),
-                     weight_quant=MOE_WQ_INT8 if weight_quant in ("int8", MOE_WQ_INT8)
-                     else MOE_WQ_NONE)
+                     weight_quant=_WQ.get(weight_quant, weight_quant))
 
 
 def config_for(shape, T: Optional[int] = None) -> MoeConfig:
@@ -240,16 +241,35 @@ def moe_quantize_int8(w, q_out, scale_out, stream=None):
                                    _stream(stream)))
 
 
-def quantize_expert_weights(t: Dict[str, object]) -> Dict[str, object]:
-    """A copy of a weight dict whose routed w1 / w2 are INT8 codes with their
-    w1_scale / w2_scale, made on the device by moe_quantize_int8."""
+def moe_quantize_int4(w, q_out, scale_out, stream=None):
+    """Per-row INT4 codes (two per byte, [rows, cols/2] uint8) and fp32 scales
+    of a [rows, cols] bf16 or fp32 device tensor (any leading shape)."""
     import torch
+    dt = MOE_F32 if w.dtype == torch.float32 else MOE_BF16
+    cols = int(w.shape[-1])
+    rows = int(w.numel() // cols)
+    _check(lib().moe_quantize_int4(_p(w), dt, rows, cols, _p(q_out), _p(scale_out),
+                                   _stream(stream)))
+
+
+def quantize_expert_weights(t: Dict[str, object], bits: int = 8) -> Dict[str, object]:
+    """A copy of a weight dict whose routed w1 / w2 are INT8 (bits=8) or packed
+    INT4 (bits=4) codes with their w1_scale / w2_scale, made on the device by
+    moe_quantize_int8 / moe_quantize_int4."""
+    import torch
+    if bits not in (8, 4):
+        raise ValueError("bits must be 8 or 4")
     out = dict(t)
     for name in ("w1", "w2"):
         w = t[name]
-        q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
         sc = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
-        moe_quantize_int8(w, q, sc)
+        if bits == 8:
+            q = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+            moe_quantize_int8(w, q, sc)
+        else:
+            q = torch.empty(tuple(w.shape[:-1]) + (w.shape[-1] // 2,), dtype=torch.uint8,
+                            device=w.device)
+            moe_quantize_int4(w, q, sc)
         out[name] = q
         out[name + "_scale"] = sc
     return out
@@ -396,9 +416,11 @@ class MoELayer:
         if tuple(wr.shape) != (N, cfg.d_model):
             raise ValueError(f"router weight {tuple(wr.shape)} does not match N={N}, "
                              f"d_model={cfg.d_model}")
-        if tuple(tensors["w1"].shape) != (N, cfg.d_ff, cfg.d_model):
+        # packed INT4 codes hold two elements per byte along the row
+        div = 2 if cfg.weight_quant == MOE_WQ_INT4 else 1
+        if tuple(tensors["w1"].shape) != (N, cfg.d_ff, cfg.d_model // div):
             raise ValueError("w1 must be [N, d_ff, d_model] and match the router's N")
-        if tuple(tensors["w2"].shape) != (N, cfg.d_model, cfg.d_ff):
+        if tuple(tensors["w2"].shape) != (N, cfg.d_model, cfg.d_ff // div):
             raise ValueError("w2 must be [N, d_model, d_ff] and match the router's N")
 
     def forward(self, x, aux: bool = False, out=None, stream=None):

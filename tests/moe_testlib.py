@@ -40,6 +40,27 @@ def oracle_expert_source_int8(inp):
     return get
 
 
+def oracle_expert_source_int4(inp):
+    """The same with INT4 weights (the oracle's 4-bit quantisation)."""
+    base = oracle_expert_source(inp)
+
+    def get(e):
+        w1, b1, w2, b2 = base(e)
+        q1, s1 = O.quantize_int4(w1)
+        q2, s2 = O.quantize_int4(w2)
+        return O.dequantize_int4(q1, s1), b1, O.dequantize_int4(q2, s2), b2
+    return get
+
+
+def oracle_expert_source_for(inp):
+    wq = getattr(inp.shape, "weight_quant", "none")
+    if wq == "int8":
+        return oracle_expert_source_int8(inp)
+    if wq == "int4":
+        return oracle_expert_source_int4(inp)
+    return oracle_expert_source(inp)
+
+
 def prefetching_source(get, n, window=8, workers=8):
     """An expert source that prepares experts e+1 .. e+window (widened to
     fp64) in worker threads while the caller works on expert e.  The oracle
@@ -73,8 +94,7 @@ def oracle_run(inp, capacity, out_tokens=None, return_y_perm=False):
     shared = None
     if s.d_ff_shared:
         shared = (inp.f32("ws1"), inp.f32("ws2"))
-    src = oracle_expert_source_int8(inp) if getattr(s, "weight_quant", "none") == "int8" \
-        else oracle_expert_source(inp)
+    src = oracle_expert_source_for(inp)
     if s.n_experts * s.d_model * s.d_ff >= (1 << 26):
         src = prefetching_source(src, s.n_experts)
     return O.moe_forward(inp.f32("x"), inp.f32("w_router"), src, s.top_k,
@@ -86,8 +106,9 @@ def oracle_run(inp, capacity, out_tokens=None, return_y_perm=False):
 
 def device_tensors(inp, device="cuda"):
     t = inputs.to_torch(inp, device)
-    if getattr(inp.shape, "weight_quant", "none") == "int8":
-        t = moe.quantize_expert_weights(t)
+    wq = getattr(inp.shape, "weight_quant", "none")
+    if wq in ("int8", "int4"):
+        t = moe.quantize_expert_weights(t, bits=8 if wq == "int8" else 4)
     return t
 
 

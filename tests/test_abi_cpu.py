@@ -73,7 +73,7 @@ def test_bad_configs_are_rejected(kw, code):
 
 def test_weight_quant_checks():
     cfg = _cfg()
-    cfg.weight_quant = 2
+    cfg.weight_quant = 3
     assert _route(cfg) == moe.MOE_ERR_INVALID_ARG
     cfg = _cfg(dtype="f32")
     cfg.weight_quant = moe.MOE_WQ_INT8
@@ -255,3 +255,26 @@ def test_noalloc_layer_rejects_layers_beyond_its_scratch():
                                                None, None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert moe.lib().moe_layer_forward_noalloc(ctypes.byref(small), FAKE, ctypes.byref(W), FAKE,
                                                None, FAKE + 4, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_int4_checks():
+    # INT4 codes need bf16 layers and d_model, d_ff multiples of 128
+    cfg = _cfg(d_model=192, weight_quant="int4")
+    assert _route(cfg) == moe.MOE_ERR_UNSUPPORTED
+    cfg = _cfg(d_model=128, d_ff=192, weight_quant="int4")
+    assert _route(cfg) == moe.MOE_ERR_UNSUPPORTED
+    cfg = _cfg(dtype="f32", d_model=128, d_ff=256, weight_quant="int4")
+    assert _route(cfg) == moe.MOE_ERR_UNSUPPORTED
+    cfg = _cfg(d_model=128, d_ff=256, weight_quant="int4")
+    assert moe.workspace_size(cfg, "layer") > 0
+    L = moe.lib()
+    assert L.moe_quantize_int4(None, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int4(FAKE, moe.MOE_BF16, 0, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int4(FAKE, moe.MOE_BF16, 4, 100, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_int4(FAKE, 5, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # training entry points are inference-only for quantised experts
+    W = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=FAKE, w1_scale=FAKE, w2_scale=FAKE)
+    S = moe.MoeSaved(**{n: FAKE for n in moe.SAVED_FIELDS})
+    assert L.moe_layer_forward_train(ctypes.byref(cfg), FAKE, ctypes.byref(W), FAKE, None,
+                                     ctypes.byref(S), FAKE * 256, 1 << 40,
+                                     None) == moe.MOE_ERR_UNSUPPORTED

@@ -41,9 +41,13 @@ def _gpu():
     moe.lib()
 
 
-@pytest.mark.parametrize("quant", ["none", "int8"])
+# INT4 codes need d and f multiples of 128
+SIZES = [(d, f, q) for d, f in [(320, 384), (256, 512), (384, 640)]
+         for q in ("none", "int8", "int4") if q != "int4" or (d % 128 == 0 and f % 128 == 0)]
+
+
 @pytest.mark.parametrize("name", sorted(COUNTS))
-@pytest.mark.parametrize("d,f", [(320, 384), (256, 512)])
+@pytest.mark.parametrize("d,f,quant", SIZES, ids=[f"{d}x{f}-{q}" for d, f, q in SIZES])
 def test_expert_blocks(name, d, f, quant):
     _check_blocks(name, COUNTS[name], d, f, quant)
 
@@ -58,6 +62,14 @@ def test_wide_tiles_int8():
     pattern = [0, 1, 5, 33, 64, 65, 96, 97, 127, 128, 2, 17, 129, 40, 200, 257]
     counts = [pattern[(e * 7) % len(pattern)] for e in range(256)]
     _check_blocks("wide_int8", counts, 832, 1216, "int8")
+
+
+def test_wide_tiles_int4():
+    """The same wide tiles with INT4 codes (d = 896, f = 1152: both GEMMs end
+    in a partial wide tile of 384 and 128 columns)."""
+    pattern = [0, 1, 5, 33, 64, 65, 96, 97, 127, 128, 2, 17, 129, 40, 200, 257]
+    counts = [pattern[(e * 5) % len(pattern)] for e in range(256)]
+    _check_blocks("wide_int4", counts, 896, 1152, "int4")
 
 
 def _check_blocks(name, counts, d, f, quant):
@@ -84,8 +96,8 @@ def _check_blocks(name, counts, d, f, quant):
 
     t = {"w_router": u16(w1[:, :1, :].copy()), "w1": u16(w1), "b1": u16(b1), "w2": u16(w2),
          "b2": u16(b2)}
-    if quant == "int8":
-        t = moe.quantize_expert_weights(t)
+    if quant in ("int8", "int4"):
+        t = moe.quantize_expert_weights(t, bits=8 if quant == "int8" else 4)
     W = moe.make_weights(t)
     xd = u16(x)
     y = torch.full((rows, d), 0, dtype=torch.int16, device=dev)
@@ -108,6 +120,9 @@ def _check_blocks(name, counts, d, f, quant):
         if quant == "int8":
             W1 = O.dequantize_int8(*O.quantize_int8(W1))
             W2 = O.dequantize_int8(*O.quantize_int8(W2))
+        elif quant == "int4":
+            W1 = O.dequantize_int4(*O.quantize_int4(W1))
+            W2 = O.dequantize_int4(*O.quantize_int4(W2))
         ref = O.expert_ffn(xf[lo:hi], W1, inputs.bf16_widen(b1[e]), W2, inputs.bf16_widen(b2[e]))
         got = yh[lo:hi]
         assert np.isfinite(got).all(), f"expert {e}: rows left unwritten or non-finite"

@@ -1,5 +1,5 @@
 """GPU parity at the five workload sizes (and the three weight-bound ones again
-with INT8 expert weights), in the launch configuration bench.py times (the
+with INT8 and with INT4 expert weights), in the launch configuration bench.py times (the
 same C-ABI stage calls).
 
 Every output is compared whole against the oracle run over the whole batch:
@@ -22,7 +22,8 @@ from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, W_TOL, check_routing_and_di
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("shape", C.ALL + C.INT8, ids=[s.name for s in C.ALL + C.INT8])
+@pytest.mark.parametrize("shape", C.ALL + C.INT8 + C.INT4,
+                         ids=[s.name for s in C.ALL + C.INT8 + C.INT4])
 def test_full_size(shape):
     import torch
     if not torch.cuda.is_available():
