@@ -412,13 +412,14 @@ def main():
     ws_d = moe.alloc_workspace(cfg, "dispatch", dev)
     ws_f = moe.alloc_workspace(cfg, "expert_ffn", dev)
     ws_a = moe.alloc_workspace(cfg, "aux", dev)
+    parts = moe.alloc_route_partials(cfg, dev) if cfg.aux_alpha else None
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     names = ("route", "dispatch", "expert_ffn", "combine") + (("aux",) if cfg.aux_alpha else ())
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        moe.moe_route(cfg, t["x"], W, logits, idx, w, ws_r, stream=sp)
+        moe.moe_route(cfg, t["x"], W, logits, idx, w, ws_r, stream=sp, partials=parts)
         if ev: ev[1].record(stream)
         moe.moe_dispatch(cfg, idx, t["x"], counts, offsets, slot_row, row_token, x_perm, ndrop,
                          ws_d, stream=sp)
@@ -429,7 +430,8 @@ def main():
         moe.moe_combine(cfg, y_perm, slot_row, w, y_shared, out, stream=sp)
         if ev: ev[4].record(stream)
         if cfg.aux_alpha:
-            moe.moe_aux_loss(cfg, logits, counts, loss, ws_a, stream=sp)
+            # from the routing partials the select kernel wrote
+            moe.moe_aux_loss(cfg, None, counts, loss, ws_a, stream=sp, partials=parts)
             if ev: ev[5].record(stream)
 
     for _ in range(args.warmup):

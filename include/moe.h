@@ -129,6 +129,18 @@ size_t moe_workspace_size(const moe_config_t *cfg, moe_stage_t stage);
  * Returns -1 for T < 1, N < 1 or capacity_factor not finite and > 0. */
 int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double capacity_factor);
 
+/* Bytes of the routing-partials buffer of moe_route ((size_t)-1 if cfg is
+ * invalid).  With nb = ceil(T / 4) blocks of four consecutive tokens it holds,
+ * in this order, each array starting on a 256-byte boundary:
+ *   ppart [nb, N] fp64  sum over the block's tokens of softmax_N(logits_t)
+ *   zpart [nb]    fp64  sum over the block's tokens of (logsumexp logits_t)^2
+ *   spw   [nb, N] fp64  sum of the routing weights topk_w[t, k] routed to e
+ *   spcnt [nb, N] int32 number of (t, k) routed to e (before capacity drops)
+ * (sums in token order, pairs in (token, slot) order).  moe_aux_loss,
+ * moe_router_z_loss and moe_routing_stats reduce it without reading the
+ * logits or the routing again. */
+size_t moe_route_partials_size(const moe_config_t *cfg);
+
 /* Router scoring and Top-K routing (lmnt.cn §2.1 gate scoring equation and
  * the TopK-then-Softmax order; yunthe.com reference forward; yunthe.com
  * per-expert bias b_i for selection).
@@ -141,10 +153,14 @@ int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double capacity_f
  *            NaN scores order as -inf.
  *   topk_w   [dev] [T, K] fp32 out: softmax over the K chosen unbiased logits
  *            (computed in fp64, rounded once).
+ *   partials [dev] out or NULL, 256-byte aligned, moe_route_partials_size(cfg)
+ *            bytes: the routing partials of the aux loss (P, lmnt.cn §5.1-5.2),
+ *            the z-loss (lmnt.cn §5.3) and the routing statistics (lmnt.cn
+ *            §8.2), formed while each token's logits are in registers.
  *   ws       [dev] >= moe_workspace_size(cfg, MOE_STAGE_ROUTE) bytes (fp64
  *            partial dot products). */
 int moe_route(const moe_config_t *cfg, const void *x, const moe_weights_t *w, float *logits,
-              int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              int32_t *topk_idx, float *topk_w, void *partials, void *ws, size_t ws_bytes,
               hipStream_t stream);
 
 /* Dispatch: permute tokens from token order to contiguous per-expert blocks
@@ -199,12 +215,18 @@ int moe_combine(const moe_config_t *cfg, const void *y_perm, const int32_t *slot
  * of the pre-drop 0/1 selection mask, so sum f = K) and P_e the mean over
  * tokens of softmax_N(logits[t])_e.  Exponentials in fp32, all sums and
  * products in fp64, with a fixed reduction order (deterministic); written as
- * fp32.  Relative error ~1e-7.
- *   logits [dev] [T, N] fp32 in;  counts [dev] [N] int32 in (from moe_dispatch);
+ * fp32.  Relative error ~1e-7.  The same bits from the logits or from
+ * moe_route's partials.
+ *   logits   [dev] [T, N] fp32 in, or NULL;
+ *   partials [dev] in (moe_route's), or NULL: exactly one of the two;
+ *   counts [dev] [N] int32 in: moe_dispatch's pre-drop counts (f needs only
+ *            the per-expert selection counts, which dispatch has already
+ *            histogrammed; no pass over topk_idx);
  *   loss_out [dev] [1] fp32 out;  alpha = cfg->aux_alpha;
  *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes. */
-int moe_aux_loss(const moe_config_t *cfg, const float *logits, const int32_t *counts,
-                 float *loss_out, void *ws, size_t ws_bytes, hipStream_t stream);
+int moe_aux_loss(const moe_config_t *cfg, const float *logits, const void *partials,
+                 const int32_t *counts, float *loss_out, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
 
 /* Routing statistics (lmnt.cn MoE walkthrough §8.2, measuring the routing
  * distribution: tokens received per expert and the mean routing weight; the
@@ -213,29 +235,35 @@ int moe_aux_loss(const moe_config_t *cfg, const float *logits, const int32_t *co
  * mean of topk_w[t, k] over those pairs, 0 for an expert nobody chose.  Sums
  * in fp64 with a fixed order (deterministic); the means are written as fp32.
  *   topk_idx [dev] [T, K] int32 in;  topk_w [dev] [T, K] fp32 in (moe_route);
+ *            both NULL when partials are given;
+ *   partials [dev] in (moe_route's) or NULL;
  *   counts_out [dev] [N] int32 out or NULL;  weight_mean_out [dev] [N] fp32 out;
  *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes.
- * Errors: MOE_ERR_INVALID_ARG for NULL or misaligned required pointers,
- * MOE_ERR_WORKSPACE for a short or misaligned workspace. */
+ * Errors: MOE_ERR_INVALID_ARG for NULL or misaligned required pointers or
+ * both inputs given, MOE_ERR_WORKSPACE for a short or misaligned workspace. */
 int moe_routing_stats(const moe_config_t *cfg, const int32_t *topk_idx, const float *topk_w,
-                      int32_t *counts_out, float *weight_mean_out, void *ws, size_t ws_bytes,
-                      hipStream_t stream);
+                      const void *partials, int32_t *counts_out, float *weight_mean_out, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
 
 /* Router z-loss (lmnt.cn MoE walkthrough §5.3, router z-loss equation):
  * beta * (1/T) sum_t (logsumexp_e logits[t, e])^2, which penalises large
  * router logits.  Exponentials in fp32, sums and logarithm in fp64, with a
  * fixed reduction order (deterministic); written as fp32.
- *   logits [dev] [T, N] fp32 in (from moe_route);  beta: finite weight;
- *   loss_out [dev] [1] fp32 out;
+ *   logits [dev] [T, N] fp32 in (from moe_route), or NULL;
+ *   partials [dev] in (moe_route's), or NULL: exactly one of the two;
+ *   beta: finite weight;  loss_out [dev] [1] fp32 out;
  *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_AUX) bytes.
- * Errors: MOE_ERR_INVALID_ARG for NULL logits / loss_out or a non-finite
- * beta, MOE_ERR_WORKSPACE for a short or misaligned workspace. */
-int moe_router_z_loss(const moe_config_t *cfg, const float *logits, float beta, float *loss_out,
-                      void *ws, size_t ws_bytes, hipStream_t stream);
+ * Errors: MOE_ERR_INVALID_ARG for neither or both of logits / partials, NULL
+ * loss_out or a non-finite beta, MOE_ERR_WORKSPACE for a short or misaligned
+ * workspace. */
+int moe_router_z_loss(const moe_config_t *cfg, const float *logits, const void *partials,
+                      float beta, float *loss_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* The whole layer: route -> dispatch -> expert FFN (+ shared expert) ->
- * combine (-> aux loss when aux_out != NULL).  Same kernels and results as
- * calling the stages in order.
+/* The whole layer (lmnt.cn §1.2 per-token flow: gate scores, Top-K experts,
+ * dispatch, expert computation, weighted combine): route -> dispatch ->
+ * expert FFN (+ shared expert) -> combine (-> aux loss when aux_out != NULL,
+ * from the routing partials the route stage writes).  Same kernels and
+ * results as calling the stages in order.
  *   x [dev] [T, d] dtype in;  out [dev] [T, d] dtype out;
  *   aux_out [dev] [1] fp32 out or NULL;  counts_out [dev] [N] int32 out or NULL;
  *   n_dropped_out [dev] [1] int32 out or NULL;
@@ -243,6 +271,29 @@ int moe_router_z_loss(const moe_config_t *cfg, const float *logits, float beta, 
 int moe_layer_forward(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
                       void *out, float *aux_out, int32_t *counts_out, int32_t *n_dropped_out,
                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The layer with its training signals and routing statistics (lmnt.cn §5.1-5.3
+ * balance loss and router z-loss; §8.2 per-step monitoring of tokens per
+ * expert, mean routing weight and drops).  Every field is optional. */
+typedef struct {
+  float *aux_out;          /* [dev] [1] fp32 or NULL: aux loss with cfg->aux_alpha  */
+  float zloss_beta;        /* z-loss weight beta (finite; used with zloss_out)      */
+  float *zloss_out;        /* [dev] [1] fp32 or NULL: beta * mean_t lse_t^2         */
+  int32_t *counts_out;     /* [dev] [N] int32 or NULL: pre-drop pairs per expert    */
+  int32_t *n_dropped_out;  /* [dev] [1] int32 or NULL: pairs dropped by capacity    */
+  float *weight_mean_out;  /* [dev] [N] fp32 or NULL: mean routing weight per expert */
+} moe_layer_stats_t;
+
+/* moe_layer_forward with the outputs of `stats`: the aux loss, z-loss and
+ * mean routing weights come from the routing partials the select kernel
+ * writes while it holds each token's logits (no further pass over the
+ * logits), with the same bits as moe_aux_loss / moe_router_z_loss /
+ * moe_routing_stats.
+ *   stats [host] read during the call;  other arguments as moe_layer_forward;
+ *   ws [dev] >= moe_workspace_size(cfg, MOE_STAGE_LAYER) bytes. */
+int moe_layer_forward_stats(const moe_config_t *cfg, const void *x, const moe_weights_t *w,
+                            void *out, const moe_layer_stats_t *stats, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* The same layer as moe_layer_forward, for callers that cannot allocate
  * device memory: code being captured into a HIP graph, tight serving loops,

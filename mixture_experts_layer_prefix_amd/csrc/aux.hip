@@ -9,21 +9,24 @@
 //   loss = alpha * N * sum_e f_e * P_e
 // Router z-loss (lmnt.cn MoE walkthrough §5.3): beta * mean_t lse_t^2 with
 // lse_t = logsumexp_e logits[t, e].
+// Routing statistics (lmnt.cn MoE walkthrough §8.2: tokens per expert and
+// mean routing weight).
 //
-// Both use a fixed reduction order, so the results are deterministic: the row
-// max and the exponentials in fp32 (relative error ~1e-7 per term, each in
-// (0, 1]), every sum, logarithm, normalisation and product in fp64.
+// All three reduce per-block routing partials (RoutePartials, blocks of
+// kAuxTokensPerBlock = 4 tokens): the select kernel of the router writes them
+// from the rows it already holds, or the partial kernels below write the same
+// bits from the logits / routing.  Fixed reduction orders throughout, so the
+// results are deterministic: row max and exponentials in fp32 (relative
+// error ~1e-7 per term, each in (0, 1]), every sum, logarithm, normalisation
+// and product in fp64.
 //
-// Pass 1: a workgroup of 4 wavefronts takes TB = 16 tokens; a wavefront loads
-// its 4 token rows at once (lane = expert, up to 4 experts per lane), then
-// forms each row's softmax (or logsumexp) and adds it to per-lane sums in
-// token order; the 4 wavefronts' sums are added in wavefront order into
-// ppart[block, e] (or zpart[block]).
-// Pass 2, aux: a wavefront per expert adds column e of ppart (lanes stride
-// over the blocks, then a fixed butterfly) and multiplies by f_e; pass 3, one
-// workgroup reduces the experts' terms with a fixed tree.  Z-loss: one
-// wavefront adds zpart (lanes stride over the blocks, then a fixed
-// butterfly).
+// Partials from the logits: one wavefront per block, its 4 rows loaded
+// together, each row's softmax and lse^2 added to per-lane sums in token
+// order.  Partials from the routing: one workgroup per 4 blocks stages their
+// (expert, weight) pairs in LDS; thread e walks each block's pairs in
+// token-major order.  Final passes: a wavefront per expert adds column e of
+// a partial array (lanes stride over the blocks, then a fixed butterfly); the
+// aux loss then reduces the experts' terms with a fixed tree.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -32,35 +35,22 @@ namespace moe {
 namespace {
 
 constexpr int TB = kAuxTokensPerBlock;
-constexpr int RPW = TB / 4;            // token rows per wavefront
 
-// Row max and fp32 exponentials of one token row (lane = expert e, e + 64,
-// e + 128, e + 192); returns the row's sum of exponentials in fp64.
-__device__ __forceinline__ double row_exp(const float (&l)[4], int lane, int N, double (&ex)[4],
-                                          float& m) {
-  m = -INFINITY;
+// ppart [nblk, N] and zpart [nblk] from the logits: wavefront w of
+// workgroup b takes block 4 b + w.
+__global__ __launch_bounds__(256) void logit_partials_kernel(const float* __restrict__ logits,
+                                                             int T, int N, int nblk,
+                                                             double* __restrict__ ppart,
+                                                             double* __restrict__ zpart) {
+  const int lane = threadIdx.x & 63;
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= nblk) return;
+  const int t0 = blk * TB;
+  float l[TB][4];
+  // the block's rows, loaded before any arithmetic so the loads are in flight
+  // together; entries past T or N read as -inf
 #pragma unroll
-  for (int v = 0; v < 4; ++v) m = fmaxf(m, l[v]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  double s = 0.0;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    ex[v] = (lane + 64 * v < N) ? (double)expf(l[v] - m) : 0.0;
-    s += ex[v];
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  return s;
-}
-
-// The wavefront's RPW rows, loaded before any arithmetic so their loads are
-// in flight together; entries past T or N read as -inf (rows past T are
-// skipped by the callers).
-__device__ __forceinline__ void load_rows(const float* __restrict__ logits, int T, int N, int t0,
-                                          int lane, float (&l)[RPW][4]) {
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
+  for (int r = 0; r < TB; ++r) {
     const int t = t0 + r;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -68,30 +58,58 @@ __device__ __forceinline__ void load_rows(const float* __restrict__ logits, int 
       l[r][v] = (t < T && e < N) ? logits[(int64_t)t * N + e] : -INFINITY;
     }
   }
-}
-
-__global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restrict__ logits, int T,
-                                                          int N, double* __restrict__ ppart) {
-  __shared__ double part[4][256];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * TB + wave * RPW;
-  float l[RPW][4];
-  load_rows(logits, T, N, t0, lane, l);
   double ps[4] = {0.0, 0.0, 0.0, 0.0};
+  double zs = 0.0;
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
+  for (int r = 0; r < TB; ++r) {
     if (t0 + r >= T) break;
     double ex[4];
     float m;
-    const double inv = 1.0 / row_exp(l[r], lane, N, ex, m);
+    const double s = row_softmax_terms(l[r], lane, N, ex, m);
+    const double inv = 1.0 / s;
 #pragma unroll
     for (int v = 0; v < 4; ++v) ps[v] += ex[v] * inv;
+    const double lse = (double)m + log(s);
+    zs += lse * lse;
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) part[wave][lane + 64 * v] = ps[v];
+  for (int v = 0; v < 4; ++v) {
+    const int e = lane + 64 * v;
+    if (e < N) ppart[(int64_t)blk * N + e] = ps[v];
+  }
+  if (lane == 0) zpart[blk] = zs;
+}
+
+// spcnt, spw [nblk, N] from the routing: workgroup b takes blocks 4 b .. 4 b + 3.
+__global__ __launch_bounds__(256) void routing_partials_kernel(const int32_t* __restrict__ idx,
+                                                               const float* __restrict__ w,
+                                                               int T, int K, int N, int nblk,
+                                                               int32_t* __restrict__ pcnt,
+                                                               double* __restrict__ pw) {
+  __shared__ int32_t s_idx[4 * TB * 64];
+  __shared__ float s_w[4 * TB * 64];
+  const int b0 = blockIdx.x * 4;
+  const int64_t p0 = (int64_t)b0 * TB * K;
+  const int np = (int)(min((int64_t)(b0 + 4) * TB, (int64_t)T) * K - p0);
+  for (int i = threadIdx.x; i < np; i += 256) {
+    s_idx[i] = idx[p0 + i];
+    s_w[i] = w[p0 + i];
+  }
   __syncthreads();
-  for (int e = threadIdx.x; e < N; e += 256)
-    ppart[(int64_t)blockIdx.x * N + e] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
+  const int e = threadIdx.x;
+  if (e >= N) return;
+  for (int b = 0; b < 4 && b0 + b < nblk; ++b) {
+    const int i0 = b * TB * K, i1 = min(np, (b + 1) * TB * K);
+    int c = 0;
+    double sw = 0.0;
+    for (int i = i0; i < i1; ++i)
+      if (s_idx[i] == e) {
+        ++c;
+        sw += (double)s_w[i];
+      }
+    pcnt[(int64_t)(b0 + b) * N + e] = c;
+    pw[(int64_t)(b0 + b) * N + e] = sw;
+  }
 }
 
 // One wavefront per expert e: lanes stride over the blocks (their loads are
@@ -123,28 +141,6 @@ __global__ __launch_bounds__(256) void aux_final_kernel(const double* __restrict
   if (e == 0) loss[0] = (float)((double)alpha * (double)N * t[0]);
 }
 
-__global__ __launch_bounds__(256) void zloss_partial_kernel(const float* __restrict__ logits, int T,
-                                                            int N, double* __restrict__ zpart) {
-  __shared__ double part[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * TB + wave * RPW;
-  float l[RPW][4];
-  load_rows(logits, T, N, t0, lane, l);
-  double acc = 0.0;
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    if (t0 + r >= T) break;
-    double ex[4];
-    float m;
-    const double s = row_exp(l[r], lane, N, ex, m);
-    const double lse = (double)m + log(s);
-    acc += lse * lse;
-  }
-  if (lane == 0) part[wave] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) zpart[blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
-}
-
 __global__ __launch_bounds__(64) void zloss_final_kernel(const double* __restrict__ zpart, int nblk,
                                                          int T, float beta,
                                                          float* __restrict__ loss) {
@@ -154,41 +150,6 @@ __global__ __launch_bounds__(64) void zloss_final_kernel(const double* __restric
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
   if (threadIdx.x == 0) loss[0] = (float)((double)beta * (z / (double)T));
-}
-
-// Routing statistics (lmnt.cn MoE walkthrough §8.2: tokens per expert and
-// mean routing weight).  Pass 1: a workgroup stages the (expert, weight) pairs
-// of STB tokens in LDS; thread e walks them in token-major order and counts
-// the pairs routed to expert e and adds their weights (fp64).  Pass 2: a
-// wavefront per expert adds the blocks' partials (lanes stride over the
-// blocks, then a fixed butterfly).
-constexpr int STB = kStatsTokensPerBlock;
-
-__global__ __launch_bounds__(256) void stats_partial_kernel(const int32_t* __restrict__ idx,
-                                                            const float* __restrict__ w, int T,
-                                                            int K, int N,
-                                                            int32_t* __restrict__ pcnt,
-                                                            double* __restrict__ pw) {
-  __shared__ int32_t s_idx[STB * 64];
-  __shared__ float s_w[STB * 64];
-  const int64_t p0 = (int64_t)blockIdx.x * STB * K;
-  const int np = (int)(min((int64_t)(blockIdx.x + 1) * STB, (int64_t)T) * K - p0);
-  for (int i = threadIdx.x; i < np; i += 256) {
-    s_idx[i] = idx[p0 + i];
-    s_w[i] = w[p0 + i];
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < N; e += 256) {
-    int c = 0;
-    double sw = 0.0;
-    for (int i = 0; i < np; ++i)
-      if (s_idx[i] == e) {
-        ++c;
-        sw += (double)s_w[i];
-      }
-    pcnt[(int64_t)blockIdx.x * N + e] = c;
-    pw[(int64_t)blockIdx.x * N + e] = sw;
-  }
 }
 
 __global__ __launch_bounds__(64) void stats_final_kernel(const int32_t* __restrict__ pcnt,
@@ -216,29 +177,42 @@ __global__ __launch_bounds__(64) void stats_final_kernel(const int32_t* __restri
 
 }  // namespace
 
-hipError_t launch_stats(const int32_t* topk_idx, const float* topk_w, int T, int K, int N,
-                        int32_t* pcnt, double* pw, int32_t* counts, float* wmean, hipStream_t s) {
-  const int nblk = stats_blocks(T);
-  hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, topk_w, T, K, N,
-                     pcnt, pw);
-  hipLaunchKernelGGL(stats_final_kernel, dim3(N), dim3(64), 0, s, pcnt, pw, nblk, N, counts, wmean);
+hipError_t launch_logit_partials(const float* logits, int T, int N, const RoutePartials& rp,
+                                 hipStream_t s) {
+  const int nblk = aux_blocks(T);
+  hipLaunchKernelGGL(logit_partials_kernel, dim3((nblk + 3) / 4), dim3(256), 0, s, logits, T, N,
+                     nblk, rp.ppart, rp.zpart);
   return hipGetLastError();
 }
 
-hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,
-                        float* loss_out, hipStream_t s) {
+hipError_t launch_routing_partials(const int32_t* topk_idx, const float* topk_w, int T, int K,
+                                   int N, const RoutePartials& rp, hipStream_t s) {
   const int nblk = aux_blocks(T);
-  hipLaunchKernelGGL(zloss_partial_kernel, dim3(nblk), dim3(256), 0, s, logits, T, N, zpart);
-  hipLaunchKernelGGL(zloss_final_kernel, dim3(1), dim3(64), 0, s, zpart, nblk, T, beta, loss_out);
+  hipLaunchKernelGGL(routing_partials_kernel, dim3((nblk + 3) / 4), dim3(256), 0, s, topk_idx,
+                     topk_w, T, K, N, nblk, rp.spcnt, rp.spw);
   return hipGetLastError();
 }
 
-hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
-                      double* ppart, double* term, float* loss_out, hipStream_t s) {
+hipError_t launch_aux_final(const RoutePartials& rp, const int32_t* counts, int T, int N,
+                            float alpha, double* term, float* loss_out, hipStream_t s) {
   const int nblk = aux_blocks(T);
-  hipLaunchKernelGGL(aux_partial_kernel, dim3(nblk), dim3(256), 0, s, logits, T, N, ppart);
-  hipLaunchKernelGGL(aux_column_kernel, dim3(N), dim3(64), 0, s, ppart, nblk, counts, T, N, term);
+  hipLaunchKernelGGL(aux_column_kernel, dim3(N), dim3(64), 0, s, rp.ppart, nblk, counts, T, N,
+                     term);
   hipLaunchKernelGGL(aux_final_kernel, dim3(1), dim3(256), 0, s, term, N, alpha, loss_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zloss_final(const RoutePartials& rp, int T, float beta, float* loss_out,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(zloss_final_kernel, dim3(1), dim3(64), 0, s, rp.zpart, aux_blocks(T), T, beta,
+                     loss_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_final(const RoutePartials& rp, int T, int N, int32_t* counts, float* wmean,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(stats_final_kernel, dim3(N), dim3(64), 0, s, rp.spcnt, rp.spw, aux_blocks(T),
+                     N, counts, wmean);
   return hipGetLastError();
 }
 

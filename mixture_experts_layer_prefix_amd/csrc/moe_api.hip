@@ -125,12 +125,42 @@ struct FfnWs {
   void* h;
   void* h_shared;
 };
+// The routing-partials buffer (moe_route's optional output, and the
+// workspace copy the loss / statistics entry points and the layer use):
+// ppart [nb, N] fp64, zpart [nb] fp64, spw [nb, N] fp64, spcnt [nb, N] int32,
+// nb = aux_blocks(T), each array 256-byte aligned in that order.
+struct PartLayout {
+  size_t ppart, zpart, spw, spcnt, total;
+};
+PartLayout part_layout(const moe_config_t* c) {
+  const size_t nb = (size_t)moe::aux_blocks(c->T), N = (size_t)c->n_experts;
+  PartLayout L;
+  size_t off = 0;
+  L.ppart = off;
+  off = align_up(off + nb * N * sizeof(double));
+  L.zpart = off;
+  off = align_up(off + nb * sizeof(double));
+  L.spw = off;
+  off = align_up(off + nb * N * sizeof(double));
+  L.spcnt = off;
+  off = align_up(off + nb * N * sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+moe::RoutePartials partials_at(void* base, const moe_config_t* c) {
+  const PartLayout L = part_layout(c);
+  char* b = static_cast<char*>(base);
+  moe::RoutePartials rp;
+  rp.ppart = reinterpret_cast<double*>(b + L.ppart);
+  rp.zpart = reinterpret_cast<double*>(b + L.zpart);
+  rp.spw = reinterpret_cast<double*>(b + L.spw);
+  rp.spcnt = reinterpret_cast<int32_t*>(b + L.spcnt);
+  return rp;
+}
+
 struct AuxWs {
-  double* ppart;
+  moe::RoutePartials rp;  // partials computed here when the caller has none
   double* term;
-  double* zpart;
-  double* spw;          // routing statistics partials
-  int32_t* spcnt;
 };
 struct LayerWs {
   float* logits;
@@ -180,11 +210,9 @@ void carve_ffn(Carver& cv, const moe_config_t* c, FfnWs* w, bool hidden = true) 
 }
 
 void carve_aux(Carver& cv, const moe_config_t* c, AuxWs* w) {
-  w->ppart = cv.take<double>((size_t)moe::aux_blocks(c->T) * c->n_experts * sizeof(double));
+  char* parts = cv.take<char>(part_layout(c).total);
+  w->rp = parts ? partials_at(parts, c) : moe::RoutePartials{};
   w->term = cv.take<double>((size_t)c->n_experts * sizeof(double));
-  w->zpart = cv.take<double>((size_t)moe::aux_blocks(c->T) * sizeof(double));
-  w->spw = cv.take<double>((size_t)moe::stats_blocks(c->T) * c->n_experts * sizeof(double));
-  w->spcnt = cv.take<int32_t>((size_t)moe::stats_blocks(c->T) * c->n_experts * sizeof(int32_t));
 }
 
 void carve_layer(Carver& cv, const moe_config_t* c, LayerWs* w) {
@@ -416,11 +444,13 @@ int hip_status(hipError_t e, const char* where) {
 }
 
 // ---------------------------------------------------------------- stages (checked)
+// parts: the routing partials to write with the selection, or null.
 int do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
-             int32_t* idx, float* tw, const RouteWs& rw, hipStream_t s) {
+             int32_t* idx, float* tw, const RouteWs& rw, hipStream_t s,
+             const moe::RoutePartials* parts = nullptr) {
   return hip_status(moe::launch_route(c->dtype, x, w->w_router, w->b_router, w->logit_offset,
                                       w->sel_bias, logits, idx, tw, rw.part, c->T, c->d_model,
-                                      c->n_experts, c->top_k, s),
+                                      c->n_experts, c->top_k, parts, s),
                     "moe_route launch");
 }
 
@@ -563,10 +593,17 @@ int do_combine(const moe_config_t* c, const void* y_perm, const int32_t* slot_ro
                     "moe_combine launch");
 }
 
-int do_aux(const moe_config_t* c, const float* logits, const int32_t* counts, float* loss,
-           const AuxWs& aw, hipStream_t s) {
-  return hip_status(moe::launch_aux(logits, counts, c->T, c->n_experts, c->aux_alpha, aw.ppart,
-                                    aw.term, loss, s),
+// The aux loss from routing partials (rp), which hold the probability sums
+// already, or are first formed from the logits when `logits` is not null.
+int do_aux(const moe_config_t* c, const float* logits, const moe::RoutePartials& rp,
+           const int32_t* counts, float* loss, const AuxWs& aw, hipStream_t s) {
+  if (logits) {
+    int r = hip_status(moe::launch_logit_partials(logits, c->T, c->n_experts, rp, s),
+                       "aux partials launch");
+    if (r != MOE_OK) return r;
+  }
+  return hip_status(moe::launch_aux_final(rp, counts, c->T, c->n_experts, c->aux_alpha, aw.term,
+                                          loss, s),
                     "moe_aux_loss launch");
 }
 
@@ -815,18 +852,22 @@ int check_saved(const moe_config_t* c, const moe_saved_t* sv) {
 
 // The whole layer on a caller-sized workspace (moe_layer_forward and
 // moe_layer_forward_noalloc).
+// The routing partials are written by the select kernel while it holds each
+// token's logits, so the aux loss, the z-loss and the mean routing weights
+// only reduce them (no further pass over the logits).
 int layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_t* w, void* out,
-                  float* aux_out, int32_t* counts_out, int32_t* n_dropped_out, void* ws,
-                  size_t ws_bytes, hipStream_t stream) {
+                  const moe_layer_stats_t& st, void* ws, size_t ws_bytes, hipStream_t stream) {
   int r = check_ws(cfg, MOE_STAGE_LAYER, ws, ws_bytes);
   if (r != MOE_OK) return r;
   Carver cv{static_cast<char*>(ws)};
   LayerWs lw;
   carve_layer(cv, cfg, &lw);
-  int32_t* counts = counts_out ? counts_out : lw.counts;
-  int32_t* ndrop = n_dropped_out ? n_dropped_out : lw.n_dropped;
+  int32_t* counts = st.counts_out ? st.counts_out : lw.counts;
+  int32_t* ndrop = st.n_dropped_out ? st.n_dropped_out : lw.n_dropped;
+  const bool parts = st.aux_out || st.zloss_out || st.weight_mean_out;
 
-  r = do_route(cfg, x, w, lw.logits, lw.idx, lw.w, lw.route, stream);
+  r = do_route(cfg, x, w, lw.logits, lw.idx, lw.w, lw.route, stream,
+               parts ? &lw.aux.rp : nullptr);
   if (r != MOE_OK) return r;
   r = do_dispatch(cfg, lw.idx, x, counts, lw.offsets, lw.slot_row, lw.row_token, lw.x_perm,
                   ndrop, lw.disp, stream);
@@ -836,8 +877,19 @@ int layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_t* w
   if (r != MOE_OK) return r;
   r = do_combine(cfg, lw.y_perm, lw.slot_row, lw.w, lw.y_shared, out, stream);
   if (r != MOE_OK) return r;
-  if (aux_out) {
-    r = do_aux(cfg, lw.logits, counts, aux_out, lw.aux, stream);
+  if (st.aux_out) {
+    r = do_aux(cfg, nullptr, lw.aux.rp, counts, st.aux_out, lw.aux, stream);
+    if (r != MOE_OK) return r;
+  }
+  if (st.zloss_out) {
+    r = hip_status(moe::launch_zloss_final(lw.aux.rp, cfg->T, st.zloss_beta, st.zloss_out, stream),
+                   "z-loss launch");
+    if (r != MOE_OK) return r;
+  }
+  if (st.weight_mean_out) {
+    r = hip_status(moe::launch_stats_final(lw.aux.rp, cfg->T, cfg->n_experts, nullptr,
+                                           st.weight_mean_out, stream),
+                   "routing statistics launch");
     if (r != MOE_OK) return r;
   }
   return MOE_OK;
@@ -911,8 +963,15 @@ int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double cf) {
   return (int32_t)q;
 }
 
+size_t moe_route_partials_size(const moe_config_t* cfg) {
+  int code;
+  if (!check_config(cfg, &code).empty()) return (size_t)-1;
+  return part_layout(cfg).total;
+}
+
 int moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w, float* logits,
-              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+              int32_t* topk_idx, float* topk_w, void* partials, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
   MOE_CHECK_CFG(cfg);
   MOE_REQUIRE_PTR(x, "x");
   int r = check_weights(cfg, w, true, false);
@@ -920,12 +979,16 @@ int moe_route(const moe_config_t* cfg, const void* x, const moe_weights_t* w, fl
   MOE_OPTIONAL_PTR(logits, "logits");
   MOE_REQUIRE_PTR(topk_idx, "topk_idx");
   MOE_REQUIRE_PTR(topk_w, "topk_w");
+  if (partials && reinterpret_cast<uintptr_t>(partials) % kAlign)
+    return fail(MOE_ERR_INVALID_ARG, "partials must be 256-byte aligned");
   r = check_ws(cfg, MOE_STAGE_ROUTE, ws, ws_bytes);
   if (r != MOE_OK) return r;
   Carver cv{static_cast<char*>(ws)};
   RouteWs rw;
   carve_route(cv, cfg, &rw);
-  return do_route(cfg, x, w, logits, topk_idx, topk_w, rw, stream);
+  if (!partials) return do_route(cfg, x, w, logits, topk_idx, topk_w, rw, stream);
+  const moe::RoutePartials rp = partials_at(partials, cfg);
+  return do_route(cfg, x, w, logits, topk_idx, topk_w, rw, stream, &rp);
 }
 
 int moe_dispatch(const moe_config_t* cfg, const int32_t* topk_idx, const void* x,
@@ -984,18 +1047,31 @@ int moe_combine(const moe_config_t* cfg, const void* y_perm, const int32_t* slot
   return do_combine(cfg, y_perm, slot_row, topk_w, y_shared, out, stream);
 }
 
-int moe_aux_loss(const moe_config_t* cfg, const float* logits, const int32_t* counts,
-                 float* loss_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+// Exactly one of logits / partials.
+int check_logits_or_partials(const float* logits, const void* partials) {
+  if (!logits == !partials)
+    return fail(MOE_ERR_INVALID_ARG, "pass exactly one of logits and partials");
+  MOE_OPTIONAL_PTR(logits, "logits");
+  if (partials && reinterpret_cast<uintptr_t>(partials) % kAlign)
+    return fail(MOE_ERR_INVALID_ARG, "partials must be 256-byte aligned");
+  return MOE_OK;
+}
+
+int moe_aux_loss(const moe_config_t* cfg, const float* logits, const void* partials,
+                 const int32_t* counts, float* loss_out, void* ws, size_t ws_bytes,
+                 hipStream_t stream) {
   MOE_CHECK_CFG(cfg);
-  MOE_REQUIRE_PTR(logits, "logits");
+  int r = check_logits_or_partials(logits, partials);
+  if (r != MOE_OK) return r;
   MOE_REQUIRE_PTR(counts, "counts");
   if (!loss_out) return fail(MOE_ERR_INVALID_ARG, "loss_out is NULL");
-  int r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
+  r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
   if (r != MOE_OK) return r;
   Carver cv{static_cast<char*>(ws)};
   AuxWs aw;
   carve_aux(cv, cfg, &aw);
-  return do_aux(cfg, logits, counts, loss_out, aw, stream);
+  const moe::RoutePartials rp = partials ? partials_at(const_cast<void*>(partials), cfg) : aw.rp;
+  return do_aux(cfg, logits, rp, counts, loss_out, aw, stream);
 }
 
 int moe_quantize_int8(const void* w, int32_t dtype, int64_t rows, int32_t cols, int8_t* q,
@@ -1023,11 +1099,18 @@ int moe_quantize_int4(const void* w, int32_t dtype, int64_t rows, int32_t cols, 
 }
 
 int moe_routing_stats(const moe_config_t* cfg, const int32_t* topk_idx, const float* topk_w,
-                      int32_t* counts_out, float* weight_mean_out, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
+                      const void* partials, int32_t* counts_out, float* weight_mean_out, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
   MOE_CHECK_CFG(cfg);
-  MOE_REQUIRE_PTR(topk_idx, "topk_idx");
-  MOE_REQUIRE_PTR(topk_w, "topk_w");
+  if (partials) {
+    if (topk_idx || topk_w)
+      return fail(MOE_ERR_INVALID_ARG, "pass either topk_idx and topk_w or partials");
+    if (reinterpret_cast<uintptr_t>(partials) % kAlign)
+      return fail(MOE_ERR_INVALID_ARG, "partials must be 256-byte aligned");
+  } else {
+    MOE_REQUIRE_PTR(topk_idx, "topk_idx");
+    MOE_REQUIRE_PTR(topk_w, "topk_w");
+  }
   MOE_OPTIONAL_PTR(counts_out, "counts_out");
   if (!weight_mean_out) return fail(MOE_ERR_INVALID_ARG, "weight_mean_out is NULL");
   int r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
@@ -1035,24 +1118,41 @@ int moe_routing_stats(const moe_config_t* cfg, const int32_t* topk_idx, const fl
   Carver cv{static_cast<char*>(ws)};
   AuxWs aw;
   carve_aux(cv, cfg, &aw);
-  return hip_status(moe::launch_stats(topk_idx, topk_w, cfg->T, cfg->top_k, cfg->n_experts,
-                                      aw.spcnt, aw.spw, counts_out, weight_mean_out, stream),
+  moe::RoutePartials rp = aw.rp;
+  if (partials) {
+    rp = partials_at(const_cast<void*>(partials), cfg);
+  } else {
+    r = hip_status(moe::launch_routing_partials(topk_idx, topk_w, cfg->T, cfg->top_k,
+                                                cfg->n_experts, rp, stream),
+                   "routing statistics partials launch");
+    if (r != MOE_OK) return r;
+  }
+  return hip_status(moe::launch_stats_final(rp, cfg->T, cfg->n_experts, counts_out,
+                                            weight_mean_out, stream),
                     "moe_routing_stats launch");
 }
 
-int moe_router_z_loss(const moe_config_t* cfg, const float* logits, float beta, float* loss_out,
-                      void* ws, size_t ws_bytes, hipStream_t stream) {
+int moe_router_z_loss(const moe_config_t* cfg, const float* logits, const void* partials,
+                      float beta, float* loss_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   MOE_CHECK_CFG(cfg);
-  MOE_REQUIRE_PTR(logits, "logits");
+  int r = check_logits_or_partials(logits, partials);
+  if (r != MOE_OK) return r;
   if (!loss_out) return fail(MOE_ERR_INVALID_ARG, "loss_out is NULL");
   if (!isfinite(beta)) return fail(MOE_ERR_INVALID_ARG, "beta is not finite");
-  int r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
+  r = check_ws(cfg, MOE_STAGE_AUX, ws, ws_bytes);
   if (r != MOE_OK) return r;
   Carver cv{static_cast<char*>(ws)};
   AuxWs aw;
   carve_aux(cv, cfg, &aw);
-  return hip_status(moe::launch_zloss(logits, cfg->T, cfg->n_experts, beta, aw.zpart, loss_out,
-                                      stream),
+  moe::RoutePartials rp = aw.rp;
+  if (partials) {
+    rp = partials_at(const_cast<void*>(partials), cfg);
+  } else {
+    r = hip_status(moe::launch_logit_partials(logits, cfg->T, cfg->n_experts, rp, stream),
+                   "z-loss partials launch");
+    if (r != MOE_OK) return r;
+  }
+  return hip_status(moe::launch_zloss_final(rp, cfg->T, beta, loss_out, stream),
                     "moe_router_z_loss launch");
 }
 
@@ -1065,7 +1165,24 @@ int moe_layer_forward(const moe_config_t* cfg, const void* x, const moe_weights_
   if (r != MOE_OK) return r;
   MOE_REQUIRE_PTR(out, "out");
   MOE_OPTIONAL_PTR(counts_out, "counts_out");
-  return layer_forward(cfg, x, w, out, aux_out, counts_out, n_dropped_out, ws, ws_bytes, stream);
+  const moe_layer_stats_t st{aux_out, 0.f, nullptr, counts_out, n_dropped_out, nullptr};
+  return layer_forward(cfg, x, w, out, st, ws, ws_bytes, stream);
+}
+
+int moe_layer_forward_stats(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
+                            void* out, const moe_layer_stats_t* stats, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  MOE_CHECK_CFG(cfg);
+  MOE_REQUIRE_PTR(x, "x");
+  int r = check_weights(cfg, w, true, true);
+  if (r != MOE_OK) return r;
+  MOE_REQUIRE_PTR(out, "out");
+  if (!stats) return fail(MOE_ERR_INVALID_ARG, "stats is NULL");
+  MOE_OPTIONAL_PTR(stats->counts_out, "stats.counts_out");
+  MOE_OPTIONAL_PTR(stats->weight_mean_out, "stats.weight_mean_out");
+  if (stats->zloss_out && !isfinite(stats->zloss_beta))
+    return fail(MOE_ERR_INVALID_ARG, "stats.zloss_beta is not finite");
+  return layer_forward(cfg, x, w, out, *stats, ws, ws_bytes, stream);
 }
 
 int moe_layer_forward_noalloc(const moe_config_t* cfg, const void* x, const moe_weights_t* w,
@@ -1086,8 +1203,8 @@ int moe_layer_forward_noalloc(const moe_config_t* cfg, const void* x, const moe_
   int code = MOE_OK;
   void* ptr = scratch_for_current_device(&code);
   if (!ptr) return code;
-  return layer_forward(cfg, x, w, out, aux_out, counts_out, n_dropped_out, ptr, kScratchBytes,
-                       stream);
+  const moe_layer_stats_t st{aux_out, 0.f, nullptr, counts_out, n_dropped_out, nullptr};
+  return layer_forward(cfg, x, w, out, st, ptr, kScratchBytes, stream);
 }
 
 // ---------------------------------------------------------------- training entry points
@@ -1135,7 +1252,8 @@ int moe_layer_forward_train(const moe_config_t* cfg, const void* x, const moe_we
   LayerTrainWs lw;
   carve_layer_train(cv, cfg, &lw);
   const moe_saved_t& sv = *saved;
-  r = do_route(cfg, x, w, sv.logits, sv.topk_idx, sv.topk_w, lw.route, stream);
+  r = do_route(cfg, x, w, sv.logits, sv.topk_idx, sv.topk_w, lw.route, stream,
+               aux_out ? &lw.aux.rp : nullptr);
   if (r != MOE_OK) return r;
   r = do_dispatch(cfg, sv.topk_idx, x, sv.counts, sv.expert_offsets, sv.slot_row, sv.row_token,
                   sv.x_perm, sv.n_dropped, lw.disp, stream);
@@ -1145,7 +1263,7 @@ int moe_layer_forward_train(const moe_config_t* cfg, const void* x, const moe_we
   if (r != MOE_OK) return r;
   r = do_combine(cfg, sv.y_perm, sv.slot_row, sv.topk_w, lw.y_shared, out, stream);
   if (r != MOE_OK) return r;
-  if (aux_out) return do_aux(cfg, sv.logits, sv.counts, aux_out, lw.aux, stream);
+  if (aux_out) return do_aux(cfg, nullptr, lw.aux.rp, sv.counts, aux_out, lw.aux, stream);
   return MOE_OK;
 }
 

@@ -86,6 +86,31 @@ __device__ __forceinline__ float gelu_grad_erf(float z) {
          z * expf(-0.5f * z * z) * 0.39894228040143267794f;
 }
 
+// Softmax over the N experts of one token row held by a wavefront (lane l
+// holds experts l, l + 64, l + 128, l + 192; entries past N are ignored): the
+// row max m (fp32), the exponentials ex[v] = exp(l[v] - m) (fp32, widened),
+// and their sum (fp64; each lane adds its four in order, then a fixed
+// butterfly).  The aux-loss, z-loss and routing kernels all use this one
+// routine, so the probabilities and logsumexps they derive from a row are
+// the same bits wherever they are computed.
+__device__ __forceinline__ double row_softmax_terms(const float (&l)[4], int lane, int N,
+                                                    double (&ex)[4], float& m) {
+  m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) m = fmaxf(m, l[v]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  double s = 0.0;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    ex[v] = (lane + 64 * v < N) ? (double)expf(l[v] - m) : 0.0;
+    s += ex[v];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  return s;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
@@ -103,10 +128,11 @@ template <> struct Elem<uint16_t> {
 // softmax over the K chosen.  `part` holds route_splits(T, d, N) * T * N
 // doubles.
 int route_splits(int T, int d, int N);
+struct RoutePartials;
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* b_router,
                         const float* logit_offset, const float* sel_bias, float* logits,
                         int32_t* topk_idx, float* topk_w, double* part, int T, int d, int N,
-                        int K, hipStream_t s);
+                        int K, const RoutePartials* parts, hipStream_t s);
 
 // Dispatch: histogram, scan, stable rank and row copy.
 constexpr int kDispatchTokensPerBlock = 256;
@@ -202,12 +228,34 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* slot_row
                           const float* topk_w, const void* y_shared, void* out, int T, int d,
                           int K, hipStream_t s);
 
-// Aux loss: per-block partial sums of softmax probabilities (ppart holds
-// aux_blocks(T) * N doubles), per-expert terms (term: N doubles), the sum.
-constexpr int kAuxTokensPerBlock = 16;
+// Routing partials: per block of kAuxTokensPerBlock tokens, the sums over
+// its tokens (in token order) of softmax_N(logits_t) (ppart [nblk, N]), of
+// lse_t^2 (zpart [nblk]), and, per expert, the count and the routing-weight
+// sum of the (token, slot) pairs routed to it (spcnt, spw [nblk, N], pairs in
+// token-major order).  The select kernel writes them when asked, and the aux
+// loss, z-loss and statistics kernels write the same bits from the logits /
+// routing alone.
+struct RoutePartials {
+  double* ppart;
+  double* zpart;
+  double* spw;
+  int32_t* spcnt;
+};
+// Routing partials from the logits (ppart, zpart) and from the routing
+// (spcnt, spw); the final reductions of the aux loss (term: N doubles), the
+// z-loss and the statistics.
+constexpr int kAuxTokensPerBlock = 4;
 inline int aux_blocks(int T) { return (T + kAuxTokensPerBlock - 1) / kAuxTokensPerBlock; }
-hipError_t launch_aux(const float* logits, const int32_t* counts, int T, int N, float alpha,
-                      double* ppart, double* term, float* loss_out, hipStream_t s);
+hipError_t launch_logit_partials(const float* logits, int T, int N, const RoutePartials& rp,
+                                 hipStream_t s);
+hipError_t launch_routing_partials(const int32_t* topk_idx, const float* topk_w, int T, int K,
+                                   int N, const RoutePartials& rp, hipStream_t s);
+hipError_t launch_aux_final(const RoutePartials& rp, const int32_t* counts, int T, int N,
+                            float alpha, double* term, float* loss_out, hipStream_t s);
+hipError_t launch_zloss_final(const RoutePartials& rp, int T, float beta, float* loss_out,
+                              hipStream_t s);
+hipError_t launch_stats_final(const RoutePartials& rp, int T, int N, int32_t* counts, float* wmean,
+                              hipStream_t s);
 // Per-row symmetric INT8 quantisation (dtype 0 fp32, 1 bf16 input).
 hipError_t launch_quantize_int8(const void* w, int dtype, int64_t rows, int cols, int8_t* q,
                                 float* scale, hipStream_t s);
@@ -241,12 +289,6 @@ __device__ __forceinline__ uint4 int4x8_to_bf16x8(uint32_t v) {
 }
 hipError_t launch_quantize_int4(const void* w, int dtype, int64_t rows, int cols, uint8_t* q,
                                 float* scale, hipStream_t s);
-// Routing statistics: per-expert selection counts and mean routing weight
-// (pcnt / pw hold stats_blocks(T) * N partials each).
-constexpr int kStatsTokensPerBlock = 64;
-inline int stats_blocks(int T) { return (T + kStatsTokensPerBlock - 1) / kStatsTokensPerBlock; }
-hipError_t launch_stats(const int32_t* topk_idx, const float* topk_w, int T, int K, int N,
-                        int32_t* pcnt, double* pw, int32_t* counts, float* wmean, hipStream_t s);
 // ---------------------------------------------------------------- backward
 // h = GELU(z) and d_z = d_h * GELU'(z) over rows [0, *nrows) (or rows_max
 // when nrows is null) of [*, width] matrices.
@@ -283,10 +325,5 @@ hipError_t launch_route_bwd(int dtype, const void* x, const void* w_router, cons
                             const int32_t* counts, float aux_coef, float z_coef, float* dl,
                             float* part, float* d_w_router, float* d_b_router, float* d_x_router,
                             int T, int d, int N, int K, hipStream_t s);
-
-// Router z-loss: beta * mean_t logsumexp(logits[t])^2 in fp64; zpart holds
-// aux_blocks(T) doubles.
-hipError_t launch_zloss(const float* logits, int T, int N, float beta, double* zpart,
-                        float* loss_out, hipStream_t s);
 
 }  // namespace moe

@@ -25,7 +25,10 @@
 //      identically for x and W_r -- the dot product does not depend on it;
 //   2. select: one wavefront per token sums the S partials in slice order,
 //      adds the router bias and offset in fp64, rounds once to fp32, writes
-//      the logits, and picks the Top-K with a 64-lane arg-max reduction.
+//      the logits, and picks the Top-K with a 64-lane arg-max reduction;
+//      optionally it also writes the per-block routing partials of the aux
+//      loss (lmnt.cn §5.1-5.2), the router z-loss (§5.3) and the routing
+//      statistics (§8.2) from the row it holds.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -154,13 +157,23 @@ __device__ __forceinline__ bool better(float sa, int ea, float sb, int eb) {
 }
 
 // One wavefront per token (4 per workgroup); lane = expert (4 per lane, N <= 256).
+// PART: the workgroup's four tokens are one block of the routing partials
+// (kAuxTokensPerBlock = 4): while the row is in registers, the wavefront
+// forms its softmax_N probabilities and lse^2 with row_softmax_terms, the
+// same routine and order as the aux-loss and z-loss kernels, and the
+// workgroup adds the four tokens in token order; the K (expert, weight)
+// picks give the block's per-expert counts and weight sums in (token, slot)
+// order.  The loss and statistics kernels then never read the logits again.
+template <bool PART>
 __global__ __launch_bounds__(256) void select_kernel(
     const double* __restrict__ part, int S, const float* __restrict__ b_router,
     const float* __restrict__ logit_offset, const float* __restrict__ sel_bias,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int Ttok, int N, int K) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= Ttok) return;
+    int Ttok, int N, int K, RoutePartials rp) {
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  const bool valid = t < Ttok;
+  if (!PART && !valid) return;   // (with partials every wavefront reaches the barrier)
   const int lane = threadIdx.x & 63;
   float lg[4], sc[4];
   bool taken[4];
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(256) void select_kernel(
     lg[v] = -INFINITY;
     sc[v] = -INFINITY;
     taken[v] = false;
-    if (e < N) {
+    if (valid && e < N) {
       // the slices in order; eight loads in flight before their adds
       double z = part[(int64_t)t * N + e];
       int s = 1;
@@ -231,9 +244,55 @@ __global__ __launch_bounds__(256) void select_kernel(
   double sum = ex;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  if (lane < K) {
+  const float wk = (float)(ex / sum);
+  if (valid && lane < K) {
     topk_idx[(int64_t)t * K + lane] = my_e;
-    topk_w[(int64_t)t * K + lane] = (float)(ex / sum);
+    topk_w[(int64_t)t * K + lane] = wk;
+  }
+  if constexpr (PART) {
+    __shared__ double sp[4][256];
+    __shared__ double sz[4];
+    __shared__ int32_t pe[4][64];
+    __shared__ float pw[4][64];
+    if (valid) {
+      double px[4];
+      float rm;
+      const double s = row_softmax_terms(lg, lane, N, px, rm);
+      const double inv = 1.0 / s;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sp[wave][lane + 64 * v] = px[v] * inv;
+      if (lane == 0) {
+        const double lse = (double)rm + log(s);
+        sz[wave] = lse * lse;
+      }
+      if (lane < K) {
+        pe[wave][lane] = my_e;
+        pw[wave][lane] = wk;
+      }
+    } else {
+      // tokens past T add nothing (+0.0 leaves the non-negative sums as they are)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sp[wave][lane + 64 * v] = 0.0;
+      if (lane == 0) sz[wave] = 0.0;
+      if (lane < K) pe[wave][lane] = -1;
+    }
+    __syncthreads();
+    const int e = threadIdx.x;
+    const int64_t blk = blockIdx.x;
+    if (e < N) {
+      rp.ppart[blk * N + e] = ((sp[0][e] + sp[1][e]) + sp[2][e]) + sp[3][e];
+      int c = 0;
+      double sw = 0.0;
+      for (int w = 0; w < 4; ++w)
+        for (int k = 0; k < K; ++k)
+          if (pe[w][k] == e) {
+            ++c;
+            sw += (double)pw[w][k];
+          }
+      rp.spcnt[blk * N + e] = c;
+      rp.spw[blk * N + e] = sw;
+    }
+    if (threadIdx.x == 0) rp.zpart[blk] = ((sz[0] + sz[1]) + sz[2]) + sz[3];
   }
 }
 
@@ -289,7 +348,7 @@ int route_splits(int T, int d, int N) {
 hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* b_router,
                         const float* logit_offset, const float* sel_bias, float* logits,
                         int32_t* topk_idx, float* topk_w, double* part, int T, int d, int N,
-                        int K, hipStream_t s) {
+                        int K, const RoutePartials* parts, hipStream_t s) {
   const Shape sh = shape_for(T, N);
   const int S = route_splits(T, d, N);
   const int chunks = d / KC;
@@ -298,8 +357,14 @@ hipError_t launch_route(int dtype, const void* x, const void* w_router, const fl
                      ? launch_gemm_t<float>(sh, S, klen, x, w_router, part, T, d, N, s)
                      : launch_gemm_t<uint16_t>(sh, S, klen, x, w_router, part, T, d, N, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_kernel, dim3((T + 3) / 4), dim3(256), 0, s, part, S, b_router,
-                     logit_offset, sel_bias, logits, topk_idx, topk_w, T, N, K);
+  static_assert(kAuxTokensPerBlock == 4, "one routing-partial block per select workgroup");
+  if (parts)
+    hipLaunchKernelGGL(select_kernel<true>, dim3((T + 3) / 4), dim3(256), 0, s, part, S, b_router,
+                       logit_offset, sel_bias, logits, topk_idx, topk_w, T, N, K, *parts);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3((T + 3) / 4), dim3(256), 0, s, part, S,
+                       b_router, logit_offset, sel_bias, logits, topk_idx, topk_w, T, N, K,
+                       RoutePartials{});
   return hipGetLastError();
 }
 

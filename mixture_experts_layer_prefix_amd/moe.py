@@ -24,6 +24,7 @@ STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "l
 ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
                 "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_router_z_loss",
                 "moe_routing_stats", "moe_quantize_int8", "moe_quantize_int4", "moe_layer_forward",
+                "moe_route_partials_size", "moe_layer_forward_stats",
                 "moe_expert_ffn_train", "moe_layer_forward_train", "moe_combine_backward",
                 "moe_expert_ffn_backward", "moe_route_backward", "moe_dispatch_backward",
                 "moe_layer_backward", "moe_layer_forward_noalloc", "moe_last_error")
@@ -59,6 +60,12 @@ class MoeGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
 
 
+class MoeLayerStats(ctypes.Structure):
+    _fields_ = [("aux_out", ctypes.c_void_p), ("zloss_beta", ctypes.c_float),
+                ("zloss_out", ctypes.c_void_p), ("counts_out", ctypes.c_void_p),
+                ("n_dropped_out", ctypes.c_void_p), ("weight_mean_out", ctypes.c_void_p)]
+
+
 class MoEError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"libmoe error {code}: {msg}")
@@ -83,17 +90,21 @@ def lib():
     L.moe_workspace_size.restype = sz
     L.moe_capacity_from_factor.argtypes = [i32, i32, ctypes.c_double]
     L.moe_capacity_from_factor.restype = i32
-    L.moe_route.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_partials_size.argtypes = [cfgp]
+    L.moe_route_partials_size.restype = sz
+    L.moe_route.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_ffn.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, sz, vp]
     L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
-    L.moe_aux_loss.argtypes = [cfgp, vp, vp, vp, vp, sz, vp]
-    L.moe_router_z_loss.argtypes = [cfgp, vp, ctypes.c_float, vp, vp, sz, vp]
-    L.moe_routing_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_aux_loss.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_router_z_loss.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp, sz, vp]
+    L.moe_routing_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_quantize_int8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     L.moe_quantize_int4.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     L.moe_layer_forward.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward_noalloc.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp]
+    L.moe_layer_forward_stats.argtypes = [cfgp, vp, wp, vp, ctypes.POINTER(MoeLayerStats), vp, sz,
+                                          vp]
     svp, gp, f32 = ctypes.POINTER(MoeSaved), ctypes.POINTER(MoeGrads), ctypes.c_float
     L.moe_expert_ffn_train.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_layer_forward_train.argtypes = [cfgp, vp, wp, vp, vp, svp, vp, sz, vp]
@@ -106,7 +117,8 @@ def lib():
     L.moe_layer_backward.argtypes = [cfgp, vp, wp, svp, vp, f32, f32, f32, vp, gp, vp, sz, vp]
     for name in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_aux_loss",
                  "moe_router_z_loss", "moe_routing_stats", "moe_quantize_int8", "moe_quantize_int4",
-                 "moe_layer_forward", "moe_layer_forward_noalloc", "moe_expert_ffn_train",
+                 "moe_layer_forward", "moe_layer_forward_noalloc", "moe_layer_forward_stats",
+                 "moe_expert_ffn_train",
                  "moe_layer_forward_train",
                  "moe_combine_backward", "moe_expert_ffn_backward", "moe_route_backward",
                  "moe_dispatch_backward", "moe_layer_backward"):
@@ -185,10 +197,24 @@ def _ws(ws):
 
 
 # ---------------------------------------------------------------- entry points
-def moe_route(cfg, x, w: MoeWeights, logits, topk_idx, topk_w, ws=None, stream=None):
+def route_partials_size(cfg: MoeConfig) -> int:
+    n = lib().moe_route_partials_size(ctypes.byref(cfg))
+    if n == ctypes.c_size_t(-1).value:
+        raise MoEError(MOE_ERR_INVALID_ARG, "invalid config")
+    return n
+
+
+def alloc_route_partials(cfg: MoeConfig, device="cuda"):
+    """A device buffer for moe_route's routing partials (256-byte aligned)."""
+    import torch
+    return torch.empty(route_partials_size(cfg), dtype=torch.uint8, device=device)
+
+
+def moe_route(cfg, x, w: MoeWeights, logits, topk_idx, topk_w, ws=None, stream=None,
+              partials=None):
     p, n = _ws(ws)
     _check(lib().moe_route(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(logits), _p(topk_idx),
-                           _p(topk_w), p, n, _stream(stream)))
+                           _p(topk_w), _p(partials), p, n, _stream(stream)))
 
 
 def moe_dispatch(cfg, topk_idx, x, counts, expert_offsets, slot_row, row_token, x_perm,
@@ -212,22 +238,26 @@ def moe_combine(cfg, y_perm, slot_row, topk_w, y_shared, out, stream=None):
                              _p(y_shared), _p(out), _stream(stream)))
 
 
-def moe_aux_loss(cfg, logits, counts, loss_out, ws, stream=None):
+def moe_aux_loss(cfg, logits, counts, loss_out, ws, stream=None, partials=None):
+    """From the logits, or (logits=None) from moe_route's partials."""
     p, n = _ws(ws)
-    _check(lib().moe_aux_loss(ctypes.byref(cfg), _p(logits), _p(counts), _p(loss_out), p, n,
-                              _stream(stream)))
+    _check(lib().moe_aux_loss(ctypes.byref(cfg), _p(logits), _p(partials), _p(counts),
+                              _p(loss_out), p, n, _stream(stream)))
 
 
-def moe_router_z_loss(cfg, logits, beta, loss_out, ws, stream=None):
+def moe_router_z_loss(cfg, logits, beta, loss_out, ws, stream=None, partials=None):
+    """From the logits, or (logits=None) from moe_route's partials."""
     p, n = _ws(ws)
-    _check(lib().moe_router_z_loss(ctypes.byref(cfg), _p(logits), float(beta), _p(loss_out), p, n,
-                                   _stream(stream)))
+    _check(lib().moe_router_z_loss(ctypes.byref(cfg), _p(logits), _p(partials), float(beta),
+                                   _p(loss_out), p, n, _stream(stream)))
 
 
-def moe_routing_stats(cfg, topk_idx, topk_w, counts_out, weight_mean_out, ws, stream=None):
+def moe_routing_stats(cfg, topk_idx, topk_w, counts_out, weight_mean_out, ws, stream=None,
+                      partials=None):
+    """From the routing, or (topk_idx = topk_w = None) from moe_route's partials."""
     p, n = _ws(ws)
-    _check(lib().moe_routing_stats(ctypes.byref(cfg), _p(topk_idx), _p(topk_w), _p(counts_out),
-                                   _p(weight_mean_out), p, n, _stream(stream)))
+    _check(lib().moe_routing_stats(ctypes.byref(cfg), _p(topk_idx), _p(topk_w), _p(partials),
+                                   _p(counts_out), _p(weight_mean_out), p, n, _stream(stream)))
 
 
 def moe_quantize_int8(w, q_out, scale_out, stream=None):
@@ -281,6 +311,17 @@ def moe_layer_forward(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,
     _check(lib().moe_layer_forward(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(out),
                                    _p(aux_out), _p(counts_out), _p(n_dropped_out), p, n,
                                    _stream(stream)))
+
+
+def moe_layer_forward_stats(cfg, x, w: MoeWeights, out, aux_out=None, zloss_beta=0.0,
+                            zloss_out=None, counts_out=None, n_dropped_out=None,
+                            weight_mean_out=None, ws=None, stream=None):
+    st = MoeLayerStats(aux_out=_p(aux_out), zloss_beta=float(zloss_beta), zloss_out=_p(zloss_out),
+                       counts_out=_p(counts_out), n_dropped_out=_p(n_dropped_out),
+                       weight_mean_out=_p(weight_mean_out))
+    p, n = _ws(ws)
+    _check(lib().moe_layer_forward_stats(ctypes.byref(cfg), _p(x), ctypes.byref(w), _p(out),
+                                         ctypes.byref(st), p, n, _stream(stream)))
 
 
 def moe_layer_forward_noalloc(cfg, x, w: MoeWeights, out, aux_out=None, counts_out=None,

@@ -211,3 +211,57 @@ def check_routing_and_dispatch(g, o, inp, capacity):
     werr = np.abs(g["w"].astype(np.float64) - o["w"]) / np.maximum(np.abs(o["w"]), 1e-30)
     assert werr.max() <= W_TOL, f"routing weight rel err {werr.max()}"
     assert g["x_perm_ok"], "x_perm rows are not exact copies of x[row_token]"
+
+
+def check_fused_partials(cfg, t, g, beta=1e-3, device="cuda"):
+    """moe_route's routing partials give the aux loss, z-loss and routing
+    statistics bit for bit equal to those formed from the logits / routing,
+    and moe_layer_forward_stats (which uses them) equals the staged calls."""
+    import torch
+    T, N, K, d = cfg.T, cfg.n_experts, cfg.top_k, cfg.d_model
+    W = moe.make_weights(t)
+    f32 = dict(dtype=torch.float32, device=device)
+    i32 = dict(dtype=torch.int32, device=device)
+    logits = torch.empty(T, N, **f32)
+    idx = torch.empty(T, K, **i32)
+    w = torch.empty(T, K, **f32)
+    parts = moe.alloc_route_partials(cfg, device)
+    moe.moe_route(cfg, t["x"], W, logits, idx, w, moe.alloc_workspace(cfg, "route", device),
+                  partials=parts)
+    torch.cuda.synchronize()
+    assert (logits.cpu().numpy().view(np.uint32) == g["logits"].view(np.uint32)).all()
+    assert (idx.cpu().numpy() == g["idx"]).all()
+    assert (w.cpu().numpy().view(np.uint32) == g["w"].view(np.uint32)).all()
+    counts = torch.from_numpy(g["counts"]).to(device)
+    ws = moe.alloc_workspace(cfg, "aux", device)
+    alpha = cfg.aux_alpha
+    if alpha == 0:
+        cfg.aux_alpha = 0.01
+    a_u, a_f, z_u, z_f = (torch.empty(1, **f32) for _ in range(4))
+    moe.moe_aux_loss(cfg, logits, counts, a_u, ws)
+    moe.moe_aux_loss(cfg, None, counts, a_f, ws, partials=parts)
+    moe.moe_router_z_loss(cfg, logits, beta, z_u, ws)
+    moe.moe_router_z_loss(cfg, None, beta, z_f, ws, partials=parts)
+    c_u, c_f = torch.empty(N, **i32), torch.empty(N, **i32)
+    m_u, m_f = torch.empty(N, **f32), torch.empty(N, **f32)
+    moe.moe_routing_stats(cfg, idx, w, c_u, m_u, ws)
+    moe.moe_routing_stats(cfg, None, None, c_f, m_f, ws, partials=parts)
+    torch.cuda.synchronize()
+    assert torch.equal(a_u, a_f), (float(a_u), float(a_f))
+    assert torch.equal(z_u, z_f), (float(z_u), float(z_f))
+    assert torch.equal(c_u, c_f) and torch.equal(m_u, m_f)
+    assert (c_u.cpu().numpy() == g["counts"]).all()
+    # the monitored layer call: same kernels, same bits
+    dt = torch.float32 if cfg.dtype == moe.MOE_F32 else torch.bfloat16
+    out = torch.empty(T, d, dtype=dt, device=device)
+    l_aux, l_z, l_m = torch.empty(1, **f32), torch.empty(1, **f32), torch.empty(N, **f32)
+    l_c, l_nd = torch.empty(N, **i32), torch.empty(1, **i32)
+    moe.moe_layer_forward_stats(cfg, t["x"], W, out, aux_out=l_aux, zloss_beta=beta, zloss_out=l_z,
+                                counts_out=l_c, n_dropped_out=l_nd, weight_mean_out=l_m,
+                                ws=moe.alloc_workspace(cfg, "layer", device))
+    torch.cuda.synchronize()
+    cfg.aux_alpha = alpha
+    assert torch.equal(out.float().cpu(), torch.from_numpy(g["out"]))
+    assert torch.equal(l_aux, a_u) and torch.equal(l_z, z_u) and torch.equal(l_m, m_u)
+    assert torch.equal(l_c, c_u) and int(l_nd.item()) == g["n_dropped"]
+    return float(a_u.item()), float(z_u.item()), m_u.cpu().numpy()

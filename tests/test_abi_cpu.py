@@ -48,7 +48,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails it
 
 def _route(cfg, x=FAKE, wr=FAKE, idx=FAKE, w=FAKE):
     W = moe.MoeWeights(w_router=wr)
-    return moe.lib().moe_route(ctypes.byref(cfg), x, ctypes.byref(W), None, idx, w, FAKE * 256,
+    return moe.lib().moe_route(ctypes.byref(cfg), x, ctypes.byref(W), None, idx, w, None, FAKE * 256,
                                1 << 40, None)
 
 
@@ -114,22 +114,44 @@ def test_null_and_misaligned_pointers_rejected():
     assert _route(cfg, idx=None) == moe.MOE_ERR_INVALID_ARG
     L = moe.lib()
     assert L.moe_combine(ctypes.byref(cfg), FAKE, FAKE, FAKE, None, None, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_aux_loss(ctypes.byref(cfg), FAKE, FAKE, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_router_z_loss(ctypes.byref(cfg), None, ctypes.c_float(1e-3), FAKE, FAKE * 256,
-                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, ctypes.c_float(1e-3), None, FAKE * 256,
-                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, ctypes.c_float(float("nan")), FAKE,
+    assert L.moe_aux_loss(ctypes.byref(cfg), FAKE, None, FAKE, None, None, 0,
+                          None) == moe.MOE_ERR_INVALID_ARG
+    # exactly one of logits and routing partials
+    assert L.moe_aux_loss(ctypes.byref(cfg), None, None, FAKE, FAKE, FAKE * 256, 1 << 30,
+                          None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_aux_loss(ctypes.byref(cfg), FAKE, FAKE * 256, FAKE, FAKE, FAKE * 256, 1 << 30,
+                          None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_aux_loss(ctypes.byref(cfg), None, FAKE + 16, FAKE, FAKE, FAKE * 256, 1 << 30,
+                          None) == moe.MOE_ERR_INVALID_ARG                     # misaligned partials
+    assert L.moe_router_z_loss(ctypes.byref(cfg), None, None, ctypes.c_float(1e-3), FAKE,
+                               FAKE * 256, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, None, ctypes.c_float(1e-3), None,
+                               FAKE * 256, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, None, ctypes.c_float(float("nan")), FAKE,
                                FAKE * 256, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert b"beta" in L.moe_last_error()
-    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, ctypes.c_float(1e-3), FAKE, None, 0,
+    assert L.moe_router_z_loss(ctypes.byref(cfg), FAKE, None, ctypes.c_float(1e-3), FAKE, None, 0,
                                None) == moe.MOE_ERR_WORKSPACE
-    assert L.moe_routing_stats(ctypes.byref(cfg), None, FAKE, None, FAKE, FAKE * 256, 1 << 30,
-                               None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_routing_stats(ctypes.byref(cfg), FAKE, FAKE, None, None, FAKE * 256, 1 << 30,
-                               None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_routing_stats(ctypes.byref(cfg), FAKE, FAKE, None, FAKE, FAKE * 256, 16,
+    assert L.moe_routing_stats(ctypes.byref(cfg), None, FAKE, None, None, FAKE, FAKE * 256,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(ctypes.byref(cfg), FAKE, FAKE, None, None, None, FAKE * 256,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_routing_stats(ctypes.byref(cfg), FAKE, FAKE, FAKE * 256, None, FAKE, FAKE * 256,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG       # both inputs
+    assert L.moe_routing_stats(ctypes.byref(cfg), FAKE, FAKE, None, None, FAKE, FAKE * 256, 16,
                                None) == moe.MOE_ERR_WORKSPACE
+    # routing partials: buffer size and alignment
+    assert moe.route_partials_size(cfg) > 0
+    assert moe.lib().moe_route(ctypes.byref(cfg), FAKE, ctypes.byref(moe.MoeWeights(w_router=FAKE)),
+                               None, FAKE, FAKE, FAKE + 16, FAKE * 256, 1 << 40,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    st = moe.MoeLayerStats(zloss_beta=float("inf"), zloss_out=FAKE)
+    Wl = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=FAKE)
+    assert L.moe_layer_forward_stats(ctypes.byref(cfg), FAKE, ctypes.byref(Wl), FAKE,
+                                     ctypes.byref(st), FAKE * 256, 1 << 40,
+                                     None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_stats(ctypes.byref(cfg), FAKE, ctypes.byref(Wl), FAKE, None,
+                                     FAKE * 256, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
     W = moe.MoeWeights(w_router=FAKE, w1=FAKE, w2=None)
     assert L.moe_expert_ffn(ctypes.byref(cfg), FAKE, FAKE, ctypes.byref(W), None, FAKE, None,
                             FAKE, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG

@@ -4,7 +4,9 @@ same C-ABI stage calls).
 
 Every output is compared whole against the oracle run over the whole batch:
 routing, dispatch, aux loss, router z-loss and routing statistics over every
-token (integers bit-exact), the layer output [T, d_model] and the expert
+token (integers bit-exact; the losses and statistics formed from the select
+kernel's routing partials equal those formed from the logits bit for bit),
+the layer output [T, d_model] and the expert
 outputs in dispatch order y_perm [M, d_model] over every element (relative
 L2 within the tolerance of the layer's dtype)."""
 import gc
@@ -16,8 +18,9 @@ from mixture_experts_layer_prefix_amd import configs as C
 from mixture_experts_layer_prefix_amd import inputs, moe
 from oracle import moe_oracle as O
 
-from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, W_TOL, check_routing_and_dispatch,
-                         device_tensors, oracle_run, rel_l2, run_stages, say)
+from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, W_TOL, check_fused_partials,
+                         check_routing_and_dispatch, device_tensors, oracle_run, rel_l2,
+                         run_stages, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +48,9 @@ def test_full_size(shape):
     moe.moe_routing_stats(cfg, torch.from_numpy(g["idx"]).cuda(), torch.from_numpy(g["w"]).cuda(),
                           sc, sm, moe.alloc_workspace(cfg, "aux"))
     g_zl, g_sc, g_sm = float(zl.item()), sc.cpu().numpy(), sm.cpu().numpy()
+    # the select kernel's routing partials give the same bits; so does the
+    # monitored layer call
+    check_fused_partials(cfg, t, g)
     M = int(g["expert_offsets"][-1])
     y_perm = g.pop("y_perm")[:M].float().cpu().numpy()
     del t, zl, sc, sm

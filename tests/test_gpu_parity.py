@@ -8,8 +8,9 @@ from mixture_experts_layer_prefix_amd import configs as C
 from mixture_experts_layer_prefix_amd import inputs, moe
 from oracle import moe_oracle as O
 
-from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, W_TOL, check_routing_and_dispatch,
-                         device_tensors, oracle_run, rel_l2, run_layer, run_stages, say)
+from moe_testlib import (AUX_TOL, BF16_TOL, F32_TOL, W_TOL, check_fused_partials,
+                         check_routing_and_dispatch, device_tensors, oracle_run, rel_l2,
+                         run_layer, run_stages, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -104,6 +105,9 @@ def _compare(name, shape, inp, cfg):
     assert (lay["counts"] == g["counts"]).all() and lay["n_dropped"] == g["n_dropped"]
     if cfg.aux_alpha:
         assert lay["aux"] == g["aux"]
+    # the routing partials written by the select kernel give the same bits,
+    # and the monitored layer call equals the stages
+    check_fused_partials(cfg, t, g)
     return g, o
 
 
