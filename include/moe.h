@@ -185,7 +185,10 @@ int moe_dispatch(const moe_config_t *cfg, const int32_t *topk_idx, const void *x
 
 /* Per-expert FFN as grouped GEMMs over the ragged expert blocks (yunthe.com
  * reference forward: Linear, GELU, Linear; batched per expert as a grouped
- * GEMM).  GELU is the exact erf form, fused into the first GEMM's epilogue.
+ * GEMM).  GELU(z) = z/2 (1 + erf(z / sqrt 2)), fused into the first GEMM's
+ * epilogue: fp32 layers use the library erff; bf16 layers (every GEMM path)
+ * use erf from Abramowitz-Stegun formula 7.1.26, whose GELU is within 2.2e-7
+ * absolute of the exact one (<= 0.013 bf16 ulp of the result for |z| < 3).
  *   x_perm         [dev] [T*K, d] dtype in (first expert_offsets[N] rows used).
  *   expert_offsets [dev] [N+1] int32 in (as written by moe_dispatch).
  *   x              [dev] [T, d] dtype in: input of the shared expert; may be

@@ -116,7 +116,7 @@ __device__ __forceinline__ uint4 ld_row16(const uint4* p) {
   }
 }
 // Per-slot rows of T*K rows x nvec pieces: non-temporal beyond half the MALL.
-inline bool rows_nt(int64_t rows, int nvec) { return rows * nvec * 16 > (int64_t(128) << 20); }
+inline bool rows_nt(int64_t rows, int nvec) { return rows * nvec * 16 > nontemporal_rows_bytes(); }
 
 // One wavefront per token (wave-uniform index, so the slot rows and weights
 // are scalar loads); slots in groups of KB.  For each group, a lane walks its

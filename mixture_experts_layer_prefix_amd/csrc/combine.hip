@@ -13,6 +13,8 @@
 // One wavefront per token; each lane moves 16-byte pieces of the rows, so a
 // wavefront reads 1 KiB of a row per instruction, and many such loads are in
 // flight per lane; no atomics, every output element written exactly once.
+#include <stdlib.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -159,12 +161,22 @@ void launch_combine_t(const void* y_perm, const int32_t* slot_row, const float* 
 
 }  // namespace
 
+int64_t nontemporal_rows_bytes() {
+  const char* e = getenv("MOE_NONTEMPORAL_ROWS_BYTES");
+  if (e && *e) {
+    char* end = nullptr;
+    const long long v = strtoll(e, &end, 10);
+    if (end && *end == 0 && v >= 0) return (int64_t)v;
+  }
+  return int64_t(128) << 20;
+}
+
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* slot_row,
                           const float* topk_w, const void* y_shared, void* out, int T, int d,
                           int K, hipStream_t s) {
   const int nvec = d * (dtype == 0 ? 4 : 2) / 16;
   // expert rows beyond half of the 256 MB MALL: non-temporal loads
-  const bool nt = (int64_t)T * K * nvec * 16 > (int64_t(128) << 20);
+  const bool nt = (int64_t)T * K * nvec * 16 > nontemporal_rows_bytes();
   if (dtype == 0)
     nt ? launch_combine_t<float, true>(y_perm, slot_row, topk_w, y_shared, out, T, nvec, K, s)
        : launch_combine_t<float, false>(y_perm, slot_row, topk_w, y_shared, out, T, nvec, K, s);

@@ -7,7 +7,7 @@
 // weight byte is used for only rows_e multiply-adds.  The weights of each
 // touched expert are therefore split over many workgroups along the output
 // dimension, and each wavefront streams 16 NR weight rows (NR = 1 for bf16,
-// 2 for INT8 weights) through v_mfma_f32_16x16x32_bf16 with the expert's
+// 2 for INT8, 4 for INT4 weights) through v_mfma_f32_16x16x32_bf16 with the expert's
 // (up to 16) token rows as the other operand, eight 16-byte loads per lane
 // and row tile in flight per step (four per tile for INT8: 128 codes each).
 // Workgroup (bx, e): outputs [64 NR bx, 64 NR (bx + 1)) of expert e, one
@@ -15,7 +15,8 @@
 // index E stands for the dense shared problem when one is present (its
 // weights are always in the activation dtype; launches with INT8 routed
 // weights carry none).
-// KS = 4 (long reductions, Kd > Nd): a workgroup takes 16 NR outputs and its
+// KS = 4 (long reductions, Kd > Nd; with INT4 codes any Kd >= 2048): a
+// workgroup takes 16 NR outputs and its
 // four wavefronts split the model dimension in quarters; the four partial
 // sums are added in wavefront order through LDS.  Four times as many,
 // shorter workgroups keep every CU streaming: with one wavefront per 16
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
         const int r = g0 + (lane >> 4) * 4 + v;
         if (r < r1) {
           float z = QW ? fmaf(acc[j][v], sc[j], bv[j]) : acc[j][v] + bv[j];
-          if (GELU) z = gelu_erf(z);
+          if (GELU) z = gelu_as(z);
           C[(int64_t)r * Nd + col] = f32_to_bf16(z);
         }
       }
@@ -288,8 +289,11 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_
   const int E = a.E + (a.As ? 1 : 0);
   if (E == 0) return hipSuccess;
   // long reductions: the four wavefronts of a workgroup split the model dimension
-  const bool ks = a.Kd > a.Nd && a.Kd >= 4096;
   const bool q4 = a.wscale && a.w4;
+  // INT4 codes: the k-split also for Kd >= 2048 (the decode-shaped first GEMM
+  // has four times fewer workgroups than with bf16 weights otherwise;
+  // same-GPU A/B: the INT4 decode stage 0.248 -> 0.235 ms)
+  const bool ks = (a.Kd > a.Nd && a.Kd >= 4096) || (q4 && a.Kd >= 2048);
   const int npw = 16 * (q4 ? skinny_nr<true, true>()
                            : (a.wscale ? skinny_nr<true>() : skinny_nr<false>()));   // per wavefront
   const int per_wg = ks ? npw : npw * NTHR / 64;

@@ -502,8 +502,9 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
       // launch: its weights are re-read by every m-tile of the T tokens.  Not
       // in the training forward either, which keeps z and runs the GELU as a
       // kernel of its own (there the Switch-shaped forward ran 5% slower).
+      // (the activations of this launch: its A operand, T*K rows of Kd)
       g.w_stream = path == PATH_TILED && !train && !g.wscale && Ts == 0 && weight_bound(c) &&
-                   (int64_t)c->T * c->top_k * c->d_model * (int64_t)elem_bytes(c->dtype) <=
+                   (int64_t)c->T * c->top_k * g.Kd * (int64_t)elem_bytes(c->dtype) <=
                        (int64_t(128) << 20);
       e = moe::launch_tile_list(offs, Nr, bm, bn, g.Nd, Ts, merge, fw.bound[list],
                                 fw.list[list], fw.count + list, s, g.wide_rows);

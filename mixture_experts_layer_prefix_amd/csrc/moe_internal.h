@@ -49,8 +49,13 @@ __device__ __forceinline__ float gelu_erf(float z) {
 // which the code evaluates with the -1/2 folded into the coefficients: one
 // reciprocal, one exp2 and ten other VALU operations (this runs on every
 // element of the first GEMM's output, at a quarter of the MFMA tile's time
-// budget when it was written naively).  Its error is 1e-4 of a bf16 ulp of
-// the result.
+// budget when it was written naively).  Against the exact GELU (a CPU sweep
+// of z in [-9, 9]): absolute error <= 2.2e-7 everywhere, i.e. <= 0.013 bf16
+// ulp of the result for |z| < 3 and <= 0.4 ulp for -5 < z < -3; below -5,
+// where |GELU(z)| < 1.5e-6, the relative error grows (a few ulp, and more
+// far out) while the absolute error stays below 2.3e-9.  Every bf16 path
+// (prefill and decode GEMMs, training forward and backward) uses this form;
+// the fp32 layer uses the library erff.
 __device__ __forceinline__ float gelu_as(float z) {
   const float az = fabsf(z);
   const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189f, az, 1.0f));   // p / sqrt(2)
@@ -222,6 +227,13 @@ hipError_t launch_gemm_f32(const GemmArgs& a, bool gelu, hipStream_t s);
 // Decode-shaped grouped GEMM (bf16): streams each touched expert's weights once.
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int max_rows_per_expert,
                                    hipStream_t s);
+
+// Bytes of per-slot rows (T*K rows of d elements) above which the combine,
+// combine-backward and unpermute kernels load them non-temporally: half of
+// the 256 MB MALL.  MOE_NONTEMPORAL_ROWS_BYTES (a decimal byte count) in the
+// environment replaces it, read on every launch; tests set it to 0 to run the
+// non-temporal variants on small layers.
+int64_t nontemporal_rows_bytes();
 
 // Combine.
 hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* slot_row,

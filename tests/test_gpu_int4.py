@@ -85,6 +85,9 @@ CASES = {
     # evenly (4480 = 35 blocks of 128)
     "skinny_ksplit_ragged_w4": C.DECODE.with_(T=12, d_model=256, d_ff=4480, n_experts=16,
                                               weight_quant="int4"),
+    # the first GEMM's Kd = 2048 also splits over the four wavefronts (INT4 only)
+    "skinny_ksplit_gemm1_w4": C.DECODE.with_(T=10, d_model=2048, d_ff=2560, n_experts=16,
+                                             weight_quant="int4"),
     "skinny_shared_w4": C.DEEPSEEK_FINE.with_(T=6, d_model=128, d_ff=256, n_experts=64, top_k=8,
                                               d_ff_shared=128, weight_quant="int4"),
 }
