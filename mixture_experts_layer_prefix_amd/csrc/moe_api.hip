@@ -483,13 +483,15 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
     hipError_t e = hipSuccess;
     if (path != PATH_SKINNY) {
       const int merge = path == PATH_TILED ? moe::gemm_bf16_merge_rows() : 0;
-      // Wide tiles for small blocks: with INT8 weights, whose A rows are half
-      // of a short tile's load bytes (same-GPU: Switch-shaped INT8 stage 5%
-      // faster; with bf16 weights the Switch-shaped first GEMM lost 4%), and
-      // only where there are rounds of tiles to spare (about four of the
-      // chip's 256 CUs' worth), so that halving the tiles of the small blocks
-      // (each twice as long) does not unbalance the last round.
-      g.wide_rows = path == PATH_TILED && g.wscale &&
+      // Wide tiles for small blocks: with INT8 / INT4 weights, whose A rows
+      // are half of a short tile's load bytes (same-GPU: Switch-shaped INT8
+      // stage 5% faster), and with bf16 weights in fine-grained layers of at
+      // least 128 experts (same-GPU: the DeepSeek-shaped stage 3.71 -> 3.61
+      // ms, both GEMMs gaining; the Switch shape's 64 experts lose 2% in the
+      // first GEMM), and only where there are rounds of tiles to spare (about
+      // four of the chip's 256 CUs' worth), so that halving the tiles of the
+      // small blocks (each twice as long) does not unbalance the last round.
+      g.wide_rows = path == PATH_TILED && (g.wscale || c->n_experts >= 128) &&
                             (int64_t)Nr * ((g.Nd + bn - 1) / bn) >= 1024
                         ? moe::gemm_bf16_wide_rows() : 0;
       // Non-temporal loads of bf16 weights where each expert's weights are

@@ -64,6 +64,15 @@ def test_wide_tiles_int8():
     _check_blocks("wide_int8", counts, 832, 1216, "int8")
 
 
+def test_wide_tiles_bf16():
+    """bf16 weights take the wide tiles too in layers of at least 128 experts
+    (the same 256 experts, d = 832, f = 1216: partial last wide tiles of 320
+    and 192 columns)."""
+    pattern = [0, 1, 5, 33, 64, 65, 96, 97, 127, 128, 2, 17, 129, 40, 200, 257]
+    counts = [pattern[(e * 3) % len(pattern)] for e in range(256)]
+    _check_blocks("wide_bf16", counts, 832, 1216, "none")
+
+
 def test_wide_tiles_int4():
     """The same wide tiles with INT4 codes (d = 896, f = 1152: both GEMMs end
     in a partial wide tile of 384 and 128 columns)."""
