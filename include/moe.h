@@ -76,6 +76,27 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  * stay in dtype. */
 typedef enum { MOE_WQ_NONE = 0, MOE_WQ_INT8 = 1, MOE_WQ_INT4 = 2 } moe_weight_quant_t;
 
+/* How moe_route forms the logits (lmnt.cn §2.1 gate scoring; the Top-K
+ * decisions are the same on both paths).
+ * MOE_ROUTER_EXACT: every dot product accumulated in fp64 on the fp64
+ *   matrix cores, rounded once to fp32.
+ * MOE_ROUTER_CERTIFIED (dtype MOE_BF16 only): the bf16 matrix cores with
+ *   fp32 sums of 32 products folded into fp64, plus a proven bound B on the
+ *   error of each dot product.  A token whose Top-K set and order follow
+ *   from the bounds alone keeps these approximate logits; for every other
+ *   token each expert whose score interval reaches the K-th largest lower
+ *   bound is recomputed in fp64 before the selection.  topk_idx is the same
+ *   as on the exact path; a logit may differ from the exact one by the
+ *   bound (B <= ~4e-6 * |x_t| * |W_r[e]|), the K chosen logits of a
+ *   recomputed token not at all.
+ * MOE_ROUTER_AUTO: CERTIFIED for bf16 layers with 2 T N d >= 2^31 (where
+ *   the fp64 router GEMM is a visible share of the layer), else EXACT. */
+typedef enum {
+  MOE_ROUTER_AUTO = 0,
+  MOE_ROUTER_EXACT = 1,
+  MOE_ROUTER_CERTIFIED = 2
+} moe_router_t;
+
 typedef struct {
   int32_t T;           /* tokens in the batch                                  */
   int32_t d_model;     /* d                                                    */
@@ -87,6 +108,7 @@ typedef struct {
   int32_t dtype;       /* moe_dtype_t of x, expert weights, intermediates, out */
   float aux_alpha;     /* alpha of the aux loss (used by moe_layer_forward)    */
   int32_t weight_quant;/* moe_weight_quant_t of the routed experts' w1 / w2    */
+  int32_t router;      /* moe_router_t: how the router logits are formed        */
 } moe_config_t;
 
 typedef struct {
@@ -141,13 +163,19 @@ int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double capacity_f
  * logits or the routing again. */
 size_t moe_route_partials_size(const moe_config_t *cfg);
 
+/* The router path (MOE_ROUTER_EXACT or MOE_ROUTER_CERTIFIED) that cfg->router
+ * resolves to; -1 if cfg is invalid or asks for CERTIFIED with fp32. */
+int moe_router_path(const moe_config_t *cfg);
+
 /* Router scoring and Top-K routing (lmnt.cn §2.1 gate scoring equation and
  * the TopK-then-Softmax order; yunthe.com reference forward; yunthe.com
  * per-expert bias b_i for selection).
  *   x        [dev] [T, d] dtype
  *   logits   [dev] [T, N] fp32 out, or NULL.  logits = fp32 rounding of the
  *            dot product accumulated in fp64, plus b_router and
- *            logit_offset added in fp64 before that single rounding.
+ *            logit_offset added in fp64 before that single rounding (on the
+ *            certified path the dot product may be the bounded
+ *            approximation, see moe_router_t).
  *   topk_idx [dev] [T, K] int32 out: the K experts with the largest
  *            fp32(logit + sel_bias), ordered by (score desc, index asc);
  *            NaN scores order as -inf.
@@ -157,8 +185,8 @@ size_t moe_route_partials_size(const moe_config_t *cfg);
  *            bytes: the routing partials of the aux loss (P, lmnt.cn §5.1-5.2),
  *            the z-loss (lmnt.cn §5.3) and the routing statistics (lmnt.cn
  *            §8.2), formed while each token's logits are in registers.
- *   ws       [dev] >= moe_workspace_size(cfg, MOE_STAGE_ROUTE) bytes (fp64
- *            partial dot products). */
+ *   ws       [dev] >= moe_workspace_size(cfg, MOE_STAGE_ROUTE) bytes (partial
+ *            dot products). */
 int moe_route(const moe_config_t *cfg, const void *x, const moe_weights_t *w, float *logits,
               int32_t *topk_idx, float *topk_w, void *partials, void *ws, size_t ws_bytes,
               hipStream_t stream);

@@ -46,6 +46,11 @@ std::string check_config(const moe_config_t* c, int* code) {
   if (c->weight_quant != MOE_WQ_NONE && c->weight_quant != MOE_WQ_INT8 &&
       c->weight_quant != MOE_WQ_INT4)
     return "weight_quant must be MOE_WQ_NONE, MOE_WQ_INT8 or MOE_WQ_INT4";
+  if (c->router != MOE_ROUTER_AUTO && c->router != MOE_ROUTER_EXACT &&
+      c->router != MOE_ROUTER_CERTIFIED)
+    return "router must be MOE_ROUTER_AUTO, MOE_ROUTER_EXACT or MOE_ROUTER_CERTIFIED";
+  if (c->router == MOE_ROUTER_CERTIFIED && c->dtype != MOE_BF16)
+    return "MOE_ROUTER_CERTIFIED needs dtype MOE_BF16";
   *code = MOE_ERR_UNSUPPORTED;
   if (c->weight_quant != MOE_WQ_NONE && c->dtype != MOE_BF16)
     return "INT8 and INT4 expert weights need dtype MOE_BF16";
@@ -72,6 +77,14 @@ GemmPath gemm_path(const moe_config_t* c) {
   // Decode-shaped: on average at most 8 rows per routed expert.
   if ((int64_t)c->T * c->top_k <= 8LL * c->n_experts) return PATH_SKINNY;
   return PATH_TILED;
+}
+
+// The certified bf16 router where the fp64 router GEMM would be a visible
+// share of the layer (2 T N d >= 2^31 flops), or where asked for.
+bool router_certified(const moe_config_t* c) {
+  if (c->router == MOE_ROUTER_CERTIFIED) return true;
+  if (c->router == MOE_ROUTER_EXACT || c->dtype != MOE_BF16) return false;
+  return 2.0 * c->T * c->n_experts * (double)c->d_model >= 2147483648.0;
 }
 
 // Rows per tile of the tiled GEMMs (the bf16 kernel shrinks its wave layout
@@ -112,7 +125,7 @@ struct Carver {
 };
 
 struct RouteWs {
-  double* part;         // fp64 partial dot products, one slab per model-dim slice
+  void* part;           // partial dot products, one slab per model-dim slice
 };
 struct DispatchWs {
   int32_t* blkcnt;
@@ -181,8 +194,8 @@ struct LayerWs {
 };
 
 void carve_route(Carver& cv, const moe_config_t* c, RouteWs* w) {
-  const int S = moe::route_splits(c->T, c->d_model, c->n_experts);
-  w->part = cv.take<double>((size_t)S * c->T * c->n_experts * sizeof(double));
+  w->part = cv.take<void>(
+      moe::route_ws_bytes(c->T, c->d_model, c->n_experts, router_certified(c)));
 }
 
 void carve_dispatch(Carver& cv, const moe_config_t* c, DispatchWs* w) {
@@ -448,9 +461,9 @@ int hip_status(hipError_t e, const char* where) {
 int do_route(const moe_config_t* c, const void* x, const moe_weights_t* w, float* logits,
              int32_t* idx, float* tw, const RouteWs& rw, hipStream_t s,
              const moe::RoutePartials* parts = nullptr) {
-  return hip_status(moe::launch_route(c->dtype, x, w->w_router, w->b_router, w->logit_offset,
-                                      w->sel_bias, logits, idx, tw, rw.part, c->T, c->d_model,
-                                      c->n_experts, c->top_k, parts, s),
+  return hip_status(moe::launch_route(c->dtype, router_certified(c), x, w->w_router, w->b_router,
+                                      w->logit_offset, w->sel_bias, logits, idx, tw, rw.part,
+                                      c->T, c->d_model, c->n_experts, c->top_k, parts, s),
                     "moe_route launch");
 }
 
@@ -964,6 +977,12 @@ int32_t moe_capacity_from_factor(int32_t T, int32_t n_experts, double cf) {
   const unsigned __int128 q = (num + den - 1) / den;
   if (q > 0x7fffffff) return -1;
   return (int32_t)q;
+}
+
+int moe_router_path(const moe_config_t* cfg) {
+  int code;
+  if (!check_config(cfg, &code).empty()) return -1;
+  return router_certified(cfg) ? MOE_ROUTER_CERTIFIED : MOE_ROUTER_EXACT;
 }
 
 size_t moe_route_partials_size(const moe_config_t* cfg) {

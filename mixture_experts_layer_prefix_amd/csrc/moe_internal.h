@@ -129,15 +129,16 @@ template <> struct Elem<uint16_t> {
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch(es).
 
-// Router logits (fp64 MFMA, split over the model dimension) + Top-K +
-// softmax over the K chosen.  `part` holds route_splits(T, d, N) * T * N
-// doubles.
+// Router logits (fp64 MFMA split over the model dimension, or the certified
+// bf16-MFMA path) + Top-K + softmax over the K chosen.  `ws` holds
+// route_ws_bytes(T, d, N, certified) bytes, 256-byte aligned.
 int route_splits(int T, int d, int N);
+size_t route_ws_bytes(int T, int d, int N, bool certified);
 struct RoutePartials;
-hipError_t launch_route(int dtype, const void* x, const void* w_router, const float* b_router,
-                        const float* logit_offset, const float* sel_bias, float* logits,
-                        int32_t* topk_idx, float* topk_w, double* part, int T, int d, int N,
-                        int K, const RoutePartials* parts, hipStream_t s);
+hipError_t launch_route(int dtype, bool certified, const void* x, const void* w_router,
+                        const float* b_router, const float* logit_offset, const float* sel_bias,
+                        float* logits, int32_t* topk_idx, float* topk_w, void* ws, int T, int d,
+                        int N, int K, const RoutePartials* parts, hipStream_t s);
 
 // Dispatch: histogram, scan, stable rank and row copy.
 constexpr int kDispatchTokensPerBlock = 256;

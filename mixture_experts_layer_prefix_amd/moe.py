@@ -18,13 +18,15 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_WQ_NONE, MOE_WQ_INT8, MOE_WQ_INT4 = 0, 1, 2
 _WQ = {"none": MOE_WQ_NONE, "int8": MOE_WQ_INT8, "int4": MOE_WQ_INT4}
+MOE_ROUTER_AUTO, MOE_ROUTER_EXACT, MOE_ROUTER_CERTIFIED = 0, 1, 2
+_ROUTER = {"auto": MOE_ROUTER_AUTO, "exact": MOE_ROUTER_EXACT, "certified": MOE_ROUTER_CERTIFIED}
 STAGES = {"route": 0, "dispatch": 1, "expert_ffn": 2, "combine": 3, "aux": 4, "layer": 5,
           "expert_ffn_train": 6, "layer_train": 7, "expert_ffn_backward": 8,
           "route_backward": 9, "layer_backward": 10}
 ENTRY_POINTS = ("moe_workspace_size", "moe_capacity_from_factor", "moe_route", "moe_dispatch",
                 "moe_expert_ffn", "moe_combine", "moe_aux_loss", "moe_router_z_loss",
                 "moe_routing_stats", "moe_quantize_int8", "moe_quantize_int4", "moe_layer_forward",
-                "moe_route_partials_size", "moe_layer_forward_stats",
+                "moe_route_partials_size", "moe_router_path", "moe_layer_forward_stats",
                 "moe_expert_ffn_train", "moe_layer_forward_train", "moe_combine_backward",
                 "moe_expert_ffn_backward", "moe_route_backward", "moe_dispatch_backward",
                 "moe_layer_backward", "moe_layer_forward_noalloc", "moe_last_error")
@@ -36,7 +38,7 @@ class MoeConfig(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("aux_alpha", ctypes.c_float),
-                ("weight_quant", ctypes.c_int32)]
+                ("weight_quant", ctypes.c_int32), ("router", ctypes.c_int32)]
 
 
 _WEIGHT_FIELDS = ("w_router", "b_router", "logit_offset", "sel_bias", "w1", "b1", "w2", "b2",
@@ -92,6 +94,8 @@ def lib():
     L.moe_capacity_from_factor.restype = i32
     L.moe_route_partials_size.argtypes = [cfgp]
     L.moe_route_partials_size.restype = sz
+    L.moe_router_path.argtypes = [cfgp]
+    L.moe_router_path.restype = ctypes.c_int
     L.moe_route.argtypes = [cfgp, vp, wp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_ffn.argtypes = [cfgp, vp, vp, wp, vp, vp, vp, vp, sz, vp]
@@ -155,23 +159,33 @@ def capacity_from_factor(T: int, n_experts: int, capacity_factor: float) -> int:
 
 
 def make_config(T, d_model, d_ff, n_experts, top_k, *, capacity=0, d_ff_shared=0, dtype="bf16",
-                aux_alpha=0.0, weight_quant="none") -> MoeConfig:
+                aux_alpha=0.0, weight_quant="none", router="auto") -> MoeConfig:
     return MoeConfig(T=T, d_model=d_model, d_ff=d_ff, n_experts=n_experts, top_k=top_k,
                      capacity=capacity or 0, d_ff_shared=d_ff_shared,
                      dtype=MOE_F32 if dtype in ("f32", MOE_F32) else MOE_BF16,
                      aux_alpha=float(aux_alpha),
-                     weight_quant=_WQ.get(weight_quant, weight_quant))
+                     weight_quant=_WQ.get(weight_quant, weight_quant),
+                     router=_ROUTER.get(router, router))
 
 
-def config_for(shape, T: Optional[int] = None) -> MoeConfig:
-    """MoeConfig of a workload shape (configs.MoEShape), optionally with another T."""
+def router_path(cfg: MoeConfig) -> str:
+    """'exact' or 'certified': the router path cfg.router resolves to."""
+    p = lib().moe_router_path(ctypes.byref(cfg))
+    if p < 0:
+        raise ValueError("invalid config")
+    return "certified" if p == MOE_ROUTER_CERTIFIED else "exact"
+
+
+def config_for(shape, T: Optional[int] = None, router="auto") -> MoeConfig:
+    """MoeConfig of a workload shape (configs.MoEShape), optionally with another T
+    and router path."""
     T = shape.T if T is None else T
     cap = 0
     if shape.capacity_factor is not None:
         cap = capacity_from_factor(T, shape.n_experts, shape.capacity_factor)
     return make_config(T, shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, capacity=cap,
                        d_ff_shared=shape.d_ff_shared, dtype=shape.dtype, aux_alpha=shape.aux_alpha,
-                       weight_quant=getattr(shape, "weight_quant", "none"))
+                       weight_quant=getattr(shape, "weight_quant", "none"), router=router)
 
 
 def make_weights(t: Dict[str, object]) -> MoeWeights:

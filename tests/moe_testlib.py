@@ -13,6 +13,11 @@ BF16_TOL = 1e-2     # relative L2 of the layer output, bf16 storage / fp32 accum
 F32_TOL = 1e-5      # relative L2 of the layer output, fp32 layer
 W_TOL = 1e-6        # relative error of each routing weight
 AUX_TOL = 1e-5      # relative error of the aux loss
+# Certified bf16 router: each logit within CERT_C0 * |x_t| * |W_r[e]| of the
+# exact one (the library's own coefficient is about 34 * 2^-23), routing
+# weights within CERT_W_TOL (two logits' errors through the softmax).
+CERT_C0 = 40 * 2.0 ** -23
+CERT_W_TOL = 1e-5
 
 
 def say(msg):
@@ -124,6 +129,7 @@ def run_stages(cfg, t, device="cuda"):
     idx = torch.empty(T, K, **i32)
     w = torch.empty(T, K, **f32)
     moe.moe_route(cfg, t["x"], W, logits, idx, w, moe.alloc_workspace(cfg, "route", device))
+    router_path = moe.router_path(cfg)
     counts = torch.empty(N, **i32)
     offsets = torch.empty(N + 1, **i32)
     slot_row = torch.empty(T, K, **i32)
@@ -146,6 +152,7 @@ def run_stages(cfg, t, device="cuda"):
                slot_row=slot_row, row_token=row_token[:M], n_dropped=ndrop, out=out.float(),
                aux=loss)
     res = {k: v.cpu().numpy() for k, v in res.items()}
+    res["router_path"] = router_path
     res["n_dropped"] = int(res["n_dropped"][0])
     res["aux"] = float(res["aux"][0])
     res["x_perm_ok"] = bool(torch.equal(x_perm[:M], t["x"][row_token[:M].long()]))
@@ -187,14 +194,41 @@ def report_decision_mismatch(g_logits, o_logits, sel_bias, g_idx, o_idx):
     return bad
 
 
-def check_routing_and_dispatch(g, o, inp, capacity):
-    """Integer results bit-exact, floats within tolerance."""
-    s = inp.shape
-    # logits: same fp32 value (allow one ulp where fp64 sum order differs)
-    ud = ulp_diff_f32(g["logits"], o["logits"])
+def router_logit_bound(inp):
+    """Per-logit error allowance of the certified router, [T, N]."""
+    def rows(a):
+        a = inputs.bf16_widen(a) if a.dtype == np.uint16 else a
+        return np.sqrt(np.einsum("ij,ij->i", a.astype(np.float64), a.astype(np.float64)))
+    return CERT_C0 * rows(inp.x)[:, None] * rows(inp.w_router)[None, :]
+
+
+def check_logits(g_logits, o_logits, inp, path):
+    """Exact path: the same fp32 value (one ulp where the fp64 sum order
+    differs).  Certified path: within the error allowance (plus one ulp)."""
+    if path == "certified":
+        g64, o64 = g_logits.astype(np.float64), o_logits.astype(np.float64)
+        ulp = np.spacing(np.abs(o_logits)).astype(np.float64)
+        diff = np.abs(g64 - o64)
+        bound = router_logit_bound(inp)
+        assert np.isfinite(g64).all() == np.isfinite(o64).all()
+        fin = np.isfinite(o64)
+        assert (diff[fin] <= bound[fin] + ulp[fin]).all(), \
+            f"certified logits off by {np.max(diff[fin] / (bound[fin] + ulp[fin])):.3g} x the bound"
+        say(f"  certified router: logits max |err| {diff[fin].max():.3e} "
+            f"({np.max(diff[fin] / bound[fin]):.2e} of the bound), "
+            f"{int((ulp_diff_f32(g_logits, o_logits) <= 1).mean() * 100)}% within one ulp")
+        return
+    ud = ulp_diff_f32(g_logits, o_logits)
     assert ud.max() <= 1, f"logits differ by up to {ud.max()} ulp"
     if (ud > 0).any():
         say(f"  note: {(ud > 0).sum()} logits differ by one ulp")
+
+
+def check_routing_and_dispatch(g, o, inp, capacity):
+    """Integer results bit-exact, floats within tolerance."""
+    s = inp.shape
+    path = g.get("router_path", "exact")
+    check_logits(g["logits"], o["logits"], inp, path)
     # the selection and dispatch steps, applied to the GPU's own logits
     g_sel = O.topk_select(O.selection_scores(g["logits"], inp.sel_bias), s.top_k)
     assert (g_sel == g["idx"]).all(), "top-K of the GPU logits differs from the GPU idx"
@@ -209,7 +243,8 @@ def check_routing_and_dispatch(g, o, inp, capacity):
         assert (o[key] == g[key]).all(), key
     assert o["n_dropped"] == g["n_dropped"]
     werr = np.abs(g["w"].astype(np.float64) - o["w"]) / np.maximum(np.abs(o["w"]), 1e-30)
-    assert werr.max() <= W_TOL, f"routing weight rel err {werr.max()}"
+    wtol = CERT_W_TOL if path == "certified" else W_TOL
+    assert werr.max() <= wtol, f"routing weight rel err {werr.max()}"
     assert g["x_perm_ok"], "x_perm rows are not exact copies of x[row_token]"
 
 

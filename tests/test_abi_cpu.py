@@ -88,6 +88,34 @@ def test_weight_quant_checks():
     assert b"w2_scale" in L.moe_last_error()
 
 
+def test_router_choice():
+    """The router field: bad values and CERTIFIED with fp32 are rejected; AUTO
+    resolves by the size of the router GEMM (2 T N d >= 2^31) for bf16; the
+    certified path's workspace is its own."""
+    L = moe.lib()
+    cfg = _cfg()
+    cfg.router = 3
+    assert _route(cfg) == moe.MOE_ERR_INVALID_ARG
+    assert b"router" in L.moe_last_error()
+    assert L.moe_router_path(ctypes.byref(cfg)) == -1
+    cfg = _cfg(dtype="f32", router="certified")
+    assert _route(cfg) == moe.MOE_ERR_INVALID_ARG
+    assert b"CERTIFIED" in L.moe_last_error()
+    assert moe.router_path(_cfg(router="certified")) == "certified"
+    assert moe.router_path(_cfg(router="exact", T=8192, d_model=2048, n_experts=64)) == "exact"
+    assert moe.router_path(_cfg()) == "exact"
+    assert moe.router_path(_cfg(T=8192, d_model=2048, n_experts=64)) == "certified"   # 2^31
+    assert moe.router_path(_cfg(T=8191, d_model=2048, n_experts=64)) == "exact"
+    assert moe.router_path(_cfg(T=4096, d_model=7168, n_experts=256, top_k=8)) == "certified"
+    assert moe.router_path(_cfg(dtype="f32", T=8192, d_model=2048, n_experts=64)) == "exact"
+    # workspace: fp64 slices on the exact path; fp32 slices + norms on the certified one
+    ex = _cfg(T=4096, d_model=7168, n_experts=256, top_k=8, router="exact")
+    ce = _cfg(T=4096, d_model=7168, n_experts=256, top_k=8, router="certified")
+    bex = L.moe_workspace_size(ctypes.byref(ex), moe.STAGES["route"])
+    bce = L.moe_workspace_size(ctypes.byref(ce), moe.STAGES["route"])
+    assert bex >= 4096 * 256 * 8 and bce >= 4096 * 256 * 4 and bex != bce
+
+
 def test_quantize_rejects_bad_arguments():
     L = moe.lib()
     assert L.moe_quantize_int8(None, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
