@@ -49,7 +49,12 @@ constexpr int skinny_nr() { return Q4 ? 4 : (QW ? 2 : 1); }
 // INT4 weights (Q4, with QW): a lane loads 16 bytes = 32 codes per 128-wide
 // k-block (its slice is k = 128j + 32*(lane/16) .. +32) and feeds four MFMAs
 // with 8 codes each, activations in the same order of k; four 16-row tiles
-// per wavefront share each activation load (64 outputs per wavefront).
+// per wavefront share each activation load (64 outputs per wavefront).  The
+// codes are widened as bf16(136 + q) (int4x8_to_bf16x8_o136), and one more
+// MFMA per 32 k multiplies the activations by a constant -136 into a
+// separate accumulator that is added to every tile: sum x (q + 136) -
+// 136 sum x = sum x q, with an fp32 cancellation error near 2e-5 of the
+// result for unit-scale activations (bf16 output rounding: 4e-3).
 template <bool GELU, bool QW, int KS, bool Q4 = false>
 __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   constexpr int NR = skinny_nr<QW, Q4>();
@@ -138,50 +143,46 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
     const int Kb = Kd / 2;             // bytes per row of codes
     const uint8_t* w4 = static_cast<const uint8_t*>(a.W) + (int64_t)e * Nd * Kb +
                         (int64_t)(n0 + (lane & 15)) * Kb + (lane >> 4) * 16;
-    constexpr int U4 = 2;              // 128-wide k-blocks in flight
+    // one 128-wide k-block per step: more registers for a deeper stream
+    // measured slower (two blocks 0.24 ms, three 0.26, four 0.29, and with
+    // the next block's codes loaded a step ahead 0.27-0.28, against 0.22 for
+    // one: the wavefronts per SIMD, not the loads in flight, set the rate)
+    // codes widened with the +136 offset; kM136 carries the correction
+    const bf16x8 kM136 = __builtin_bit_cast(
+        bf16x8, make_uint4(0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u));   // -136
     for (int g0 = r0; g0 < r1; g0 += 16) {
       const int ar = g0 + (lane & 15);
       const bool arow_ok = ar < r1;
       const uint16_t* arow = A + (int64_t)(arow_ok ? ar : r0) * Kd + (lane >> 4) * 32;
-      f32x4 acc[NR];
+      f32x4 acc[NR], accm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NR; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int k0 = kb; k0 < ke; k0 += 128 * U4) {
-        const int nb = min(U4, (ke - k0) / 128);
-        uint4 wv[NR][U4], av[U4][4];
+      for (int k0 = kb; k0 < ke; k0 += 128) {
+        uint4 wv[NR], av[4];
 #pragma unroll
-        for (int u = 0; u < U4; ++u)
-          if (u < nb) {
+        for (int j = 0; j < NR; ++j)
+          wv[j] = *reinterpret_cast<const uint4*>(w4 + (int64_t)16 * j * Kb + k0 / 2);
 #pragma unroll
-            for (int j = 0; j < NR; ++j)
-              wv[j][u] = *reinterpret_cast<const uint4*>(w4 + (int64_t)16 * j * Kb +
-                                                         (k0 + u * 128) / 2);
+        for (int m = 0; m < 4; ++m) {
+          av[m] = *reinterpret_cast<const uint4*>(arow + k0 + 8 * m);
+          if (!arow_ok) av[m] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 am = __builtin_bit_cast(bf16x8, av[m]);
+#pragma unroll
+          for (int j = 0; j < NR; ++j) {
+            const uint32_t wd = m == 0 ? wv[j].x : m == 1 ? wv[j].y : m == 2 ? wv[j].z : wv[j].w;
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                am, __builtin_bit_cast(bf16x8, int4x8_to_bf16x8_o136(wd)), acc[j], 0, 0, 0);
           }
-#pragma unroll
-        for (int u = 0; u < U4; ++u)
-          if (u < nb) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              av[u][m] = *reinterpret_cast<const uint4*>(arow + k0 + u * 128 + 8 * m);
-              if (!arow_ok) av[u][m] = make_uint4(0, 0, 0, 0);
-            }
-          }
-#pragma unroll
-        for (int u = 0; u < U4; ++u)
-          if (u < nb) {
-#pragma unroll
-            for (int j = 0; j < NR; ++j)
-#pragma unroll
-              for (int m = 0; m < 4; ++m) {
-                const uint32_t wd = m == 0 ? wv[j][u].x
-                                  : m == 1 ? wv[j][u].y
-                                  : m == 2 ? wv[j][u].z : wv[j][u].w;
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, av[u][m]),
-                    __builtin_bit_cast(bf16x8, int4x8_to_bf16x8(wd)), acc[j], 0, 0, 0);
-              }
-          }
+          accm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, kM136, accm, 0, 0, 0);
+        }
       }
+      // every column of accm holds -136 * sum_k x[row, k] over this
+      // wavefront's k-range: the same element layout as acc[j]
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[j] += accm;
       if (!reduce(acc)) continue;
       store(acc, g0, sc, bv);
     }

@@ -300,6 +300,23 @@ __device__ __forceinline__ uint4 int4x8_to_bf16x8(uint32_t v) {
   }
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
+// The same 8 codes widened with an offset: bf16(136 + q) = 0x4300 | (n ^ 8)
+// for the nibble n of q (exact: 128 + (q + 8) with q + 8 in [0, 15] is the
+// mantissa of a bf16 in [128, 256)).  Two logic operations split the word's
+// nibbles into bytes, one byte permutation and one OR per output word --
+// about 1.5 operations per code against 2.5 for the conversions above; the
+// caller removes 136 * sum(activations).
+__device__ __forceinline__ uint4 int4x8_to_bf16x8_o136(uint32_t v) {
+  const uint32_t u = v ^ 0x88888888u;
+  const uint32_t lo = u & 0x0F0F0F0Fu;            // nibbles 0, 2, 4, 6 as bytes
+  const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;     // nibbles 1, 3, 5, 7
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)   // bytes: lo[j], 0, hi[j], 0
+    o[j] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j) |
+           0x43004300u;
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
 hipError_t launch_quantize_int4(const void* w, int dtype, int64_t rows, int cols, uint8_t* q,
                                 float* scale, hipStream_t s);
 // ---------------------------------------------------------------- backward
