@@ -193,8 +193,24 @@ struct W4Layout<9> : W4Cols {   // 64 < R <= 96 (the load split needs a multiple
   static constexpr bool EXTRA = false;
 };
 template <>
-struct W4Layout<10> {   // wide tiles: R <= 128, 512 columns
+struct W4Layout<10> {   // wide tiles: 96 < R <= 128, 512 columns
   static constexpr int NW = 4, WN = 4, MI = 4, NI = 4, AROWS = WIDE_AR, AR = WIDE_AR;
+  static constexpr int BNL = WIDE_BN, CST = WIDE_CST;
+  static constexpr bool EXTRA = false;
+};
+// Wide tiles of fewer rows multiply fewer padding rows (the fine-grained
+// shape's experts hold 20-300 rows; 121 of its 256 have at most 96): the
+// same LDS layout, 64 or 128 A rows loaded (the load split needs a multiple
+// of 64), 64 or 96 rows multiplied.
+template <>
+struct W4Layout<12> {   // wide tiles: R <= 64
+  static constexpr int NW = 4, WN = 4, MI = 2, NI = 4, AROWS = 64, AR = WIDE_AR;
+  static constexpr int BNL = WIDE_BN, CST = WIDE_CST;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<13> {   // wide tiles: 64 < R <= 96
+  static constexpr int NW = 4, WN = 4, MI = 3, NI = 4, AROWS = WIDE_AR, AR = WIDE_AR;
   static constexpr int BNL = WIDE_BN, CST = WIDE_CST;
   static constexpr bool EXTRA = false;
 };
@@ -802,7 +818,13 @@ gemm_bf16_w4_kernel(GemmArgs a) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   if constexpr (!KM && !WG) {
     if (tr.wide) {   // routed tiles only
-      w4_tile<GELU, QW, NS, 10, WG, KM, false, Q4>(a, tr, lds, acc);
+      const int rows = tr.row_end - tr.row0;
+      if (rows > 96)
+        w4_tile<GELU, QW, NS, 10, WG, KM, false, Q4>(a, tr, lds, acc);
+      else if (rows > 64)
+        w4_tile<GELU, QW, NS, 13, WG, KM, false, Q4>(a, tr, lds, acc);
+      else
+        w4_tile<GELU, QW, NS, 12, WG, KM, false, Q4>(a, tr, lds, acc);
       return;
     }
   }
