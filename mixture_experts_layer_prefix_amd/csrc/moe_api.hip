@@ -498,13 +498,15 @@ int do_ffn(const moe_config_t* c, const void* x_perm, const int32_t* offsets,
       const int merge = path == PATH_TILED ? moe::gemm_bf16_merge_rows() : 0;
       // Wide tiles for small blocks: with INT8 / INT4 weights, whose A rows
       // are half of a short tile's load bytes (same-GPU: Switch-shaped INT8
-      // stage 5% faster), and with bf16 weights in fine-grained layers of at
-      // least 128 experts (same-GPU: the DeepSeek-shaped stage 3.71 -> 3.61
-      // ms, both GEMMs gaining; the Switch shape's 64 experts lose 2% in the
-      // first GEMM), and only where there are rounds of tiles to spare (about
-      // four of the chip's 256 CUs' worth), so that halving the tiles of the
-      // small blocks (each twice as long) does not unbalance the last round.
-      g.wide_rows = path == PATH_TILED && (g.wscale || c->n_experts >= 128) &&
+      // stage 5% faster), and with bf16 weights in layers of at least 64
+      // experts (same-GPU: the DeepSeek-shaped stage 3.71 -> 3.61 ms with
+      // 128-row wide tiles, both GEMMs gaining; with the 64- and 96-row wide
+      // layouts the Switch shape's 64 experts gain too, 0.994 -> 0.981 ms,
+      // where 128-row wide tiles had lost 2%), and only where there are
+      // rounds of tiles to spare (about four of the chip's 256 CUs' worth),
+      // so that halving the tiles of the small blocks (each twice as long)
+      // does not unbalance the last round.
+      g.wide_rows = path == PATH_TILED && (g.wscale || c->n_experts >= 64) &&
                             (int64_t)Nr * ((g.Nd + bn - 1) / bn) >= 1024
                         ? moe::gemm_bf16_wide_rows() : 0;
       // Non-temporal loads of bf16 weights where each expert's weights are
