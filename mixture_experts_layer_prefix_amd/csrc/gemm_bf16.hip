@@ -183,7 +183,12 @@ struct W4Layout<3> : W4Cols {   // 256 < R <= 320
   static constexpr bool EXTRA = true;
 };
 template <>
-struct W4Layout<8> : W4Cols {   // 128 < R <= 192
+struct W4Layout<14> : W4Cols {   // 128 < R <= 160: one row of four 160 x 64 wavefront tiles
+  static constexpr int NW = 4, WN = 4, MI = 5, NI = 2, AROWS = 192, AR = W4_AR;
+  static constexpr bool EXTRA = false;
+};
+template <>
+struct W4Layout<8> : W4Cols {   // 160 < R <= 192
   static constexpr int NW = 4, WN = 2, MI = 3, NI = 4, AROWS = 192, AR = W4_AR;
   static constexpr bool EXTRA = false;
 };
@@ -254,6 +259,12 @@ struct W4Layout<7> : W4Cols {   // eight wavefronts, 256 < R <= 320 (384 A rows 
 // is read once more, by the second GEMM; the forward expert stage still ran
 // 0.6-0.8% faster on the three prefill shapes (the second GEMM's output,
 // which the combine reads right away, measured better without).
+// Accumulator (ni, mi) of a wavefront tile: acc[ni][mi] for up to 4 x 4
+// blocks; layouts with more than four row blocks (and at most 16 blocks in
+// all) number the blocks ni * MI + mi across the same 16 registers tiles.
+constexpr int acc_r(int MI, int ni, int mi) { return MI <= 4 ? ni : (ni * MI + mi) >> 2; }
+constexpr int acc_c(int MI, int ni, int mi) { return MI <= 4 ? mi : (ni * MI + mi) & 3; }
+
 template <bool NT>
 __device__ __forceinline__ void store_out(uint16_t* dst, const uint16_t* src) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -518,7 +529,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       const bf16x8 fb = wfrag(fbr[ni]);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa[mi], acc[ni][mi], 0, 0, 0);
+        acc[acc_r(MI, ni, mi)][acc_c(MI, ni, mi)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            fb, fa[mi], acc[acc_r(MI, ni, mi)][acc_c(MI, ni, mi)], 0, 0, 0);
       // The folded rows' accumulators live in ordinary VGPRs (the 256
       // accumulation registers hold the main 256 x 256): the compiler keeps
       // all MFMA results in one register class, so these four are written
@@ -717,7 +729,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
         float z[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          z[q] = QW ? fmaf(acc[ni][mi][g * 4 + q], sv[q], bv[q]) : acc[ni][mi][g * 4 + q] + bv[q];
+          const float av = acc[acc_r(MI, ni, mi)][acc_c(MI, ni, mi)][g * 4 + q];
+          z[q] = QW ? fmaf(av, sv[q], bv[q]) : av + bv[q];
           if (GELU) z[q] = gelu_as(z[q]);
         }
         // v_cvt_pk_bf16_f32: round to nearest even, two values per instruction
@@ -789,8 +802,10 @@ __device__ __forceinline__ void w4_rows(const GemmArgs& a, const TileRef& tr, ui
     w4_tile<GELU, QW, NS, 3, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else if (rows > 192)
     w4_tile<GELU, QW, NS, 0, WG, KM, NTW, Q4>(a, tr, lds, acc);
-  else if (rows > 128)
+  else if (rows > 160)
     w4_tile<GELU, QW, NS, 8, WG, KM, NTW, Q4>(a, tr, lds, acc);
+  else if (rows > 128)
+    w4_tile<GELU, QW, NS, 14, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else if (rows > 96)
     w4_tile<GELU, QW, NS, 1, WG, KM, NTW, Q4>(a, tr, lds, acc);
   else if (rows > 64)

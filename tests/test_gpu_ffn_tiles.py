@@ -23,13 +23,13 @@ SENTINEL = 0x7FC1   # a bf16 NaN pattern the kernels never write
 COUNTS = {
     # a remainder of up to 64 rows after a full tile is folded into it
     # (257, 319, 320, 1057, 1088), 65 or more is not (321); last tiles of 96,
-    # 97, 192 and 193 rows (352, 353, 448, 449)
-    "tiles256": [0, 1, 63, 64, 65, 128, 129, 256, 257, 319, 320, 321, 352, 353, 384, 448, 449,
-                 511, 700, 1057, 1088],
+    # 97, 160, 161, 192 and 193 rows (352, 353, 416, 417, 448, 449)
+    "tiles256": [0, 1, 63, 64, 65, 128, 129, 256, 257, 319, 320, 321, 352, 353, 384, 416, 417,
+                 448, 449, 511, 700, 1057, 1088],
     # many experts of about a tile or less (a fine-grained layout), on both
-    # sides of the 64-, 96-, 128-, 192- and 256-row layout boundaries
-    "small_blocks": [0, 1, 63, 64, 65, 96, 97, 127, 128, 129, 160, 192, 193, 200, 255, 256, 257,
-                     130, 3, 0, 40],
+    # sides of the 64-, 96-, 128-, 160-, 192- and 256-row layout boundaries
+    "small_blocks": [0, 1, 63, 64, 65, 96, 97, 127, 128, 129, 160, 161, 192, 193, 200, 255, 256,
+                     257, 130, 3, 0, 40],
 }
 
 
