@@ -136,7 +136,7 @@ def test_non_finite_tokens():
     assert (diff <= bound + np.spacing(np.abs(ge["logits"][fin]))).all()
 
 
-@pytest.mark.parametrize("T,N,K,d", [(1, 8, 2, 128), (1000, 100, 5, 384), (257, 200, 8, 64),
+@pytest.mark.parametrize("T,N,K,d", [(1, 8, 2, 128), (50, 1, 1, 64), (1000, 100, 5, 384), (257, 200, 8, 64),
                                      (64, 4, 4, 128), (513, 256, 1, 192), (96, 33, 32, 256)])
 def test_ragged_shapes(T, N, K, d):
     shape = C.DEEPSEEK_FINE.with_(T=T, d_model=d, d_ff=64, n_experts=N, top_k=K, d_ff_shared=0)
