@@ -285,8 +285,10 @@ struct TileT {
 // [kseg[e], kseg[e+1]) of out [C, ldo]: out[c][kseg[e] + j] = in[off[e] + j][c]
 // for j < R_e and 0 in the padding up to kseg[e+1]; colsum[e][c] (if not null)
 // = sum over the expert's rows of in[.][c] (fp32, fixed order, stored as T).
-// grid (C/64, number of segments); a workgroup walks its segment 64 rows at a
-// time.
+// grid (C/64, number of segments, row split); a workgroup walks every
+// gridDim.z-th 64-row tile of its segment (the shared expert's single
+// segment of T rows is split so that its launch fills the chip; with
+// colsum the row split is 1).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_segments_kernel(
     const T* __restrict__ in, const int32_t* __restrict__ off, const int32_t* __restrict__ kseg,
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(256) void transpose_segments_kernel(
   float part[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) part[p] = 0.f;
-  for (int j0 = 0; j0 < KP; j0 += TD) {
+  for (int j0 = blockIdx.z * TD; j0 < KP; j0 += gridDim.z * TD) {
     for (int i = threadIdx.x; i < TD * TT::CPR; i += 256) {
       const int r = i / TT::CPR, cc = (i % TT::CPR) * TT::VEC;
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -750,8 +752,15 @@ hipError_t launch_unpermute(int dtype, const void* d_x_perm, const int32_t* slot
 
 hipError_t launch_transpose_segments(int dtype, const void* in, const int32_t* off,
                                      const int32_t* kseg, int nseg, int C, int ldo, void* out,
-                                     void* colsum, hipStream_t s) {
-  const dim3 grid(C / TD, nseg);
+                                     void* colsum, hipStream_t s, int max_rows) {
+  // a single segment of max_rows rows: split its 64-row tiles over enough
+  // workgroups for about eight per CU (column sums need one walk per column)
+  int rs = 1;
+  if (nseg == 1 && !colsum && max_rows > TD) {
+    const int tiles = (max_rows + TD - 1) / TD, cols = C / TD;
+    rs = max(1, min(tiles, (2048 + cols - 1) / cols));
+  }
+  const dim3 grid(C / TD, nseg, rs);
   if (dtype == 0)
     hipLaunchKernelGGL(transpose_segments_kernel<float>, grid, dim3(256), 0, s,
                        static_cast<const float*>(in), off, kseg, C, ldo, static_cast<float*>(out),

@@ -786,9 +786,11 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   sa.Nd = d;
   r = bwd_gemm(c, sa, fw.list[5], fw.count + 5, fw.bound[5], nullptr, 0, T, s, "dgrad GEMM launch");
   if (r != MOE_OK) return r;
-  MOE_TRY(moe::launch_transpose_segments(dt, d_out, fw.off2, fw.kseg2, 1, d, ldt, fw.tb1, nullptr, s),
+  MOE_TRY(moe::launch_transpose_segments(dt, d_out, fw.off2, fw.kseg2, 1, d, ldt, fw.tb1, nullptr, s,
+                                          c->T),
           "transpose launch");
-  MOE_TRY(moe::launch_transpose_segments(dt, hs, fw.off2, fw.kseg2, 1, fs, ldt, fw.tb2, nullptr, s),
+  MOE_TRY(moe::launch_transpose_segments(dt, hs, fw.off2, fw.kseg2, 1, fs, ldt, fw.tb2, nullptr, s,
+                                          c->T),
           "transpose launch");
   moe::GemmArgs sw{};
   sw.A = fw.tb1;                        // dWs2 [d, fs]
@@ -801,9 +803,11 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   sw.wg_rows = d;
   r = bwd_gemm(c, sw, fw.list[6], fw.count + 6, fw.bound[6], fw.wr2_d, 1, 0, s, "wgrad GEMM launch");
   if (r != MOE_OK) return r;
-  MOE_TRY(moe::launch_transpose_segments(dt, fw.dhs, fw.off2, fw.kseg2, 1, fs, ldt, fw.tb1, nullptr, s),
+  MOE_TRY(moe::launch_transpose_segments(dt, fw.dhs, fw.off2, fw.kseg2, 1, fs, ldt, fw.tb1, nullptr, s,
+                                          c->T),
           "transpose launch");
-  MOE_TRY(moe::launch_transpose_segments(dt, x, fw.off2, fw.kseg2, 1, d, ldt, fw.tb2, nullptr, s),
+  MOE_TRY(moe::launch_transpose_segments(dt, x, fw.off2, fw.kseg2, 1, d, ldt, fw.tb2, nullptr, s,
+                                          c->T),
           "transpose launch");
   sw.C = g->d_ws1;                      // dWs1 [fs, d]
   sw.Nd = d;

@@ -336,9 +336,11 @@ hipError_t launch_unpermute(int dtype, const void* d_x_perm, const int32_t* slot
                             int d, int K, hipStream_t s);
 // Rows of segment e of in [*, C] -> columns [kseg[e], kseg[e+1]) of out
 // [C, ldo], zero padded; colsum [nseg, C] (or null) = per-segment column sums.
+// max_rows: an upper bound of a single segment's rows (splits its rows over
+// workgroups), 0 if unknown.
 hipError_t launch_transpose_segments(int dtype, const void* in, const int32_t* off,
                                      const int32_t* kseg, int nseg, int C, int ldo, void* out,
-                                     void* colsum, hipStream_t s);
+                                     void* colsum, hipStream_t s, int max_rows = 0);
 // kseg = scan of the segment lengths rounded up to 32; wa[e] = e * ra,
 // wb[e] = e * rb (the output-row offsets of two weight-gradient GEMMs).
 hipError_t launch_seg_offsets(const int32_t* off, int N, int ra, int rb, int32_t* kseg,
