@@ -13,14 +13,19 @@ pytestmark = pytest.mark.gpu
 
 # a capacity-limited top-1 layer with the aux loss, and a fine-grained top-4
 # layer with a shared expert; each at a larger and then a smaller batch (the
-# smaller fine-grained batch takes the decode-shaped GEMM path)
+# smaller fine-grained batch takes the decode-shaped GEMM path); then the
+# fine-grained layer again with the certified router (its own workspace
+# layout in the scratch)
+_FINE = dict(d_model=512, d_ff=256, n_experts=16, top_k=4, d_ff_shared=256)
 CASES = [
-    C.SWITCH_CAPACITY.with_(name="noalloc_switch", T=512, d_model=256, d_ff=512, n_experts=16),
-    C.SWITCH_CAPACITY.with_(name="noalloc_switch", T=64, d_model=256, d_ff=512, n_experts=16),
-    C.DEEPSEEK_FINE.with_(name="noalloc_fine", T=256, d_model=512, d_ff=256, n_experts=16,
-                          top_k=4, d_ff_shared=256),
-    C.DEEPSEEK_FINE.with_(name="noalloc_fine", T=24, d_model=512, d_ff=256, n_experts=16,
-                          top_k=4, d_ff_shared=256),
+    (C.SWITCH_CAPACITY.with_(name="noalloc_switch", T=512, d_model=256, d_ff=512, n_experts=16),
+     "auto"),
+    (C.SWITCH_CAPACITY.with_(name="noalloc_switch", T=64, d_model=256, d_ff=512, n_experts=16),
+     "auto"),
+    (C.DEEPSEEK_FINE.with_(name="noalloc_fine", T=256, **_FINE), "auto"),
+    (C.DEEPSEEK_FINE.with_(name="noalloc_fine", T=24, **_FINE), "auto"),
+    (C.DEEPSEEK_FINE.with_(name="noalloc_fine", T=320, **_FINE), "certified"),
+    (C.DEEPSEEK_FINE.with_(name="noalloc_fine", T=40, **_FINE), "certified"),
 ]
 
 
@@ -38,12 +43,13 @@ def test_noalloc_layer_equals_layer_forward():
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible")
     dev = "cuda"
-    for i, shape in enumerate(CASES):
+    for i, (shape, router) in enumerate(CASES):
         print(f"noalloc call {i}: {shape.name} T={shape.T} d={shape.d_model} f={shape.d_ff} "
-              f"N={shape.n_experts} K={shape.top_k} fs={shape.d_ff_shared}", flush=True)
+              f"N={shape.n_experts} K={shape.top_k} fs={shape.d_ff_shared} router={router}",
+              flush=True)
         inp = inputs.make_inputs(shape, seed=i)
         t = inputs.to_torch(inp, dev)
-        cfg = moe.config_for(shape)
+        cfg = moe.config_for(shape, router=router)
         assert moe.workspace_size(cfg, "layer") <= moe.NOALLOC_SCRATCH_BYTES
         W = moe.make_weights(t)
         aux = bool(shape.aux_alpha)
