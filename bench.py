@@ -299,7 +299,8 @@ def main_train(args, shape, inp, t):
         "dtype": shape.dtype, "data": "synthetic (seeded, N(0,1) x and d_out, N(0,1/fan_in) weights)",
         "config": {"workload": shape.name, "pass": "train", "T": T, "d_model": d,
                    "d_ff": cfg.d_ff, "n_experts": N, "top_k": K, "capacity": cfg.capacity,
-                   "d_ff_shared": cfg.d_ff_shared, "parallelism": "single GPU"},
+                   "d_ff_shared": cfg.d_ff_shared, "router": moe.router_path(cfg),
+                   "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "roofline": roof,
     }
@@ -488,7 +489,7 @@ def main():
         "config": {"workload": shape.name, "T": T, "d_model": d, "d_ff": cfg.d_ff,
                    "n_experts": N, "top_k": K, "capacity": cfg.capacity,
                    "d_ff_shared": cfg.d_ff_shared, "weight_quant": shape.weight_quant,
-                   "parallelism": "single GPU"},
+                   "router": moe.router_path(cfg), "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "event_ms_per_step": round(step_ms, 4),
         "roofline": roof,
