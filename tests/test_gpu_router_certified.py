@@ -102,6 +102,24 @@ def test_duplicated_rows_exact_ties():
     assert (np.isin(gc_["idx"], [3, 7]).sum(axis=1) == 2).any()
 
 
+def test_massive_ties():
+    """256 experts whose router rows take 4 distinct values (64 copies each,
+    no selection bias): every token's Top-8 sits inside a 64-way tie, so
+    every token is recomputed and the ties fall back to index order."""
+    shape = C.DEEPSEEK_FINE.with_(T=300, d_model=512, d_ff=64, n_experts=256, top_k=8,
+                                  d_ff_shared=0)
+    inp = inputs.make_inputs(shape, seed=9)
+    w = inp.w_router.copy()
+    w[:] = w[np.arange(256) % 4]
+    inp.w_router = w
+    inp.sel_bias = None
+    say("case 64-way ties: 4 distinct router rows over 256 experts")
+    gc_, _, _ = _both_paths(shape, inp)
+    # the eight winners are the eight lowest indices of the best row class
+    best = np.argmax(gc_["logits"][:, :4], axis=1)
+    assert (gc_["idx"] == best[:, None] + 4 * np.arange(8)[None, :]).all()
+
+
 def test_all_zero_router():
     shape = C.MIXTRAL_PREFILL.with_(T=200, d_model=256, d_ff=128, n_experts=40, top_k=3)
     inp = inputs.make_inputs(shape)
