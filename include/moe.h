@@ -40,7 +40,8 @@
  *     return enqueues nothing.  moe_last_error() gives a thread-local message.
  *     A failed launch returns MOE_ERR_HIP.  No C++ exception crosses the ABI.
  *   - Limits: 1 <= K <= N <= 256, K <= 64, T >= 1, d_model, d_ff and
- *     d_ff_shared multiples of 64, T*K*max(d_model, d_ff) < 2^31.
+ *     d_ff_shared multiples of 64, T*K*max(d_model, d_ff) < 2^31,
+ *     d_model*d_ff and d_model*d_ff_shared < 2^31.
  *   - Results are deterministic: the same inputs give bitwise-identical
  *     outputs on every call.
  */

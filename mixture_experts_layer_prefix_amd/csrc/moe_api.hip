@@ -65,6 +65,10 @@ std::string check_config(const moe_config_t* c, int* code) {
   const int64_t wide_s = c->d_ff_shared > c->d_model ? c->d_ff_shared : c->d_model;
   if (mmax * wide >= (int64_t(1) << 31) || (int64_t)c->T * wide_s >= (int64_t(1) << 31))
     return "T*K*max(d_model, d_ff) must be < 2^31";
+  // (the GEMMs address one expert's weight matrix with 32-bit byte offsets)
+  if ((int64_t)c->d_model * c->d_ff >= (int64_t(1) << 31) ||
+      (int64_t)c->d_model * c->d_ff_shared >= (int64_t(1) << 31))
+    return "d_model*d_ff and d_model*d_ff_shared must be < 2^31";
   *code = MOE_OK;
   return "";
 }

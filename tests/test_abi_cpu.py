@@ -63,12 +63,27 @@ def _route(cfg, x=FAKE, wr=FAKE, idx=FAKE, w=FAKE):
     (dict(d_model=96), moe.MOE_ERR_UNSUPPORTED),
     (dict(d_ff=100), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 20, d_model=4096, top_k=8, n_experts=8), moe.MOE_ERR_UNSUPPORTED),
+    # T*K*d = 2^31 exactly (one token past the largest accepted batch)
+    (dict(T=1 << 24, d_model=64, d_ff=64, top_k=2, n_experts=8), moe.MOE_ERR_UNSUPPORTED),
+    # one expert's weight matrix of 2^31 elements
+    (dict(T=1, d_model=32768, d_ff=65536, top_k=2, n_experts=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1, d_model=65536, d_ff=64, d_ff_shared=32768, top_k=2, n_experts=8),
+     moe.MOE_ERR_UNSUPPORTED),
 ])
+
 def test_bad_configs_are_rejected(kw, code):
     cfg = _cfg(**kw)
     assert _route(cfg) == code
     assert moe.lib().moe_last_error()
     assert moe.lib().moe_workspace_size(ctypes.byref(cfg), 5) == ctypes.c_size_t(-1).value
+
+
+def test_largest_accepted_batch():
+    """T*K*d = 2^31 - 128: accepted, and its workspaces have a size."""
+    cfg = _cfg(T=(1 << 24) - 1, d_model=64, d_ff=64, top_k=2, n_experts=8)
+    for stage in ("route", "dispatch", "expert_ffn", "layer"):
+        assert moe.lib().moe_workspace_size(ctypes.byref(cfg), moe.STAGES[stage]) \
+            != ctypes.c_size_t(-1).value, stage
 
 
 def test_weight_quant_checks():
