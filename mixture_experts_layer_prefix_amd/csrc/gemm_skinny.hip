@@ -15,7 +15,7 @@
 // index E stands for the dense shared problem when one is present (its
 // weights are always in the activation dtype; launches with INT8 routed
 // weights carry none).
-// KS = 4 (long reductions, Kd > Nd; with INT4 codes any Kd >= 2048): a
+// KS = 4 (long reductions, Kd >= 2048): a
 // workgroup takes 16 NR outputs and its
 // four wavefronts split the model dimension in quarters; the four partial
 // sums are added in wavefront order through LDS.  Four times as many,
@@ -289,12 +289,13 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_
                                    hipStream_t s) {
   const int E = a.E + (a.As ? 1 : 0);
   if (E == 0) return hipSuccess;
-  // long reductions: the four wavefronts of a workgroup split the model dimension
+  // long reductions: the four wavefronts of a workgroup split the model
+  // dimension whenever it is at least 2048 (four times as many, shorter
+  // workgroups; same-GPU A/B of the decode-shaped stage, whose first GEMM
+  // has Kd = 4096 < Nd: INT4 0.248 -> 0.235 ms, INT8 0.393 -> 0.379 ms,
+  // bf16 0.577 -> 0.564 ms)
   const bool q4 = a.wscale && a.w4;
-  // INT4 codes: the k-split also for Kd >= 2048 (the decode-shaped first GEMM
-  // has four times fewer workgroups than with bf16 weights otherwise;
-  // same-GPU A/B: the INT4 decode stage 0.248 -> 0.235 ms)
-  const bool ks = (a.Kd > a.Nd && a.Kd >= 4096) || (q4 && a.Kd >= 2048);
+  const bool ks = a.Kd >= 2048;
   const int npw = 16 * (q4 ? skinny_nr<true, true>()
                            : (a.wscale ? skinny_nr<true>() : skinny_nr<false>()));   // per wavefront
   const int per_wg = ks ? npw : npw * NTHR / 64;
