@@ -6,10 +6,11 @@
 // With a handful of tokens per expert the work is a weight stream: every
 // weight byte is used for only rows_e multiply-adds.  The weights of each
 // touched expert are therefore split over many workgroups along the output
-// dimension, and each wavefront streams 16 NR weight rows (NR = 1 for bf16,
-// 2 for INT8, 4 for INT4 weights) through v_mfma_f32_16x16x32_bf16 with the expert's
-// (up to 16) token rows as the other operand, eight 16-byte loads per lane
-// and row tile in flight per step (four per tile for INT8: 128 codes each).
+// dimension, and each wavefront streams 16 NR weight rows (NR = 2 for bf16
+// and INT8, 4 for INT4 weights) through v_mfma_f32_16x16x32_bf16 with the
+// expert's (up to 16) token rows as the other operand, four 16-byte loads
+// per lane and row tile in flight per step (two per tile for INT8: 128 codes
+// each, one for INT4).
 // Workgroup (bx, e): outputs [64 NR bx, 64 NR (bx + 1)) of expert e, one
 // wavefront per 16 NR outputs; experts with no rows exit at once.  Expert
 // index E stands for the dense shared problem when one is present (its
@@ -31,15 +32,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NTHR = 256;
-constexpr int U = 8;                    // k-steps of 32 in flight (bf16 weights)
+constexpr int U = 4;                    // k-steps of 32 in flight (bf16 weights)
 // NR 16-row MFMA tiles per wavefront: 16 * NR output features per
 // wavefront, 4x that per workgroup (KS = 1).  The tiles share each
 // activation fragment: INT8 weights take NR = 2, since a wavefront's
 // activation loads are two thirds of its load instructions there (same-GPU:
-// the decode-shaped INT8 stage 10% faster); with bf16 weights NR = 2
-// measured 5% slower and NR = 1 stays.
+// the decode-shaped INT8 stage 10% faster).  With the k-split of every
+// Kd >= 2048 (below), bf16 weights take NR = 2 too and 4 k-steps in flight,
+// INT8 codes 2 k-blocks (same-GPU A/B, two runs each: bf16 0.564 -> 0.537
+// ms, INT8 0.378 -> 0.356 ms; bf16 with NR = 1 and 8 k-steps had been the
+// better choice before the k-split).
 template <bool QW, bool Q4 = false>
-constexpr int skinny_nr() { return Q4 ? 4 : (QW ? 2 : 1); }
+constexpr int skinny_nr() { return Q4 ? 4 : 2; }
 
 // INT8 weights (QW): a lane loads 16 codes = one 16-byte load per 64-wide
 // k-block (its slice is k = 64j + 16*(lane/16) .. +16) and feeds two MFMAs
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   } else if constexpr (QW) {
     const int8_t* w8 = static_cast<const int8_t*>(a.W) + (int64_t)e * Nd * Kd +
                        (int64_t)(n0 + (lane & 15)) * Kd + (lane >> 4) * 16;
-    constexpr int U8 = 8 / NR;        // 64-wide k-blocks in flight
+    constexpr int U8 = 2;             // 64-wide k-blocks in flight
     for (int g0 = r0; g0 < r1; g0 += 16) {
       const int ar = g0 + (lane & 15);
       const bool arow_ok = ar < r1;
