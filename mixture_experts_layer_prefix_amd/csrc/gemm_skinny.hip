@@ -30,6 +30,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NTHR = 256;
 constexpr int U = 4;                    // k-steps of 32 in flight (bf16 weights)
@@ -287,6 +288,193 @@ __global__ __launch_bounds__(NTHR) void gemm_skinny_kernel(GemmArgs a) {
   }
 }
 
+// k-major weights: the backward's input gradients (d_h = d_y W2_e, d_x_perm =
+// d_z W1_e) read the forward's weights as W_e [Kd, Nd] with Nd contiguous,
+// so a 16-byte load holds one k of several output columns while the MFMA
+// wants 8 consecutive k of one column in a lane.  Each lane loads 8 rows of
+// W (k = 8 (lane/16) + t of the 32-wide k-step, t = 0..7) at its 4 columns
+// n0 + 4 (lane%16) .. +3, 8 bytes each (16 lanes read 128 contiguous bytes
+// of a row), and transposes the 8 x 4 block in registers: one v_perm_b32 per
+// output dword, joining the same half of two rows.  MFMA c (c = 0..3) then
+// produces columns n0 + 4 (lane%16) + c, so a lane's 4 results of an output
+// row are adjacent: 8-byte stores, 128 contiguous bytes per row and lane
+// group.  Up to 32 rows (two 16-row groups sharing each weight fragment) per
+// pass over the weights.  A wavefront covers 64 columns; workgroups split
+// long reductions over their 4 wavefronts as above (KS = 4).
+template <int RG, int UK>
+__device__ __forceinline__ void kmaj_pass(const uint16_t* __restrict__ A,
+                                          __amdgpu_buffer_rsrc_t wr, uint32_t loff, int Kd, int Nd,
+                                          int g0, int r0, int r1, int kb, int ke, int lane,
+                                          f32x4 (&acc)[2][4]) {
+  // buffer loads of W_e: row k's byte offset k * rb is wave-uniform (the
+  // scalar offset), this lane's place in the row the vector offset loff, so
+  // every load shares one address register
+  const uint32_t rb = (uint32_t)Nd * 2u;
+  auto wload = [&](int k) -> uint2 {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(wr, loff, (int)((uint32_t)k * rb), 0);
+    return make_uint2(v.x, v.y);
+  };
+  const uint16_t* arow[RG];
+  bool aok[RG];
+#pragma unroll
+  for (int q = 0; q < RG; ++q) {
+    const int ar = g0 + 16 * q + (lane & 15);
+    aok[q] = ar < r1;
+    arow[q] = A + (int64_t)(aok[q] ? ar : r0) * Kd + (lane >> 4) * 8;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[q][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const uint2 (&wv)[8], const uint4 (&av)[RG]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t dw[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = (c >> 1) ? wv[2 * m].y : wv[2 * m].x;
+        const uint32_t hi = (c >> 1) ? wv[2 * m + 1].y : wv[2 * m + 1].x;
+        dw[m] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+      const bf16x8 b = __builtin_bit_cast(bf16x8, make_uint4(dw[0], dw[1], dw[2], dw[3]));
+#pragma unroll
+      for (int q = 0; q < RG; ++q)
+        acc[q][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[q]), b,
+                                                            acc[q][c], 0, 0, 0);
+    }
+  };
+  int k0 = kb;
+  for (; k0 + 32 * UK <= ke; k0 += 32 * UK) {
+    uint2 wv[UK][8];
+    uint4 av[UK][RG];
+#pragma unroll
+    for (int u = 0; u < UK; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) wv[u][t] = wload(k0 + 32 * u + t);
+#pragma unroll
+    for (int u = 0; u < UK; ++u)
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        av[u][q] = *reinterpret_cast<const uint4*>(arow[q] + k0 + 32 * u);
+        if (!aok[q]) av[u][q] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int u = 0; u < UK; ++u) step(wv[u], av[u]);
+  }
+  for (; k0 < ke; k0 += 32) {
+    uint2 wv[8];
+    uint4 av[RG];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) wv[t] = wload(k0 + t);
+#pragma unroll
+    for (int q = 0; q < RG; ++q) {
+      av[q] = *reinterpret_cast<const uint4*>(arow[q] + k0);
+      if (!aok[q]) av[q] = make_uint4(0, 0, 0, 0);
+    }
+    step(wv, av);
+  }
+}
+
+// k-steps of 32 in flight: 4 with one 16-row group, 2 with two (the same
+// registers)
+#ifndef KMAJ_UK1
+#define KMAJ_UK1 4
+#endif
+#ifndef KMAJ_UK2
+#define KMAJ_UK2 2
+#endif
+template <int KS>
+__global__ __launch_bounds__(NTHR) void gemm_skinny_kmaj_kernel(GemmArgs a) {
+  constexpr int NPW = 64, NPB = NPW * NTHR / 64;
+  const int e = blockIdx.y;
+  const int Kd = a.Kd, Nd = a.Nd;
+  const uint16_t* A;
+  const uint16_t* W;
+  uint16_t* C;
+  int r0, r1;
+  if (e == a.E) {
+    A = static_cast<const uint16_t*>(a.As);
+    W = static_cast<const uint16_t*>(a.Ws);
+    C = static_cast<uint16_t*>(a.Cs);
+    r0 = 0;
+    r1 = a.Ts;
+  } else {
+    A = static_cast<const uint16_t*>(a.A);
+    W = static_cast<const uint16_t*>(a.W) + (int64_t)e * Nd * Kd;
+    C = static_cast<uint16_t*>(a.C);
+    r0 = a.offsets[e];
+    r1 = a.offsets[e + 1];
+  }
+  if (r1 <= r0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // KS > 1: one n0 for the whole workgroup (uniform exit, every wavefront
+  // reaches the reduction's barriers); Nd is a multiple of 64
+  const int n0 = KS == 1 ? blockIdx.x * NPB + wave * NPW : blockIdx.x * NPW;
+  if (n0 >= Nd) return;
+  int kb = 0, ke = Kd;
+  if constexpr (KS > 1) {
+    const int kq = ((Kd + KS - 1) / KS + 31) / 32 * 32;
+    kb = min(Kd, __builtin_amdgcn_readfirstlane(wave) * kq);
+    ke = min(Kd, kb + kq);
+  }
+  // this lane's rows 8 (lane/16) + t of every k-step, columns n0 + 4 (lane%16)
+  // .. +3, as a byte offset from the row's start
+  // Kd * Nd * 2 < 2^32 bytes (d_model * d_ff < 2^31)
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W), (short)0, (int)((uint32_t)Kd * (uint32_t)Nd * 2u), 0x00020000);
+  const uint32_t loff = (uint32_t)((8 * (lane >> 4)) * Nd + n0 + 4 * (lane & 15)) * 2u;
+  __shared__ f32x4 red[KS][2][4][64];
+  for (int g0 = r0; g0 < r1; g0 += 32) {
+    f32x4 acc[2][4];
+    // the row count is uniform over the workgroup: every wavefront takes the
+    // same branch and reaches the barriers below
+    const int ng = r1 - g0 > 16 ? 2 : 1;
+    if (ng == 2)
+      kmaj_pass<2, KMAJ_UK2>(A, wr, loff, Kd, Nd, g0, r0, r1, kb, ke, lane, acc);
+    else
+      kmaj_pass<1, KMAJ_UK1>(A, wr, loff, Kd, Nd, g0, r0, r1, kb, ke, lane, acc);
+    if constexpr (KS > 1) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (q < ng) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) red[wave][q][c][lane] = acc[q][c];
+        }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          if (q < ng) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              acc[q][c] = red[0][q][c][lane];
+#pragma unroll
+              for (int w = 1; w < KS; ++w) acc[q][c] += red[w][q][c][lane];
+            }
+          }
+      }
+      __syncthreads();
+      if (wave != 0) continue;
+    }
+    // 16x16 accumulator layout: element v of lane l holds row (l/16)*4 + v of
+    // its group, column l%16 of the MFMA, i.e. output column n0 + 4 (l%16) + c
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = g0 + 16 * q + (lane >> 4) * 4 + v;
+        if (q < ng && r < r1) {
+          const uint32_t lo = (uint32_t)f32_to_bf16(acc[q][0][v]) |
+                              ((uint32_t)f32_to_bf16(acc[q][1][v]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(acc[q][2][v]) |
+                              ((uint32_t)f32_to_bf16(acc[q][3][v]) << 16);
+          *reinterpret_cast<uint2*>(C + (int64_t)r * Nd + n0 + 4 * (lane & 15)) = make_uint2(lo, hi);
+        }
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_per_expert*/,
@@ -333,6 +521,20 @@ hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int /*max_rows_
     else
       hipLaunchKernelGGL((gemm_skinny_kernel<false, false, 1>), grid, dim3(NTHR), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny_kmaj_bf16(const GemmArgs& a, hipStream_t s) {
+  const int E = a.E + (a.As ? 1 : 0);
+  if (E == 0) return hipSuccess;
+  // the same k-split rule as the n-major kernel
+  const bool ks = a.Kd >= 2048;
+  const int per_wg = ks ? 64 : 64 * NTHR / 64;
+  const dim3 grid((a.Nd + per_wg - 1) / per_wg, E);
+  if (ks)
+    hipLaunchKernelGGL((gemm_skinny_kmaj_kernel<4>), grid, dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kmaj_kernel<1>), grid, dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

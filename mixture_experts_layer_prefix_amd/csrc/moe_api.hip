@@ -690,6 +690,17 @@ int bwd_gemm(const moe_config_t* c, moe::GemmArgs g, int4* list, int32_t* count,
   return e == hipSuccess ? MOE_OK : hip_status(e, what);
 }
 
+// One input-gradient GEMM (weights read k-major): on decode-shaped layers the
+// weight-streaming kernel (no tile list; same-GPU, the decode-shaped
+// backward's two routed input-gradient GEMMs took 0.93 ms on the tiled kernel),
+// else bwd_gemm.
+int dgrad_gemm(const moe_config_t* c, const moe::GemmArgs& g, int4* list, int32_t* count,
+               int64_t bound, const int32_t* offs, int Nr, int Ts, hipStream_t s) {
+  if (gemm_path(c) == PATH_SKINNY)
+    return hip_status(moe::launch_gemm_skinny_kmaj_bf16(g, s), "dgrad GEMM launch");
+  return bwd_gemm(c, g, list, count, bound, offs, Nr, Ts, s, "dgrad GEMM launch");
+}
+
 int do_combine_bwd(const moe_config_t* c, const void* d_out, const void* y_perm,
                    const int32_t* slot_row, const float* tw, void* d_y_perm, float* d_tw,
                    hipStream_t s) {
@@ -729,7 +740,7 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   a.Kd = d;
   a.Nd = f;
   a.E = N;
-  r = bwd_gemm(c, a, fw.list[0], fw.count + 0, fw.bound[0], offsets, N, 0, s, "dgrad GEMM launch");
+  r = dgrad_gemm(c, a, fw.list[0], fw.count + 0, fw.bound[0], offsets, N, 0, s);
   if (r != MOE_OK) return r;
   MOE_TRY(moe::launch_gelu_bwd(dt, z, fw.dh, offsets + N, M, f, s), "GELU backward launch");
   a.A = fw.dh;                          // d_x_perm [M, d] = d_z [M, f] . W1_e [f, d]
@@ -737,7 +748,7 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   a.C = d_x_perm;
   a.Kd = f;
   a.Nd = d;
-  r = bwd_gemm(c, a, fw.list[1], fw.count + 1, fw.bound[1], offsets, N, 0, s, "dgrad GEMM launch");
+  r = dgrad_gemm(c, a, fw.list[1], fw.count + 1, fw.bound[1], offsets, N, 0, s);
   if (r != MOE_OK) return r;
   // dW2 [N, d, f]: A = d_y^T [d, ldt], W = h^T [f, ldt]
   MOE_TRY(moe::launch_transpose_segments(dt, d_y_perm, offsets, fw.kseg, N, d, ldt, fw.tb1, g->d_b2, s),
@@ -780,7 +791,7 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   sa.Ts = T;
   sa.Kd = d;
   sa.Nd = fs;
-  r = bwd_gemm(c, sa, fw.list[4], fw.count + 4, fw.bound[4], nullptr, 0, T, s, "dgrad GEMM launch");
+  r = dgrad_gemm(c, sa, fw.list[4], fw.count + 4, fw.bound[4], nullptr, 0, T, s);
   if (r != MOE_OK) return r;
   MOE_TRY(moe::launch_gelu_bwd(dt, zs, fw.dhs, nullptr, T, fs, s), "GELU backward launch");
   sa.As = fw.dhs;                       // d_x_shared [T, d] = d_zs . Ws1 [fs, d]
@@ -788,7 +799,7 @@ int do_ffn_bwd(const moe_config_t* c, const void* x_perm, const int32_t* offsets
   sa.Cs = d_x_shared;
   sa.Kd = fs;
   sa.Nd = d;
-  r = bwd_gemm(c, sa, fw.list[5], fw.count + 5, fw.bound[5], nullptr, 0, T, s, "dgrad GEMM launch");
+  r = dgrad_gemm(c, sa, fw.list[5], fw.count + 5, fw.bound[5], nullptr, 0, T, s);
   if (r != MOE_OK) return r;
   MOE_TRY(moe::launch_transpose_segments(dt, d_out, fw.off2, fw.kseg2, 1, d, ldt, fw.tb1, nullptr, s,
                                           c->T),

@@ -228,6 +228,9 @@ hipError_t launch_gemm_f32(const GemmArgs& a, bool gelu, hipStream_t s);
 // Decode-shaped grouped GEMM (bf16): streams each touched expert's weights once.
 hipError_t launch_gemm_skinny_bf16(const GemmArgs& a, bool gelu, int max_rows_per_expert,
                                    hipStream_t s);
+// Decode-shaped GEMM with k-major weights (W_e stored [Kd, Nd]; bf16, no
+// bias or activation): the backward's input gradients.
+hipError_t launch_gemm_skinny_kmaj_bf16(const GemmArgs& a, hipStream_t s);
 
 // Bytes of per-slot rows (T*K rows of d elements) above which the combine,
 // combine-backward and unpermute kernels load them non-temporally: half of

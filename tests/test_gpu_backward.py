@@ -44,7 +44,26 @@ CASES = {
     # one token: 14 of 16 experts empty (zero weight gradients from empty
     # k-segments), one-token router slices and d_x tile
     "t1_empty_experts": C.MIXTRAL_PREFILL.with_(T=1, d_model=128, d_ff=192, n_experts=16),
+    # decode-shaped input gradients (weights streamed k-major): d_model 2240
+    # splits over a workgroup's four wavefronts in ragged quarters (576, 576,
+    # 576, 512), d_ff 576 leaves a 32-wide k tail and a partial workgroup of
+    # 192 of 256 columns in the second GEMM
+    "decode_ksplit": C.DECODE.with_(T=24, d_model=2240, d_ff=576, n_experts=32),
+    # every token routed to expert 3 (logit offset +30): 40 rows, a pass of
+    # two 16-row groups, then one of 8 rows
+    "decode_hot_expert": C.DECODE.with_(T=40, d_model=2048, d_ff=320, n_experts=16),
+    # decode with a shared expert: its 20 dense rows in the same kernels
+    "decode_shared": C.DECODE.with_(T=20, d_model=256, d_ff=192, n_experts=16, d_ff_shared=128),
 }
+
+
+def _hot_expert(inp):
+    off = inp.logit_offset.copy()
+    off[3] += 30.0
+    inp.logit_offset = off
+
+
+MUTATE = {"decode_hot_expert": _hot_expert}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -73,6 +92,8 @@ def _run(name):
     import torch
     shape = CASES[name]
     inp = inputs.make_inputs(shape, seed=0)
+    if name in MUTATE:
+        MUTATE[name](inp)
     cfg = moe.config_for(shape)
     cap = cfg.capacity if cfg.capacity > 0 else None
     zbeta = ZBETA if name != "tiled_ragged" else 0.0
@@ -129,6 +150,8 @@ def test_backward_matches_oracle(name):
         assert e <= tol, (key, e)
     # experts that received no rows: exactly zero gradients
     kept = np.diff(sv["expert_offsets"])
+    if name == "decode_hot_expert":
+        assert kept[3] == shape.T, kept
     for e in np.nonzero(kept == 0)[0]:
         assert not g["d_w1"][e].any() and not g["d_w2"][e].any(), f"expert {e}"
         if "d_b1" in g:
