@@ -129,14 +129,18 @@ def cpu_baseline(shape, inp, n_tok):
 def algorithmic_backward(shape, counts, M):
     """FLOPs and minimum HBM bytes of the expert FFN backward stage: four
     GEMMs per expert (two input gradients, two weight gradients) of 2*M*d*f
-    each; bytes = weights read once, weight gradients written once, x_perm,
-    z, h, d_y read once, d_x_perm written once (the shared expert alike)."""
+    each; bytes = the touched experts' weights read once, the weight
+    gradients of all N experts written once (the stage's outputs are the
+    whole [N, f, d] and [N, d, f] stacks: zeros for an expert without rows),
+    x_perm, z, h, d_y read once, d_x_perm written once (the shared expert
+    alike)."""
     d, f, fs = shape.d_model, shape.d_ff, shape.d_ff_shared
     T = shape.T
     eb = 4 if shape.dtype == "f32" else 2
     touched = int((counts > 0).sum())
+    N = len(counts)
     flops = 4 * 2 * M * d * f + (4 * 2 * T * d * fs if fs else 0)
-    wbytes = 2 * (touched * 2 * d * f + (2 * d * fs if fs else 0)) * eb
+    wbytes = ((touched + N) * 2 * d * f + (2 * 2 * d * fs if fs else 0)) * eb
     abytes = (3 * M * d + 2 * M * f) * eb + ((3 * T * d + 2 * T * fs) * eb if fs else 0)
     return flops, wbytes + abytes, touched
 
