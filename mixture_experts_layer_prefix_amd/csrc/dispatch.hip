@@ -10,7 +10,9 @@
 //   off     = exclusive scan of kept_e;  row = off[e] + pos(p)
 //   slot_row[p] = kept ? row : -1;  row_token[row] = t;  x_perm[row] = x[t].
 //
-// Four launches, all deterministic (no result depends on atomic order):
+// Four launches (two when the tokens form one chunk of 256: hist, scan and
+// rank then run in one workgroup), all deterministic (no result depends on
+// atomic order):
 //   1. hist:    each workgroup counts its 256-token chunk per expert (LDS).
 //   2. scan:    one workgroup turns the per-chunk counts into per-chunk
 //               starting positions, counts, kept counts, offsets, n_dropped.
@@ -43,6 +45,33 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < N; e += blockDim.x) blkcnt[(int64_t)blockIdx.x * N + e] = hist[e];
 }
 
+// Offsets from the per-expert pair counts: thread e (< N, of 256) holds expert
+// e's count `run`; kept = min(run, cap), offsets = exclusive scan of kept,
+// offsets[N] = the kept total, n_dropped = pairs - kept total.
+__device__ __forceinline__ void expert_scan(int e, int run, int N, int cap, int64_t pairs,
+                                            int32_t* __restrict__ offsets,
+                                            int32_t* __restrict__ n_dropped, int* wsum) {
+  const int kept = (e < N) ? min(run, cap) : 0;
+  // exclusive scan of kept over e: wave-level inclusive scan, then wave sums
+  const int lane = e & 63, wave = e >> 6;
+  int v = kept;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  const int excl = base + v - kept;
+  if (e < N) offsets[e] = excl;
+  if (e == N - 1) {
+    offsets[N] = excl + kept;
+    n_dropped[0] = (int32_t)(pairs - (int64_t)(excl + kept));
+  }
+}
+
 // One workgroup of 256 threads; thread e owns expert e (N <= 256).
 __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ blkcnt, int nblk,
                                                    int N, int cap, int64_t pairs,
@@ -72,44 +101,19 @@ __global__ __launch_bounds__(256) void scan_kernel(const int32_t* __restrict__ b
     }
     counts[e] = run;
   }
-  const int kept = (e < N) ? min(run, cap) : 0;
-  // exclusive scan of kept over e: wave-level inclusive scan, then wave sums
-  const int lane = e & 63, wave = e >> 6;
-  int v = kept;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  const int excl = base + v - kept;
-  if (e < N) offsets[e] = excl;
-  if (e == N - 1) {
-    offsets[N] = excl + kept;
-    n_dropped[0] = (int32_t)(pairs - (int64_t)(excl + kept));
-  }
+  expert_scan(e, run, N, cap, pairs, offsets, n_dropped, wsum);
 }
 
-// One wavefront per chunk of DB tokens.
-__global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ idx, int T, int K,
-                                                  int N, int cap,
-                                                  const int32_t* __restrict__ blkoff,
-                                                  const int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ slot_row,
-                                                  int32_t* __restrict__ row_token) {
-  __shared__ int run[MAXN];
-  __shared__ int off_s[MAXN];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < N; e += 64) {
-    run[e] = blkoff[(int64_t)blockIdx.x * N + e];
-    off_s[e] = offsets[e];
-  }
-  __syncthreads();
-  const int64_t p0 = (int64_t)blockIdx.x * DB * K;
-  const int64_t p1 = min((int64_t)(blockIdx.x + 1) * DB, (int64_t)T) * K;
+// Positions of the pairs [p0, p1), in order: run[e] holds the position the
+// next pair of expert e takes and off_s[e] its block's first row.  Wavefront
+// 0 (lanes `lane`) ranks 64 pairs per step; lanes with equal experts are
+// matched with ballots.  Every wavefront of the workgroup calls this (the
+// trip counts are uniform) and reaches its barriers; `active` is true in
+// wavefront 0 only.
+__device__ __forceinline__ void rank_walk(const int32_t* __restrict__ idx, int64_t p0, int64_t p1,
+                                          int K, int N, int cap, int* run, const int* off_s,
+                                          int32_t* __restrict__ slot_row,
+                                          int32_t* __restrict__ row_token, int lane, bool active) {
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   // the expert indices of RB 64-slot steps are loaded together, then the
   // steps run in slot order
@@ -119,14 +123,14 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int64_t p = pc + 64 * u + lane;
-      ev[u] = p < p1 ? idx[p] : -1;
+      ev[u] = (active && p < p1) ? idx[p] : -1;
     }
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int64_t pb = pc + 64 * u;
-      if (pb >= p1) break;   // wave-uniform
+      if (pb >= p1) break;   // uniform over the workgroup
       const int64_t p = pb + lane;
-      const bool inb = p < p1;
+      const bool inb = active && p < p1;
       const int e = ev[u];
       const bool valid = inb && e >= 0 && e < N;
       // lanes holding the same valid expert: AND of per-bit ballots
@@ -157,6 +161,58 @@ __global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ id
       __syncthreads();
     }
   }
+}
+
+// One wavefront per chunk of DB tokens.
+__global__ __launch_bounds__(64) void rank_kernel(const int32_t* __restrict__ idx, int T, int K,
+                                                  int N, int cap,
+                                                  const int32_t* __restrict__ blkoff,
+                                                  const int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ slot_row,
+                                                  int32_t* __restrict__ row_token) {
+  __shared__ int run[MAXN];
+  __shared__ int off_s[MAXN];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < N; e += 64) {
+    run[e] = blkoff[(int64_t)blockIdx.x * N + e];
+    off_s[e] = offsets[e];
+  }
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * DB * K;
+  const int64_t p1 = min((int64_t)(blockIdx.x + 1) * DB, (int64_t)T) * K;
+  rank_walk(idx, p0, p1, K, N, cap, run, off_s, slot_row, row_token, lane, true);
+}
+
+// All of hist, scan and rank in one workgroup of 256 threads when the tokens
+// form one chunk (T <= DB): the per-expert counts in LDS, thread e's scan,
+// then wavefront 0's walk from position 0 of every expert.  The same results
+// as the three launches (one chunk: every expert's chunk start is 0).
+__global__ __launch_bounds__(256) void dispatch_small_kernel(
+    const int32_t* __restrict__ idx, int T, int K, int N, int cap, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
+    int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token) {
+  __shared__ int hist[MAXN];
+  __shared__ int off_s[MAXN];
+  __shared__ int wsum[4];
+  const int e = threadIdx.x;
+  if (e < N) hist[e] = 0;
+  __syncthreads();
+  const int64_t pairs = (int64_t)T * K;
+  for (int64_t p = threadIdx.x; p < pairs; p += blockDim.x) {
+    const int x = idx[p];
+    if (x >= 0 && x < N) atomicAdd(&hist[x], 1);
+  }
+  __syncthreads();
+  const int run = e < N ? hist[e] : 0;
+  if (e < N) counts[e] = run;
+  expert_scan(e, run, N, cap, pairs, offsets, n_dropped, wsum);
+  if (e < N) {
+    off_s[e] = offsets[e];
+    hist[e] = 0;              // the walk's running positions
+  }
+  __syncthreads();
+  rank_walk(idx, 0, pairs, K, N, cap, hist, off_s, slot_row, row_token, threadIdx.x & 63,
+            (threadIdx.x >> 6) == 0);
 }
 
 // One wavefront per token (its index made wave-uniform, so the slot rows are
@@ -296,11 +352,16 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, size_t row_by
                            int32_t* n_dropped, int32_t* blkcnt, int32_t* blkoff, hipStream_t s) {
   const int nblk = dispatch_blocks(T);
   const int cap = capacity > 0 ? capacity : 0x7fffffff;
-  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, T, K, N, blkcnt);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blkcnt, nblk, N, cap,
-                     (int64_t)T * K, blkoff, counts, offsets, n_dropped);
-  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(64), 0, s, topk_idx, T, K, N, cap, blkoff,
-                     offsets, slot_row, row_token);
+  if (nblk == 1) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(256), 0, s, topk_idx, T, K, N, cap,
+                       counts, offsets, n_dropped, slot_row, row_token);
+  } else {
+    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(256), 0, s, topk_idx, T, K, N, blkcnt);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, blkcnt, nblk, N, cap,
+                       (int64_t)T * K, blkoff, counts, offsets, n_dropped);
+    hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(64), 0, s, topk_idx, T, K, N, cap, blkoff,
+                       offsets, slot_row, row_token);
+  }
   // the pieces a lane copies per row, all in one batch when they fit in 16
   const int row_vec = (int)(row_bytes / 16), per_lane = (row_vec + 63) / 64;
   const uint4* xs = static_cast<const uint4*>(x);

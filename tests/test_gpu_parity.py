@@ -146,6 +146,20 @@ def test_skinny_expert_with_more_than_16_rows(d_ff):
     assert g["counts"][0] == 40
 
 
+@pytest.mark.parametrize("T", [256, 257])
+def test_dispatch_chunk_boundary(T):
+    """256 tokens form one dispatch chunk (hist, scan and rank in one
+    workgroup), 257 two; top-32 of 64 experts (8192 pairs walked in one
+    chunk) with a capacity of 100 that drops most pairs."""
+    shape = C.DEEPSEEK_FINE.with_(T=T, d_model=64, d_ff=64, n_experts=64, top_k=32,
+                                  d_ff_shared=0)
+    inp = inputs.make_inputs(shape, seed=T)
+    cfg = moe.config_for(shape)
+    cfg.capacity = 100
+    g, o = _compare(f"chunk_boundary_T{T}", shape, inp, cfg)
+    assert g["n_dropped"] > 0 and (g["counts"] > 100).any()
+
+
 def test_capacity_one():
     shape = C.TINY_FP32.with_(T=64)
     inp = inputs.make_inputs(shape)
