@@ -12,10 +12,12 @@
 //     wave arrangement is picked per tile from its row count, and a short
 //     remainder of an expert's rows rides in its last full tile;
 //   - operands move global -> LDS with 16-byte direct-to-LDS loads (no VGPR
-//     staging), 32-wide k-steps.  bf16 forward tiles load k-pairs: one wave
-//     instruction fills 8 LDS rows of 128 bytes (two k-steps of a row) into
-//     two pair buffers; INT8, weight-gradient and k-major tiles fill 16 rows
-//     of 64 bytes per instruction into four stages.  The 16-byte chunks of
+//     staging), 32-wide k-steps.  bf16 and INT8 forward tiles load k-pairs:
+//     one wave instruction fills 8 LDS rows of 128 bytes (two k-steps of an
+//     activation or bf16 weight row) or 16 rows of 64 bytes (two k-steps of
+//     INT8 codes) into two pair buffers; INT4, weight-gradient and k-major
+//     tiles fill 16 rows of 64 bytes per instruction into four stages.  The
+//     16-byte chunks of
 //     each LDS row are XOR-swizzled (swz, swz8) so fragment reads hit every
 //     bank once per 16 lanes;
 //   - the MFMA takes the weight fragment as its first operand, so each lane
@@ -26,7 +28,7 @@
 //   - variants: INT8 and INT4 weights (codes widened in registers), weight gradients
 //     over per-expert k-segments (and a two-workgroups-per-CU kernel of 256 x
 //     128 tiles for short segments), k-major weights for input gradients.
-// MOE_KPAIRS=0 builds the four-stage loop for the bf16 forward tiles too.
+// MOE_KPAIRS=0 builds the four-stage loop for the bf16 and INT8 forward tiles too.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -386,10 +388,15 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   };
 
   // k-pairs: one direct load moves 8 rows x 128 bytes (two k-steps of a
-  // row), into two pair buffers of (AR + BNL) rows x 128 bytes each
-  constexpr bool P2 = MOE_KPAIRS && !QW && !WG && !KM;
+  // row), into two pair buffers of (AR + BNL) rows x 128 bytes each.  INT8
+  // codes: the weight region of a pair buffer holds the codes of its two
+  // k-steps as 64-byte rows, 16 rows per direct load, laid out and swizzled
+  // like the four-stage loop's even stages; the activation rows stay 128
+  // bytes (they are most of an INT8 tile's load bytes).
+  constexpr bool P2 = MOE_KPAIRS && !Q4 && !WG && !KM;
   constexpr int NLA2 = Lay::AROWS / 8 / NW, NLB2 = Lay::BNL / 8 / NW;
-  static_assert(!P2 || (NLA2 * 8 * NW == Lay::AROWS && NLB2 % 2 == 0), "pair loads split evenly");
+  constexpr int NLBP = QW ? NLB : NLB2;   // weight loads per wavefront per pair
+  static_assert(!P2 || (NLA2 * 8 * NW == Lay::AROWS && NLBP % 2 == 0), "pair loads split evenly");
   constexpr int PST = (Lay::AR + Lay::BNL) * 2 * BK;   // bf16 elements per pair buffer
   static_assert(!P2 || NS == 4, "the pair buffers take the four stages' LDS");
   uint32_t oA2[P2 ? NLA2 : 1], oB2[P2 ? NLB2 : 1];
@@ -411,8 +418,12 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     for (int i = 0; i < NLA2; ++i) lds_load16(A + oA2[i] + k0, base + i * 8 * 2 * BK);
   };
   auto issue_b2 = [&](int buf, int k0, auto i0_tag, auto i1_tag) {
-    char* base = reinterpret_cast<char*>(lds + buf * PST + Lay::AR * 2 * BK) + wave * NLB2 * 1024;
-    if constexpr (NTW) {
+    char* base = reinterpret_cast<char*>(lds + buf * PST + Lay::AR * 2 * BK) + wave * NLBP * 1024;
+    if constexpr (QW) {
+#pragma unroll
+      for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
+        lds_load16(W + offB[i] + (uint32_t)k0, base + i * 1024);
+    } else if constexpr (NTW) {
 #pragma unroll
       for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
         lds_load16<2>(W + oB2[i] + (uint32_t)k0 * 2, base + i * 1024);
@@ -499,17 +510,32 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     }
   };
   // k-pairs: fragments of half kk of k-step ks (0, 1) of the pair in buffer buf
+  // (INT8 codes: the k order of read_half's INT8 fragments, k = 16 h + 8 kk
+  // + 0..7 of the step; the half kk = 0 reads the 16 codes of both halves)
   auto read_q = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int ks, int kk) {
     const uint16_t* As = lds + buf * PST;
     const uint16_t* Bs = As + Lay::AR * 2 * BK;
-    const int pc = ((ks * 4 + kk * 2 + (lane >> 5)) ^ sw8) * 8;
+    const int pc = ((ks * 4 + (QW ? (lane >> 5) * 2 + kk : kk * 2 + (lane >> 5))) ^ sw8) * 8;
     const int ar = (wm * WROWS + (lane & 31)) * 2 * BK, br = (wn * WCOLS + (lane & 31)) * 2 * BK;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
       fa[i] = *reinterpret_cast<const bf16x8*>(As + ar + i * 32 * 2 * BK + pc);
     if constexpr (EX)
       fa[MI] = *reinterpret_cast<const bf16x8*>(As + (W4_TM + wm * 32 + (lane & 31)) * 2 * BK + pc);
-    if constexpr (!QW) {
+    if constexpr (QW && !Q4) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (kk == 0) {
+          const uint4 q = *reinterpret_cast<const uint4*>(
+              reinterpret_cast<const char*>(Bs) + browq + i * 32 * 64 +
+              (((2 * ks + (lane >> 5)) ^ sw) * 16));
+          fb[i] = make_uint2(q.x, q.y);
+          fbq[i] = make_uint2(q.z, q.w);
+        } else {
+          fb[i] = fbq[i];
+        }
+      }
+    } else if constexpr (!QW) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         fb[i] = *reinterpret_cast<const bf16x8*>(Bs + br + i * 32 * 2 * BK + pc);
@@ -574,7 +600,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   // fragments and issues the A rows of pair p+2 into the buffer just freed.
   const int NP = KT / 2;
   issue_a2(0, 0);
-  issue_b2(0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, NLB2>{});
+  issue_b2(0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, NLBP>{});
   issue_a2(1, min(1, NP - 1) * 2 * BK);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLA2) : "memory");
   barrier();
@@ -584,18 +610,19 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     const int kn = min(p + 1, NP - 1) * 2 * BK, kn2 = min(p + 2, NP - 1) * 2 * BK;
     __builtin_amdgcn_sched_barrier(0);
     read_q(fa1, fb1, buf, 0, 1);
-    issue_b2(nb, kn, std::integral_constant<int, 0>{}, std::integral_constant<int, NLB2 / 2>{});
+    issue_b2(nb, kn, std::integral_constant<int, 0>{}, std::integral_constant<int, NLBP / 2>{});
     mfma_half(fa0, fb0);
-    interleave(std::integral_constant<int, NLB2 / 2>{}, std::integral_constant<int, NI>{});
+    // (INT8 codes: weight fragments are read in the halves kk = 0 only)
+    interleave(std::integral_constant<int, NLBP / 2>{}, std::integral_constant<int, QW ? 0 : NI>{});
     __builtin_amdgcn_sched_barrier(0);
     read_q(fa0, fb0, buf, 1, 0);
-    issue_b2(nb, kn, std::integral_constant<int, NLB2 / 2>{}, std::integral_constant<int, NLB2>{});
+    issue_b2(nb, kn, std::integral_constant<int, NLBP / 2>{}, std::integral_constant<int, NLBP>{});
     mfma_half(fa1, fb1);
-    interleave(std::integral_constant<int, NLB2 - NLB2 / 2>{}, std::integral_constant<int, NI>{});
+    interleave(std::integral_constant<int, NLBP - NLBP / 2>{}, std::integral_constant<int, NI>{});
     __builtin_amdgcn_sched_barrier(0);
     read_q(fa1, fb1, buf, 1, 1);
     mfma_half(fa0, fb0);
-    interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, NI>{});
+    interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, QW ? 0 : NI>{});
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     barrier();
