@@ -560,15 +560,18 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       // The folded rows' accumulators live in ordinary VGPRs (the 256
       // accumulation registers hold the main 256 x 256): the compiler keeps
       // all MFMA results in one register class, so these four are written
-      // out with VGPR operands.  The compiler does not see an MFMA here, so
-      // the hazards it would cover are covered by placement: the weight
-      // fragment (from an LDS read, or widened by VALU code for INT8) was
-      // already read by the compiler's MFMAs just above, which wait as the
-      // hardware requires; fa[MI] comes from an LDS read covered by the wait
-      // counts; each accx[ni] is next read by the same MFMA a whole half
-      // later, and the epilogue pads before reading it.
+      // out with VGPR operands.  The compiler does not see an MFMA here and
+      // inserts no wait states for it, and it may schedule the statement
+      // right after the VALU instructions that write its operands (the INT8
+      // weight fragment is widened by v_perm_b32 code; the compiler was seen
+      // to place this MFMA one instruction after that write, which made the
+      // folded rows' results depend on timing).  So the statement carries
+      // its own pad: s_nop 4 gives 5 wait states, more than a VALU write
+      // followed by an MFMA source read needs.  fa[MI] comes from an LDS
+      // read covered by the wait counts; each accx[ni] is next read by the
+      // same MFMA a whole half later, and the epilogue pads before reading it.
       if constexpr (EX)
-        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+        asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
             : "+v"(accx[ni])
             : "v"(fb), "v"(fa[MI]));
     }

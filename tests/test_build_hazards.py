@@ -2,13 +2,15 @@
 
 The accumulators of the rows folded into a 320-row tile live in ordinary
 VGPRs and are updated by inline-asm v_mfma_f32_32x32x16_bf16, which the
-compiler's hazard recognizer does not see.  Their safety rests on placement:
-(1) nothing but those asm MFMAs touches the accumulators during the k-loop,
-and (2) after the last one, an asm block of three `s_nop 7` (24 wait states)
-comes before any other instruction reads or writes them.  This test compiles
-gemm_bf16.hip for gfx950 to assembly and checks (2) in every kernel that
-holds such MFMAs, so a compiler or schedule change that moves an access of
-the accumulators ahead of the pad fails here rather than silently on the GPU."""
+compiler's hazard recognizer does not see.  Their safety rests on
+(1) nothing but those asm MFMAs touching the accumulators during the k-loop,
+(2) after the last one, an asm block of three `s_nop 7` (24 wait states)
+coming before any other instruction reads or writes them, and (3) each asm
+MFMA carrying an `s_nop 4` of its own, since the compiler may schedule it
+right after the VALU code that writes its operands (the widened INT8 weight
+fragment).  These tests compile gemm_bf16.hip for gfx950 to assembly and
+check (2) and (3) in every kernel that holds such MFMAs, so a compiler or
+schedule change that breaks them fails here rather than silently on the GPU."""
 import os
 import re
 import shutil
@@ -145,3 +147,17 @@ def test_folded_row_mfmas_are_padded_before_any_other_access(asm):
                     work.append(sl)
         assert any(k == "pad" for b in blocks for k, _ in b["items"]), f"{name}: no pad"
     assert checked > 0, "no kernel with folded-row MFMAs found"
+
+
+def test_folded_row_mfmas_carry_their_source_pad(asm):
+    """Every asm block holding a folded-row MFMA pads with s_nop 4 or more
+    right before it: the compiler inserts no wait states for the statement,
+    and a VALU write of its weight fragment was seen one instruction ahead."""
+    blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", asm, flags=re.S)
+    mf = [b for b in blocks if "v_mfma_f32_32x32x16_bf16" in b]
+    assert mf, "no folded-row asm MFMA found"
+    for b in mf:
+        ins = [ln.strip() for ln in b.strip().split("\n") if ln.strip()]
+        i = next(k for k, t in enumerate(ins) if t.startswith("v_mfma"))
+        assert i > 0 and re.match(r"s_nop (\d+)$", ins[i - 1]) and \
+            int(ins[i - 1].split()[1]) >= 4, f"unpadded folded-row MFMA: {ins}"
