@@ -12,14 +12,13 @@
 //     wave arrangement is picked per tile from its row count, and a short
 //     remainder of an expert's rows rides in its last full tile;
 //   - operands move global -> LDS with 16-byte direct-to-LDS loads (no VGPR
-//     staging), 32-wide k-steps.  bf16 and INT8 forward tiles load k-pairs:
-//     one wave instruction fills 8 LDS rows of 128 bytes (two k-steps of an
+//     staging), 32-wide k-steps.  Forward tiles load k-pairs: one wave
+//     instruction fills 8 LDS rows of 128 bytes (two k-steps of an
 //     activation or bf16 weight row) or 16 rows of 64 bytes (two k-steps of
-//     INT8 codes) into two pair buffers; INT4, weight-gradient and k-major
-//     tiles fill 16 rows of 64 bytes per instruction into four stages.  The
-//     16-byte chunks of
-//     each LDS row are XOR-swizzled (swz, swz8) so fragment reads hit every
-//     bank once per 16 lanes;
+//     INT8 codes, four of INT4 codes) into two pair buffers; weight-gradient
+//     and k-major tiles fill 16 rows of 64 bytes per instruction into four
+//     stages.  The 16-byte chunks of each LDS row are XOR-swizzled (swz,
+//     swz8) so fragment reads hit every bank once per 16 lanes;
 //   - the MFMA takes the weight fragment as its first operand, so each lane
 //     ends up with 4 consecutive output columns of one row; the output tile
 //     is staged through LDS and written as whole rows;
@@ -28,7 +27,7 @@
 //   - variants: INT8 and INT4 weights (codes widened in registers), weight gradients
 //     over per-expert k-segments (and a two-workgroups-per-CU kernel of 256 x
 //     128 tiles for short segments), k-major weights for input gradients.
-// MOE_KPAIRS=0 builds the four-stage loop for the bf16 and INT8 forward tiles too.
+// MOE_KPAIRS=0 builds the four-stage loop for the forward tiles too.
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -392,8 +391,12 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   // codes: the weight region of a pair buffer holds the codes of its two
   // k-steps as 64-byte rows, 16 rows per direct load, laid out and swizzled
   // like the four-stage loop's even stages; the activation rows stay 128
-  // bytes (they are most of an INT8 tile's load bytes).
-  constexpr bool P2 = MOE_KPAIRS && !Q4 && !WG && !KM;
+  // bytes (they are most of an INT8 tile's load bytes).  INT4 codes: a
+  // 64-byte row holds four k-steps (two pairs), so pairs 2g and 2g + 1 read
+  // the codes that were loaded with pair 2g into the weight region of
+  // buffer g mod 2, and only the odd pairs issue code loads (for the next
+  // group, into the other region).
+  constexpr bool P2 = MOE_KPAIRS && !WG && !KM;
   constexpr int NLA2 = Lay::AROWS / 8 / NW, NLB2 = Lay::BNL / 8 / NW;
   constexpr int NLBP = QW ? NLB : NLB2;   // weight loads per wavefront per pair
   static_assert(!P2 || (NLA2 * 8 * NW == Lay::AROWS && NLBP % 2 == 0), "pair loads split evenly");
@@ -422,7 +425,7 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
     if constexpr (QW) {
 #pragma unroll
       for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
-        lds_load16(W + offB[i] + (uint32_t)k0, base + i * 1024);
+        lds_load16(W + offB[i] + (uint32_t)(Q4 ? k0 / 2 : k0), base + i * 1024);
     } else if constexpr (NTW) {
 #pragma unroll
       for (int i = decltype(i0_tag)::value; i < decltype(i1_tag)::value; ++i)
@@ -512,7 +515,8 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   // k-pairs: fragments of half kk of k-step ks (0, 1) of the pair in buffer buf
   // (INT8 codes: the k order of read_half's INT8 fragments, k = 16 h + 8 kk
   // + 0..7 of the step; the half kk = 0 reads the 16 codes of both halves)
-  auto read_q = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int ks, int kk) {
+  // (pq: the pair's index, which places INT4 codes)
+  auto read_q = [&](bf16x8 (&fa)[MX], BF (&fb)[NI], int buf, int ks, int kk, int pq) {
     const uint16_t* As = lds + buf * PST;
     const uint16_t* Bs = As + Lay::AR * 2 * BK;
     const int pc = ((ks * 4 + (QW ? (lane >> 5) * 2 + kk : kk * 2 + (lane >> 5))) ^ sw8) * 8;
@@ -522,7 +526,23 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
       fa[i] = *reinterpret_cast<const bf16x8*>(As + ar + i * 32 * 2 * BK + pc);
     if constexpr (EX)
       fa[MI] = *reinterpret_cast<const bf16x8*>(As + (W4_TM + wm * 32 + (lane & 31)) * 2 * BK + pc);
-    if constexpr (QW && !Q4) {
+    if constexpr (Q4) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (kk == 0) {
+          // chunk 2 (pq mod 2) + ks (the k-step inside the group of four) of
+          // the region of buffer (pq / 2) mod 2; lane half h reads its 8 bytes
+          const char* Bq =
+              reinterpret_cast<const char*>(lds + ((pq >> 1) & 1) * PST + Lay::AR * 2 * BK);
+          const uint2 q = *reinterpret_cast<const uint2*>(
+              Bq + browq + i * 32 * 64 + (((2 * (pq & 1) + ks) ^ sw) * 16) + (lane >> 5) * 8);
+          fb[i] = q.x;
+          fbq[i] = q.y;
+        } else {
+          fb[i] = fbq[i];
+        }
+      }
+    } else if constexpr (QW) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         if (kk == 0) {
@@ -607,34 +627,54 @@ __device__ __forceinline__ void w4_tile(const GemmArgs& a, const TileRef& tr, ui
   issue_a2(1, min(1, NP - 1) * 2 * BK);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLA2) : "memory");
   barrier();
-  read_q(fa0, fb0, 0, 0, 0);
-  for (int p = 0; p < NP; ++p) {
+  read_q(fa0, fb0, 0, 0, 0, 0);
+  // pair p; PH = p mod 2 (INT4 codes: the odd pairs load the next group's)
+  auto pair_step = [&](int p, auto ph_tag) {
+    constexpr bool LOADW = !Q4 || decltype(ph_tag)::value == 1;
+    constexpr int NVW = LOADW ? NLBP / 2 : 0;
     const int buf = p & 1, nb = buf ^ 1;
-    const int kn = min(p + 1, NP - 1) * 2 * BK, kn2 = min(p + 2, NP - 1) * 2 * BK;
+    const int kn2 = min(p + 2, NP - 1) * 2 * BK;
+    // weight rows of pair p + 1 into buffer nb; INT4: the codes of group
+    // (p + 1) / 2 into region ((p + 1) / 2) mod 2 (past the end: the last
+    // group's codes again, into the region no pair reads any more)
+    const int wreg = Q4 ? ((p + 1) >> 1) & 1 : nb;
+    const int kw = (Q4 ? min(p + 1, NP - 2) : min(p + 1, NP - 1)) * 2 * BK;
     __builtin_amdgcn_sched_barrier(0);
-    read_q(fa1, fb1, buf, 0, 1);
-    issue_b2(nb, kn, std::integral_constant<int, 0>{}, std::integral_constant<int, NLBP / 2>{});
+    read_q(fa1, fb1, buf, 0, 1, p);
+    if constexpr (LOADW)
+      issue_b2(wreg, kw, std::integral_constant<int, 0>{}, std::integral_constant<int, NLBP / 2>{});
     mfma_half(fa0, fb0);
-    // (INT8 codes: weight fragments are read in the halves kk = 0 only)
-    interleave(std::integral_constant<int, NLBP / 2>{}, std::integral_constant<int, QW ? 0 : NI>{});
+    // (INT8 / INT4 codes: weight fragments are read in the halves kk = 0 only)
+    interleave(std::integral_constant<int, NVW>{}, std::integral_constant<int, QW ? 0 : NI>{});
     __builtin_amdgcn_sched_barrier(0);
-    read_q(fa0, fb0, buf, 1, 0);
-    issue_b2(nb, kn, std::integral_constant<int, NLBP / 2>{}, std::integral_constant<int, NLBP>{});
+    read_q(fa0, fb0, buf, 1, 0, p);
+    if constexpr (LOADW)
+      issue_b2(wreg, kw, std::integral_constant<int, NLBP / 2>{}, std::integral_constant<int, NLBP>{});
     mfma_half(fa1, fb1);
-    interleave(std::integral_constant<int, NLBP - NLBP / 2>{}, std::integral_constant<int, NI>{});
+    interleave(std::integral_constant<int, LOADW ? NLBP - NLBP / 2 : 0>{},
+               std::integral_constant<int, NI>{});
     __builtin_amdgcn_sched_barrier(0);
-    read_q(fa1, fb1, buf, 1, 1);
+    read_q(fa1, fb1, buf, 1, 1, p);
     mfma_half(fa0, fb0);
     interleave(std::integral_constant<int, 0>{}, std::integral_constant<int, QW ? 0 : NI>{});
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_q(fa0, fb0, nb, 0, 0);
+    read_q(fa0, fb0, nb, 0, 0, p + 1);
     issue_a2(buf, kn2);
     mfma_half(fa1, fb1);
     interleave(std::integral_constant<int, NLA2>{}, std::integral_constant<int, NI>{});
     __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (Q4) {
+    // Kd is a multiple of 128 for INT4 codes: NP is even
+    for (int p = 0; p < NP; p += 2) {
+      pair_step(p, std::integral_constant<int, 0>{});
+      pair_step(p + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int p = 0; p < NP; ++p) pair_step(p, std::integral_constant<int, 0>{});
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   } else if (!WG || KT > 0) {
