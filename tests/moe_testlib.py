@@ -214,8 +214,10 @@ def check_logits(g_logits, o_logits, inp, path):
         fin = np.isfinite(o64)
         assert (diff[fin] <= bound[fin] + ulp[fin]).all(), \
             f"certified logits off by {np.max(diff[fin] / (bound[fin] + ulp[fin])):.3g} x the bound"
+        pos = fin & (bound > 0)   # (an all-zero router has a zero bound)
+        rel = np.max(diff[pos] / bound[pos]) if pos.any() else 0.0
         say(f"  certified router: logits max |err| {diff[fin].max():.3e} "
-            f"({np.max(diff[fin] / bound[fin]):.2e} of the bound), "
+            f"({rel:.2e} of the bound), "
             f"{int((ulp_diff_f32(g_logits, o_logits) <= 1).mean() * 100)}% within one ulp")
         return
     ud = ulp_diff_f32(g_logits, o_logits)
