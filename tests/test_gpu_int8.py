@@ -137,7 +137,7 @@ def test_skinny_int8_expert_with_more_than_16_rows(d_ff):
     assert err <= BF16_TOL
 
 
-@pytest.mark.parametrize("quant", ["int8", "none"])
+@pytest.mark.parametrize("quant", ["int8", "int4", "none"])
 def test_folded_tiles_repeat_bit_identical(quant):
     """Folded 320-row tiles (experts of 257-320 rows) over many k-pairs give
     the same bits on every call and match the oracle.  Their rows are
@@ -145,7 +145,8 @@ def test_folded_tiles_repeat_bit_identical(quant):
     the VALU code widening an INT8 weight fragment; without the pad inside
     the asm statement the folded rows' results depended on timing (seen as a
     whole-layer call differing from the staged entry points at the
-    DeepSeek-V3-shaped INT8 size)."""
+    DeepSeek-V3-shaped INT8 size, and as a 4% error of an INT4 folded tile).
+    INT4 codes here span eight groups of four k-steps (two regions)."""
     import torch
     shape = C.MIXTRAL_PREFILL.with_(T=600, d_model=1024, d_ff=512, n_experts=4,
                                     weight_quant=quant)
