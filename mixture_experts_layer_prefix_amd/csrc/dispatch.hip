@@ -298,10 +298,11 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
                                                         int BM, int BN, int Nd, int Ts, int merge,
                                                         int wide_rows, int4* __restrict__ list,
                                                         int32_t* __restrict__ count) {
-  __shared__ int wsum[4];
+  __shared__ int wsum[4], s_nonuni;
   __shared__ int s_base[MAXN + 1], s_mt[MAXN], s_o0[MAXN], s_o1[MAXN], s_wide[MAXN];
   const int e = threadIdx.x;
   const int ntn = (Nd + BN - 1) / BN;
+  if (e == 0) s_nonuni = 0;
   const int ms = m_tiles(Ts, BM, merge);
   const int shared_tiles = ms * ntn;
   int o0 = 0, o1 = 0, mt = 0, ntn_e = ntn;
@@ -327,6 +328,7 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
   }
   if (lane == 63) wsum[wave] = v;
   __syncthreads();
+  if (e < N && (s_mt[e] != s_mt[0] || s_wide[e] != s_wide[0])) s_nonuni = 1;
   int base = 0, total = 0;
   for (int w = 0; w < 4; ++w) {
     if (w < wave) base += wsum[w];
@@ -340,7 +342,42 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
   // Workgroup b writes tiles [b * TL_PER_WG, (b + 1) * TL_PER_WG); each
   // workgroup repeats the per-expert scan above (N <= 256 values).
   const int jend = min(total, (int)(blockIdx.x + 1) * TL_PER_WG);
+  // Every expert with the same tile count (the same m-tiles and column
+  // width): the list goes band by band across the experts (band 0 of every
+  // expert, then band 1, ...) instead of expert by expert.  The list is cut
+  // into one contiguous slice per XCD, so an XCD then runs bands of several
+  // experts, and the bands holding a folded remainder (about 1.2 times a
+  // full tile each) spread over the XCDs instead of filling the slices of
+  // the experts that have one.  A band still runs on one XCD at once.
+  const int mt0 = s_mt[0], wd0 = s_wide[0];
+  const int ntn0 = wd0 ? (Nd + 2 * BN - 1) / (2 * BN) : ntn;
+  const int gm0 = min(mt0, 8), band0 = max(1, 32 / max(gm0, 1));
+  const bool uniform = N > 1 && !s_nonuni && mt0 > 0 &&
+                       ((mt0 + gm0 - 1) / gm0) * ((ntn0 + band0 - 1) / band0) <= 512;
   for (int j = blockIdx.x * TL_PER_WG + threadIdx.x; j < jend; j += blockDim.x) {
+    if (uniform) {
+      // band k of expert x starts at N * (first local tile of band k) +
+      // x * (size of band k)
+      int rem = j, lb = 0, ex = 0, loc = 0;
+      bool found = false;
+      for (int g0 = 0; g0 < mt0 && !found; g0 += gm0) {
+        const int gsz = min(gm0, mt0 - g0);
+        for (int b0 = 0; b0 < ntn0 && !found; b0 += band0) {
+          const int size = min(band0, ntn0 - b0) * gsz;
+          if (rem < N * size) {
+            ex = rem / size;
+            loc = lb + rem % size;
+            found = true;
+          } else {
+            rem -= N * size;
+            lb += size;
+          }
+        }
+      }
+      list[shared_tiles + j] = band_tile(loc, mt0, ntn0, wd0 ? 2 * BN : BN,
+                                         ex | (wd0 ? kWideTile : 0), s_o0[ex], s_o1[ex], BM);
+      continue;
+    }
     int lo = 0, hi = N - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
